@@ -1,0 +1,171 @@
+"""CPU oracle for paged decode attention and the copy-on-write block copy.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+library (``paged_kv_cache_280_amd``) never imports it, and the two share no code.
+
+``oracle.cpp`` holds the plain loops (fp32 oracle, fp64 twin, per-row debug form
+with the softmax weights, byte copy of blocks).  This module compiles it with
+``g++ -O2 -fopenmp`` (no fast-math) and exposes numpy-level wrappers.
+
+Parity pins (what fixes the oracle other than itself) live in
+``tests/test_oracle_pins.py``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.cpp`` into ``liboracle.so`` beside it and return the path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(lib):
+    p = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.oracle_paged_decode_f32.argtypes = [p, p, p, p, p, i32, ctypes.c_float, p, i32, i32,
+                                            i32, i32, i32, i64, i32]
+    lib.oracle_paged_decode_f32.restype = ctypes.c_int
+    lib.oracle_paged_decode_f64.argtypes = [p, p, p, p, p, i32, ctypes.c_double, p, i32, i32,
+                                            i32, i32, i32, i64, i32]
+    lib.oracle_paged_decode_f64.restype = ctypes.c_int
+    lib.oracle_paged_decode_probs_f32.argtypes = [p, p, p, p, p, i32, ctypes.c_float, i32,
+                                                  i32, i32, i32, i32, i64, i32, i32, p, p]
+    lib.oracle_paged_decode_probs_f32.restype = ctypes.c_int
+    lib.oracle_copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32]
+    lib.oracle_copy_blocks.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _u16(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        a = a.view(np.uint16)
+    return a
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def paged_decode(q, k_pool, v_pool, block_tables, context_lens, block_size, scale,
+                 num_kv_heads, precision="f32", threads=0, lib=None):
+    """Reference decode.  Arrays are numpy; q/k_pool/v_pool hold bf16 bit patterns
+    (uint16 or int16).  Shapes: q [S][Hq][D]; k_pool [NB][Hkv][D/8][B][8];
+    v_pool [NB][Hkv][D][B]; block_tables [S][M] int32; context_lens [S] int32.
+    Returns float32 (or float64) [S][Hq][D]."""
+    q, kp, vp = _u16(q), _u16(k_pool), _u16(v_pool)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S, Hq, D = q.shape
+    M = tables.shape[1] if tables.ndim == 2 else 0
+    NB = kp.shape[0]
+    B = int(block_size)
+    if kp.size != NB * num_kv_heads * D * B or vp.size != kp.size:
+        raise OracleError("pool size does not match [NB][Hkv][..] with D=%d B=%d" % (D, B))
+    lib = lib or _load()
+    if precision == "f32":
+        out = np.zeros((S, Hq, D), np.float32)
+        rc = lib.oracle_paged_decode_f32(_ptr(q), _ptr(kp), _ptr(vp), _ptr(tables), _ptr(lens),
+                                         B, float(scale), _ptr(out), S, Hq, num_kv_heads, D, M,
+                                         NB, int(threads))
+    elif precision == "f64":
+        out = np.zeros((S, Hq, D), np.float64)
+        rc = lib.oracle_paged_decode_f64(_ptr(q), _ptr(kp), _ptr(vp), _ptr(tables), _ptr(lens),
+                                         B, float(scale), _ptr(out), S, Hq, num_kv_heads, D, M,
+                                         NB, int(threads))
+    else:
+        raise ValueError(precision)
+    if rc != 0:
+        raise OracleError("oracle_paged_decode returned %d" % rc)
+    return out
+
+
+def paged_decode_probs(q, k_pool, v_pool, block_tables, context_lens, block_size, scale,
+                       num_kv_heads, seq, head, lib=None):
+    """Debug form: (out_row float32 [D], softmax weights float32 [L]) for one (seq, head)."""
+    q, kp, vp = _u16(q), _u16(k_pool), _u16(v_pool)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S, Hq, D = q.shape
+    M = tables.shape[1]
+    L = int(lens[seq])
+    out = np.zeros(D, np.float32)
+    probs = np.zeros(max(L, 1), np.float32)
+    rc = (lib or _load()).oracle_paged_decode_probs_f32(_ptr(q), _ptr(kp), _ptr(vp), _ptr(tables),
+                                               _ptr(lens), int(block_size), float(scale), S, Hq,
+                                               num_kv_heads, D, M, kp.shape[0], int(seq),
+                                               int(head), _ptr(out), _ptr(probs))
+    if rc != 0:
+        raise OracleError("oracle_paged_decode_probs returned %d" % rc)
+    return out, probs[:L]
+
+
+def copy_blocks(k_pools, v_pools, pairs, lib=None):
+    """Byte copy of whole blocks, in place, on lists of numpy pools (one per layer).
+    ``pairs`` is int32 [P][2] of (src, dst)."""
+    pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    n_layers = len(k_pools)
+    if n_layers == 0 or pairs.shape[0] == 0:
+        return
+    nb = k_pools[0].shape[0]
+    block_bytes = k_pools[0].nbytes // nb
+    for a in list(k_pools) + list(v_pools):
+        if not a.flags["C_CONTIGUOUS"] or a.nbytes != nb * block_bytes:
+            raise OracleError("pools must be contiguous and of equal size")
+    kp = (ctypes.c_void_p * n_layers)(*[_ptr(a) for a in k_pools])
+    vp = (ctypes.c_void_p * n_layers)(*[_ptr(a) for a in v_pools])
+    rc = (lib or _load()).oracle_copy_blocks(ctypes.cast(kp, ctypes.c_void_p),
+                                    ctypes.cast(vp, ctypes.c_void_p), n_layers, nb, block_bytes,
+                                    _ptr(pairs), pairs.shape[0])
+    if rc != 0:
+        raise OracleError("oracle_copy_blocks returned %d" % rc)
+
+
+class Variant:
+    """The same wrappers bound to another build of ``oracle.cpp`` (used by the
+    tests that plant a mistake in a copy of the oracle and check that a pin fails)."""
+
+    OracleError = OracleError
+
+    def __init__(self, path: str):
+        self._lib = _bind(ctypes.CDLL(path))
+
+    def paged_decode(self, *args, **kwargs):
+        return paged_decode(*args, lib=self._lib, **kwargs)
+
+    def paged_decode_probs(self, *args, **kwargs):
+        return paged_decode_probs(*args, lib=self._lib, **kwargs)
+
+    def copy_blocks(self, *args, **kwargs):
+        return copy_blocks(*args, lib=self._lib, **kwargs)

@@ -1,0 +1,219 @@
+// Reference oracle for paged decode attention -- TEST INFRASTRUCTURE ONLY.
+//
+// Only the test-suite, the smoke check and the CPU-baseline leg of the benchmark
+// may load this code.  The product library never links or calls it, and it shares
+// no source, header, helper or table with the GPU path.
+//
+// What it computes (plain definition, written out):
+//   * "KV cache, PagedAttention" (aiwiki.vn), paragraph on query/key/value: the
+//     query of the current position is compared with the keys of every position it
+//     may attend to, and the resulting attention weights combine the values.
+//   * "PagedAttention (vLLM)" (troisinh.com), section "Cơ chế Block Table": the
+//     cache is split into fixed-size blocks; a per-sequence block table maps the
+//     logical block j (tokens j*B .. j*B+B-1) to a physical block anywhere in the
+//     pool; a sequence of L tokens occupies ceil(L/B) blocks.
+//   * same page, section "Tại sao nó hoạt động": the kernel follows the block
+//     table to fetch K/V from scattered places, then takes a softmax.
+//   * same page, section "Ý tưởng cốt lõi": physical placement does not matter,
+//     only the logical position does.
+//
+// Readings where the pages are silent (each is listed in the design notes):
+//   * scale is an argument; x_t = scale * (q . k_t), summed over d in ascending
+//     order, multiplied by scale after the sum;
+//   * query head h reads KV head h / (Hq/Hkv) (contiguous grouping);
+//   * L = 0 gives an all-zero output;
+//   * softmax is the max-subtracted form: w_t = exp(x_t - max), p_t = w_t / sum w;
+//   * bf16 inputs are widened exactly to the accumulator type;
+//   * pool layout (one pool per layer, per K and per V):
+//       K  [num_blocks][Hkv][D/8][B][8]   element (b,g,o,d) at
+//          (((b*Hkv + g)*(D/8) + d/8)*B + o)*8 + d%8
+//       V  [num_blocks][Hkv][D][B]        element (b,g,o,d) at
+//          ((b*Hkv + g)*D + d)*B + o
+//   * block_tables is int32 [S][M] row-major; only the first ceil(L/B) entries of
+//     row s are read.  Tail slots of the last block, padding entries of a table
+//     row and unreferenced blocks are never read.
+//
+// Precision: the accumulator type is a template parameter.  The fp32
+// instantiation is the oracle the GPU is compared against; the fp64 one measures
+// the fp32 oracle's own rounding error.  Sums run in ascending index order.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+// bf16 is the upper half of an IEEE binary32; widening is exact.
+inline float bf16_bits_to_float(uint16_t bits) {
+  uint32_t w = static_cast<uint32_t>(bits) << 16;
+  float f;
+  std::memcpy(&f, &w, sizeof f);
+  return f;
+}
+
+inline double exp_acc(double x) { return std::exp(x); }
+inline float exp_acc(float x) { return std::exp(x); }  // libm expf
+
+struct Shape {
+  int32_t S, Hq, Hkv, D, B, M;
+  int64_t NB;
+};
+
+inline int64_t k_index(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t d) {
+  return (((b * sh.Hkv + g) * (sh.D / 8) + d / 8) * sh.B + o) * 8 + d % 8;
+}
+
+inline int64_t v_index(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t d) {
+  return ((b * sh.Hkv + g) * sh.D + d) * sh.B + o;
+}
+
+// One (sequence, query head) pair.  Returns 0, or a negative code when the
+// inputs break the contract (a block id outside the pool).
+template <typename Acc>
+int decode_one(const Shape& sh, const uint16_t* q, const uint16_t* kp, const uint16_t* vp,
+               const int32_t* tables, const int32_t* lens, Acc scale, int s, int h,
+               Acc* out_row, Acc* probs_row /* may be null; length >= L */) {
+  const int L = lens[s];
+  for (int d = 0; d < sh.D; ++d) out_row[d] = Acc(0);
+  if (L == 0) return 0;
+  const int G = sh.Hq / sh.Hkv;
+  const int g = h / G;
+  const uint16_t* qrow = q + (static_cast<int64_t>(s) * sh.Hq + h) * sh.D;
+
+  std::vector<Acc> x(L);
+  std::vector<int64_t> blk(L);
+  for (int t = 0; t < L; ++t) {
+    const int j = t / sh.B;
+    const int64_t b = tables[static_cast<int64_t>(s) * sh.M + j];
+    if (b < 0 || b >= sh.NB) return -1;
+    blk[t] = b;
+    const int o = t % sh.B;
+    Acc dot = Acc(0);
+    for (int d = 0; d < sh.D; ++d)
+      dot += Acc(bf16_bits_to_float(qrow[d])) * Acc(bf16_bits_to_float(kp[k_index(sh, b, g, o, d)]));
+    x[t] = scale * dot;
+  }
+  Acc m = x[0];
+  for (int t = 1; t < L; ++t)
+    if (x[t] > m) m = x[t];
+  Acc z = Acc(0);
+  for (int t = 0; t < L; ++t) {
+    x[t] = exp_acc(x[t] - m);
+    z += x[t];
+  }
+  for (int t = 0; t < L; ++t) x[t] = x[t] / z;  // x now holds the weights p_t
+  if (probs_row)
+    for (int t = 0; t < L; ++t) probs_row[t] = x[t];
+  for (int d = 0; d < sh.D; ++d) {
+    Acc acc = Acc(0);
+    for (int t = 0; t < L; ++t)
+      acc += x[t] * Acc(bf16_bits_to_float(vp[v_index(sh, blk[t], g, t % sh.B, d)]));
+    out_row[d] = acc;
+  }
+  return 0;
+}
+
+template <typename Acc>
+int decode_all(const uint16_t* q, const uint16_t* kp, const uint16_t* vp, const int32_t* tables,
+               const int32_t* lens, int32_t B, double scale, Acc* out, int32_t S, int32_t Hq,
+               int32_t Hkv, int32_t D, int32_t M, int64_t NB, int32_t threads) {
+  if (!q || !kp || !vp || !tables || !lens || !out) return -2;
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || M < 0 || NB < 0) return -3;
+  if (Hq % Hkv != 0 || D % 8 != 0) return -3;
+  for (int s = 0; s < S; ++s)
+    if (lens[s] < 0 || static_cast<int64_t>(lens[s]) > static_cast<int64_t>(M) * B) return -4;
+  const Shape sh{S, Hq, Hkv, D, B, M, NB};
+  const int64_t pairs = static_cast<int64_t>(S) * Hq;
+  int status = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : status)
+#endif
+  for (int64_t i = 0; i < pairs; ++i) {
+    const int s = static_cast<int>(i / Hq), h = static_cast<int>(i % Hq);
+    const int rc = decode_one<Acc>(sh, q, kp, vp, tables, lens, static_cast<Acc>(scale), s, h,
+                                   out + i * D, nullptr);
+    if (rc < status) status = rc;
+  }
+  return status;
+}
+
+}  // namespace
+
+extern "C" {
+
+// fp32 oracle.  q, k_pool, v_pool hold raw bf16 bit patterns.  out is float [S][Hq][D].
+// Returns 0, -1 (a table entry outside [0, num_blocks)), -2 (null pointer),
+// -3 (bad shape), -4 (a context length outside [0, M*B]).  threads <= 0 keeps the
+// OpenMP default.
+int oracle_paged_decode_f32(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t block_size, float scale, float* out, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_blocks_per_seq, int64_t num_blocks, int32_t threads) {
+  return decode_all<float>(q, k_pool, v_pool, block_tables, context_lens, block_size, scale, out,
+                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                           num_blocks, threads);
+}
+
+// The same computation with a double accumulator and double output.
+int oracle_paged_decode_f64(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t block_size, double scale, double* out, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_blocks_per_seq, int64_t num_blocks, int32_t threads) {
+  return decode_all<double>(q, k_pool, v_pool, block_tables, context_lens, block_size, scale, out,
+                            num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                            num_blocks, threads);
+}
+
+// Debug form for one (sequence, query head): writes the D outputs and the L
+// softmax weights p_t (fp32).  probs must hold context_lens[seq] floats.
+int oracle_paged_decode_probs_f32(const uint16_t* q, const uint16_t* k_pool,
+                                  const uint16_t* v_pool, const int32_t* block_tables,
+                                  const int32_t* context_lens, int32_t block_size, float scale,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, int32_t seq, int32_t head, float* out_row,
+                                  float* probs) {
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out_row || !probs) return -2;
+  if (seq < 0 || seq >= num_seqs || head < 0 || head >= num_q_heads) return -3;
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim % 8 != 0) return -3;
+  const Shape sh{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                 num_blocks};
+  return decode_one<float>(sh, q, k_pool, v_pool, block_tables, context_lens, scale, seq, head,
+                           out_row, probs);
+}
+
+// Copy-on-write block copy ("Copy-on-Write cho Beam Search", troisinh.com): for
+// every (src, dst) pair and every layer, the bytes of block dst become the bytes
+// of block src, in K and in V; nothing else changes.  Pools are given as arrays of
+// host pointers, one per layer.  Returns 0, -2 (null), -3 (bad sizes), -1 (a block
+// id outside the pool).
+int oracle_copy_blocks(uint8_t* const* k_pools, uint8_t* const* v_pools, int32_t num_layers,
+                       int64_t num_blocks, int64_t block_bytes, const int32_t* pairs,
+                       int32_t num_pairs) {
+  if (num_pairs < 0 || num_layers < 0 || block_bytes < 0) return -3;
+  if (num_pairs == 0 || num_layers == 0) return 0;
+  if (!k_pools || !v_pools || !pairs) return -2;
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return -1;
+  }
+  for (int32_t l = 0; l < num_layers; ++l) {
+    if (!k_pools[l] || !v_pools[l]) return -2;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      const int64_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+      std::memmove(k_pools[l] + dst * block_bytes, k_pools[l] + src * block_bytes, block_bytes);
+      std::memmove(v_pools[l] + dst * block_bytes, v_pools[l] + src * block_bytes, block_bytes);
+    }
+  }
+  return 0;
+}
+
+}  // extern "C"
