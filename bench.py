@@ -1,0 +1,240 @@
+"""Benchmark of paged decode attention on one MI355X.
+
+Default workload (one step = one decode token for every sequence through every
+layer): 8 sequences x 16,000 tokens, 32 layers each with its own K and V pool,
+32 query heads / 8 KV heads, head_dim 128, block size 16, random physical
+placement.  Inputs are synthetic (seeded bf16 N(0,1)) and resident in HBM before
+timing starts.  The 32 pools hold 16.8 GB, far beyond the 256 MB last-level
+cache, so every layer's blocks come from HBM.
+
+Prints one JSON line: decode tokens/s (value), KV GB/s, the roofline of the main
+decode kernel (HIP events around every launch in the timed region) and the CPU
+oracle timed on a bounded sample of the same workload.
+
+Other workloads (--workload chat|mix) are for measurements beside the headline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode: achieved KV GB/s (% of HBM peak) + decode tokens/s, 1 GPU"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_280_amd", "csrc", "pkv_decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long", choices=["long", "chat", "mix"])
+    ap.add_argument("--block-size", type=int, default=16)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def source_sha():
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_key):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload_key)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def build_workload(args, dev):
+    import torch
+
+    import workloads as wl
+
+    if args.workload == "long":
+        case = wl.case_long(args.seed, block_size=args.block_size)
+        layers = case.num_layers
+        desc = ("long-context decode: 8 seqs x 16000 tokens, 32 layers, 32 q / 8 KV heads, "
+                "head_dim 128, block %d" % case.block_size)
+    elif args.workload == "chat":
+        case = wl.case_chat(args.seed, block_size=args.block_size)
+        layers = 1
+        desc = "chat-batch decode: 64 seqs, 32 q / 8 KV heads, head_dim 128, block %d" % case.block_size
+    else:
+        case = wl.case_mix(args.seed, args.block_size)
+        layers = 1
+        desc = ("continuous-batching mix: 256 seqs (13 at 32768), 64 q / 8 KV heads, head_dim 128, "
+                "block %d, 100 GB pool" % case.block_size)
+    pools = []
+    for layer in range(layers):
+        q, k, v, tabs, lens = wl.device_tensors(case, dev, layer=layer)
+        pools.append((q, k, v))
+    torch.cuda.synchronize()
+    return case, layers, desc, pools, tabs, lens
+
+
+def flush_buffer(dev, nbytes=1 << 30):
+    import torch
+
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+
+
+def cpu_baseline(case, pools, tabs, lens, layers, args, gpu_tokens_per_step):
+    """The oracle on the host cores over a bounded sample: whole sequences of
+    layer 0, as many as fit the time target, scaled to a full step."""
+    import torch
+
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    q, kd, vd = pools[0]
+    order = np.arange(case.num_seqs)
+    done_tokens = 0
+    elapsed = 0.0
+    seqs_done = 0
+    for s in order:
+        L = int(case.context_lens[s])
+        nb = -(-L // case.block_size)
+        ids = case.block_tables[s, :nb]
+        idx = torch.from_numpy(ids.astype(np.int64)).to(kd.device)
+        kh = kd[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = vd[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+        qh = q[s:s + 1].view(torch.int16).cpu().numpy().view(np.uint16)
+        tab = np.arange(nb, dtype=np.int32)[None, :]
+        t0 = time.perf_counter()
+        oracle.paged_decode(qh, kh, vh, tab, np.array([L], np.int32), case.block_size, case.scale,
+                            case.num_kv_heads, threads=threads)
+        elapsed += time.perf_counter() - t0
+        done_tokens += L
+        seqs_done += 1
+        if elapsed >= args.cpu_seconds:
+            break
+    total_tokens = int(case.context_lens.sum())
+    step_seconds = elapsed * (total_tokens / max(done_tokens, 1)) * layers
+    return {
+        "value": case.num_seqs / step_seconds,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d of %d sequences of layer 0 (%d context tokens) in %.1f s on %d threads; "
+                  "scaled by context tokens to all sequences and %d layers"
+                  % (seqs_done, case.num_seqs, done_tokens, elapsed, threads, layers),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library's decode runs on a single device "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+    from paged_kv_cache_280_amd.accounting import decode_algorithmic_bytes
+
+    pkv.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case, layers, desc, pools, tabs, lens = build_workload(args, dev)
+    S, Hq, Hkv, D, B = (case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                        case.block_size)
+    max_ctx = case.max_context_len
+    ws_bytes = pkv.paged_attn_decode_workspace_bytes(S, Hq, Hkv, D, B, max_ctx)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(p[0]) for p in pools]
+    per_call_bytes = decode_algorithmic_bytes(case.context_lens, Hq, Hkv, D, B)
+    flush = flush_buffer(dev) if args.workload != "long" else None
+
+    stream = torch.cuda.current_stream(dev)
+    n_ev = args.steps * layers
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_ev)]
+
+    def step(timed_events=None):
+        for layer in range(layers):
+            q, k, v = pools[layer]
+            if flush is not None:
+                flush.zero_()
+            e = timed_events[layer] if timed_events is not None else None
+            if e is not None:
+                e[0].record(stream)
+            pkv.paged_attn_decode_partials(q, k, v, tabs, lens, B, case.scale, outs[layer],
+                                           workspace=ws, max_context_len=max_ctx)
+            if e is not None:
+                e[1].record(stream)
+            pkv.paged_attn_decode_reduce(q, k, v, tabs, lens, B, case.scale, outs[layer],
+                                         workspace=ws, max_context_len=max_ctx)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i * layers:(i + 1) * layers])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    step_bytes = per_call_bytes * layers
+    tokens_per_s = S / (ms_per_step / 1e3)
+    kv_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = per_call_bytes / kern_avg_s / 1e9
+    traffic = measured_traffic(args.workload)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "num_seqs": S, "context_len": int(case.context_lens.max()),
+                   "layers": layers, "block_size": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": D},
+        "kv_gbs": round(kv_gbs, 1),
+        "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "decode_partials_kernel",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(per_call_bytes),
+                     "avg_launch_us": round(kern_avg_s * 1e6, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, pools, tabs, lens, layers, args, tokens_per_s)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache decode library (AMD MI355X, gfx950).
+ *
+ * The operation follows "PagedAttention (vLLM) - Virtual memory cho AI"
+ * (troisinh.com) and "KV cache, PagedAttention" (aiwiki.vn):
+ *   - the KV cache lives in fixed-size blocks of B tokens scattered over device
+ *     memory; a per-sequence block table maps logical block j (tokens
+ *     j*B .. j*B+B-1) to a physical block id (troisinh.com, section
+ *     "Cơ chế Block Table"; aiwiki.vn, paragraph on paging);
+ *   - decode attention: for every sequence s and query head h, the query is
+ *     compared with the keys of the context_lens[s] cached positions, and the
+ *     softmax weights combine the values (aiwiki.vn, paragraph on query, key
+ *     and value); the kernel follows the block table to gather K/V from
+ *     scattered places (troisinh.com, section "Tại sao nó hoạt động");
+ *   - copy-on-write: sequences sharing a prefix share its physical blocks, and
+ *     a shared block is copied before a sharer writes into it (troisinh.com,
+ *     section "Copy-on-Write cho Beam Search").
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers owned by the caller, unless a
+ *     comment says "host".  The library keeps no pointer after it returns and
+ *     allocates no device memory.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *     enqueued on it and the call returns at once; buffers must stay alive until
+ *     that work has finished.
+ *   - Every check below is made on the host before anything is enqueued; on an
+ *     error nothing is enqueued and a negative PKV_ERR_* code is returned.
+ *   - bf16 means IEEE binary32 truncated to its upper 16 bits (stored as
+ *     uint16); outputs are rounded to nearest, ties to even.
+ *
+ * KV pool layout (one K pool and one V pool per layer; B = block_size,
+ * D = head_dim, Hkv = num_kv_heads, NB = num_blocks), bf16:
+ *   K  [NB][Hkv][D/8][B][8] : element (block b, head g, slot o, dim d) at
+ *                             (((b*Hkv + g)*(D/8) + d/8)*B + o)*8 + d%8
+ *   V  [NB][Hkv][D][B]      : element (b, g, o, d) at ((b*Hkv + g)*D + d)*B + o
+ * Each (block, head) tile is one contiguous run of B*D*2 bytes, and a whole block
+ * (all heads) is one contiguous run of Hkv*B*D*2 bytes.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+/* Status codes. */
+#define PKV_OK 0
+#define PKV_ERR_NULL -1        /* a required pointer is NULL */
+#define PKV_ERR_SHAPE -2       /* inconsistent sizes (e.g. num_q_heads % num_kv_heads != 0) */
+#define PKV_ERR_UNSUPPORTED -3 /* head_dim, block_size or group size outside the built set */
+#define PKV_ERR_WORKSPACE -4   /* workspace smaller than paged_attn_decode_workspace_bytes() */
+#define PKV_ERR_ALIGNMENT -5   /* q, k_cache, v_cache, out or workspace not 16-byte aligned */
+#define PKV_ERR_DEVICE -6      /* the HIP runtime could not report the current device */
+#define PKV_ERR_LAUNCH -7      /* a kernel launch failed (hipGetLastError) */
+
+/* Version of this ABI (PKV_ABI_VERSION of the build). */
+int32_t pkv_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* pkv_status_string(int32_t status);
+
+/*
+ * Bytes of device scratch paged_attn_decode needs for these sizes on the
+ * current device.  The scratch holds the partial softmax states of (sequence,
+ * KV head) pairs whose context is split across workers (split-K).  Returns 0
+ * for sizes paged_attn_decode would reject.
+ */
+size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int32_t max_context_len);
+
+/*
+ * Paged decode attention (the operation described at the top of this file):
+ *
+ *   out[s][h][:] = sum_t p_t * V[b_t][g][o_t][:],
+ *   p_t = softmax_t(scale * q[s][h][:] . K[b_t][g][o_t][:]),  t = 0 .. L-1,
+ *
+ * with L = context_lens[s], g = h / (num_q_heads / num_kv_heads),
+ * b_t = block_tables[s][t / block_size], o_t = t % block_size.
+ *
+ *   q             bf16 [num_seqs][num_q_heads][head_dim]
+ *   k_cache       bf16 K pool, layout above, num_blocks blocks
+ *   v_cache       bf16 V pool, layout above
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq], row-major; only the first
+ *                 ceil(L/block_size) entries of row s are read, and each must lie
+ *                 in [0, num_blocks).  Entries outside that range are clamped into
+ *                 it (no memory outside the pool is read; that sequence's output
+ *                 is then meaningless).
+ *   context_lens  int32 [num_seqs]; 0 <= L <= max_blocks_per_seq*block_size.  L = 0
+ *                 gives an all-zero output row.  Values outside the range are
+ *                 clamped into it.
+ *   block_size    8, 16 or 32
+ *   scale         multiplier of q.k (for example 1/sqrt(head_dim))
+ *   out           bf16 [num_seqs][num_q_heads][head_dim]; must not overlap an input
+ *   num_q_heads   a multiple of num_kv_heads, with num_q_heads/num_kv_heads <= 16
+ *   head_dim      64 or 128
+ *   max_context_len  host-side upper bound of context_lens; it sizes the launch
+ *                 (no device-to-host read happens).  A bound that is too small
+ *                 only costs speed; it must be <= max_blocks_per_seq*block_size.
+ *   workspace     device scratch of at least workspace_bytes >=
+ *                 paged_attn_decode_workspace_bytes(...) bytes; contents need no
+ *                 initialisation and are overwritten.  Calls that overlap in time
+ *                 must not share a workspace.
+ *
+ * Slots past L in a sequence's last block, table entries past ceil(L/B) and
+ * blocks no table references are never read into the arithmetic.  Results are
+ * deterministic: the same inputs give the same bits, and renumbering physical
+ * blocks (with the tables rewritten to match) does not change a bit.
+ * Enqueues two kernels: paged_attn_decode_partials then paged_attn_decode_reduce.
+ */
+int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t block_size, float scale, void* out, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t max_blocks_per_seq, int64_t num_blocks,
+                          int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * The two halves of paged_attn_decode, for callers that time or schedule them
+ * separately; same arguments and checks.  _partials enqueues the main kernel: it
+ * writes out[] for every (sequence, KV head) pair handled whole by one worker and
+ * a partial softmax state into the workspace for the others.  _reduce enqueues
+ * the merge of those partial states (fixed order, deterministic) and writes the
+ * zero rows of empty sequences.  _reduce must follow _partials on the same
+ * stream with the same arguments and workspace.
+ */
+int32_t paged_attn_decode_partials(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t block_size, float scale, void* out, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_blocks_per_seq, int64_t num_blocks,
+                                   int32_t max_context_len, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+int32_t paged_attn_decode_reduce(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t block_size, float scale, void* out, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
+ * Copy-on-write block copy: for every pair i and every layer l,
+ *   K_l[dst_i] := K_l[src_i]  and  V_l[dst_i] := V_l[src_i]   (whole blocks, bytes).
+ *
+ *   k_caches, v_caches  HOST arrays of num_layers device pointers, one pool per
+ *                 layer (read during the call only; at most 128 layers)
+ *   num_blocks    blocks per pool; pairs naming an id outside [0, num_blocks) are
+ *                 skipped on the device (nothing outside the pools is touched)
+ *   block_bytes   bytes of one block in one pool (num_kv_heads*block_size*head_dim*2
+ *                 for bf16); a positive multiple of 16, pools 16-byte aligned
+ *   src_dst_pairs int32 [num_pairs][2] of (src, dst), DEVICE memory
+ *   num_pairs     0 is a no-op
+ * Destinations must be distinct and no destination may also be a source; then
+ * the result does not depend on the order of the pairs and is bit-exact.
+ */
+int32_t copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                    int64_t num_blocks, int64_t block_bytes, const int32_t* src_dst_pairs,
+                    int32_t num_pairs, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,20 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+The computation lives in the HIP library ``libpkv.so`` (C ABI in
+``include/pkv.h``); this package is its thin Python binding plus host-side
+helpers (byte accounting, the block manager).
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    PkvError,
+    abi_version,
+    copy_blocks,
+    load_library,
+    paged_attn_decode,
+    paged_attn_decode_partials,
+    paged_attn_decode_reduce,
+    paged_attn_decode_workspace_bytes,
+    status_string,
+)

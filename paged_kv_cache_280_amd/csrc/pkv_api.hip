@@ -1,0 +1,227 @@
+// C ABI of the library (declared in include/pkv.h): host-side argument checks,
+// launch sizing and dispatch to the kernels.  No device memory is allocated here.
+
+#include <math.h>
+#include <stdlib.h>
+
+#include <atomic>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultWavesPerCu = 8;
+
+// Compute units of each device, read once (0 = not read yet).
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int current_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+    return -1;
+  if (dev < kMaxDevices) g_cu_count[dev].store(cu, std::memory_order_relaxed);
+  return cu;
+}
+
+// Resident decode workers (waves) per compute unit; PKV_WAVES_PER_CU overrides
+// the default for launch-shape sweeps.
+int waves_per_cu() {
+  static const int v = [] {
+    const char* e = getenv("PKV_WAVES_PER_CU");
+    const int x = e ? atoi(e) : 0;
+    return (x >= 1 && x <= 32) ? x : kDefaultWavesPerCu;
+  }();
+  return v;
+}
+
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
+bool supported_block_size(int32_t b) { return b == 8 || b == 16 || b == 32; }
+
+// Number of decode workers: one per resident wave slot, never more than the
+// tiles a batch bounded by max_context_len can hold.
+int64_t worker_count(int cu, int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  const int64_t tiles_bound = static_cast<int64_t>(num_seqs) * num_kv_heads *
+                              ((static_cast<int64_t>(max_context_len) + kTile - 1) / kTile);
+  int64_t n = static_cast<int64_t>(cu) * waves_per_cu();
+  if (tiles_bound < n) n = tiles_bound;
+  return n < 1 ? 1 : n;
+}
+
+size_t workspace_for(int64_t workers, int32_t group, int32_t head_dim) {
+  return static_cast<size_t>(workers) * 2 * record_floats(group, head_dim) * sizeof(float);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t check_shapes(int32_t block_size, float scale, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                     int64_t num_blocks, int32_t max_context_len) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || max_context_len < 0 || !isfinite(scale))
+    return PKV_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return PKV_ERR_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > 0x7fffffffLL) return PKV_ERR_SHAPE;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (num_q_heads / num_kv_heads > kMaxGroup) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+enum Phase { kPartials = 1, kReduce = 2, kBoth = 3 };
+
+int32_t decode_impl(int phase, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t block_size,
+                    float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                    int64_t num_blocks, int32_t max_context_len, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const int32_t st = check_shapes(block_size, scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  max_blocks_per_seq, num_blocks, max_context_len);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !workspace)
+    return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(workspace))
+    return PKV_ERR_ALIGNMENT;
+  const int cu = current_cu_count();
+  if (cu <= 0) return PKV_ERR_DEVICE;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int64_t workers = worker_count(cu, num_seqs, num_kv_heads, max_context_len);
+  if (workspace_bytes < workspace_for(workers, group, head_dim)) return PKV_ERR_WORKSPACE;
+
+  DecodeBuffers b;
+  b.q = static_cast<const uint16_t*>(q);
+  b.k = static_cast<const uint16_t*>(k_cache);
+  b.v = static_cast<const uint16_t*>(v_cache);
+  b.tables = block_tables;
+  b.lens = context_lens;
+  b.out = static_cast<uint16_t*>(out);
+  b.ws = static_cast<float*>(workspace);
+  DecodeDims d;
+  d.S = num_seqs;
+  d.Hq = num_q_heads;
+  d.Hkv = num_kv_heads;
+  d.G = group;
+  d.M = max_blocks_per_seq;
+  d.n_workers = static_cast<int32_t>(workers);
+  d.NB = num_blocks;
+  d.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if ((phase & kPartials) && max_context_len > 0) {
+    if (launch_decode_partials(b, d, head_dim, block_size, s) != hipSuccess) return PKV_ERR_LAUNCH;
+  }
+  if (phase & kReduce) {
+    const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
+    int64_t groups = (pairs + kWavesPerGroup - 1) / kWavesPerGroup;
+    if (groups > cu) groups = cu;
+    if (launch_decode_reduce(b, d, head_dim, block_size, static_cast<int>(groups), s) != hipSuccess)
+      return PKV_ERR_LAUNCH;
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int32_t status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "inconsistent sizes";
+    case PKV_ERR_UNSUPPORTED: return "head_dim, block_size or group size not supported";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_ALIGNMENT: return "a buffer is not 16-byte aligned";
+    case PKV_ERR_DEVICE: return "could not query the current HIP device";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int32_t max_context_len) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+      num_q_heads % num_kv_heads != 0 || !pkv::supported_head_dim(head_dim) ||
+      !pkv::supported_block_size(block_size) || num_q_heads / num_kv_heads > pkv::kMaxGroup)
+    return 0;
+  const int cu = pkv::current_cu_count();
+  if (cu <= 0) return 0;
+  const int64_t workers = pkv::worker_count(cu, num_seqs, num_kv_heads, max_context_len);
+  return pkv::workspace_for(workers, num_q_heads / num_kv_heads, head_dim);
+}
+
+int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t block_size, float scale, void* out, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t max_blocks_per_seq, int64_t num_blocks,
+                          int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return pkv::decode_impl(pkv::kBoth, q, k_cache, v_cache, block_tables, context_lens, block_size,
+                          scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          max_blocks_per_seq, num_blocks, max_context_len, workspace,
+                          workspace_bytes, stream);
+}
+
+int32_t paged_attn_decode_partials(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t block_size, float scale, void* out, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_blocks_per_seq, int64_t num_blocks,
+                                   int32_t max_context_len, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return pkv::decode_impl(pkv::kPartials, q, k_cache, v_cache, block_tables, context_lens,
+                          block_size, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          max_blocks_per_seq, num_blocks, max_context_len, workspace,
+                          workspace_bytes, stream);
+}
+
+int32_t paged_attn_decode_reduce(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t block_size, float scale, void* out, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return pkv::decode_impl(pkv::kReduce, q, k_cache, v_cache, block_tables, context_lens,
+                          block_size, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          max_blocks_per_seq, num_blocks, max_context_len, workspace,
+                          workspace_bytes, stream);
+}
+
+int32_t copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                    int64_t num_blocks, int64_t block_bytes, const int32_t* src_dst_pairs,
+                    int32_t num_pairs, void* stream) {
+  if (num_pairs < 0 || num_layers < 0 || num_blocks < 0 || block_bytes < 0) return PKV_ERR_SHAPE;
+  if (num_pairs == 0 || num_layers == 0) return PKV_OK;
+  if (!k_caches || !v_caches || !src_dst_pairs) return PKV_ERR_NULL;
+  if (num_layers > pkv::kMaxLayers) return PKV_ERR_UNSUPPORTED;
+  if (block_bytes == 0 || block_bytes % 16 != 0 || num_blocks == 0) return PKV_ERR_SHAPE;
+  for (int32_t l = 0; l < num_layers; ++l) {
+    if (!k_caches[l] || !v_caches[l]) return PKV_ERR_NULL;
+    if (!pkv::aligned16(k_caches[l]) || !pkv::aligned16(v_caches[l])) return PKV_ERR_ALIGNMENT;
+  }
+  if (pkv::launch_copy_blocks(k_caches, v_caches, num_layers, num_blocks, block_bytes,
+                              src_dst_pairs, num_pairs, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return PKV_ERR_LAUNCH;
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,500 @@
+// Paged decode attention for gfx950 (CDNA4): block-table walk, MFMA scores,
+// online softmax, MFMA value accumulation, split-K across persistent workers and a
+// deterministic merge of split (sequence, KV head) pairs.
+//
+// What is computed: "KV cache, PagedAttention" (aiwiki.vn), paragraph on query, key
+// and value -- the query of the current position scores every cached key, and the
+// softmax of the scores weights the cached values.  Where the K/V rows are: a
+// per-sequence block table maps logical block j to a physical block of B tokens
+// anywhere in the pool ("PagedAttention (vLLM)", troisinh.com, section "Cơ chế
+// Block Table"); the kernel gathers the rows it needs by walking that table (same
+// page, section "Tại sao nó hoạt động").
+//
+// Work decomposition.  The unit of work is a 16-token tile of one (sequence, KV
+// head) pair.  Units are numbered sequence-major, then KV head, then tile, and the
+// N workers (one wave each) take equal contiguous ranges of that numbering, so
+// every worker streams the same number of K/V bytes whatever the mix of context
+// lengths.  A worker's range is cut into segments at (sequence, head) boundaries.
+// A segment that covers a whole pair writes the output directly; a segment that
+// covers part of a pair writes its softmax state (reference max m, sum l,
+// unnormalised accumulator O; fp32) to the workspace, and the reduce kernel merges
+// the states of each split pair in worker order.
+//
+// Per tile (one wave, 16 tokens x D dims, up to 16 query heads of one KV head):
+//   scores  S[token][head] = K_tile (16 x D) * q^T (D x 16)  -- D/32 MFMA 16x16x32 bf16
+//   weights p = exp2(S*scale*log2e - m), m a per-head reference max shared by the
+//           four lanes holding that head; m moves up (and O, l are rescaled) only
+//           when a score exceeds it by more than 2^8, so p <= 256 and the
+//           cross-lane max runs only on those rare tiles; p rounded to bf16
+//   values  O^T[dim][head] += V_tile^T (D x 16) * P^T (16 x 16) -- D/16 MFMA 16x16x16
+//   sum     l[head] += sum_t P[head][t] -- one more MFMA against a block of ones,
+//           so l adds exactly the bf16 weights that O used
+// The pool layouts put each lane's MFMA operand in 16 (K) or 8 (V) contiguous
+// bytes, so tiles go from HBM straight into operand registers with coalesced
+// loads, and the score MFMA's output registers are already the weight operand of
+// the value MFMA (no shuffles, no LDS).  Loads run kPipe-1 tiles ahead of the
+// arithmetic inside each segment.
+
+#include <math.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kPipe = 3;                  // tile buffers in registers (kPipe-1 loads in flight)
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: weights stay below 2^8
+
+__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t cap) {
+  return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+__device__ __forceinline__ int32_t tiles_of(int32_t L) { return (L + kTile - 1) / kTile; }
+
+__device__ __forceinline__ int32_t clamp_block(int32_t b, int64_t nb) {
+  return b < 0 ? 0 : (b >= nb ? static_cast<int32_t>(nb - 1) : b);
+}
+
+__device__ __forceinline__ int32_t wave_sum(int32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Work units (tiles) of sequences [0, s_end): Hkv * sum ceil(L_s / 16).
+__device__ int64_t units_before(const int32_t* __restrict__ lens, const DecodeDims& d,
+                                int32_t cap, int32_t s_end, int lane) {
+  int64_t tot = 0;
+  for (int32_t base = 0; base < s_end; base += kWave) {
+    const int32_t s = base + lane;
+    const int32_t T = s < s_end ? tiles_of(clamp_len(lens[s], cap)) : 0;
+    tot += uniform(wave_sum(T));
+  }
+  return tot * d.Hkv;
+}
+
+// The sequence whose unit range contains unit u, and the first unit of that range.
+__device__ void locate(const int32_t* __restrict__ lens, const DecodeDims& d, int32_t cap,
+                       int64_t u, int lane, int32_t& s_out, int64_t& start_out) {
+  int64_t acc = 0;
+  for (int32_t base = 0; base < d.S; base += kWave) {
+    const int32_t s = base + lane;
+    const int32_t T = s < d.S ? tiles_of(clamp_len(lens[s], cap)) : 0;
+    const int32_t incl = wave_inclusive_scan(T, lane);
+    const int64_t chunk_units =
+        static_cast<int64_t>(__builtin_amdgcn_readlane(incl, kWave - 1)) * d.Hkv;
+    if (u < acc + chunk_units) {
+      const uint64_t hit = __ballot(acc + static_cast<int64_t>(incl) * d.Hkv > u);
+      const int32_t first = uniform(__builtin_ctzll(hit));
+      s_out = base + first;
+      start_out = acc + static_cast<int64_t>(__builtin_amdgcn_readlane(incl - T, first)) * d.Hkv;
+      return;
+    }
+    acc += chunk_units;
+  }
+  s_out = d.S;
+  start_out = acc;
+}
+
+// Range of worker w: units [w*U/N, (w+1)*U/N).  worker_of(u) is the largest w
+// whose range starts at or before u.
+__device__ __forceinline__ int64_t range_begin(int64_t w, int64_t U, int64_t N) {
+  return w * U / N;
+}
+
+__device__ __forceinline__ int64_t worker_of(int64_t u, int64_t U, int64_t N) {
+  return ((u + 1) * N - 1) / U;
+}
+
+template <int D, int B>
+struct TileRegs {
+  u32x4_t k[D / 32];  // score MFMA A operand: token lane%16, dims c*32 + (lane/16)*8 .. +7
+  u32x2_t v[D / 16];  // value MFMA A operand: dim mt*16 + lane%16, tokens (lane/16)*4 .. +3
+};
+
+// Where one (sequence, KV head) pair's tiles come from.
+struct PairCursor {
+  const uint16_t* k;        // K pool
+  const uint16_t* v;        // V pool
+  const int32_t* trow;      // block-table row of the sequence
+  int64_t head_off;         // g * (elements of one (block, head) tile)
+  int64_t block_stride;     // elements of one block (all heads)
+  int64_t nb;
+  int32_t nblk;             // ceil(L / B)
+};
+
+// Issue the loads of tile t.
+template <int D, int B>
+__device__ __forceinline__ void load_tile(TileRegs<D, B>& r, const PairCursor& pc, int32_t t,
+                                          int lane) {
+  const int32_t tok0 = t * kTile;
+  if constexpr (B >= kTile) {
+    const int32_t b = clamp_block(pc.trow[tok0 / B], pc.nb);
+    const int32_t ob = tok0 % B;
+    const int64_t base = static_cast<int64_t>(b) * pc.block_stride + pc.head_off;
+    const uint16_t* kt = pc.k + base;
+    const uint16_t* vt = pc.v + base;
+    const uint32_t koff = static_cast<uint32_t>(((lane >> 4) * B + ob + (lane & 15)) * 8);
+    const uint32_t voff = static_cast<uint32_t>((lane & 15) * B + ob + (lane >> 4) * 4);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      r.k[c] = *reinterpret_cast<const u32x4_t*>(kt + koff + c * 4 * B * 8);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+      r.v[mt] = *reinterpret_cast<const u32x2_t*>(vt + voff + mt * 16 * B);
+  } else {
+    // B == 8: the tile spans logical blocks 2t and 2t+1 (the second clamped to the
+    // sequence's last block; its lanes are masked when it lies past the context).
+    static_assert(B == 8, "block sizes below 16 other than 8 are not built");
+    const int32_t j0 = tok0 / B;
+    const int32_t j1 = j0 + 1 < pc.nblk ? j0 + 1 : pc.nblk - 1;
+    const int64_t base0 = static_cast<int64_t>(clamp_block(pc.trow[j0], pc.nb)) * pc.block_stride;
+    const int64_t base1 = static_cast<int64_t>(clamp_block(pc.trow[j1], pc.nb)) * pc.block_stride;
+    const int64_t kb = ((lane & 15) < 8 ? base0 : base1) + pc.head_off;
+    const int64_t vb = ((lane >> 4) < 2 ? base0 : base1) + pc.head_off;
+    const uint16_t* kt = pc.k + kb + ((lane >> 4) * B + (lane & 7)) * 8;
+    const uint16_t* vt = pc.v + vb + (lane & 15) * B + ((lane >> 4) & 1) * 4;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) r.k[c] = *reinterpret_cast<const u32x4_t*>(kt + c * 4 * B * 8);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+      r.v[mt] = *reinterpret_cast<const u32x2_t*>(vt + mt * 16 * B);
+  }
+}
+
+// Softmax state of one wave over one segment.
+template <int D>
+struct SegState {
+  f32x4_t o[D / 16];  // O^T[dim mt*16 + (lane/16)*4 + i][head lane%16]
+  f32x4_t l;          // every entry: sum of the bf16 weights of head lane%16
+  float m;            // reference max of head lane%16 (log2 domain)
+};
+
+// One tile: scores, softmax weights, value and sum accumulation.  `valid` is the
+// number of tokens of the tile inside the context (16 except in the last tile).
+template <int D, int B>
+__device__ __forceinline__ void compute_tile(TileRegs<D, B>& r, const bf16x8_t (&qop)[D / 32],
+                                             SegState<D>& st, float c, int32_t valid, int lane) {
+  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int cc = 0; cc < D / 32; ++cc)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[cc]), qop[cc],
+                                                 sc, 0, 0, 0);
+  const int32_t tq = (lane >> 4) * 4;  // first of the four tokens this lane scores
+  float x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = fmaf(sc[i], c, -st.m);
+  if (valid < kTile) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (tq + i >= valid) x[i] = -INFINITY;
+    const int32_t n = valid - tq;
+    const uint64_t keep = n >= 4 ? ~0ull : (n <= 0 ? 0ull : ((1ull << (16 * n)) - 1));
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      r.v[mt].x &= static_cast<uint32_t>(keep);
+      r.v[mt].y &= static_cast<uint32_t>(keep >> 32);
+    }
+  }
+  const bool over = x[0] > kRescaleThreshold || x[1] > kRescaleThreshold ||
+                    x[2] > kRescaleThreshold || x[3] > kRescaleThreshold;
+  if (__ballot(over)) {
+    // Move the reference max of every head up to its max over everything seen so
+    // far (always taken on a segment's first tile, where m = -inf and x = +inf).
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = (valid < kTile && tq + i >= valid) ? -INFINITY : sc[i] * c;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) st.o[mt] *= alpha;
+    st.l *= alpha;
+    st.m = m_new;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = sv[i] - m_new;
+  }
+  bf16x4_t pb;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pb[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[i]));
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt)
+    st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, r.v[mt]), pb,
+                                                         st.o[mt], 0, 0, 0);
+  const bf16x4_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f),
+                         static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  st.l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, st.l, 0, 0, 0);
+}
+
+struct Ctx {
+  const uint16_t* __restrict__ q;
+  const uint16_t* __restrict__ k;
+  const uint16_t* __restrict__ v;
+  const int32_t* __restrict__ tables;
+  const int32_t* __restrict__ lens;
+  uint16_t* __restrict__ out;
+  float* __restrict__ ws;
+};
+
+// Tiles [t0, t1) of (sequence s, KV head g); writes the output rows when the
+// segment is the whole pair, else the partial record `rec`.
+template <int D, int B>
+__device__ void run_segment(const Ctx& cx, const DecodeDims& d, int32_t s, int32_t g, int32_t t0,
+                            int32_t t1, int32_t L, int32_t T, int64_t rec, int lane) {
+  constexpr int64_t kTileElems = static_cast<int64_t>(D) * B;
+  PairCursor pc;
+  pc.k = cx.k;
+  pc.v = cx.v;
+  pc.trow = cx.tables + static_cast<int64_t>(s) * d.M;
+  pc.block_stride = kTileElems * d.Hkv;
+  pc.head_off = kTileElems * g;
+  pc.nb = d.NB;
+  pc.nblk = (L + B - 1) / B;
+  const int32_t h = lane & 15;
+
+  bf16x8_t qop[D / 32];
+  if (h < d.G) {
+    const uint16_t* qr = cx.q + (static_cast<int64_t>(s) * d.Hq + g * d.G + h) * D + (lane >> 4) * 8;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+      qop[c] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qr + c * 32));
+  } else {
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) qop[c] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+  }
+
+  SegState<D> st;
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) st.o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+
+  const int32_t n = t1 - t0;
+  TileRegs<D, B> r[kPipe];
+  if (n >= kPipe) {
+#pragma unroll
+    for (int i = 0; i < kPipe - 1; ++i) load_tile<D, B>(r[i], pc, t0 + i, lane);
+    int32_t i = 0;
+    // Steady state: every step computes tile i and loads tile i + kPipe - 1; the
+    // loop runs whole groups of kPipe steps whose loads all exist.
+    while (i + 2 * kPipe - 1 <= n) {
+#pragma unroll
+      for (int k = 0; k < kPipe; ++k) {
+        load_tile<D, B>(r[(k + kPipe - 1) % kPipe], pc, t0 + i + k + kPipe - 1, lane);
+        compute_tile<D, B>(r[k], qop, st, d.c, min(kTile, L - (t0 + i + k) * kTile), lane);
+      }
+      i += kPipe;
+    }
+    // Remainder: between kPipe-1 and 2*kPipe-2 tiles, the first of them still loading.
+    const int32_t rem = n - i;
+#pragma unroll
+    for (int k = 0; k < 2 * kPipe - 2; ++k) {
+      if (k < rem) {
+        if (k + kPipe - 1 < rem)
+          load_tile<D, B>(r[(k + kPipe - 1) % kPipe], pc, t0 + i + k + kPipe - 1, lane);
+        compute_tile<D, B>(r[k % kPipe], qop, st, d.c, min(kTile, L - (t0 + i + k) * kTile), lane);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kPipe - 1; ++k)
+      if (k < n) load_tile<D, B>(r[k], pc, t0 + k, lane);
+#pragma unroll
+    for (int k = 0; k < kPipe - 1; ++k)
+      if (k < n) compute_tile<D, B>(r[k], qop, st, d.c, min(kTile, L - (t0 + k) * kTile), lane);
+  }
+
+  if (h < d.G) {
+    const float l_tot = st.l[0];
+    if (t0 == 0 && t1 == T) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = cx.out + (static_cast<int64_t>(s) * d.Hq + g * d.G + h) * D + (lane >> 4) * 4;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        bf16x4_t y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = static_cast<__bf16>(st.o[mt][i] * inv);
+        *reinterpret_cast<u32x2_t*>(orow + mt * 16) = __builtin_bit_cast(u32x2_t, y);
+      }
+    } else {
+      float* base = cx.ws + rec * record_floats(d.G, D);
+      float* orow = base + h * D + (lane >> 4) * 4;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<f32x4_t*>(orow + mt * 16) = st.o[mt];
+      if (lane < 16) {
+        base[d.G * D + h] = st.m;
+        base[d.G * D + d.G + h] = l_tot;
+      }
+    }
+  }
+}
+
+template <int D, int B>
+__global__ __launch_bounds__(kWave* kWavesPerGroup) void decode_partials_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+    uint16_t* __restrict__ out, float* __restrict__ ws, DecodeDims d) {
+  const Ctx cx{q, k, v, tables, lens, out, ws};
+  const int lane = __lane_id();
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
+  const int32_t cap = d.M * B;
+  const int64_t U = units_before(lens, d, cap, d.S, lane);
+  const int64_t N = min(static_cast<int64_t>(d.n_workers), U);
+  if (w >= N) return;
+  int64_t u = range_begin(w, U, N);
+  const int64_t u_end = range_begin(w + 1, U, N);
+  int32_t s;
+  int64_t start;
+  locate(lens, d, cap, u, lane, s, start);
+  int32_t L = clamp_len(lens[s], cap);
+  int32_t T = tiles_of(L);
+  int32_t g = static_cast<int32_t>((u - start) / T);
+  int32_t t = static_cast<int32_t>((u - start) - static_cast<int64_t>(g) * T);
+  int64_t rec = 2 * w;  // first segment -> slot 0, later ones -> slot 1
+  while (true) {
+    const int32_t t_end = static_cast<int32_t>(min(static_cast<int64_t>(T), t + (u_end - u)));
+    run_segment<D, B>(cx, d, s, g, t, t_end, L, T, rec, lane);
+    u += t_end - t;
+    if (u >= u_end) break;
+    rec = 2 * w + 1;
+    t = 0;
+    if (++g == d.Hkv) {
+      g = 0;
+      do {
+        ++s;
+        L = s < d.S ? clamp_len(lens[s], cap) : 1;
+      } while (L == 0);
+      if (s >= d.S) break;
+      T = tiles_of(L);
+    }
+  }
+}
+
+// Merge of split pairs and zero rows of empty sequences.  Each wave takes a
+// contiguous range of (sequence, KV head) pairs.
+template <int D>
+__global__ __launch_bounds__(kWave* kWavesPerGroup) void decode_reduce_kernel(
+    const int32_t* __restrict__ lens, uint16_t* __restrict__ out, const float* __restrict__ ws,
+    DecodeDims d, int32_t B) {
+  constexpr int kPerLane = D / kWave;
+  const int lane = __lane_id();
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * kWavesPerGroup;
+  const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
+  const int64_t per = (pairs + n_waves - 1) / n_waves;
+  const int64_t p0 = wave * per;
+  const int64_t p1 = min(pairs, p0 + per);
+  if (p0 >= p1) return;
+  const int32_t cap = d.M * B;
+  const int64_t U = units_before(lens, d, cap, d.S, lane);
+  const int64_t N = min(static_cast<int64_t>(d.n_workers), U);
+  const int64_t rf = record_floats(d.G, D);
+  int32_t s = static_cast<int32_t>(p0 / d.Hkv);
+  int32_t g = static_cast<int32_t>(p0 % d.Hkv);
+  int64_t seq_start = units_before(lens, d, cap, s, lane);
+  int32_t T = tiles_of(clamp_len(lens[s], cap));
+  for (int64_t p = p0; p < p1; ++p) {
+    if (T == 0) {
+      for (int32_t h = 0; h < d.G; ++h) {
+        uint16_t* orow = out + (static_cast<int64_t>(s) * d.Hq + g * d.G + h) * D + lane * kPerLane;
+#pragma unroll
+        for (int j = 0; j < kPerLane; ++j) orow[j] = 0;
+      }
+    } else {
+      const int64_t u0 = seq_start + static_cast<int64_t>(g) * T;
+      const int64_t wa = worker_of(u0, U, N);
+      const int64_t wb = worker_of(u0 + T - 1, U, N);
+      if (wa != wb) {
+        for (int32_t h = 0; h < d.G; ++h) {
+          float mx = -INFINITY;
+          for (int64_t w = wa; w <= wb; ++w) {
+            const float* rec = ws + (2 * w + (range_begin(w, U, N) >= u0 ? 0 : 1)) * rf;
+            mx = fmaxf(mx, rec[d.G * D + h]);
+          }
+          float lsum = 0.f;
+          float acc[kPerLane];
+#pragma unroll
+          for (int j = 0; j < kPerLane; ++j) acc[j] = 0.f;
+          for (int64_t w = wa; w <= wb; ++w) {
+            const float* rec = ws + (2 * w + (range_begin(w, U, N) >= u0 ? 0 : 1)) * rf;
+            const float e = __builtin_amdgcn_exp2f(rec[d.G * D + h] - mx);
+            lsum += e * rec[d.G * D + d.G + h];
+            const float* orow = rec + h * D + lane * kPerLane;
+#pragma unroll
+            for (int j = 0; j < kPerLane; ++j) acc[j] += e * orow[j];
+          }
+          const float inv = 1.0f / lsum;
+          uint16_t* orow = out + (static_cast<int64_t>(s) * d.Hq + g * d.G + h) * D + lane * kPerLane;
+#pragma unroll
+          for (int j = 0; j < kPerLane; ++j)
+            orow[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j] * inv));
+        }
+      }
+    }
+    if (++g == d.Hkv) {
+      g = 0;
+      seq_start += static_cast<int64_t>(d.Hkv) * T;
+      if (++s < d.S) T = tiles_of(clamp_len(lens[s], cap));
+    }
+  }
+}
+
+template <int D, int B>
+hipError_t launch_partials_t(const DecodeBuffers& b, const DecodeDims& d, hipStream_t stream) {
+  const int groups = (d.n_workers + kWavesPerGroup - 1) / kWavesPerGroup;
+  if (groups <= 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_partials_kernel<D, B>), dim3(groups), dim3(kWave * kWavesPerGroup),
+                     0, stream, b.q, b.k, b.v, b.tables, b.lens, b.out, b.ws, d);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_partials(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                                  hipStream_t stream) {
+  if (D == 128) {
+    if (B == 16) return launch_partials_t<128, 16>(b, d, stream);
+    if (B == 32) return launch_partials_t<128, 32>(b, d, stream);
+    if (B == 8) return launch_partials_t<128, 8>(b, d, stream);
+  } else if (D == 64) {
+    if (B == 16) return launch_partials_t<64, 16>(b, d, stream);
+    if (B == 32) return launch_partials_t<64, 32>(b, d, stream);
+    if (B == 8) return launch_partials_t<64, 8>(b, d, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_reduce(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                                int reduce_groups, hipStream_t stream) {
+  if (reduce_groups <= 0) return hipSuccess;
+  if (D == 128)
+    hipLaunchKernelGGL((decode_reduce_kernel<128>), dim3(reduce_groups),
+                       dim3(kWave * kWavesPerGroup), 0, stream, b.lens, b.out, b.ws, d, B);
+  else if (D == 64)
+    hipLaunchKernelGGL((decode_reduce_kernel<64>), dim3(reduce_groups),
+                       dim3(kWave * kWavesPerGroup), 0, stream, b.lens, b.out, b.ws, d, B);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,53 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Tokens per compute tile: the M (or K) extent of one 16x16 MFMA.
+constexpr int kTile = 16;
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kMaxGroup = 16;   // query heads per KV head served by one MFMA column tile
+constexpr int kMaxLayers = 128; // copy_blocks pool pointers travel as kernel arguments
+
+// Buffers of one decode call.  The kernels take them as separate __restrict__
+// parameters so that reads of the block table and lengths become scalar loads.
+struct DecodeBuffers {
+  const uint16_t* q;        // bf16 [S][Hq][D]
+  const uint16_t* k;        // K pool
+  const uint16_t* v;        // V pool
+  const int32_t* tables;    // int32 [S][M]
+  const int32_t* lens;      // int32 [S]
+  uint16_t* out;            // bf16 [S][Hq][D]
+  float* ws;                // partial records: [n_workers][2][record_floats(G, D)] fp32
+};
+
+// Sizes of one decode call (passed by value).
+struct DecodeDims {
+  int32_t S, Hq, Hkv, G, M;
+  int32_t n_workers;        // workers launched; the kernels use min(n_workers, units)
+  int64_t NB;
+  float c;                  // scale * log2(e): scores are kept in the log2 domain
+};
+
+// Floats in one partial record: O[G][D], then m[G], then l[G], padded to a
+// multiple of four floats so every record starts 16-byte aligned.
+__host__ __device__ inline int64_t record_floats(int G, int D) {
+  return static_cast<int64_t>(G) * D + ((2 * G + 3) / 4) * 4;
+}
+
+// Launchers (pkv_decode.hip).  Return a hipError_t.
+hipError_t launch_decode_partials(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                                  hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                                int reduce_groups, hipStream_t stream);
+
+// Launcher (pkv_copy.hip).
+hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                              int64_t num_blocks, int64_t block_bytes, const int32_t* pairs,
+                              int32_t num_pairs, hipStream_t stream);
+
+}  // namespace pkv
