@@ -141,7 +141,7 @@ def test_census_through_the_keys():
 
 
 def test_determinism_run_to_run():
-    case = wl.case_mix(3, 16, pool_bytes=2e9)
+    case = wl.case_mix(3, 16, pool_bytes=5e9)
     q = wl.host_q(case)
     import torch
 
@@ -167,7 +167,8 @@ def test_split_sizes_agree_with_the_oracle():
     kp, vp = wl.host_pools(case)
     ref = oracle_out(case, q, kp, vp)
     outs = []
-    for mc in (500, 512, 700, case.max_blocks_per_seq * 16):
+    cap = case.max_blocks_per_seq * 16
+    for mc in (500, 512, cap - 16, cap):
         got = bf16_to_f32(run_gpu(case, q, kp, vp, max_context_len=mc))
         assert_parity(got, ref, "max_context_len=%d" % mc)
         outs.append(got)
