@@ -19,7 +19,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -100,46 +99,48 @@ def flush_buffer(dev, nbytes=1 << 30):
     return torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
 
 
-def cpu_baseline(case, pools, tabs, lens, layers, args, gpu_tokens_per_step):
-    """The oracle on the host cores over a bounded sample: whole sequences of
-    layer 0, as many as fit the time target, scaled to a full step."""
+def cpu_baseline(case, pools, layers, args):
+    """The oracle on the host cores over a bounded sample of the same workload:
+    whole (layer, sequence) pairs in order until about ``--cpu-seconds`` of oracle
+    time, scaled by context tokens to the full step."""
     import torch
 
     import oracle
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
-    q, kd, vd = pools[0]
-    order = np.arange(case.num_seqs)
     done_tokens = 0
     elapsed = 0.0
-    seqs_done = 0
-    for s in order:
-        L = int(case.context_lens[s])
-        nb = -(-L // case.block_size)
-        ids = case.block_tables[s, :nb]
-        idx = torch.from_numpy(ids.astype(np.int64)).to(kd.device)
-        kh = kd[idx].view(torch.int16).cpu().numpy().view(np.uint16)
-        vh = vd[idx].view(torch.int16).cpu().numpy().view(np.uint16)
-        qh = q[s:s + 1].view(torch.int16).cpu().numpy().view(np.uint16)
-        tab = np.arange(nb, dtype=np.int32)[None, :]
-        t0 = time.perf_counter()
-        oracle.paged_decode(qh, kh, vh, tab, np.array([L], np.int32), case.block_size, case.scale,
-                            case.num_kv_heads, threads=threads)
-        elapsed += time.perf_counter() - t0
-        done_tokens += L
-        seqs_done += 1
+    pairs_done = 0
+    for layer in range(layers):
+        q, kd, vd = pools[layer]
+        for s in range(case.num_seqs):
+            L = int(case.context_lens[s])
+            nb = -(-L // case.block_size)
+            idx = torch.from_numpy(case.block_tables[s, :nb].astype(np.int64)).to(kd.device)
+            kh = kd[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+            vh = vd[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+            qh = q[s:s + 1].view(torch.int16).cpu().numpy().view(np.uint16)
+            tab = np.arange(nb, dtype=np.int32)[None, :]
+            t0 = time.perf_counter()
+            oracle.paged_decode(qh, kh, vh, tab, np.array([L], np.int32), case.block_size,
+                                case.scale, case.num_kv_heads, threads=threads)
+            elapsed += time.perf_counter() - t0
+            done_tokens += L
+            pairs_done += 1
+            if elapsed >= args.cpu_seconds:
+                break
         if elapsed >= args.cpu_seconds:
             break
-    total_tokens = int(case.context_lens.sum())
-    step_seconds = elapsed * (total_tokens / max(done_tokens, 1)) * layers
+    total_tokens = int(case.context_lens.sum()) * layers
+    step_seconds = elapsed * total_tokens / max(done_tokens, 1)
     return {
-        "value": case.num_seqs / step_seconds,
+        "value": round(case.num_seqs / step_seconds, 4),
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "%d of %d sequences of layer 0 (%d context tokens) in %.1f s on %d threads; "
-                  "scaled by context tokens to all sequences and %d layers"
-                  % (seqs_done, case.num_seqs, done_tokens, elapsed, threads, layers),
+        "sample": "%d of %d (layer, sequence) pairs, %d context tokens, %.1f s of oracle time on "
+                  "%d threads, scaled by context tokens to the full step"
+                  % (pairs_done, case.num_seqs * layers, done_tokens, elapsed, threads),
     }
 
 
@@ -190,11 +191,41 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # The step (all layers' launches) is captured once into a HIP graph and
+    # replayed: the timed region then holds GPU work only, no Python per launch.
+    graph = None
+    try:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+    except Exception as e:  # capture unsupported: time eager launches instead
+        print("graph capture failed (%s); timing eager launches" % e, file=sys.stderr)
+        graph = None
+
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # Per-launch duration of the main decode kernel: HIP events around every
+    # launch of eager steps on the same stream.
     for i in range(args.steps):
         step(ev[i * layers:(i + 1) * layers])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
 
     ms_per_step = elapsed * 1e3 / args.steps
     kern_ms = [a.elapsed_time(b) for a, b in ev]
@@ -221,6 +252,7 @@ def main():
         "config": {"workload": desc, "num_seqs": S, "context_len": int(case.context_lens.max()),
                    "layers": layers, "block_size": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D},
+        "graph": graph is not None,
         "kv_gbs": round(kv_gbs, 1),
         "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": "decode_partials_kernel",
@@ -232,7 +264,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(case, pools, tabs, lens, layers, args, tokens_per_s)
+        line["cpu_baseline"] = cpu_baseline(case, pools, layers, args)
     print(json.dumps(line), flush=True)
 
 

@@ -123,9 +123,9 @@ int32_t decode_impl(int phase, const void* q, const void* k_cache, const void* v
     if (launch_decode_partials(b, d, head_dim, block_size, s) != hipSuccess) return PKV_ERR_LAUNCH;
   }
   if (phase & kReduce) {
+    // one work-group per (sequence, KV head) pair, up to four per compute unit
     const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
-    int64_t groups = (pairs + kWavesPerGroup - 1) / kWavesPerGroup;
-    if (groups > cu) groups = cu;
+    int64_t groups = pairs < 4LL * cu ? pairs : 4LL * cu;
     if (launch_decode_reduce(b, d, head_dim, block_size, static_cast<int>(groups), s) != hipSuccess)
       return PKV_ERR_LAUNCH;
   }

@@ -389,65 +389,122 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void decode_partials_kernel(
   }
 }
 
-// Merge of split pairs and zero rows of empty sequences.  Each wave takes a
-// contiguous range of (sequence, KV head) pairs.
+// Merge of split pairs and zero rows of empty sequences.  One work-group per
+// (sequence, KV head) pair at a time, over a contiguous range of pairs.  The
+// records of a split pair come in chunks of kMergeChunk workers: their (m, l) go
+// through LDS, one thread per head folds them into the running max and sum, and
+// every thread accumulates its outputs (head, dim) from all records of the chunk
+// with independent loads.  The order of the records is fixed (worker order), so
+// the result does not depend on timing.
+constexpr int kMergeThreads = kWave * kWavesPerGroup;
+constexpr int kMergeChunk = 64;
+
 template <int D>
-__global__ __launch_bounds__(kWave* kWavesPerGroup) void decode_reduce_kernel(
+__global__ __launch_bounds__(kMergeThreads) void decode_reduce_kernel(
     const int32_t* __restrict__ lens, uint16_t* __restrict__ out, const float* __restrict__ ws,
     DecodeDims d, int32_t B) {
-  constexpr int kPerLane = D / kWave;
-  const int lane = __lane_id();
-  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
-  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * kWavesPerGroup;
+  constexpr int kOutPerThread = (kMaxGroup * D + kMergeThreads - 1) / kMergeThreads;
+  __shared__ float sm_m[kMergeChunk][kMaxGroup];
+  __shared__ float sm_e[kMergeChunk][kMaxGroup];
+  __shared__ float sm_l[kMergeChunk][kMaxGroup];
+  __shared__ int64_t sm_base[kMergeChunk];
+  __shared__ float s_run_m[kMaxGroup], s_run_l[kMaxGroup], s_scale[kMaxGroup];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
   const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
-  const int64_t per = (pairs + n_waves - 1) / n_waves;
-  const int64_t p0 = wave * per;
+  const int64_t per = (pairs + gridDim.x - 1) / gridDim.x;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * per;
   const int64_t p1 = min(pairs, p0 + per);
   if (p0 >= p1) return;
   const int32_t cap = d.M * B;
   const int64_t U = units_before(lens, d, cap, d.S, lane);
   const int64_t N = min(static_cast<int64_t>(d.n_workers), U);
   const int64_t rf = record_floats(d.G, D);
+  const int GD = d.G * D;
   int32_t s = static_cast<int32_t>(p0 / d.Hkv);
   int32_t g = static_cast<int32_t>(p0 % d.Hkv);
   int64_t seq_start = units_before(lens, d, cap, s, lane);
   int32_t T = tiles_of(clamp_len(lens[s], cap));
   for (int64_t p = p0; p < p1; ++p) {
+    uint16_t* orow = out + (static_cast<int64_t>(s) * d.Hq + g * d.G) * D;  // G rows of D
     if (T == 0) {
-      for (int32_t h = 0; h < d.G; ++h) {
-        uint16_t* orow = out + (static_cast<int64_t>(s) * d.Hq + g * d.G + h) * D + lane * kPerLane;
-#pragma unroll
-        for (int j = 0; j < kPerLane; ++j) orow[j] = 0;
-      }
+      for (int i = tid; i < GD; i += kMergeThreads) orow[i] = 0;
     } else {
       const int64_t u0 = seq_start + static_cast<int64_t>(g) * T;
       const int64_t wa = worker_of(u0, U, N);
       const int64_t wb = worker_of(u0 + T - 1, U, N);
       if (wa != wb) {
-        for (int32_t h = 0; h < d.G; ++h) {
-          float mx = -INFINITY;
-          for (int64_t w = wa; w <= wb; ++w) {
-            const float* rec = ws + (2 * w + (range_begin(w, U, N) >= u0 ? 0 : 1)) * rf;
-            mx = fmaxf(mx, rec[d.G * D + h]);
-          }
-          float lsum = 0.f;
-          float acc[kPerLane];
+        // worker wa holds this pair in slot 1 unless its range starts exactly at u0;
+        // every later worker starts inside the pair and holds it in slot 0
+        const int64_t first_slot = range_begin(wa, U, N) < u0 ? 1 : 0;
+        float acc[kOutPerThread];
 #pragma unroll
-          for (int j = 0; j < kPerLane; ++j) acc[j] = 0.f;
-          for (int64_t w = wa; w <= wb; ++w) {
-            const float* rec = ws + (2 * w + (range_begin(w, U, N) >= u0 ? 0 : 1)) * rf;
-            const float e = __builtin_amdgcn_exp2f(rec[d.G * D + h] - mx);
-            lsum += e * rec[d.G * D + d.G + h];
-            const float* orow = rec + h * D + lane * kPerLane;
-#pragma unroll
-            for (int j = 0; j < kPerLane; ++j) acc[j] += e * orow[j];
-          }
-          const float inv = 1.0f / lsum;
-          uint16_t* orow = out + (static_cast<int64_t>(s) * d.Hq + g * d.G + h) * D + lane * kPerLane;
-#pragma unroll
-          for (int j = 0; j < kPerLane; ++j)
-            orow[j] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[j] * inv));
+        for (int j = 0; j < kOutPerThread; ++j) acc[j] = 0.f;
+        if (tid < d.G) {
+          s_run_m[tid] = -INFINITY;
+          s_run_l[tid] = 0.f;
         }
+        for (int64_t c0 = wa; c0 <= wb; c0 += kMergeChunk) {
+          const int kc = static_cast<int>(min(static_cast<int64_t>(kMergeChunk), wb + 1 - c0));
+          if (tid < kc) {
+            const int64_t w = c0 + tid;
+            sm_base[tid] = (2 * w + (w == wa ? first_slot : 0)) * rf;
+          }
+          __syncthreads();
+          for (int i = tid; i < kc * d.G; i += kMergeThreads) {
+            const int k = i / d.G, h = i % d.G;
+            const float* rec = ws + sm_base[k];
+            sm_m[k][h] = rec[GD + h];
+            sm_l[k][h] = rec[GD + d.G + h];
+          }
+          __syncthreads();
+          if (tid < d.G) {
+            const int h = tid;
+            float cm = s_run_m[h];
+            for (int k = 0; k < kc; ++k) cm = fmaxf(cm, sm_m[k][h]);
+            const float scale_old = __builtin_amdgcn_exp2f(s_run_m[h] - cm);
+            float lsum = s_run_l[h] * scale_old;
+            for (int k = 0; k < kc; ++k) {
+              const float e = __builtin_amdgcn_exp2f(sm_m[k][h] - cm);
+              sm_e[k][h] = e;
+              lsum += e * sm_l[k][h];
+            }
+            s_scale[h] = scale_old;
+            s_run_m[h] = cm;
+            s_run_l[h] = lsum;
+          }
+          __syncthreads();
+#pragma unroll
+          for (int j = 0; j < kOutPerThread; ++j) {
+            const int i = tid + j * kMergeThreads;
+            if (i < GD) {
+              const int h = i / D;
+              float a = acc[j] * s_scale[h];
+              int k = 0;
+              for (; k + 4 <= kc; k += 4) {
+                const float o0 = ws[sm_base[k] + i], o1 = ws[sm_base[k + 1] + i];
+                const float o2 = ws[sm_base[k + 2] + i], o3 = ws[sm_base[k + 3] + i];
+                a += sm_e[k][h] * o0;
+                a += sm_e[k + 1][h] * o1;
+                a += sm_e[k + 2][h] * o2;
+                a += sm_e[k + 3][h] * o3;
+              }
+              for (; k < kc; ++k) a += sm_e[k][h] * ws[sm_base[k] + i];
+              acc[j] = a;
+            }
+          }
+          __syncthreads();
+        }
+#pragma unroll
+        for (int j = 0; j < kOutPerThread; ++j) {
+          const int i = tid + j * kMergeThreads;
+          if (i < GD) {
+            const float v = acc[j] / s_run_l[i / D];
+            orow[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+          }
+        }
+        __syncthreads();
       }
     }
     if (++g == d.Hkv) {
@@ -487,11 +544,11 @@ hipError_t launch_decode_reduce(const DecodeBuffers& b, const DecodeDims& d, int
                                 int reduce_groups, hipStream_t stream) {
   if (reduce_groups <= 0) return hipSuccess;
   if (D == 128)
-    hipLaunchKernelGGL((decode_reduce_kernel<128>), dim3(reduce_groups),
-                       dim3(kWave * kWavesPerGroup), 0, stream, b.lens, b.out, b.ws, d, B);
+    hipLaunchKernelGGL((decode_reduce_kernel<128>), dim3(reduce_groups), dim3(kMergeThreads), 0,
+                       stream, b.lens, b.out, b.ws, d, B);
   else if (D == 64)
-    hipLaunchKernelGGL((decode_reduce_kernel<64>), dim3(reduce_groups),
-                       dim3(kWave * kWavesPerGroup), 0, stream, b.lens, b.out, b.ws, d, B);
+    hipLaunchKernelGGL((decode_reduce_kernel<64>), dim3(reduce_groups), dim3(kMergeThreads), 0,
+                       stream, b.lens, b.out, b.ws, d, B);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
