@@ -162,8 +162,7 @@ def main():
     S, Hq, Hkv, D, B = (case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
                         case.block_size)
     max_ctx = case.max_context_len
-    ws_bytes = pkv.paged_attn_decode_workspace_bytes(S, Hq, Hkv, D, B, max_ctx)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = pkv.new_workspace(S, Hq, Hkv, D, B, max_ctx, dev)
     outs = [torch.empty_like(p[0]) for p in pools]
     per_call_bytes = decode_algorithmic_bytes(case.context_lens, Hq, Hkv, D, B)
     flush = flush_buffer(dev) if args.workload != "long" else None
@@ -181,12 +180,10 @@ def main():
             e = timed_events[layer] if timed_events is not None else None
             if e is not None:
                 e[0].record(stream)
-            pkv.paged_attn_decode_partials(q, k, v, tabs, lens, B, case.scale, outs[layer],
-                                           workspace=ws, max_context_len=max_ctx)
+            pkv.paged_attn_decode(q, k, v, tabs, lens, B, case.scale, outs[layer],
+                                  workspace=ws, max_context_len=max_ctx)
             if e is not None:
                 e[1].record(stream)
-            pkv.paged_attn_decode_reduce(q, k, v, tabs, lens, B, case.scale, outs[layer],
-                                         workspace=ws, max_context_len=max_ctx)
 
     for _ in range(args.warmup):
         step()
@@ -255,7 +252,7 @@ def main():
         "graph": graph is not None,
         "kv_gbs": round(kv_gbs, 1),
         "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "decode_partials_kernel",
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

@@ -67,8 +67,9 @@ const char* pkv_status_string(int32_t status);
 /*
  * Bytes of device scratch paged_attn_decode needs for these sizes on the
  * current device.  The scratch holds the partial softmax states of (sequence,
- * KV head) pairs whose context is split across workers (split-K).  Returns 0
- * for sizes paged_attn_decode would reject.
+ * KV head) pairs whose context is split across workers (split-K) and which
+ * worker opens each split pair.  Returns 0 for sizes paged_attn_decode would
+ * reject.
  */
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim,
@@ -103,15 +104,15 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 (no device-to-host read happens).  A bound that is too small
  *                 only costs speed; it must be <= max_blocks_per_seq*block_size.
  *   workspace     device scratch of at least workspace_bytes >=
- *                 paged_attn_decode_workspace_bytes(...) bytes; contents need no
- *                 initialisation and are overwritten.  Calls that overlap in time
- *                 must not share a workspace.
+ *                 paged_attn_decode_workspace_bytes(...) bytes, 16-byte aligned;
+ *                 contents need no initialisation and are overwritten.  Calls
+ *                 that overlap in time must not share a workspace.
  *
  * Slots past L in a sequence's last block, table entries past ceil(L/B) and
  * blocks no table references are never read into the arithmetic.  Results are
  * deterministic: the same inputs give the same bits, and renumbering physical
  * blocks (with the tables rewritten to match) does not change a bit.
- * Enqueues two kernels: paged_attn_decode_partials then paged_attn_decode_reduce.
+ * Enqueues two kernels: the decode kernel, then the merge of split pairs.
  */
 int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* context_lens,
@@ -120,31 +121,6 @@ int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           int32_t max_blocks_per_seq, int64_t num_blocks,
                           int32_t max_context_len, void* workspace, size_t workspace_bytes,
                           void* stream);
-
-/*
- * The two halves of paged_attn_decode, for callers that time or schedule them
- * separately; same arguments and checks.  _partials enqueues the main kernel: it
- * writes out[] for every (sequence, KV head) pair handled whole by one worker and
- * a partial softmax state into the workspace for the others.  _reduce enqueues
- * the merge of those partial states (fixed order, deterministic) and writes the
- * zero rows of empty sequences.  _reduce must follow _partials on the same
- * stream with the same arguments and workspace.
- */
-int32_t paged_attn_decode_partials(const void* q, const void* k_cache, const void* v_cache,
-                                   const int32_t* block_tables, const int32_t* context_lens,
-                                   int32_t block_size, float scale, void* out, int32_t num_seqs,
-                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                   int32_t max_blocks_per_seq, int64_t num_blocks,
-                                   int32_t max_context_len, void* workspace,
-                                   size_t workspace_bytes, void* stream);
-
-int32_t paged_attn_decode_reduce(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* block_tables, const int32_t* context_lens,
-                                 int32_t block_size, float scale, void* out, int32_t num_seqs,
-                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t max_blocks_per_seq, int64_t num_blocks,
-                                 int32_t max_context_len, void* workspace, size_t workspace_bytes,
-                                 void* stream);
 
 /*
  * Copy-on-write block copy: for every pair i and every layer l,

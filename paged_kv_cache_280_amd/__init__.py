@@ -12,9 +12,8 @@ from ._binding import (  # noqa: F401
     abi_version,
     copy_blocks,
     load_library,
+    new_workspace,
     paged_attn_decode,
-    paged_attn_decode_partials,
-    paged_attn_decode_reduce,
     paged_attn_decode_workspace_bytes,
     status_string,
 )

@@ -22,8 +22,7 @@ STATUS_NAMES = {
 }
 
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "paged_attn_decode_workspace_bytes",
-           "paged_attn_decode", "paged_attn_decode_partials", "paged_attn_decode_reduce",
-           "copy_blocks")
+           "paged_attn_decode", "copy_blocks")
 
 
 class PkvError(RuntimeError):
@@ -52,10 +51,8 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_decode_workspace_bytes.restype = sz
     decode_args = [p, p, p, p, p, i32, ctypes.c_float, p, i32, i32, i32, i32, i32, i64, i32, p,
                    sz, p]
-    for name in ("paged_attn_decode", "paged_attn_decode_partials", "paged_attn_decode_reduce"):
-        fn = getattr(lib, name)
-        fn.argtypes = decode_args
-        fn.restype = i32
+    lib.paged_attn_decode.argtypes = decode_args
+    lib.paged_attn_decode.restype = i32
     lib.copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32, p]
     lib.copy_blocks.restype = i32
     _lib = lib
@@ -113,8 +110,25 @@ def paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_
         int(max_context_len)))
 
 
-def _decode(entry, q, k_cache, v_cache, block_tables, context_lens, block_size, scale, out,
-            max_context_len, workspace, stream):
+def new_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                  device):
+    """A workspace tensor for paged_attn_decode with these sizes."""
+    import torch
+
+    with torch.cuda.device(device):
+        need = paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                 block_size, max_context_len)
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
+                      out=None, *, max_context_len=None, workspace=None, stream=None):
+    """Paged decode attention (see ``include/pkv.h``).  Returns ``out``.
+
+    ``max_context_len`` defaults to ``max_blocks_per_seq * block_size`` (a bound
+    known without reading the lengths back); ``workspace`` (see ``new_workspace``)
+    is allocated when not given; ``stream`` defaults to torch's current stream on
+    q's device."""
     import torch
 
     lib = load_library()
@@ -127,43 +141,19 @@ def _decode(entry, q, k_cache, v_cache, block_tables, context_lens, block_size, 
             out = torch.empty_like(q)
         _check(out.shape == q.shape and out.dtype == torch.bfloat16 and out.is_contiguous()
                and out.device == q.device, "out must match q")
-        need = paged_attn_decode_workspace_bytes(S, Hq, Hkv, D, block_size, max_context_len)
         if workspace is None:
-            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+            workspace = new_workspace(S, Hq, Hkv, D, block_size, max_context_len, q.device)
         _check(workspace.is_cuda and workspace.device == q.device and workspace.is_contiguous(),
                "workspace must be a contiguous tensor on q's device")
         ws_bytes = workspace.numel() * workspace.element_size()
-        rc = getattr(lib, entry)(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                 block_tables.data_ptr(), context_lens.data_ptr(), int(block_size),
-                                 float(scale), out.data_ptr(), S, Hq, Hkv, D, M, NB,
-                                 int(max_context_len), workspace.data_ptr(), ws_bytes,
-                                 _stream_handle(q, stream))
+        rc = lib.paged_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                   block_tables.data_ptr(), context_lens.data_ptr(),
+                                   int(block_size), float(scale), out.data_ptr(), S, Hq, Hkv, D,
+                                   M, NB, int(max_context_len), workspace.data_ptr(), ws_bytes,
+                                   _stream_handle(q, stream))
     if rc != 0:
-        raise PkvError(rc, entry)
+        raise PkvError(rc, "paged_attn_decode")
     return out
-
-
-def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
-                      out=None, *, max_context_len=None, workspace=None, stream=None):
-    """Paged decode attention (see ``include/pkv.h``).  Returns ``out``.
-
-    ``max_context_len`` defaults to ``max_blocks_per_seq * block_size`` (a bound
-    known without reading the lengths back); ``workspace`` is allocated when not
-    given; ``stream`` defaults to torch's current stream on q's device."""
-    return _decode("paged_attn_decode", q, k_cache, v_cache, block_tables, context_lens,
-                   block_size, scale, out, max_context_len, workspace, stream)
-
-
-def paged_attn_decode_partials(q, k_cache, v_cache, block_tables, context_lens, block_size,
-                               scale, out, *, workspace, max_context_len=None, stream=None):
-    return _decode("paged_attn_decode_partials", q, k_cache, v_cache, block_tables, context_lens,
-                   block_size, scale, out, max_context_len, workspace, stream)
-
-
-def paged_attn_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
-                             out, *, workspace, max_context_len=None, stream=None):
-    return _decode("paged_attn_decode_reduce", q, k_cache, v_cache, block_tables, context_lens,
-                   block_size, scale, out, max_context_len, workspace, stream)
 
 
 def copy_blocks(k_caches, v_caches, src_dst_pairs, stream=None):

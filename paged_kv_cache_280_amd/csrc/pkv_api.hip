@@ -57,7 +57,7 @@ int64_t worker_count(int cu, int32_t num_seqs, int32_t num_kv_heads, int32_t max
 }
 
 size_t workspace_for(int64_t workers, int32_t group, int32_t head_dim) {
-  return static_cast<size_t>(workers) * 2 * record_floats(group, head_dim) * sizeof(float);
+  return static_cast<size_t>(workspace_bytes_for(workers, group, head_dim));
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -77,9 +77,7 @@ int32_t check_shapes(int32_t block_size, float scale, int32_t num_seqs, int32_t 
   return PKV_OK;
 }
 
-enum Phase { kPartials = 1, kReduce = 2, kBoth = 3 };
-
-int32_t decode_impl(int phase, const void* q, const void* k_cache, const void* v_cache,
+int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, int32_t block_size,
                     float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
@@ -119,16 +117,11 @@ int32_t decode_impl(int phase, const void* q, const void* k_cache, const void* v
   d.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  if ((phase & kPartials) && max_context_len > 0) {
-    if (launch_decode_partials(b, d, head_dim, block_size, s) != hipSuccess) return PKV_ERR_LAUNCH;
-  }
-  if (phase & kReduce) {
-    // one work-group per (sequence, KV head) pair, up to four per compute unit
-    const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
-    int64_t groups = pairs < 4LL * cu ? pairs : 4LL * cu;
-    if (launch_decode_reduce(b, d, head_dim, block_size, static_cast<int>(groups), s) != hipSuccess)
-      return PKV_ERR_LAUNCH;
-  }
+  // merge work-groups: one per compute unit, each scanning at most 64 worker slots
+  int64_t merge_groups = workers < cu ? workers : cu;
+  if (merge_groups * 64 < workers) merge_groups = (workers + 63) / 64;
+  if (launch_decode(b, d, head_dim, block_size, static_cast<int>(merge_groups), s) != hipSuccess)
+    return PKV_ERR_LAUNCH;
   return PKV_OK;
 }
 
@@ -173,36 +166,9 @@ int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           int32_t max_blocks_per_seq, int64_t num_blocks,
                           int32_t max_context_len, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  return pkv::decode_impl(pkv::kBoth, q, k_cache, v_cache, block_tables, context_lens, block_size,
-                          scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                          max_blocks_per_seq, num_blocks, max_context_len, workspace,
-                          workspace_bytes, stream);
-}
-
-int32_t paged_attn_decode_partials(const void* q, const void* k_cache, const void* v_cache,
-                                   const int32_t* block_tables, const int32_t* context_lens,
-                                   int32_t block_size, float scale, void* out, int32_t num_seqs,
-                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                   int32_t max_blocks_per_seq, int64_t num_blocks,
-                                   int32_t max_context_len, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
-  return pkv::decode_impl(pkv::kPartials, q, k_cache, v_cache, block_tables, context_lens,
-                          block_size, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                          max_blocks_per_seq, num_blocks, max_context_len, workspace,
-                          workspace_bytes, stream);
-}
-
-int32_t paged_attn_decode_reduce(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* block_tables, const int32_t* context_lens,
-                                 int32_t block_size, float scale, void* out, int32_t num_seqs,
-                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t max_blocks_per_seq, int64_t num_blocks,
-                                 int32_t max_context_len, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
-  return pkv::decode_impl(pkv::kReduce, q, k_cache, v_cache, block_tables, context_lens,
-                          block_size, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                          max_blocks_per_seq, num_blocks, max_context_len, workspace,
-                          workspace_bytes, stream);
+  return pkv::decode_impl(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, out,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          num_blocks, max_context_len, workspace, workspace_bytes, stream);
 }
 
 int32_t copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,

@@ -17,8 +17,8 @@
 // lengths.  A worker's range is cut into segments at (sequence, head) boundaries.
 // A segment that covers a whole pair writes the output directly; a segment that
 // covers part of a pair writes its softmax state (reference max m, sum l,
-// unnormalised accumulator O; fp32) to the workspace, and the reduce kernel merges
-// the states of each split pair in worker order.
+// unnormalised accumulator O; fp32) to the workspace; a second kernel merges the
+// states of each split pair in worker order (deterministic result).
 //
 // Per tile (one wave, 16 tokens x D dims, up to 16 query heads of one KV head):
 //   scores  S[token][head] = K_tile (16 x D) * q^T (D x 16)  -- D/32 MFMA 16x16x32 bf16
@@ -256,9 +256,10 @@ struct Ctx {
 };
 
 // Tiles [t0, t1) of (sequence s, KV head g); writes the output rows when the
-// segment is the whole pair, else the partial record `rec`.
+// segment is the whole pair, else the partial record `rec`.  Returns true when it
+// wrote a partial record.
 template <int D, int B>
-__device__ void run_segment(const Ctx& cx, const DecodeDims& d, int32_t s, int32_t g, int32_t t0,
+__device__ bool run_segment(const Ctx& cx, const DecodeDims& d, int32_t s, int32_t g, int32_t t0,
                             int32_t t1, int32_t L, int32_t T, int64_t rec, int lane) {
   constexpr int64_t kTileElems = static_cast<int64_t>(D) * B;
   PairCursor pc;
@@ -346,212 +347,173 @@ __device__ void run_segment(const Ctx& cx, const DecodeDims& d, int32_t s, int32
       }
     }
   }
+  return !(t0 == 0 && t1 == T);
 }
 
+// The decode kernel.  Workspace: partial records ([n_workers][2] of
+// record_floats), then one descriptor per worker: (s, g, wb, first_slot) of the
+// split pair whose first share this worker holds, or s = -1.
 template <int D, int B>
-__global__ __launch_bounds__(kWave* kWavesPerGroup) void decode_partials_kernel(
+__global__ __launch_bounds__(kWave* kWavesPerGroup, 2) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
-    uint16_t* __restrict__ out, float* __restrict__ ws, DecodeDims d) {
+    uint16_t* __restrict__ out, float* __restrict__ ws, int4* __restrict__ desc, DecodeDims d) {
   const Ctx cx{q, k, v, tables, lens, out, ws};
   const int lane = __lane_id();
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
+  if (w >= d.n_workers) return;
   const int32_t cap = d.M * B;
-  const int64_t U = units_before(lens, d, cap, d.S, lane);
-  const int64_t N = min(static_cast<int64_t>(d.n_workers), U);
-  if (w >= N) return;
-  int64_t u = range_begin(w, U, N);
-  const int64_t u_end = range_begin(w + 1, U, N);
-  int32_t s;
-  int64_t start;
-  locate(lens, d, cap, u, lane, s, start);
-  int32_t L = clamp_len(lens[s], cap);
-  int32_t T = tiles_of(L);
-  int32_t g = static_cast<int32_t>((u - start) / T);
-  int32_t t = static_cast<int32_t>((u - start) - static_cast<int64_t>(g) * T);
-  int64_t rec = 2 * w;  // first segment -> slot 0, later ones -> slot 1
-  while (true) {
-    const int32_t t_end = static_cast<int32_t>(min(static_cast<int64_t>(T), t + (u_end - u)));
-    run_segment<D, B>(cx, d, s, g, t, t_end, L, T, rec, lane);
-    u += t_end - t;
-    if (u >= u_end) break;
-    rec = 2 * w + 1;
-    t = 0;
-    if (++g == d.Hkv) {
-      g = 0;
-      do {
-        ++s;
-        L = s < d.S ? clamp_len(lens[s], cap) : 1;
-      } while (L == 0);
-      if (s >= d.S) break;
-      T = tiles_of(L);
+
+  // Rows of empty sequences are zeros.
+  for (int64_t se = w; se < d.S; se += d.n_workers) {
+    if (clamp_len(lens[se], cap) == 0) {
+      uint16_t* row = out + se * d.Hq * D;
+      for (int32_t i = lane * 8; i < d.Hq * D; i += kWave * 8)
+        *reinterpret_cast<u32x4_t*>(row + i) = u32x4_t{0, 0, 0, 0};
     }
   }
-}
 
-// Merge of split pairs and zero rows of empty sequences.  One work-group per
-// (sequence, KV head) pair at a time, over a contiguous range of pairs.  The
-// records of a split pair come in chunks of kMergeChunk workers: their (m, l) go
-// through LDS, one thread per head folds them into the running max and sum, and
-// every thread accumulates its outputs (head, dim) from all records of the chunk
-// with independent loads.  The order of the records is fixed (worker order), so
-// the result does not depend on timing.
-constexpr int kMergeThreads = kWave * kWavesPerGroup;
-constexpr int kMergeChunk = 64;
-
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void decode_reduce_kernel(
-    const int32_t* __restrict__ lens, uint16_t* __restrict__ out, const float* __restrict__ ws,
-    DecodeDims d, int32_t B) {
-  constexpr int kOutPerThread = (kMaxGroup * D + kMergeThreads - 1) / kMergeThreads;
-  __shared__ float sm_m[kMergeChunk][kMaxGroup];
-  __shared__ float sm_e[kMergeChunk][kMaxGroup];
-  __shared__ float sm_l[kMergeChunk][kMaxGroup];
-  __shared__ int64_t sm_base[kMergeChunk];
-  __shared__ float s_run_m[kMaxGroup], s_run_l[kMaxGroup], s_scale[kMaxGroup];
-
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
-  const int64_t per = (pairs + gridDim.x - 1) / gridDim.x;
-  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * per;
-  const int64_t p1 = min(pairs, p0 + per);
-  if (p0 >= p1) return;
-  const int32_t cap = d.M * B;
+  int4 opened = {-1, 0, 0, 0};
   const int64_t U = units_before(lens, d, cap, d.S, lane);
   const int64_t N = min(static_cast<int64_t>(d.n_workers), U);
-  const int64_t rf = record_floats(d.G, D);
-  const int GD = d.G * D;
-  int32_t s = static_cast<int32_t>(p0 / d.Hkv);
-  int32_t g = static_cast<int32_t>(p0 % d.Hkv);
-  int64_t seq_start = units_before(lens, d, cap, s, lane);
-  int32_t T = tiles_of(clamp_len(lens[s], cap));
-  for (int64_t p = p0; p < p1; ++p) {
-    uint16_t* orow = out + (static_cast<int64_t>(s) * d.Hq + g * d.G) * D;  // G rows of D
-    if (T == 0) {
-      for (int i = tid; i < GD; i += kMergeThreads) orow[i] = 0;
-    } else {
-      const int64_t u0 = seq_start + static_cast<int64_t>(g) * T;
-      const int64_t wa = worker_of(u0, U, N);
-      const int64_t wb = worker_of(u0 + T - 1, U, N);
-      if (wa != wb) {
-        // worker wa holds this pair in slot 1 unless its range starts exactly at u0;
-        // every later worker starts inside the pair and holds it in slot 0
-        const int64_t first_slot = range_begin(wa, U, N) < u0 ? 1 : 0;
-        float acc[kOutPerThread];
-#pragma unroll
-        for (int j = 0; j < kOutPerThread; ++j) acc[j] = 0.f;
-        if (tid < d.G) {
-          s_run_m[tid] = -INFINITY;
-          s_run_l[tid] = 0.f;
-        }
-        for (int64_t c0 = wa; c0 <= wb; c0 += kMergeChunk) {
-          const int kc = static_cast<int>(min(static_cast<int64_t>(kMergeChunk), wb + 1 - c0));
-          if (tid < kc) {
-            const int64_t w = c0 + tid;
-            sm_base[tid] = (2 * w + (w == wa ? first_slot : 0)) * rf;
-          }
-          __syncthreads();
-          for (int i = tid; i < kc * d.G; i += kMergeThreads) {
-            const int k = i / d.G, h = i % d.G;
-            const float* rec = ws + sm_base[k];
-            sm_m[k][h] = rec[GD + h];
-            sm_l[k][h] = rec[GD + d.G + h];
-          }
-          __syncthreads();
-          if (tid < d.G) {
-            const int h = tid;
-            float cm = s_run_m[h];
-            for (int k = 0; k < kc; ++k) cm = fmaxf(cm, sm_m[k][h]);
-            const float scale_old = __builtin_amdgcn_exp2f(s_run_m[h] - cm);
-            float lsum = s_run_l[h] * scale_old;
-            for (int k = 0; k < kc; ++k) {
-              const float e = __builtin_amdgcn_exp2f(sm_m[k][h] - cm);
-              sm_e[k][h] = e;
-              lsum += e * sm_l[k][h];
-            }
-            s_scale[h] = scale_old;
-            s_run_m[h] = cm;
-            s_run_l[h] = lsum;
-          }
-          __syncthreads();
-#pragma unroll
-          for (int j = 0; j < kOutPerThread; ++j) {
-            const int i = tid + j * kMergeThreads;
-            if (i < GD) {
-              const int h = i / D;
-              float a = acc[j] * s_scale[h];
-              int k = 0;
-              for (; k + 4 <= kc; k += 4) {
-                const float o0 = ws[sm_base[k] + i], o1 = ws[sm_base[k + 1] + i];
-                const float o2 = ws[sm_base[k + 2] + i], o3 = ws[sm_base[k + 3] + i];
-                a += sm_e[k][h] * o0;
-                a += sm_e[k + 1][h] * o1;
-                a += sm_e[k + 2][h] * o2;
-                a += sm_e[k + 3][h] * o3;
-              }
-              for (; k < kc; ++k) a += sm_e[k][h] * ws[sm_base[k] + i];
-              acc[j] = a;
-            }
-          }
-          __syncthreads();
-        }
-#pragma unroll
-        for (int j = 0; j < kOutPerThread; ++j) {
-          const int i = tid + j * kMergeThreads;
-          if (i < GD) {
-            const float v = acc[j] / s_run_l[i / D];
-            orow[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-          }
-        }
-        __syncthreads();
+  if (w < N) {
+    int64_t u = range_begin(w, U, N);
+    const int64_t u_end = range_begin(w + 1, U, N);
+    int32_t s;
+    int64_t start;  // first unit of sequence s
+    locate(lens, d, cap, u, lane, s, start);
+    int32_t L = clamp_len(lens[s], cap);
+    int32_t T = tiles_of(L);
+    int32_t g = static_cast<int32_t>((u - start) / T);
+    int32_t t = static_cast<int32_t>((u - start) - static_cast<int64_t>(g) * T);
+    int64_t rec = 2 * w;  // first segment -> slot 0, later ones -> slot 1
+    while (true) {
+      const int32_t t_end = static_cast<int32_t>(min(static_cast<int64_t>(T), t + (u_end - u)));
+      if (run_segment<D, B>(cx, d, s, g, t, t_end, L, T, rec, lane) && t == 0) {
+        // This worker holds the first share of a pair that later workers continue.
+        const int64_t u0 = start + static_cast<int64_t>(g) * T;
+        opened = int4{s, g, static_cast<int32_t>(worker_of(u0 + T - 1, U, N)),
+                      static_cast<int32_t>(rec - 2 * w)};
+      }
+      u += t_end - t;
+      if (u >= u_end) break;
+      rec = 2 * w + 1;
+      t = 0;
+      if (++g == d.Hkv) {
+        g = 0;
+        start += static_cast<int64_t>(d.Hkv) * T;
+        do {
+          ++s;
+          L = s < d.S ? clamp_len(lens[s], cap) : 1;
+        } while (L == 0);
+        if (s >= d.S) break;
+        T = tiles_of(L);
       }
     }
-    if (++g == d.Hkv) {
-      g = 0;
-      seq_start += static_cast<int64_t>(d.Hkv) * T;
-      if (++s < d.S) T = tiles_of(clamp_len(lens[s], cap));
+  }
+  if (lane == 0) desc[w] = opened;
+}
+
+// Merge of split pairs.  Work-group b reads the descriptors of its slice of
+// workers in one parallel pass and keeps the valid ones (each names a split pair
+// opened by worker wa and closed by wb).  For each such pair every thread takes
+// outputs (head, dim) in turn and folds the records of wa..wb into each in worker
+// order, kMergeChunk records per batch of independent loads, with a running max.
+// The order is fixed, so the result does not depend on timing.
+constexpr int kMergeThreads = 512;
+constexpr int kMergeChunk = 16;
+constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __restrict__ desc,
+                                                              uint16_t* __restrict__ out,
+                                                              const float* __restrict__ ws,
+                                                              DecodeDims d) {
+  __shared__ int32_t s_list[kMergeSlice];
+  __shared__ int32_t s_count;
+  const int tid = threadIdx.x;
+  const int64_t per = (d.n_workers + gridDim.x - 1) / gridDim.x;
+  const int64_t w0 = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t w1 = min(w0 + per, static_cast<int64_t>(d.n_workers));
+  if (tid == 0) s_count = 0;
+  __syncthreads();
+  if (w0 + tid < w1 && desc[w0 + tid].x >= 0) s_list[atomicAdd(&s_count, 1)] = static_cast<int32_t>(w0 + tid);
+  __syncthreads();
+  const int32_t n = s_count;
+  const int64_t rf = record_floats(d.G, D);
+  const int32_t GD = d.G * D;
+  for (int32_t p = 0; p < n; ++p) {
+    const int64_t wa = s_list[p];
+    const int4 ds = desc[wa];
+    const int64_t wb = ds.z;
+    const int64_t first = (2 * wa + ds.w) * rf;  // record of wa; later workers use slot 0
+    uint16_t* orow = out + (static_cast<int64_t>(ds.x) * d.Hq + ds.y * d.G) * D;
+    for (int32_t i = tid; i < GD; i += kMergeThreads) {
+      const int32_t h = i / D;
+      float run_m = -INFINITY, run_l = 0.f, acc = 0.f;
+      for (int64_t c0 = wa; c0 <= wb; c0 += kMergeChunk) {
+        float m[kMergeChunk], l[kMergeChunk], o[kMergeChunk];
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) {
+          if (c0 + k <= wb) {
+            const float* rec = ws + (c0 + k == wa ? first : 2 * (c0 + k) * rf);
+            m[k] = rec[GD + h];
+            l[k] = rec[GD + d.G + h];
+            o[k] = rec[i];
+          } else {
+            m[k] = -INFINITY;
+            l[k] = 0.f;
+            o[k] = 0.f;
+          }
+        }
+        float cm = run_m;
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) cm = fmaxf(cm, m[k]);
+        const float scale = __builtin_amdgcn_exp2f(run_m - cm);
+        run_l *= scale;
+        acc *= scale;
+        run_m = cm;
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) {
+          const float e = __builtin_amdgcn_exp2f(m[k] - cm);
+          run_l += e * l[k];
+          acc += e * o[k];
+        }
+      }
+      orow[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc / run_l));
     }
   }
 }
 
 template <int D, int B>
-hipError_t launch_partials_t(const DecodeBuffers& b, const DecodeDims& d, hipStream_t stream) {
+hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
+                    hipStream_t stream) {
   const int groups = (d.n_workers + kWavesPerGroup - 1) / kWavesPerGroup;
   if (groups <= 0) return hipSuccess;
-  hipLaunchKernelGGL((decode_partials_kernel<D, B>), dim3(groups), dim3(kWave * kWavesPerGroup),
-                     0, stream, b.q, b.k, b.v, b.tables, b.lens, b.out, b.ws, d);
+  int4* desc = reinterpret_cast<int4*>(reinterpret_cast<char*>(b.ws) +
+                                       records_bytes(d.n_workers, d.G, D));
+  hipLaunchKernelGGL((decode_kernel<D, B>), dim3(groups), dim3(kWave * kWavesPerGroup), 0, stream,
+                     b.q, b.k, b.v, b.tables, b.lens, b.out, b.ws, desc, d);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(merge_groups), dim3(kMergeThreads), 0, stream, desc,
+                     b.out, b.ws, d);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_partials(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                                  hipStream_t stream) {
+hipError_t launch_decode(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                         int merge_groups, hipStream_t stream) {
   if (D == 128) {
-    if (B == 16) return launch_partials_t<128, 16>(b, d, stream);
-    if (B == 32) return launch_partials_t<128, 32>(b, d, stream);
-    if (B == 8) return launch_partials_t<128, 8>(b, d, stream);
+    if (B == 16) return launch_t<128, 16>(b, d, merge_groups, stream);
+    if (B == 32) return launch_t<128, 32>(b, d, merge_groups, stream);
+    if (B == 8) return launch_t<128, 8>(b, d, merge_groups, stream);
   } else if (D == 64) {
-    if (B == 16) return launch_partials_t<64, 16>(b, d, stream);
-    if (B == 32) return launch_partials_t<64, 32>(b, d, stream);
-    if (B == 8) return launch_partials_t<64, 8>(b, d, stream);
+    if (B == 16) return launch_t<64, 16>(b, d, merge_groups, stream);
+    if (B == 32) return launch_t<64, 32>(b, d, merge_groups, stream);
+    if (B == 8) return launch_t<64, 8>(b, d, merge_groups, stream);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_decode_reduce(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                                int reduce_groups, hipStream_t stream) {
-  if (reduce_groups <= 0) return hipSuccess;
-  if (D == 128)
-    hipLaunchKernelGGL((decode_reduce_kernel<128>), dim3(reduce_groups), dim3(kMergeThreads), 0,
-                       stream, b.lens, b.out, b.ws, d, B);
-  else if (D == 64)
-    hipLaunchKernelGGL((decode_reduce_kernel<64>), dim3(reduce_groups), dim3(kMergeThreads), 0,
-                       stream, b.lens, b.out, b.ws, d, B);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -22,7 +22,7 @@ struct DecodeBuffers {
   const int32_t* tables;    // int32 [S][M]
   const int32_t* lens;      // int32 [S]
   uint16_t* out;            // bf16 [S][Hq][D]
-  float* ws;                // partial records: [n_workers][2][record_floats(G, D)] fp32
+  float* ws;                // workspace: partial records, then per-worker descriptors
 };
 
 // Sizes of one decode call (passed by value).
@@ -39,11 +39,19 @@ __host__ __device__ inline int64_t record_floats(int G, int D) {
   return static_cast<int64_t>(G) * D + ((2 * G + 3) / 4) * 4;
 }
 
-// Launchers (pkv_decode.hip).  Return a hipError_t.
-hipError_t launch_decode_partials(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                                  hipStream_t stream);
-hipError_t launch_decode_reduce(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                                int reduce_groups, hipStream_t stream);
+// Workspace of a decode call: partial records ([n_workers][2][record_floats]),
+// then one 16-byte descriptor per worker.
+__host__ __device__ inline int64_t records_bytes(int64_t workers, int G, int D) {
+  return workers * 2 * record_floats(G, D) * static_cast<int64_t>(sizeof(float));
+}
+inline int64_t workspace_bytes_for(int64_t workers, int G, int D) {
+  return records_bytes(workers, G, D) + workers * 16;
+}
+
+// Launches the decode kernel and the merge kernel (pkv_decode.hip).  Returns a
+// hipError_t.
+hipError_t launch_decode(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                         int merge_groups, hipStream_t stream);
 
 // Launcher (pkv_copy.hip).
 hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,

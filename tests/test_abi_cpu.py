@@ -31,7 +31,6 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["pkv_abi_version", "pkv_status_string",
                             "paged_attn_decode_workspace_bytes", "paged_attn_decode",
-                            "paged_attn_decode_partials", "paged_attn_decode_reduce",
                             "copy_blocks"])
 
 
