@@ -45,7 +45,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes three times (the "
+                         "reference kernel that scales hardware byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes):
+    import torch
+
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                      "launches": 3}), flush=True)
 
 
 def source_sha():
@@ -146,6 +162,9 @@ def cpu_baseline(case, pools, layers, args):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library's decode runs on a single device "
               "(no collectives); run with --gpus 1", file=sys.stderr)

@@ -238,6 +238,71 @@ def case_random(seed, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                 tab, 1.0 / math.sqrt(head_dim), poison_block=poison, seed=seed)
 
 
+@dataclasses.dataclass
+class PrefixScript:
+    """Parallel sampling with a shared prompt prefix: every prompt's prefix is
+    stored once and forked to n_samples sequences, which then append divergent
+    tails.  Block placement is left to the block manager (seeded free order)."""
+    num_prompts: int
+    num_samples: int
+    prefix_len: int
+    tails: np.ndarray          # int32 [num_prompts][num_samples]
+    block_size: int
+    num_blocks: int
+    free_order: np.ndarray     # int32 permutation of the pool
+    num_q_heads: int = 32
+    num_kv_heads: int = 8
+    head_dim: int = 128
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def prefix_script(seed=0, prefix_len=1020, num_prompts=16, num_samples=8, tail_max=256,
+                  block_size=16, spare_blocks=8) -> PrefixScript:
+    """16 prompts x 8 samples; tails ~ U_int[0, tail_max]; the pool holds what the
+    script needs (prefix blocks once, each sample's tail blocks and one copy per
+    sample that writes into a shared, partly filled block) plus spare blocks."""
+    rng = np.random.default_rng(seed)
+    tails = rng.integers(0, tail_max + 1, size=(num_prompts, num_samples)).astype(np.int32)
+    B = block_size
+    pre_blocks = -(-prefix_len // B)
+    need = num_prompts * pre_blocks
+    for p in range(num_prompts):
+        for k in range(num_samples):
+            need += -(-(prefix_len + int(tails[p, k])) // B) - pre_blocks
+            need += 1 if (prefix_len % B and tails[p, k] > 0) else 0
+    nb = need + spare_blocks
+    return PrefixScript(num_prompts, num_samples, prefix_len, tails, B, nb,
+                        rng.permutation(nb).astype(np.int32), seed=seed)
+
+
+def token_kv(seed, tag, n_tokens, num_kv_heads, head_dim):
+    """bf16 K and V rows [n_tokens][Hkv][D] for one tagged run of tokens."""
+    rng = np.random.default_rng([seed, 3] + list(tag))
+    k = randn_bf16(rng, (n_tokens, num_kv_heads, head_dim))
+    v = randn_bf16(rng, (n_tokens, num_kv_heads, head_dim))
+    return k, v
+
+
+def write_tokens(k_pool, v_pool, slots, k_rows, v_rows):
+    """Write token rows into (block, slot) positions of host pools in the library
+    layout.  slots: sequence of (block, offset); rows: [n][Hkv][D] bf16 bits."""
+    if len(slots) == 0:
+        return
+    b = np.array([s[0] for s in slots], dtype=np.int64)
+    o = np.array([s[1] for s in slots], dtype=np.int64)
+    n, hkv, d = k_rows.shape
+    # K [NB][Hkv][D/8][B][8]: element (b, g, o, d) at [b, g, d // 8, o, d % 8]
+    k_pool[b[:, None, None], np.arange(hkv)[None, :, None], (np.arange(d) // 8)[None, None, :],
+           o[:, None, None], (np.arange(d) % 8)[None, None, :]] = k_rows
+    # V [NB][Hkv][D][B]
+    v_pool[b[:, None, None], np.arange(hkv)[None, :, None], np.arange(d)[None, None, :],
+           o[:, None, None]] = v_rows
+
+
 # ---------------------------------------------------------------------------
 # Host materialisation (numpy)
 # ---------------------------------------------------------------------------
