@@ -70,8 +70,9 @@ def source_sha():
 
 
 def measured_traffic(workload_key):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source; else None."""
+    """HBM bytes per decode call (decode kernel + merge kernel, read + written) from
+    the committed rocprofv3 counter summary, if it was taken on the current kernel
+    source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload_key)
     if not os.path.exists(path):
         return None
@@ -79,7 +80,7 @@ def measured_traffic(workload_key):
         t = json.load(f)
     if t.get("kernel_source_sha") != source_sha():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("hbm_bytes_per_call")
 
 
 def build_workload(args, dev):
@@ -271,7 +272,7 @@ def main():
         "graph": graph is not None,
         "kv_gbs": round(kv_gbs, 1),
         "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel",
+        "roofline": {"bound": "hbm", "kernel": "paged_attn_decode (decode_kernel + merge_kernel)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
