@@ -123,6 +123,40 @@ __device__ __forceinline__ int64_t worker_of(int64_t u, int64_t U, int64_t N) {
   return ((u + 1) * N - 1) / U;
 }
 
+// A worker's share of the batch: total units U, active workers N, its range
+// [u, u_end), the sequence s holding unit u and the first unit `start` of s.
+struct WorkerPlan {
+  int64_t U, N, u, u_end, start;
+  int32_t s;
+};
+
+// Returns false when worker w has no range.  With at most kWave sequences the
+// lengths are read once and scanned in registers; otherwise in two passes.
+__device__ bool plan_worker(const int32_t* __restrict__ lens, const DecodeDims& d, int32_t cap,
+                            int64_t w, int lane, WorkerPlan& p) {
+  if (d.S <= kWave) {
+    const int32_t T = lane < d.S ? tiles_of(clamp_len(lens[lane], cap)) : 0;
+    const int32_t incl = wave_inclusive_scan(T, lane);
+    p.U = static_cast<int64_t>(__builtin_amdgcn_readlane(incl, kWave - 1)) * d.Hkv;
+    p.N = min(static_cast<int64_t>(d.n_workers), p.U);
+    if (w >= p.N) return false;
+    p.u = range_begin(w, p.U, p.N);
+    p.u_end = range_begin(w + 1, p.U, p.N);
+    const uint64_t hit = __ballot(static_cast<int64_t>(incl) * d.Hkv > p.u);
+    const int32_t first = uniform(__builtin_ctzll(hit));
+    p.s = first;
+    p.start = static_cast<int64_t>(__builtin_amdgcn_readlane(incl - T, first)) * d.Hkv;
+    return true;
+  }
+  p.U = units_before(lens, d, cap, d.S, lane);
+  p.N = min(static_cast<int64_t>(d.n_workers), p.U);
+  if (w >= p.N) return false;
+  p.u = range_begin(w, p.U, p.N);
+  p.u_end = range_begin(w + 1, p.U, p.N);
+  locate(lens, d, cap, p.u, lane, p.s, p.start);
+  return true;
+}
+
 template <int D, int B>
 struct TileRegs {
   u32x4_t k[D / 32];  // score MFMA A operand: token lane%16, dims c*32 + (lane/16)*8 .. +7
@@ -364,24 +398,12 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 2) void decode_kernel(
   if (w >= d.n_workers) return;
   const int32_t cap = d.M * B;
 
-  // Rows of empty sequences are zeros.
-  for (int64_t se = w; se < d.S; se += d.n_workers) {
-    if (clamp_len(lens[se], cap) == 0) {
-      uint16_t* row = out + se * d.Hq * D;
-      for (int32_t i = lane * 8; i < d.Hq * D; i += kWave * 8)
-        *reinterpret_cast<u32x4_t*>(row + i) = u32x4_t{0, 0, 0, 0};
-    }
-  }
-
   int4 opened = {-1, 0, 0, 0};
-  const int64_t U = units_before(lens, d, cap, d.S, lane);
-  const int64_t N = min(static_cast<int64_t>(d.n_workers), U);
-  if (w < N) {
-    int64_t u = range_begin(w, U, N);
-    const int64_t u_end = range_begin(w + 1, U, N);
-    int32_t s;
-    int64_t start;  // first unit of sequence s
-    locate(lens, d, cap, u, lane, s, start);
+  WorkerPlan pl;
+  if (plan_worker(lens, d, cap, w, lane, pl)) {
+    const int64_t U = pl.U, N = pl.N, u_end = pl.u_end;
+    int64_t u = pl.u, start = pl.start;  // start: first unit of sequence s
+    int32_t s = pl.s;
     int32_t L = clamp_len(lens[s], cap);
     int32_t T = tiles_of(L);
     int32_t g = static_cast<int32_t>((u - start) / T);
@@ -409,6 +431,15 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 2) void decode_kernel(
         if (s >= d.S) break;
         T = tiles_of(L);
       }
+    }
+  }
+
+  // Rows of empty sequences are zeros (done last: off the path to the first loads).
+  for (int64_t se = w; se < d.S; se += d.n_workers) {
+    if (clamp_len(lens[se], cap) == 0) {
+      uint16_t* row = out + se * d.Hq * D;
+      for (int32_t i = lane * 8; i < d.Hq * D; i += kWave * 8)
+        *reinterpret_cast<u32x4_t*>(row + i) = u32x4_t{0, 0, 0, 0};
     }
   }
   if (lane == 0) desc[w] = opened;
