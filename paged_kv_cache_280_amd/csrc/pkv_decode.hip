@@ -33,7 +33,7 @@
 // bytes, so tiles go from HBM straight into operand registers with coalesced
 // loads, and the score MFMA's output registers are already the weight operand of
 // the value MFMA (no shuffles, no LDS).  Loads run kPipe-1 tiles ahead of the
-// arithmetic inside each segment.
+// arithmetic through the worker's whole range, across segment boundaries.
 
 #include <math.h>
 
@@ -289,106 +289,175 @@ struct Ctx {
   float* __restrict__ ws;
 };
 
-// Tiles [t0, t1) of (sequence s, KV head g); writes the output rows when the
-// segment is the whole pair, else the partial record `rec`.  Returns true when it
-// wrote a partial record.
+// Position in a worker's stream of tiles: tile t of (sequence s, KV head g); L
+// and T are the length and tile count of s, `start` the first unit of s.
+struct Cursor {
+  int64_t start;
+  int32_t s, g, t, T, L;
+};
+
+__device__ __forceinline__ void advance(Cursor& c, const int32_t* __restrict__ lens,
+                                        const DecodeDims& d, int32_t cap) {
+  if (++c.t < c.T) return;
+  c.t = 0;
+  if (++c.g < d.Hkv) return;
+  c.g = 0;
+  c.start += static_cast<int64_t>(d.Hkv) * c.T;
+  do {
+    ++c.s;
+    c.L = c.s < d.S ? clamp_len(lens[c.s], cap) : 1;  // past the batch only at the very end
+  } while (c.L == 0);
+  c.T = tiles_of(c.L);
+}
+
 template <int D, int B>
-__device__ bool run_segment(const Ctx& cx, const DecodeDims& d, int32_t s, int32_t g, int32_t t0,
-                            int32_t t1, int32_t L, int32_t T, int64_t rec, int lane) {
+__device__ __forceinline__ void load_at(TileRegs<D, B>& r, const Ctx& cx, const DecodeDims& d,
+                                        const Cursor& c, int lane) {
   constexpr int64_t kTileElems = static_cast<int64_t>(D) * B;
   PairCursor pc;
   pc.k = cx.k;
   pc.v = cx.v;
-  pc.trow = cx.tables + static_cast<int64_t>(s) * d.M;
+  pc.trow = cx.tables + static_cast<int64_t>(c.s) * d.M;
   pc.block_stride = kTileElems * d.Hkv;
-  pc.head_off = kTileElems * g;
+  pc.head_off = kTileElems * c.g;
   pc.nb = d.NB;
-  pc.nblk = (L + B - 1) / B;
+  pc.nblk = (c.L + B - 1) / B;
+  load_tile<D, B>(r, pc, c.t, lane);
+}
+
+// Score MFMA B operand: lane holds q[head lane%16][c*32 + (lane/16)*8 .. +7].
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8_t (&qop)[D / 32], const Ctx& cx, const DecodeDims& d,
+                                       const Cursor& c, int lane) {
   const int32_t h = lane & 15;
-
-  bf16x8_t qop[D / 32];
   if (h < d.G) {
-    const uint16_t* qr = cx.q + (static_cast<int64_t>(s) * d.Hq + g * d.G + h) * D + (lane >> 4) * 8;
+    const uint16_t* qr =
+        cx.q + (static_cast<int64_t>(c.s) * d.Hq + c.g * d.G + h) * D + (lane >> 4) * 8;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      qop[c] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qr + c * 32));
+    for (int k = 0; k < D / 32; ++k)
+      qop[k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qr + k * 32));
   } else {
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) qop[c] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+    for (int k = 0; k < D / 32; ++k) qop[k] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
   }
+}
 
-  SegState<D> st;
+// End of a segment: the output rows when it covered the whole pair, else a partial
+// record (O, then m, then l) in slot `rec`.
+template <int D>
+__device__ void finish_segment(const Ctx& cx, const DecodeDims& d, const SegState<D>& st,
+                               const Cursor& c, bool whole, int64_t rec, int lane) {
+  const int32_t h = lane & 15;
+  if (h >= d.G) return;
+  const float l_tot = st.l[0];
+  if (whole) {
+    const float inv = 1.0f / l_tot;
+    uint16_t* orow =
+        cx.out + (static_cast<int64_t>(c.s) * d.Hq + c.g * d.G + h) * D + (lane >> 4) * 4;
 #pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt) st.o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  st.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
+    for (int mt = 0; mt < D / 16; ++mt) {
+      bf16x4_t y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = static_cast<__bf16>(st.o[mt][i] * inv);
+      *reinterpret_cast<u32x2_t*>(orow + mt * 16) = __builtin_bit_cast(u32x2_t, y);
+    }
+  } else {
+    float* base = cx.ws + rec * record_floats(d.G, D);
+    float* orow = base + h * D + (lane >> 4) * 4;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<f32x4_t*>(orow + mt * 16) = st.o[mt];
+    if (lane < 16) {
+      base[d.G * D + h] = st.m;
+      base[d.G * D + d.G + h] = l_tot;
+    }
+  }
+}
 
-  const int32_t n = t1 - t0;
+// One worker: the tiles of units [u, u_end) in order, with loads running kPipe-1
+// tiles ahead of the arithmetic across (sequence, head) boundaries; the query of a
+// pair is fetched with the pair's first tile.  Returns the descriptor of the split
+// pair this worker opens (s = -1 if none).
+template <int D, int B>
+__device__ int4 run_worker(const Ctx& cx, const DecodeDims& d, const WorkerPlan& pl, int64_t w,
+                           int lane) {
+  const int32_t cap = d.M * B;
+  const int32_t n = static_cast<int32_t>(pl.u_end - pl.u);
+  Cursor lc;
+  lc.start = pl.start;
+  lc.s = pl.s;
+  lc.L = clamp_len(cx.lens[pl.s], cap);
+  lc.T = tiles_of(lc.L);
+  lc.g = static_cast<int32_t>((pl.u - pl.start) / lc.T);
+  lc.t = static_cast<int32_t>((pl.u - pl.start) - static_cast<int64_t>(lc.g) * lc.T);
+  Cursor cc = lc;
+
   TileRegs<D, B> r[kPipe];
-  if (n >= kPipe) {
-#pragma unroll
-    for (int i = 0; i < kPipe - 1; ++i) load_tile<D, B>(r[i], pc, t0 + i, lane);
-    int32_t i = 0;
-    // Steady state: every step computes tile i and loads tile i + kPipe - 1; the
-    // loop runs whole groups of kPipe steps whose loads all exist.
-    while (i + 2 * kPipe - 1 <= n) {
-#pragma unroll
-      for (int k = 0; k < kPipe; ++k) {
-        load_tile<D, B>(r[(k + kPipe - 1) % kPipe], pc, t0 + i + k + kPipe - 1, lane);
-        compute_tile<D, B>(r[k], qop, st, d.c, min(kTile, L - (t0 + i + k) * kTile), lane);
-      }
-      i += kPipe;
-    }
-    // Remainder: between kPipe-1 and 2*kPipe-2 tiles, the first of them still loading.
-    const int32_t rem = n - i;
-#pragma unroll
-    for (int k = 0; k < 2 * kPipe - 2; ++k) {
-      if (k < rem) {
-        if (k + kPipe - 1 < rem)
-          load_tile<D, B>(r[(k + kPipe - 1) % kPipe], pc, t0 + i + k + kPipe - 1, lane);
-        compute_tile<D, B>(r[k % kPipe], qop, st, d.c, min(kTile, L - (t0 + i + k) * kTile), lane);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < kPipe - 1; ++k)
-      if (k < n) load_tile<D, B>(r[k], pc, t0 + k, lane);
-#pragma unroll
-    for (int k = 0; k < kPipe - 1; ++k)
-      if (k < n) compute_tile<D, B>(r[k], qop, st, d.c, min(kTile, L - (t0 + k) * kTile), lane);
-  }
+  bf16x8_t qb[kPipe][D / 32];
+  bf16x8_t qc[D / 32];
+  SegState<D> st;
+  int32_t seg_t0 = cc.t;
+  int64_t rec = 2 * w;  // first segment -> slot 0, later ones -> slot 1
+  int4 opened = {-1, 0, 0, 0};
 
-  if (h < d.G) {
-    const float l_tot = st.l[0];
-    if (t0 == 0 && t1 == T) {
-      const float inv = 1.0f / l_tot;
-      uint16_t* orow = cx.out + (static_cast<int64_t>(s) * d.Hq + g * d.G + h) * D + (lane >> 4) * 4;
+  auto load_step = [&](int slot, int32_t li) {
+    if (lc.t == 0 || li == 0) load_q<D>(qb[slot], cx, d, lc, lane);
+    load_at<D, B>(r[slot], cx, d, lc, lane);
+    advance(lc, cx.lens, d, cap);
+  };
+  auto compute_step = [&](int slot, int32_t i) {
+    if (cc.t == 0 || i == 0) {
 #pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt) {
-        bf16x4_t y;
+      for (int k = 0; k < D / 32; ++k) qc[k] = qb[slot][k];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = static_cast<__bf16>(st.o[mt][i] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + mt * 16) = __builtin_bit_cast(u32x2_t, y);
+      for (int mt = 0; mt < D / 16; ++mt) st.o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      st.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      st.m = -INFINITY;
+      seg_t0 = cc.t;
+    }
+    compute_tile<D, B>(r[slot], qc, st, d.c, min(kTile, cc.L - cc.t * kTile), lane);
+    if (cc.t == cc.T - 1 || i == n - 1) {
+      const bool whole = seg_t0 == 0 && cc.t == cc.T - 1;
+      finish_segment<D>(cx, d, st, cc, whole, rec, lane);
+      if (!whole && seg_t0 == 0) {
+        // this worker holds the first share of a pair that later workers continue
+        const int64_t u0 = cc.start + static_cast<int64_t>(cc.g) * cc.T;
+        opened = int4{cc.s, cc.g, static_cast<int32_t>(worker_of(u0 + cc.T - 1, pl.U, pl.N)),
+                      static_cast<int32_t>(rec - 2 * w)};
       }
-    } else {
-      float* base = cx.ws + rec * record_floats(d.G, D);
-      float* orow = base + h * D + (lane >> 4) * 4;
+      rec = 2 * w + 1;
+    }
+    advance(cc, cx.lens, d, cap);
+  };
+
 #pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<f32x4_t*>(orow + mt * 16) = st.o[mt];
-      if (lane < 16) {
-        base[d.G * D + h] = st.m;
-        base[d.G * D + d.G + h] = l_tot;
-      }
+  for (int k = 0; k < kPipe - 1; ++k)
+    if (k < n) load_step(k, k);
+  int32_t i = 0;
+  // Whole groups of kPipe steps in which every step has a tile to load.
+  while (i + 2 * kPipe - 1 <= n) {
+#pragma unroll
+    for (int k = 0; k < kPipe; ++k) {
+      load_step((k + kPipe - 1) % kPipe, i + k + kPipe - 1);
+      compute_step(k, i + k);
+    }
+    i += kPipe;
+  }
+  const int32_t rem = n - i;  // fewer than 2*kPipe-1 tiles left, kPipe-1 of them loading
+#pragma unroll
+  for (int k = 0; k < 2 * kPipe - 2; ++k) {
+    if (k < rem) {
+      if (k + kPipe - 1 < rem) load_step((k + kPipe - 1) % kPipe, i + k + kPipe - 1);
+      compute_step(k % kPipe, i + k);
     }
   }
-  return !(t0 == 0 && t1 == T);
+  return opened;
 }
 
 // The decode kernel.  Workspace: partial records ([n_workers][2] of
 // record_floats), then one descriptor per worker: (s, g, wb, first_slot) of the
 // split pair whose first share this worker holds, or s = -1.
 template <int D, int B>
-__global__ __launch_bounds__(kWave* kWavesPerGroup, 2) void decode_kernel(
+__global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
     uint16_t* __restrict__ out, float* __restrict__ ws, int4* __restrict__ desc, DecodeDims d) {
@@ -400,39 +469,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 2) void decode_kernel(
 
   int4 opened = {-1, 0, 0, 0};
   WorkerPlan pl;
-  if (plan_worker(lens, d, cap, w, lane, pl)) {
-    const int64_t U = pl.U, N = pl.N, u_end = pl.u_end;
-    int64_t u = pl.u, start = pl.start;  // start: first unit of sequence s
-    int32_t s = pl.s;
-    int32_t L = clamp_len(lens[s], cap);
-    int32_t T = tiles_of(L);
-    int32_t g = static_cast<int32_t>((u - start) / T);
-    int32_t t = static_cast<int32_t>((u - start) - static_cast<int64_t>(g) * T);
-    int64_t rec = 2 * w;  // first segment -> slot 0, later ones -> slot 1
-    while (true) {
-      const int32_t t_end = static_cast<int32_t>(min(static_cast<int64_t>(T), t + (u_end - u)));
-      if (run_segment<D, B>(cx, d, s, g, t, t_end, L, T, rec, lane) && t == 0) {
-        // This worker holds the first share of a pair that later workers continue.
-        const int64_t u0 = start + static_cast<int64_t>(g) * T;
-        opened = int4{s, g, static_cast<int32_t>(worker_of(u0 + T - 1, U, N)),
-                      static_cast<int32_t>(rec - 2 * w)};
-      }
-      u += t_end - t;
-      if (u >= u_end) break;
-      rec = 2 * w + 1;
-      t = 0;
-      if (++g == d.Hkv) {
-        g = 0;
-        start += static_cast<int64_t>(d.Hkv) * T;
-        do {
-          ++s;
-          L = s < d.S ? clamp_len(lens[s], cap) : 1;
-        } while (L == 0);
-        if (s >= d.S) break;
-        T = tiles_of(L);
-      }
-    }
-  }
+  if (plan_worker(lens, d, cap, w, lane, pl)) opened = run_worker<D, B>(cx, d, pl, w, lane);
 
   // Rows of empty sequences are zeros (done last: off the path to the first loads).
   for (int64_t se = w; se < d.S; se += d.n_workers) {
