@@ -483,13 +483,15 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void decode_kernel(
 }
 
 // Merge of split pairs.  Work-group b reads the descriptors of its slice of
-// workers in one parallel pass and keeps the valid ones (each names a split pair
-// opened by worker wa and closed by wb).  For each such pair every thread takes
-// outputs (head, dim) in turn and folds the records of wa..wb into each in worker
-// order, kMergeChunk records per batch of independent loads, with a running max.
+// workers in one parallel pass and keeps the valid ones in LDS (each names a split
+// pair opened by worker wa and closed by wb).  The (pair, output) items of those
+// pairs are spread over the threads, kMergeItems per thread at a time; an item
+// folds the records of wa..wb in worker order with a running max, kMergeChunk
+// records per batch, and the loads of all of a thread's items are issued together.
 // The order is fixed, so the result does not depend on timing.
 constexpr int kMergeThreads = 512;
-constexpr int kMergeChunk = 16;
+constexpr int kMergeChunk = 8;
+constexpr int kMergeItems = 2;
 constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
 
 template <int D>
@@ -497,7 +499,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
                                                               uint16_t* __restrict__ out,
                                                               const float* __restrict__ ws,
                                                               DecodeDims d) {
-  __shared__ int32_t s_list[kMergeSlice];
+  __shared__ int4 s_desc[kMergeSlice];
+  __shared__ int32_t s_wa[kMergeSlice];
   __shared__ int32_t s_count;
   const int tid = threadIdx.x;
   const int64_t per = (d.n_workers + gridDim.x - 1) / gridDim.x;
@@ -505,50 +508,82 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
   const int64_t w1 = min(w0 + per, static_cast<int64_t>(d.n_workers));
   if (tid == 0) s_count = 0;
   __syncthreads();
-  if (w0 + tid < w1 && desc[w0 + tid].x >= 0) s_list[atomicAdd(&s_count, 1)] = static_cast<int32_t>(w0 + tid);
+  if (w0 + tid < w1) {
+    const int4 ds = desc[w0 + tid];
+    if (ds.x >= 0) {
+      const int32_t slot = atomicAdd(&s_count, 1);
+      s_desc[slot] = ds;
+      s_wa[slot] = static_cast<int32_t>(w0 + tid);
+    }
+  }
   __syncthreads();
-  const int32_t n = s_count;
   const int64_t rf = record_floats(d.G, D);
   const int32_t GD = d.G * D;
-  for (int32_t p = 0; p < n; ++p) {
-    const int64_t wa = s_list[p];
-    const int4 ds = desc[wa];
-    const int64_t wb = ds.z;
-    const int64_t first = (2 * wa + ds.w) * rf;  // record of wa; later workers use slot 0
-    uint16_t* orow = out + (static_cast<int64_t>(ds.x) * d.Hq + ds.y * d.G) * D;
-    for (int32_t i = tid; i < GD; i += kMergeThreads) {
-      const int32_t h = i / D;
-      float run_m = -INFINITY, run_l = 0.f, acc = 0.f;
-      for (int64_t c0 = wa; c0 <= wb; c0 += kMergeChunk) {
-        float m[kMergeChunk], l[kMergeChunk], o[kMergeChunk];
+  const int32_t total = s_count * GD;
+  for (int32_t base = tid; base < total; base += kMergeThreads * kMergeItems) {
+    float run_m[kMergeItems], run_l[kMergeItems], acc[kMergeItems];
+    int64_t wa[kMergeItems], wb[kMergeItems], first[kMergeItems];
+    int32_t pi[kMergeItems], oi[kMergeItems];
+#pragma unroll
+    for (int it = 0; it < kMergeItems; ++it) {
+      const int32_t item = base + it * kMergeThreads;
+      run_m[it] = -INFINITY;
+      run_l[it] = 0.f;
+      acc[it] = 0.f;
+      pi[it] = item < total ? item / GD : 0;
+      oi[it] = item < total ? item - pi[it] * GD : 0;
+      wa[it] = s_wa[pi[it]];
+      wb[it] = item < total ? static_cast<int64_t>(s_desc[pi[it]].z) : wa[it] - 1;  // none
+      first[it] = (2 * wa[it] + s_desc[pi[it]].w) * rf;
+    }
+    int64_t kmax = 0;
+#pragma unroll
+    for (int it = 0; it < kMergeItems; ++it) kmax = max(kmax, wb[it] - wa[it] + 1);
+    for (int64_t c = 0; c < kmax; c += kMergeChunk) {
+      float m[kMergeItems][kMergeChunk], l[kMergeItems][kMergeChunk], o[kMergeItems][kMergeChunk];
+#pragma unroll
+      for (int it = 0; it < kMergeItems; ++it) {
+        const int32_t h = oi[it] / D;
 #pragma unroll
         for (int k = 0; k < kMergeChunk; ++k) {
-          if (c0 + k <= wb) {
-            const float* rec = ws + (c0 + k == wa ? first : 2 * (c0 + k) * rf);
-            m[k] = rec[GD + h];
-            l[k] = rec[GD + d.G + h];
-            o[k] = rec[i];
+          const int64_t wk = wa[it] + c + k;
+          if (wk <= wb[it]) {
+            const float* rec = ws + (c + k == 0 ? first[it] : 2 * wk * rf);
+            m[it][k] = rec[GD + h];
+            l[it][k] = rec[GD + d.G + h];
+            o[it][k] = rec[oi[it]];
           } else {
-            m[k] = -INFINITY;
-            l[k] = 0.f;
-            o[k] = 0.f;
+            m[it][k] = -INFINITY;
+            l[it][k] = 0.f;
+            o[it][k] = 0.f;
           }
         }
-        float cm = run_m;
+      }
 #pragma unroll
-        for (int k = 0; k < kMergeChunk; ++k) cm = fmaxf(cm, m[k]);
-        const float scale = __builtin_amdgcn_exp2f(run_m - cm);
-        run_l *= scale;
-        acc *= scale;
-        run_m = cm;
+      for (int it = 0; it < kMergeItems; ++it) {
+        float cm = run_m[it];
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) cm = fmaxf(cm, m[it][k]);
+        if (cm == -INFINITY) continue;  // item past the end, or no record in this chunk
+        const float scale = __builtin_amdgcn_exp2f(run_m[it] - cm);
+        run_l[it] *= scale;
+        acc[it] *= scale;
+        run_m[it] = cm;
 #pragma unroll
         for (int k = 0; k < kMergeChunk; ++k) {
-          const float e = __builtin_amdgcn_exp2f(m[k] - cm);
-          run_l += e * l[k];
-          acc += e * o[k];
+          const float e = __builtin_amdgcn_exp2f(m[it][k] - cm);
+          run_l[it] += e * l[it][k];
+          acc[it] += e * o[it][k];
         }
       }
-      orow[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc / run_l));
+    }
+#pragma unroll
+    for (int it = 0; it < kMergeItems; ++it) {
+      if (base + it * kMergeThreads < total) {
+        const int4 ds = s_desc[pi[it]];
+        out[(static_cast<int64_t>(ds.x) * d.Hq + ds.y * d.G) * D + oi[it]] =
+            __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[it] / run_l[it]));
+      }
     }
   }
 }
