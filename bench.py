@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode: achieved KV GB/s (% of HBM peak) + decode tokens/s, 1 GPU"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_280_amd", "csrc", "pkv_decode.hip")
+CSRC = os.path.join(ROOT, "paged_kv_cache_280_amd", "csrc")
 
 
 def parse():
@@ -66,8 +66,13 @@ def copy_calibration(nbytes):
 
 
 def source_sha():
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the library sources (a counter summary is used only for the code it
+    was taken on)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload_key):

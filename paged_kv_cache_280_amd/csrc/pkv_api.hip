@@ -13,7 +13,7 @@ namespace pkv {
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kDefaultWavesPerCu = 4;
+constexpr int kDefaultWavesPerCu = 3;
 
 // Compute units of each device, read once (0 = not read yet).
 std::atomic<int> g_cu_count[kMaxDevices];
