@@ -40,7 +40,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long", choices=["long", "chat", "mix"])
+    ap.add_argument("--workload", default="long", choices=["long", "chat", "mix", "append"])
+    ap.add_argument("--with-append", action="store_true",
+                    help="each layer call first appends the new token's K/V (kv_append), "
+                         "then decodes: the full per-layer decode step")
     ap.add_argument("--block-size", type=int, default=16)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -165,10 +168,49 @@ def cpu_baseline(case, pools, layers, args):
     }
 
 
+def append_bench(args):
+    """kv_append of a prefill-sized chunk: 8 sequences x 2048 new tokens into a pool
+    with random block placement (GQA 8 KV heads, head_dim 128, block 16).  Prints
+    one JSON line with the call time and the bytes moved (rows read + slots written)."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    S, chunk, H, D, B = 8, 2048, 8, 128, args.block_size
+    case = wl.case_random(args.seed, S, 32, H, D, B, [chunk] * S)
+    _, kd, vd, tabs, _ = wl.device_tensors(case, dev, poison=False)
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    T = S * chunk
+    k_new = torch.randn((T, H, D), generator=g, device=dev).to(torch.bfloat16)
+    v_new = torch.randn((T, H, D), generator=g, device=dev).to(torch.bfloat16)
+    seq = torch.arange(S, device=dev, dtype=torch.int32).repeat_interleave(chunk)
+    pos = torch.arange(chunk, device=dev, dtype=torch.int32).repeat(S)
+    for _ in range(args.warmup):
+        pkv.kv_append(k_new, v_new, kd, vd, tabs, seq, pos, B)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        pkv.kv_append(k_new, v_new, kd, vd, tabs, seq, pos, B)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    moved = 2 * 2 * T * H * D * 2   # K and V rows: read once, written once
+    print(json.dumps({"workload": "kv_append %d tokens (8 seqs x %d), 8 KV heads, head_dim 128, "
+                      "block %d" % (T, chunk, B), "us_per_call": round(us, 2),
+                      "bytes_per_call": moved, "gbs": round(moved / us / 1e3, 1)}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.workload == "append":
+        append_bench(args)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library's decode runs on a single device "
@@ -195,9 +237,23 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_ev)]
 
+    # --with-append: the new token of every sequence (position L-1) is written
+    # into its slot before the layer's decode
+    if args.with_append:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed + 17)
+        new_k = [torch.randn((S, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+                 for _ in range(layers)]
+        new_v = [torch.randn((S, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+                 for _ in range(layers)]
+        tok_seq = torch.arange(S, device=dev, dtype=torch.int32)
+        tok_pos = (lens - 1).to(torch.int32)
+
     def step(timed_events=None):
         for layer in range(layers):
             q, k, v = pools[layer]
+            if args.with_append:
+                pkv.kv_append(new_k[layer], new_v[layer], k, v, tabs, tok_seq, tok_pos, B)
             e = timed_events[layer] if timed_events is not None else None
             if e is not None:
                 e[0].record(stream)
@@ -271,6 +327,7 @@ def main():
                    "layers": layers, "block_size": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D},
         "graph": graph is not None,
+        "with_append": bool(args.with_append),
         "kv_gbs": round(kv_gbs, 1),
         "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": "paged_attn_decode (decode_kernel + merge_kernel)",

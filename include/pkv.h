@@ -123,6 +123,32 @@ int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           void* stream);
 
 /*
+ * KV append: write the key and value rows of num_tokens new tokens into their
+ * slots.  Token i belongs to sequence token_seq[i] at position token_pos[i], and
+ * its slot is (block_tables[seq][pos / block_size], pos % block_size): the block
+ * table maps the token's logical block to a physical one ("PagedAttention
+ * (vLLM)", troisinh.com, section "Cơ chế Block Table").  One decode step appends
+ * one token per sequence (position = its new context length - 1); a prefill
+ * chunk appends many.  The block manager must have made room first, including
+ * any copy-on-write of a shared last block.
+ *
+ *   k_new, v_new  bf16 [num_tokens][num_kv_heads][head_dim], 16-byte aligned
+ *   k_cache, v_cache  the pools (layout above), written in place
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]
+ *   token_seq, token_pos  int32 [num_tokens]
+ * A token whose sequence or position lies outside [0, num_seqs) x
+ * [0, max_blocks_per_seq*block_size), or whose table entry lies outside
+ * [0, num_blocks), is skipped on the device (nothing outside the pools is
+ * written).  Two tokens must not name the same slot.  num_tokens = 0 is a no-op.
+ * The written bytes equal the input bytes (bit-exact).
+ */
+int32_t kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int32_t* block_tables, const int32_t* token_seq,
+                  const int32_t* token_pos, int32_t num_tokens, int32_t num_seqs,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t max_blocks_per_seq, int64_t num_blocks, void* stream);
+
+/*
  * Copy-on-write block copy: for every pair i and every layer l,
  *   K_l[dst_i] := K_l[src_i]  and  V_l[dst_i] := V_l[src_i]   (whole blocks, bytes).
  *

@@ -49,6 +49,8 @@ def _bind(lib):
     lib.oracle_paged_decode_probs_f32.argtypes = [p, p, p, p, p, i32, ctypes.c_float, i32,
                                                   i32, i32, i32, i32, i64, i32, i32, p, p]
     lib.oracle_paged_decode_probs_f32.restype = ctypes.c_int
+    lib.oracle_kv_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64]
+    lib.oracle_kv_append.restype = ctypes.c_int
     lib.oracle_copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32]
     lib.oracle_copy_blocks.restype = ctypes.c_int
     return lib
@@ -131,6 +133,25 @@ def paged_decode_probs(q, k_pool, v_pool, block_tables, context_lens, block_size
     return out, probs[:L]
 
 
+def kv_append(k_new, v_new, k_pool, v_pool, block_tables, token_seq, token_pos, block_size,
+              lib=None):
+    """Write new tokens' rows (bf16 bits [T][Hkv][D]) into host pools in place."""
+    kn, vn = _u16(k_new), _u16(v_new)
+    if k_pool.dtype != np.uint16 or not k_pool.flags["C_CONTIGUOUS"] or \
+            v_pool.dtype != np.uint16 or not v_pool.flags["C_CONTIGUOUS"]:
+        raise OracleError("pools must be contiguous uint16 arrays (written in place)")
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    seq = np.ascontiguousarray(token_seq, dtype=np.int32)
+    pos = np.ascontiguousarray(token_pos, dtype=np.int32)
+    T, H, D = kn.shape
+    rc = (lib or _load()).oracle_kv_append(_ptr(kn), _ptr(vn), _ptr(k_pool), _ptr(v_pool),
+                                           _ptr(tables), _ptr(seq), _ptr(pos), T,
+                                           tables.shape[0], H, D, int(block_size),
+                                           tables.shape[1], k_pool.shape[0])
+    if rc != 0:
+        raise OracleError("oracle_kv_append returned %d" % rc)
+
+
 def copy_blocks(k_pools, v_pools, pairs, lib=None):
     """Byte copy of whole blocks, in place, on lists of numpy pools (one per layer).
     ``pairs`` is int32 [P][2] of (src, dst)."""
@@ -169,3 +190,6 @@ class Variant:
 
     def copy_blocks(self, *args, **kwargs):
         return copy_blocks(*args, lib=self._lib, **kwargs)
+
+    def kv_append(self, *args, **kwargs):
+        return kv_append(*args, lib=self._lib, **kwargs)

@@ -190,6 +190,39 @@ int oracle_paged_decode_probs_f32(const uint16_t* q, const uint16_t* k_pool,
                            out_row, probs);
 }
 
+// KV append ("Cơ chế Block Table", troisinh.com): token i of sequence seq[i] at
+// position pos[i] lives in logical block pos/B at offset pos%B; the block table
+// names the physical block.  Its K and V rows (bf16 [Hkv][D]) are copied there.
+// Tokens whose sequence, position or block id is out of range are skipped.
+// Returns 0, -2 (null), -3 (bad sizes).
+int oracle_kv_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
+                     uint16_t* v_pool, const int32_t* block_tables, const int32_t* seq,
+                     const int32_t* pos, int32_t num_tokens, int32_t num_seqs,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     int32_t max_blocks_per_seq, int64_t num_blocks) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim % 8 != 0 || block_size <= 0) return -3;
+  if (num_tokens == 0) return 0;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq || !pos) return -2;
+  const Shape sh{num_seqs, num_kv_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                 num_blocks};
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int32_t s = seq[i], p = pos[i];
+    if (s < 0 || s >= num_seqs || p < 0 ||
+        static_cast<int64_t>(p) >= static_cast<int64_t>(max_blocks_per_seq) * block_size)
+      continue;
+    const int64_t b = block_tables[static_cast<int64_t>(s) * max_blocks_per_seq + p / block_size];
+    if (b < 0 || b >= num_blocks) continue;
+    const int o = p % block_size;
+    for (int g = 0; g < num_kv_heads; ++g)
+      for (int d = 0; d < head_dim; ++d) {
+        const int64_t src = (static_cast<int64_t>(i) * num_kv_heads + g) * head_dim + d;
+        k_pool[k_index(sh, b, g, o, d)] = k_new[src];
+        v_pool[v_index(sh, b, g, o, d)] = v_new[src];
+      }
+  }
+  return 0;
+}
+
 // Copy-on-write block copy ("Copy-on-Write cho Beam Search", troisinh.com): for
 // every (src, dst) pair and every layer, the bytes of block dst become the bytes
 // of block src, in K and in V; nothing else changes.  Pools are given as arrays of

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     PkvError,
     abi_version,
     copy_blocks,
+    kv_append,
     load_library,
     new_workspace,
     paged_attn_decode,

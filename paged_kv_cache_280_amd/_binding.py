@@ -22,7 +22,7 @@ STATUS_NAMES = {
 }
 
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "paged_attn_decode_workspace_bytes",
-           "paged_attn_decode", "copy_blocks")
+           "paged_attn_decode", "kv_append", "copy_blocks")
 
 
 class PkvError(RuntimeError):
@@ -53,6 +53,8 @@ def load_library(path: str = LIB_PATH):
                    sz, p]
     lib.paged_attn_decode.argtypes = decode_args
     lib.paged_attn_decode.restype = i32
+    lib.kv_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, p]
+    lib.kv_append.restype = i32
     lib.copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32, p]
     lib.copy_blocks.restype = i32
     _lib = lib
@@ -154,6 +156,37 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
     if rc != 0:
         raise PkvError(rc, "paged_attn_decode")
     return out
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos, block_size,
+              stream=None):
+    """Write new tokens' K/V rows ([T][Hkv][D] bf16) into their slots through the
+    block table (see ``include/pkv.h``).  token_seq/token_pos: int32 [T]."""
+    import torch
+
+    lib = load_library()
+    _check(k_new.dim() == 3 and v_new.shape == k_new.shape, "k_new/v_new must be [T][Hkv][D]")
+    T, Hkv, D = k_new.shape
+    B = int(block_size)
+    _check(k_cache.dim() == 5 and tuple(k_cache.shape[1:]) == (Hkv, D // 8, B, 8),
+           "k_cache must be [num_blocks][Hkv][D/8][block_size][8]")
+    NB = int(k_cache.shape[0])
+    _check(tuple(v_cache.shape) == (NB, Hkv, D, B), "v_cache must be [num_blocks][Hkv][D][block_size]")
+    for t in (k_new, v_new, k_cache, v_cache):
+        _check(t.dtype == torch.bfloat16 and t.is_contiguous(), "bf16 contiguous tensors")
+    for t in (block_tables, token_seq, token_pos):
+        _check(t.dtype == torch.int32 and t.is_contiguous(), "int32 contiguous tensors")
+    _check(token_seq.numel() == T and token_pos.numel() == T, "one sequence id and position per token")
+    _check(block_tables.dim() == 2, "block_tables must be [num_seqs][max_blocks_per_seq]")
+    devs = {t.device for t in (k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos)}
+    _check(len(devs) == 1 and k_cache.is_cuda, "all tensors must be on one GPU")
+    with torch.cuda.device(k_cache.device):
+        rc = lib.kv_append(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                           v_cache.data_ptr(), block_tables.data_ptr(), token_seq.data_ptr(),
+                           token_pos.data_ptr(), T, int(block_tables.shape[0]), Hkv, D, B,
+                           int(block_tables.shape[1]), NB, _stream_handle(k_cache, stream))
+    if rc != 0:
+        raise PkvError(rc, "kv_append")
 
 
 def copy_blocks(k_caches, v_caches, src_dst_pairs, stream=None):

@@ -171,6 +171,43 @@ int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           num_blocks, max_context_len, workspace, workspace_bytes, stream);
 }
 
+int32_t kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int32_t* block_tables, const int32_t* token_seq,
+                  const int32_t* token_pos, int32_t num_tokens, int32_t num_seqs,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t max_blocks_per_seq, int64_t num_blocks, void* stream) {
+  if (num_tokens < 0 || num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return PKV_ERR_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > 0x7fffffffLL) return PKV_ERR_SHAPE;
+  if (!pkv::supported_head_dim(head_dim) || !pkv::supported_block_size(block_size))
+    return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !token_seq || !token_pos)
+    return PKV_ERR_NULL;
+  if (!pkv::aligned16(k_new) || !pkv::aligned16(v_new) || !pkv::aligned16(k_cache) ||
+      !pkv::aligned16(v_cache))
+    return PKV_ERR_ALIGNMENT;
+  pkv::AppendBuffers b;
+  b.k_new = static_cast<const uint16_t*>(k_new);
+  b.v_new = static_cast<const uint16_t*>(v_new);
+  b.k_cache = static_cast<uint16_t*>(k_cache);
+  b.v_cache = static_cast<uint16_t*>(v_cache);
+  b.tables = block_tables;
+  b.token_seq = token_seq;
+  b.token_pos = token_pos;
+  pkv::AppendDims a;
+  a.T = num_tokens;
+  a.S = num_seqs;
+  a.Hkv = num_kv_heads;
+  a.B = block_size;
+  a.M = max_blocks_per_seq;
+  a.NB = num_blocks;
+  if (pkv::launch_append(b, a, head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PKV_ERR_LAUNCH;
+  return PKV_OK;
+}
+
 int32_t copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                     int64_t num_blocks, int64_t block_bytes, const int32_t* src_dst_pairs,
                     int32_t num_pairs, void* stream) {

@@ -53,6 +53,24 @@ inline int64_t workspace_bytes_for(int64_t workers, int G, int D) {
 hipError_t launch_decode(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                          int merge_groups, hipStream_t stream);
 
+// KV append (pkv_append.hip).
+struct AppendBuffers {
+  const uint16_t* k_new;      // bf16 [T][Hkv][D]
+  const uint16_t* v_new;      // bf16 [T][Hkv][D]
+  uint16_t* k_cache;          // K pool
+  uint16_t* v_cache;          // V pool
+  const int32_t* tables;      // int32 [S][M]
+  const int32_t* token_seq;   // int32 [T]
+  const int32_t* token_pos;   // int32 [T]
+};
+
+struct AppendDims {
+  int32_t T, S, Hkv, B, M;
+  int64_t NB;
+};
+
+hipError_t launch_append(const AppendBuffers& b, const AppendDims& a, int D, hipStream_t stream);
+
 // Launcher (pkv_copy.hip).
 hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                               int64_t num_blocks, int64_t block_bytes, const int32_t* pairs,

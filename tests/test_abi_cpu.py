@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["pkv_abi_version", "pkv_status_string",
                             "paged_attn_decode_workspace_bytes", "paged_attn_decode",
-                            "copy_blocks"])
+                            "kv_append", "copy_blocks"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -114,3 +114,18 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
             b.load_library(str(tmp_path / "missing.so"))
         finally:
             b._lib = saved
+
+
+def test_kv_append_host_checks(lib):
+    ap = lambda **o: lib.kv_append(o.get("kn", 0x1000), o.get("vn", 0x2000), o.get("kc", 0x3000),
+                                   o.get("vc", 0x4000), o.get("tab", 0x5000), o.get("ts", 0x6000),
+                                   o.get("tp", 0x7000), o.get("T", 4), o.get("S", 2),
+                                   o.get("H", 8), o.get("D", 128), o.get("B", 16), o.get("M", 4),
+                                   o.get("NB", 10), None)
+    assert ap(T=0, kn=None) == 0
+    assert ap(T=-1) == -2
+    assert ap(NB=0) == -2
+    assert ap(D=96) == -3
+    assert ap(B=12) == -3
+    assert ap(tp=None) == -1
+    assert ap(kc=0x3008) == -5

@@ -31,6 +31,7 @@ MUTATIONS = {
     "unnormalised": ("x[t] = x[t] / z;", "x[t] = x[t] / (z + Acc(1e-3));"),
     "value_from_key_slot": ("vp[v_index(sh, blk[t], g, t % sh.B, d)]",
                             "vp[v_index(sh, blk[t], g, (t + 1) % sh.B, d)]"),
+    "append_wrong_offset": ("const int o = p % block_size;", "const int o = (p + 1) % block_size;"),
     "q_head_offset": ("q + (static_cast<int64_t>(s) * sh.Hq + h) * sh.D",
                       "q + (static_cast<int64_t>(s) * sh.Hq + g) * sh.D"),
 }

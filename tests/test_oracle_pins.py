@@ -319,3 +319,29 @@ def test_oracle_copy_blocks_moves_exactly_the_named_blocks(oracle_lib):
         assert np.array_equal(ks[l][untouched], ks0[l][untouched])
         assert np.array_equal(vs[l][untouched], vs0[l][untouched])
     oracle_lib.copy_blocks(ks, vs, np.zeros((0, 2), np.int32))
+
+
+def test_oracle_kv_append_places_rows_by_the_table(oracle_lib):
+    """Rows written through the table read back, through an independent layout view
+    (einops), at (table[s][p // B], p % B); every other element is unchanged, and
+    tokens outside the table are skipped."""
+    rng = np.random.default_rng(21)
+    for B, D in ((16, 128), (8, 64), (32, 128)):
+        case = wl.case_random(int(B + D), 3, 4, 2, D, B, [3 * B + 5, B, 1])
+        kp, vp = wl.host_pools(case, poison=False)
+        kp0, vp0 = kp.copy(), vp.copy()
+        seq = np.array([0, 0, 1, 2, 0, 1, 5, 0], np.int32)
+        pos = np.array([0, 3 * B + 4, B - 1, 0, B, 0, 0, case.max_blocks_per_seq * B], np.int32)
+        kn = wl.randn_bf16(rng, (8, 2, D))
+        vn = wl.randn_bf16(rng, (8, 2, D))
+        oracle_lib.kv_append(kn, vn, kp, vp, case.block_tables, seq, pos, B)
+        kl = rearrange(kp, "n h c b e -> n h b (c e)")
+        vl = rearrange(vp, "n h d b -> n h b d")
+        kl0 = rearrange(kp0, "n h c b e -> n h b (c e)")
+        vl0 = rearrange(vp0, "n h d b -> n h b d")
+        touched = np.zeros(kl.shape[:3], bool)
+        for i in range(6):                       # the last two tokens are out of range
+            b, o = case.block_tables[seq[i], pos[i] // B], pos[i] % B
+            assert np.array_equal(kl[b, :, o], kn[i]) and np.array_equal(vl[b, :, o], vn[i])
+            touched[b, :, o] = True
+        assert np.array_equal(kl[~touched], kl0[~touched]) and np.array_equal(vl[~touched], vl0[~touched])
