@@ -49,6 +49,9 @@ def _bind(lib):
     lib.oracle_paged_decode_probs_f32.argtypes = [p, p, p, p, p, i32, ctypes.c_float, i32,
                                                   i32, i32, i32, i32, i64, i32, i32, p, p]
     lib.oracle_paged_decode_probs_f32.restype = ctypes.c_int
+    lib.oracle_paged_attn_multi_f32.argtypes = [p, p, p, p, p, p, i32, i32, ctypes.c_float, p,
+                                                 i32, i32, i32, i32, i32, i64, i32]
+    lib.oracle_paged_attn_multi_f32.restype = ctypes.c_int
     lib.oracle_kv_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64]
     lib.oracle_kv_append.restype = ctypes.c_int
     lib.oracle_copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32]
@@ -110,6 +113,26 @@ def paged_decode(q, k_pool, v_pool, block_tables, context_lens, block_size, scal
         raise ValueError(precision)
     if rc != 0:
         raise OracleError("oracle_paged_decode returned %d" % rc)
+    return out
+
+
+def paged_attn_multi(q, k_pool, v_pool, block_tables, context_lens, query_lens, block_size,
+                     scale, num_kv_heads, threads=0, lib=None):
+    """Reference multi-token attention.  q: bf16 bits [S][Qmax][Hq][D]; the last
+    query_lens[s] positions of sequence s are its query tokens, each attending
+    causally.  Returns float32 [S][Qmax][Hq][D] (rows past query_lens[s] are 0)."""
+    q, kp, vp = _u16(q), _u16(k_pool), _u16(v_pool)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qlens = np.ascontiguousarray(query_lens, dtype=np.int32)
+    S, Qmax, Hq, D = q.shape
+    out = np.zeros((S, Qmax, Hq, D), np.float32)
+    rc = (lib or _load()).oracle_paged_attn_multi_f32(
+        _ptr(q), _ptr(kp), _ptr(vp), _ptr(tables), _ptr(lens), _ptr(qlens), Qmax,
+        int(block_size), float(scale), _ptr(out), S, Hq, num_kv_heads, D, tables.shape[1],
+        kp.shape[0], int(threads))
+    if rc != 0:
+        raise OracleError("oracle_paged_attn_multi returned %d" % rc)
     return out
 
 
@@ -193,3 +216,6 @@ class Variant:
 
     def kv_append(self, *args, **kwargs):
         return kv_append(*args, lib=self._lib, **kwargs)
+
+    def paged_attn_multi(self, *args, **kwargs):
+        return paged_attn_multi(*args, lib=self._lib, **kwargs)

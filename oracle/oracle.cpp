@@ -72,24 +72,19 @@ inline int64_t v_index(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t
   return ((b * sh.Hkv + g) * sh.D + d) * sh.B + o;
 }
 
-// One (sequence, query head) pair.  Returns 0, or a negative code when the
-// inputs break the contract (a block id outside the pool).
+// One query row attending to positions 0 .. L-1 of sequence s through its table
+// row, with KV head g.  Returns 0, or -1 when a table entry lies outside the pool.
 template <typename Acc>
-int decode_one(const Shape& sh, const uint16_t* q, const uint16_t* kp, const uint16_t* vp,
-               const int32_t* tables, const int32_t* lens, Acc scale, int s, int h,
-               Acc* out_row, Acc* probs_row /* may be null; length >= L */) {
-  const int L = lens[s];
+int attend(const Shape& sh, const uint16_t* qrow, const uint16_t* kp, const uint16_t* vp,
+           const int32_t* trow, int g, int L, Acc scale, Acc* out_row,
+           Acc* probs_row /* may be null; length >= L */) {
   for (int d = 0; d < sh.D; ++d) out_row[d] = Acc(0);
   if (L == 0) return 0;
-  const int G = sh.Hq / sh.Hkv;
-  const int g = h / G;
-  const uint16_t* qrow = q + (static_cast<int64_t>(s) * sh.Hq + h) * sh.D;
-
   std::vector<Acc> x(L);
   std::vector<int64_t> blk(L);
   for (int t = 0; t < L; ++t) {
     const int j = t / sh.B;
-    const int64_t b = tables[static_cast<int64_t>(s) * sh.M + j];
+    const int64_t b = trow[j];
     if (b < 0 || b >= sh.NB) return -1;
     blk[t] = b;
     const int o = t % sh.B;
@@ -116,6 +111,18 @@ int decode_one(const Shape& sh, const uint16_t* q, const uint16_t* kp, const uin
     out_row[d] = acc;
   }
   return 0;
+}
+
+// One (sequence, query head) pair of a decode step: the query attends to all
+// context_lens[s] cached positions.
+template <typename Acc>
+int decode_one(const Shape& sh, const uint16_t* q, const uint16_t* kp, const uint16_t* vp,
+               const int32_t* tables, const int32_t* lens, Acc scale, int s, int h,
+               Acc* out_row, Acc* probs_row) {
+  const int G = sh.Hq / sh.Hkv;
+  const uint16_t* qrow = q + (static_cast<int64_t>(s) * sh.Hq + h) * sh.D;
+  return attend<Acc>(sh, qrow, kp, vp, tables + static_cast<int64_t>(s) * sh.M, h / G, lens[s],
+                     scale, out_row, probs_row);
 }
 
 template <typename Acc>
@@ -170,6 +177,55 @@ int oracle_paged_decode_f64(const uint16_t* q, const uint16_t* k_pool, const uin
   return decode_all<double>(q, k_pool, v_pool, block_tables, context_lens, block_size, scale, out,
                             num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                             num_blocks, threads);
+}
+
+// Several query tokens per sequence (speculative verification, chunked prefill):
+// sequence s holds context_lens[s] positions, the last query_lens[s] of which are
+// its query tokens; query token i sits at position p = L - query_lens[s] + i and
+// attends to positions 0 .. p (causal).  q and out are [S][max_query_len][Hq][D];
+// rows i >= query_lens[s] of out are zero.  Returns 0 or a negative code (as
+// oracle_paged_decode_f32, plus -5 for query lengths outside [0, min(L, qmax)]).
+int oracle_paged_attn_multi_f32(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                const int32_t* query_lens, int32_t max_query_len,
+                                int32_t block_size, float scale, float* out, int32_t num_seqs,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq, int64_t num_blocks, int32_t threads) {
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_lens || !out) return -2;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim % 8 != 0 ||
+      num_q_heads % num_kv_heads != 0 || max_query_len < 0 || block_size <= 0)
+    return -3;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int L = context_lens[s], T = query_lens[s];
+    if (L < 0 || static_cast<int64_t>(L) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+      return -4;
+    if (T < 0 || T > L || T > max_query_len) return -5;
+  }
+  const Shape sh{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                 num_blocks};
+  const int G = num_q_heads / num_kv_heads;
+  const int64_t rows = static_cast<int64_t>(num_seqs) * max_query_len * num_q_heads;
+  int status = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : status)
+#endif
+  for (int64_t r = 0; r < rows; ++r) {
+    const int s = static_cast<int>(r / (static_cast<int64_t>(max_query_len) * num_q_heads));
+    const int i = static_cast<int>((r / num_q_heads) % max_query_len);
+    const int h = static_cast<int>(r % num_q_heads);
+    float* orow = out + r * head_dim;
+    if (i >= query_lens[s]) {
+      for (int d = 0; d < head_dim; ++d) orow[d] = 0.f;
+      continue;
+    }
+    const int p = context_lens[s] - query_lens[s] + i;
+    const int rc = attend<float>(sh, q + r * head_dim, k_pool, v_pool,
+                                 block_tables + static_cast<int64_t>(s) * max_blocks_per_seq,
+                                 h / G, p + 1, scale, orow, nullptr);
+    if (rc < status) status = rc;
+  }
+  return status;
 }
 
 // Debug form for one (sequence, query head): writes the D outputs and the L

@@ -21,19 +21,20 @@ MUTATIONS = {
     "v_layout_dim_minor": (
         "return ((b * sh.Hkv + g) * sh.D + d) * sh.B + o;",
         "return ((b * sh.Hkv + g) * sh.B + o) * sh.D + d;"),
-    "group_by_modulo": ("const int g = h / G;", "const int g = h % sh.Hkv;"),
+    "group_by_modulo": ("h / G, lens[s],", "h % sh.Hkv, lens[s],"),
     "drop_last_token": ("for (int t = 0; t < L; ++t) {\n    const int j",
                         "for (int t = 0; t < L - (L > 1); ++t) {\n    const int j"),
     "wrong_slot": ("const int o = t % sh.B;", "const int o = (t + 1) % sh.B;"),
     "wrong_block": ("const int j = t / sh.B;", "const int j = (t / sh.B) ^ (t >= sh.B);"),
-    "no_scale": ("x[t] = scale * dot;", "x[t] = dot;"),
-    "scale_twice": ("x[t] = scale * dot;", "x[t] = scale * scale * dot * 8;"),
+    "no_scale": ("    x[t] = scale * dot;", "    x[t] = dot;"),
+    "scale_twice": ("    x[t] = scale * dot;", "    x[t] = scale * scale * dot * 8;"),
     "unnormalised": ("x[t] = x[t] / z;", "x[t] = x[t] / (z + Acc(1e-3));"),
     "value_from_key_slot": ("vp[v_index(sh, blk[t], g, t % sh.B, d)]",
                             "vp[v_index(sh, blk[t], g, (t + 1) % sh.B, d)]"),
     "append_wrong_offset": ("const int o = p % block_size;", "const int o = (p + 1) % block_size;"),
+    "causal_off_by_one": ("h / G, p + 1, scale, orow, nullptr);", "h / G, p, scale, orow, nullptr);"),
     "q_head_offset": ("q + (static_cast<int64_t>(s) * sh.Hq + h) * sh.D",
-                      "q + (static_cast<int64_t>(s) * sh.Hq + g) * sh.D"),
+                      "q + (static_cast<int64_t>(s) * sh.Hq + h / G) * sh.D"),
 }
 
 

@@ -345,3 +345,43 @@ def test_oracle_kv_append_places_rows_by_the_table(oracle_lib):
             assert np.array_equal(kl[b, :, o], kn[i]) and np.array_equal(vl[b, :, o], vn[i])
             touched[b, :, o] = True
         assert np.array_equal(kl[~touched], kl0[~touched]) and np.array_equal(vl[~touched], vl0[~touched])
+
+
+@pytest.mark.parametrize("B,D,G,qmax", [(16, 128, 4, 4), (8, 64, 1, 16), (32, 128, 8, 2)])
+def test_multi_query_oracle_matches_causal_library_attention(oracle_lib, B, D, G, qmax):
+    """Each sequence's last query_lens[s] positions attend causally: torch's fp64
+    scaled_dot_product_attention with an explicit mask on the contiguous gather."""
+    lens = [qmax + 3, 5 * B + 1, qmax, 40]
+    qlens = [qmax, 1, qmax, 0]
+    case = wl.case_random(B + D + G, len(lens), 2 * G, 2, D, B, lens)
+    rng = np.random.default_rng(qmax)
+    q = wl.randn_bf16(rng, (len(lens), qmax, 2 * G, D))
+    kp, vp = wl.host_pools(case)
+    got = oracle_lib.paged_attn_multi(q, kp, vp, case.block_tables, case.context_lens, qlens,
+                                      B, case.scale, 2)
+    kl = rearrange(wl.f32_from_bf16(kp).astype(np.float64), "n h c b e -> n h b (c e)")
+    vl = rearrange(wl.f32_from_bf16(vp).astype(np.float64), "n h d b -> n h b d")
+    for s, (L, T) in enumerate(zip(lens, qlens)):
+        ids = case.block_tables[s, : -(-L // B)]
+        assert (got[s, T:] == 0).all()
+        if T == 0:
+            continue
+        allowed = np.arange(L)[None, :] <= (L - T + np.arange(T))[:, None]   # [T][L]
+        for h in range(2 * G):
+            K = torch.from_numpy(kl[ids, h // G].reshape(-1, D)[:L])
+            V = torch.from_numpy(vl[ids, h // G].reshape(-1, D)[:L])
+            Q = torch.from_numpy(wl.f32_from_bf16(q[s, :T, h]).astype(np.float64))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                Q[None, None], K[None, None], V[None, None],
+                attn_mask=torch.from_numpy(allowed)[None, None], scale=case.scale)[0, 0].numpy()
+            assert np.abs(got[s, :T, h] - ref).max() <= 1e-5
+
+
+def test_multi_query_with_one_token_is_decode(oracle_lib):
+    case = wl.case_random(31, 3, 8, 2, 128, 16, [17, 200, 1])
+    q = wl.host_q(case)
+    kp, vp = wl.host_pools(case)
+    dec = run(oracle_lib, case, q, kp, vp)
+    multi = oracle_lib.paged_attn_multi(q[:, None], kp, vp, case.block_tables, case.context_lens,
+                                        np.ones(3, np.int32), 16, case.scale, 2)
+    assert np.array_equal(multi[:, 0].view(np.uint32), dec.view(np.uint32))
