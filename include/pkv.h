@@ -123,6 +123,54 @@ int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           void* stream);
 
 /*
+ * Bytes of device scratch paged_attn_multi needs for these sizes on the current
+ * device (the same role as paged_attn_decode_workspace_bytes).  Returns 0 for
+ * sizes paged_attn_multi would reject.
+ */
+size_t paged_attn_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_context_len,
+                                        int32_t max_query_len);
+
+/*
+ * Multi-token paged attention with a causal mask: the attention of a prefill
+ * chunk, or of the draft tokens a speculative decoding step verifies ("vLLM
+ * PagedAttention: Bước đột phá về thông lượng suy luận LLM", vi.news.hada.io,
+ * list of advanced features).  Sequence s holds L = context_lens[s] cached
+ * positions, the last T = query_lens[s] of which are its query tokens (their K/V
+ * already written, e.g. by kv_append).  Query token i sits at position
+ * p = L - T + i and attends to positions 0 .. p:
+ *
+ *   out[s][i][h][:] = sum_{t <= p} w_t * V[b_t][g][o_t][:],
+ *   w_t = softmax_{t <= p}(scale * q[s][i][h][:] . K[b_t][g][o_t][:]),
+ *
+ * for i < T, with g, b_t, o_t as in paged_attn_decode; rows i >= T of out are
+ * zero.
+ *
+ *   q, out        bf16 [num_seqs][max_query_len][num_q_heads][head_dim]; rows
+ *                 i >= query_lens[s] of q are not read
+ *   query_lens    int32 [num_seqs]; 0 <= T <= min(L, max_query_len).  Values
+ *                 outside the range are clamped into it.
+ *   max_query_len 0 is a no-op
+ *   workspace     at least paged_attn_multi_workspace_bytes(...) bytes
+ * Every other argument is as in paged_attn_decode, with the same checks, the same
+ * error codes (plus PKV_ERR_NULL for query_lens) and the same guarantees
+ * (determinism, renumbering invariance).  With max_query_len = 1 and T = 1 for
+ * every sequence of nonzero length the result equals paged_attn_decode's bit for
+ * bit.  Query tokens are processed 32 / G at a time (G = num_q_heads /
+ * num_kv_heads; up to 32 MFMA columns of (token, head) rows): an attention kernel
+ * and a merge kernel are enqueued for each of the ceil(max_query_len / (32 / G))
+ * runs of tokens, and each run reads the K/V its tokens see.
+ */
+int32_t paged_attn_multi(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_lens, int32_t max_query_len, int32_t block_size,
+                         float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                         int64_t num_blocks, int32_t max_context_len, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * KV append: write the key and value rows of num_tokens new tokens into their
  * slots.  Token i belongs to sequence token_seq[i] at position token_pos[i], and
  * its slot is (block_tables[seq][pos / block_size], pos % block_size): the block

@@ -13,8 +13,11 @@ from ._binding import (  # noqa: F401
     copy_blocks,
     kv_append,
     load_library,
+    new_multi_workspace,
     new_workspace,
     paged_attn_decode,
     paged_attn_decode_workspace_bytes,
+    paged_attn_multi,
+    paged_attn_multi_workspace_bytes,
     status_string,
 )

@@ -22,7 +22,8 @@ STATUS_NAMES = {
 }
 
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "paged_attn_decode_workspace_bytes",
-           "paged_attn_decode", "kv_append", "copy_blocks")
+           "paged_attn_decode", "paged_attn_multi_workspace_bytes", "paged_attn_multi",
+           "kv_append", "copy_blocks")
 
 
 class PkvError(RuntimeError):
@@ -53,6 +54,11 @@ def load_library(path: str = LIB_PATH):
                    sz, p]
     lib.paged_attn_decode.argtypes = decode_args
     lib.paged_attn_decode.restype = i32
+    lib.paged_attn_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.paged_attn_multi_workspace_bytes.restype = sz
+    lib.paged_attn_multi.argtypes = [p, p, p, p, p, p, i32, i32, ctypes.c_float, p, i32, i32, i32,
+                                     i32, i32, i64, i32, p, sz, p]
+    lib.paged_attn_multi.restype = i32
     lib.kv_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, p]
     lib.kv_append.restype = i32
     lib.copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32, p]
@@ -155,6 +161,64 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
                                    _stream_handle(q, stream))
     if rc != 0:
         raise PkvError(rc, "paged_attn_decode")
+    return out
+
+
+def paged_attn_multi_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                     max_context_len, max_query_len) -> int:
+    return int(load_library().paged_attn_multi_workspace_bytes(
+        int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
+        int(max_context_len), int(max_query_len)))
+
+
+def new_multi_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                        max_context_len, max_query_len, device):
+    """A workspace tensor for paged_attn_multi with these sizes."""
+    import torch
+
+    with torch.cuda.device(device):
+        need = paged_attn_multi_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                block_size, max_context_len, max_query_len)
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+
+
+def paged_attn_multi(q, k_cache, v_cache, block_tables, context_lens, query_lens, block_size,
+                     scale, out=None, *, max_context_len=None, workspace=None, stream=None):
+    """Multi-token paged attention with a causal mask (see ``include/pkv.h``).
+    ``q`` is [num_seqs][max_query_len][num_q_heads][head_dim] bf16, ``query_lens``
+    int32 [num_seqs].  Returns ``out`` (same shape as q; rows past a sequence's
+    query tokens are zero)."""
+    import torch
+
+    lib = load_library()
+    _check(q.dim() == 4, "q must be [num_seqs][max_query_len][num_q_heads][head_dim]")
+    S, Q, Hq, D = q.shape
+    _check(q.is_contiguous(), "q must be contiguous")
+    # the pools, tables and lengths are checked as for decode, on q seen as [S][Q*Hq][D]
+    _, _, Hkv, _, NB, M = decode_shapes(q.view(S, Q * Hq, D), k_cache, v_cache, block_tables,
+                                        context_lens, block_size)
+    _check(query_lens.dim() == 1 and query_lens.shape[0] == S and query_lens.dtype == torch.int32
+           and query_lens.is_contiguous() and query_lens.device == q.device,
+           "query_lens must be contiguous int32 [num_seqs] on q's device")
+    if max_context_len is None:
+        max_context_len = M * int(block_size)
+    with torch.cuda.device(q.device):
+        if out is None:
+            out = torch.empty_like(q)
+        _check(out.shape == q.shape and out.dtype == torch.bfloat16 and out.is_contiguous()
+               and out.device == q.device, "out must match q")
+        if workspace is None:
+            workspace = new_multi_workspace(S, Hq, Hkv, D, block_size, max_context_len, Q, q.device)
+        _check(workspace.is_cuda and workspace.device == q.device and workspace.is_contiguous(),
+               "workspace must be a contiguous tensor on q's device")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        rc = lib.paged_attn_multi(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                  block_tables.data_ptr(), context_lens.data_ptr(),
+                                  query_lens.data_ptr(), Q, int(block_size), float(scale),
+                                  out.data_ptr(), S, Hq, Hkv, D, M, NB, int(max_context_len),
+                                  workspace.data_ptr(), ws_bytes, _stream_handle(q, stream))
+    if rc != 0:
+        raise PkvError(rc, "paged_attn_multi")
     return out
 
 

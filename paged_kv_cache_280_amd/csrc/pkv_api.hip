@@ -60,6 +60,13 @@ size_t workspace_for(int64_t workers, int32_t group, int32_t head_dim) {
   return static_cast<size_t>(workspace_bytes_for(workers, group, head_dim));
 }
 
+// Merge work-groups: one per compute unit, each scanning at most 64 worker slots.
+int merge_groups_for(int64_t workers, int cu) {
+  int64_t g = workers < cu ? workers : cu;
+  if (g * 64 < workers) g = (workers + 63) / 64;
+  return static_cast<int>(g);
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int32_t check_shapes(int32_t block_size, float scale, int32_t num_seqs, int32_t num_q_heads,
@@ -104,6 +111,7 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
   b.v = static_cast<const uint16_t*>(v_cache);
   b.tables = block_tables;
   b.lens = context_lens;
+  b.qlens = nullptr;
   b.out = static_cast<uint16_t*>(out);
   b.ws = static_cast<float*>(workspace);
   DecodeDims d;
@@ -115,13 +123,84 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
   d.n_workers = static_cast<int32_t>(workers);
   d.NB = num_blocks;
   d.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+  d.Qmax = 1;
+  d.Qc = 1;
+  d.q_off = 0;
+  d.R = group;
   hipStream_t s = static_cast<hipStream_t>(stream);
-
-  // merge work-groups: one per compute unit, each scanning at most 64 worker slots
-  int64_t merge_groups = workers < cu ? workers : cu;
-  if (merge_groups * 64 < workers) merge_groups = (workers + 63) / 64;
-  if (launch_decode(b, d, head_dim, block_size, static_cast<int>(merge_groups), s) != hipSuccess)
+  if (launch_decode(b, d, head_dim, block_size, merge_groups_for(workers, cu), s) != hipSuccess)
     return PKV_ERR_LAUNCH;
+  return PKV_OK;
+}
+
+// Query tokens one multi-token launch covers: as many as fill kMaxRows MFMA
+// columns (at least one), never more than max_query_len.
+int32_t tokens_per_launch(int32_t group, int32_t max_query_len) {
+  const int32_t t = kMaxRows / group;
+  return t < max_query_len ? t : max_query_len;
+}
+
+size_t multi_workspace_for(int64_t workers, int32_t group, int32_t head_dim, int32_t max_query_len) {
+  return static_cast<size_t>(
+      workspace_bytes_for(workers, group * tokens_per_launch(group, max_query_len), head_dim));
+}
+
+int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* query_lens, int32_t max_query_len, int32_t block_size,
+                   float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                   int64_t num_blocks, int32_t max_context_len, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const int32_t st = check_shapes(block_size, scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  max_blocks_per_seq, num_blocks, max_context_len);
+  if (st != PKV_OK) return st;
+  if (max_query_len < 0) return PKV_ERR_SHAPE;
+  if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_lens || !out ||
+      !workspace)
+    return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(workspace))
+    return PKV_ERR_ALIGNMENT;
+  const int cu = current_cu_count();
+  if (cu <= 0) return PKV_ERR_DEVICE;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const int64_t workers = worker_count(cu, num_seqs, num_kv_heads, max_context_len);
+  if (workspace_bytes < multi_workspace_for(workers, group, head_dim, max_query_len))
+    return PKV_ERR_WORKSPACE;
+
+  DecodeDims d;
+  d.S = num_seqs;
+  d.Hq = num_q_heads;
+  d.Hkv = num_kv_heads;
+  d.G = group;
+  d.M = max_blocks_per_seq;
+  d.n_workers = static_cast<int32_t>(workers);
+  d.NB = num_blocks;
+  d.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+  d.Qmax = max_query_len;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t per = tokens_per_launch(group, max_query_len);
+  const int64_t token_elems = static_cast<int64_t>(num_q_heads) * head_dim;
+  // One launch pair (attention, merge) per run of `per` query tokens; each
+  // launch reads the K/V its tokens see.
+  for (int32_t off = 0; off < max_query_len; off += per) {
+    d.q_off = off;
+    d.Qc = per < max_query_len - off ? per : max_query_len - off;
+    d.R = group * d.Qc;
+    DecodeBuffers b;
+    b.q = static_cast<const uint16_t*>(q) + off * token_elems;
+    b.k = static_cast<const uint16_t*>(k_cache);
+    b.v = static_cast<const uint16_t*>(v_cache);
+    b.tables = block_tables;
+    b.lens = context_lens;
+    b.qlens = query_lens;
+    b.out = static_cast<uint16_t*>(out) + off * token_elems;
+    b.ws = static_cast<float*>(workspace);
+    if (launch_multi(b, d, head_dim, block_size, merge_groups_for(workers, cu), s) != hipSuccess)
+      return PKV_ERR_LAUNCH;
+  }
   return PKV_OK;
 }
 
@@ -169,6 +248,34 @@ int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
   return pkv::decode_impl(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, out,
                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                           num_blocks, max_context_len, workspace, workspace_bytes, stream);
+}
+
+size_t paged_attn_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t block_size, int32_t max_context_len,
+                                        int32_t max_query_len) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+      max_query_len < 0 || num_q_heads % num_kv_heads != 0 || !pkv::supported_head_dim(head_dim) ||
+      !pkv::supported_block_size(block_size) || num_q_heads / num_kv_heads > pkv::kMaxGroup)
+    return 0;
+  const int cu = pkv::current_cu_count();
+  if (cu <= 0) return 0;
+  const int64_t workers = pkv::worker_count(cu, num_seqs, num_kv_heads, max_context_len);
+  return pkv::multi_workspace_for(workers, num_q_heads / num_kv_heads, head_dim,
+                                  max_query_len > 0 ? max_query_len : 1);
+}
+
+int32_t paged_attn_multi(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_lens, int32_t max_query_len, int32_t block_size,
+                         float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                         int64_t num_blocks, int32_t max_context_len, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return pkv::multi_impl(q, k_cache, v_cache, block_tables, context_lens, query_lens,
+                         max_query_len, block_size, scale, out, num_seqs, num_q_heads,
+                         num_kv_heads, head_dim, max_blocks_per_seq, num_blocks, max_context_len,
+                         workspace, workspace_bytes, stream);
 }
 
 int32_t kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -34,6 +34,15 @@
 // loads, and the score MFMA's output registers are already the weight operand of
 // the value MFMA (no shuffles, no LDS).  Loads run kPipe-1 tiles ahead of the
 // arithmetic through the worker's whole range, across segment boundaries.
+//
+// Multi-token launches (a prefill chunk, or the draft tokens a speculative step
+// verifies: "vLLM PagedAttention: Bước đột phá về thông lượng suy luận LLM",
+// vi.news.hada.io, list of advanced features).  A sequence's query tokens are its
+// last T positions; query token i sits at position L - T + i and sees positions
+// 0 .. L - T + i.  The MFMA columns then hold (query token, head) rows of the
+// pair, one or two 16-column tiles per wave, each column with its own position
+// limit; every K/V tile is loaded once for all of them.  A pair's tiles stop at
+// the last position its last query token sees.
 
 #include <math.h>
 
@@ -48,7 +57,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kPipe = 3;                  // tile buffers in registers (kPipe-1 loads in flight)
+// Tile buffers in registers (kPipe-1 loads in flight).  Two column tiles of
+// 128-dim rows leave room for two buffers only.
+template <int D, int NC>
+constexpr int pipe_depth() {
+  return (NC == 2 && D == 128) ? 2 : 3;
+}
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: weights stay below 2^8
 
 __device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -78,25 +92,58 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x, int lane) {
   return x;
 }
 
+// Context a launch processes for sequence s.  Decode: L = context_lens[s], one
+// query token.  Multi-token launch: the sequence's query tokens are its last
+// T = query_lens[s] positions (T clamped into [0, min(L, Qmax)]); the launch
+// takes the Tc of them in [q_off, q_off + Qc), and its context ends at the
+// position the last of those sees, so L_c = L - T + q_off + Tc (0 when Tc = 0).
+struct SeqLen {
+  int32_t L, T;
+};
+
+template <bool kCausal>
+__device__ __forceinline__ SeqLen seq_len(const int32_t* __restrict__ lens,
+                                          const int32_t* __restrict__ qlens, const DecodeDims& d,
+                                          int32_t cap, int32_t s) {
+  const int32_t L = clamp_len(lens[s], cap);
+  if constexpr (!kCausal) {
+    return SeqLen{L, 1};
+  } else {
+    const int32_t T = clamp_len(qlens[s], min(L, d.Qmax));
+    const int32_t Tc = clamp_len(T - d.q_off, d.Qc);
+    return SeqLen{Tc > 0 ? L - T + d.q_off + Tc : 0, Tc};
+  }
+}
+
+template <bool kCausal>
+__device__ __forceinline__ int32_t seq_tiles(const int32_t* __restrict__ lens,
+                                             const int32_t* __restrict__ qlens, const DecodeDims& d,
+                                             int32_t cap, int32_t s) {
+  return s < d.S ? tiles_of(seq_len<kCausal>(lens, qlens, d, cap, s).L) : 0;
+}
+
 // Work units (tiles) of sequences [0, s_end): Hkv * sum ceil(L_s / 16).
-__device__ int64_t units_before(const int32_t* __restrict__ lens, const DecodeDims& d,
-                                int32_t cap, int32_t s_end, int lane) {
+template <bool kCausal>
+__device__ int64_t units_before(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
+                                const DecodeDims& d, int32_t cap, int32_t s_end, int lane) {
   int64_t tot = 0;
   for (int32_t base = 0; base < s_end; base += kWave) {
     const int32_t s = base + lane;
-    const int32_t T = s < s_end ? tiles_of(clamp_len(lens[s], cap)) : 0;
+    const int32_t T = s < s_end ? seq_tiles<kCausal>(lens, qlens, d, cap, s) : 0;
     tot += uniform(wave_sum(T));
   }
   return tot * d.Hkv;
 }
 
 // The sequence whose unit range contains unit u, and the first unit of that range.
-__device__ void locate(const int32_t* __restrict__ lens, const DecodeDims& d, int32_t cap,
-                       int64_t u, int lane, int32_t& s_out, int64_t& start_out) {
+template <bool kCausal>
+__device__ void locate(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
+                       const DecodeDims& d, int32_t cap, int64_t u, int lane, int32_t& s_out,
+                       int64_t& start_out) {
   int64_t acc = 0;
   for (int32_t base = 0; base < d.S; base += kWave) {
     const int32_t s = base + lane;
-    const int32_t T = s < d.S ? tiles_of(clamp_len(lens[s], cap)) : 0;
+    const int32_t T = seq_tiles<kCausal>(lens, qlens, d, cap, s);
     const int32_t incl = wave_inclusive_scan(T, lane);
     const int64_t chunk_units =
         static_cast<int64_t>(__builtin_amdgcn_readlane(incl, kWave - 1)) * d.Hkv;
@@ -132,10 +179,11 @@ struct WorkerPlan {
 
 // Returns false when worker w has no range.  With at most kWave sequences the
 // lengths are read once and scanned in registers; otherwise in two passes.
-__device__ bool plan_worker(const int32_t* __restrict__ lens, const DecodeDims& d, int32_t cap,
-                            int64_t w, int lane, WorkerPlan& p) {
+template <bool kCausal>
+__device__ bool plan_worker(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
+                            const DecodeDims& d, int32_t cap, int64_t w, int lane, WorkerPlan& p) {
   if (d.S <= kWave) {
-    const int32_t T = lane < d.S ? tiles_of(clamp_len(lens[lane], cap)) : 0;
+    const int32_t T = seq_tiles<kCausal>(lens, qlens, d, cap, lane);
     const int32_t incl = wave_inclusive_scan(T, lane);
     p.U = static_cast<int64_t>(__builtin_amdgcn_readlane(incl, kWave - 1)) * d.Hkv;
     p.N = min(static_cast<int64_t>(d.n_workers), p.U);
@@ -148,12 +196,12 @@ __device__ bool plan_worker(const int32_t* __restrict__ lens, const DecodeDims& 
     p.start = static_cast<int64_t>(__builtin_amdgcn_readlane(incl - T, first)) * d.Hkv;
     return true;
   }
-  p.U = units_before(lens, d, cap, d.S, lane);
+  p.U = units_before<kCausal>(lens, qlens, d, cap, d.S, lane);
   p.N = min(static_cast<int64_t>(d.n_workers), p.U);
   if (w >= p.N) return false;
   p.u = range_begin(w, p.U, p.N);
   p.u_end = range_begin(w + 1, p.U, p.N);
-  locate(lens, d, cap, p.u, lane, p.s, p.start);
+  locate<kCausal>(lens, qlens, d, cap, p.u, lane, p.s, p.start);
   return true;
 }
 
@@ -213,32 +261,82 @@ __device__ __forceinline__ void load_tile(TileRegs<D, B>& r, const PairCursor& p
   }
 }
 
-// Softmax state of one wave over one segment.
+// Softmax state of one wave's column tile over one segment.
 template <int D>
 struct SegState {
-  f32x4_t o[D / 16];  // O^T[dim mt*16 + (lane/16)*4 + i][head lane%16]
-  f32x4_t l;          // every entry: sum of the bf16 weights of head lane%16
-  float m;            // reference max of head lane%16 (log2 domain)
+  f32x4_t o[D / 16];  // O^T[dim mt*16 + (lane/16)*4 + i][column lane%16]
+  f32x4_t l;          // every entry: sum of the bf16 weights of column lane%16
+  float m;            // reference max of column lane%16 (log2 domain)
 };
 
-// One tile: scores, softmax weights, value and sum accumulation.  `valid` is the
-// number of tokens of the tile inside the context (16 except in the last tile).
-template <int D, int B>
-__device__ __forceinline__ void compute_tile(TileRegs<D, B>& r, const bf16x8_t (&qop)[D / 32],
-                                             SegState<D>& st, float c, int32_t valid, int lane) {
-  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+// Column n = j*16 + lane%16 of column tile j is row n of a (sequence, KV head)
+// pair: query token qi = n / G of head n % G.  `row` is the offset of its q and
+// out row from the pair's first row (qi*Hq + n % G), or -1 when n >= R.
+template <int NC>
+struct Cols {
+  int32_t qi[NC];
+  int32_t row[NC];
+};
+
+template <int NC, bool kCausal>
+__device__ __forceinline__ Cols<NC> make_cols(const DecodeDims& d, int lane) {
+  Cols<NC> cl;
 #pragma unroll
-  for (int cc = 0; cc < D / 32; ++cc)
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[cc]), qop[cc],
-                                                 sc, 0, 0, 0);
+  for (int j = 0; j < NC; ++j) {
+    const int32_t n = j * 16 + (lane & 15);
+    if constexpr (kCausal) {
+      const int32_t qi = n / d.G;
+      cl.qi[j] = qi;
+      cl.row[j] = n < d.R ? qi * d.Hq + (n - qi * d.G) : -1;
+    } else {  // one query token: R = G
+      cl.qi[j] = 0;
+      cl.row[j] = n < d.G ? n : -1;
+    }
+  }
+  return cl;
+}
+
+// One tile for NC column tiles: scores, softmax weights, value and sum
+// accumulation.  `valid` is the number of tokens of the tile inside the context
+// (16 except in the last tile).  Multi-token launches also mask by position:
+// column j of this lane sees the tile's tokens 0 .. lim[j], and lim_lo is the
+// smallest lim of the wave (nothing is masked by position when lim_lo >= 15).
+template <int D, int B, int NC, bool kCausal>
+__device__ __forceinline__ void compute_tile(TileRegs<D, B>& r, const bf16x8_t (&qop)[NC][D / 32],
+                                             SegState<D> (&st)[NC], float c, int32_t valid,
+                                             int32_t lim_lo, const int32_t (&lim)[NC], int lane) {
+  f32x4_t sc[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    sc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < D / 32; ++cc)
+      sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[cc]),
+                                                      qop[j][cc], sc[j], 0, 0, 0);
+  }
   const int32_t tq = (lane >> 4) * 4;  // first of the four tokens this lane scores
-  float x[4];
+  float x[NC][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = fmaf(sc[i], c, -st.m);
+  for (int j = 0; j < NC; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[j][i] = fmaf(sc[j][i], c, -st[j].m);
+  if constexpr (kCausal) {
+    if (lim_lo < kTile - 1) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tq + i > lim[j]) x[j][i] = -INFINITY;
+    }
+  } else {
+    if (valid < kTile) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tq + i >= valid) x[0][i] = -INFINITY;
+    }
+  }
   if (valid < kTile) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (tq + i >= valid) x[i] = -INFINITY;
+    // V rows past the context are zeroed: their slots may hold anything
     const int32_t n = valid - tq;
     const uint64_t keep = n >= 4 ? ~0ull : (n <= 0 ? 0ull : ((1ull << (16 * n)) - 1));
 #pragma unroll
@@ -247,36 +345,50 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, B>& r, const bf16x8_t (
       r.v[mt].y &= static_cast<uint32_t>(keep >> 32);
     }
   }
-  const bool over = x[0] > kRescaleThreshold || x[1] > kRescaleThreshold ||
-                    x[2] > kRescaleThreshold || x[3] > kRescaleThreshold;
+  bool over = false;
+#pragma unroll
+  for (int j = 0; j < NC; ++j)
+    over = over || x[j][0] > kRescaleThreshold || x[j][1] > kRescaleThreshold ||
+           x[j][2] > kRescaleThreshold || x[j][3] > kRescaleThreshold;
   if (__ballot(over)) {
-    // Move the reference max of every head up to its max over everything seen so
-    // far (always taken on a segment's first tile, where m = -inf and x = +inf).
-    float sv[4];
+    // Move the reference max of every column up to its max over everything seen
+    // so far (always taken on a segment's first tile, where m = -inf and x = +inf).
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = (valid < kTile && tq + i >= valid) ? -INFINITY : sc[i] * c;
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    for (int j = 0; j < NC; ++j) {
+      float sv[4];
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) st.o[mt] *= alpha;
-    st.l *= alpha;
-    st.m = m_new;
+      for (int i = 0; i < 4; ++i) {
+        const bool masked = kCausal ? tq + i > lim[j] : (valid < kTile && tq + i >= valid);
+        sv[i] = masked ? -INFINITY : sc[j][i] * c;
+      }
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(st[j].m, mx);
+      // a column that has seen no position yet keeps m = -inf and weights 0
+      const float m_ref = (kCausal && m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(st[j].m - m_ref);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = sv[i] - m_new;
+      for (int mt = 0; mt < D / 16; ++mt) st[j].o[mt] *= alpha;
+      st[j].l *= alpha;
+      st[j].m = m_new;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[j][i] = sv[i] - m_ref;
+    }
   }
-  bf16x4_t pb;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pb[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[i]));
-#pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt)
-    st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, r.v[mt]), pb,
-                                                         st.o[mt], 0, 0, 0);
   const bf16x4_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f),
                          static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  st.l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, st.l, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    bf16x4_t pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[j][i]));
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+      st[j].o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+          __builtin_bit_cast(bf16x4_t, r.v[mt]), pb, st[j].o[mt], 0, 0, 0);
+    st[j].l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, st[j].l, 0, 0, 0);
+  }
 }
 
 struct Ctx {
@@ -285,19 +397,22 @@ struct Ctx {
   const uint16_t* __restrict__ v;
   const int32_t* __restrict__ tables;
   const int32_t* __restrict__ lens;
+  const int32_t* __restrict__ qlens;
   uint16_t* __restrict__ out;
   float* __restrict__ ws;
 };
 
 // Position in a worker's stream of tiles: tile t of (sequence s, KV head g); L
-// and T are the length and tile count of s, `start` the first unit of s.
+// and T are the context and tile count of s in this launch, Tq its query tokens,
+// `start` the first unit of s.
 struct Cursor {
   int64_t start;
-  int32_t s, g, t, T, L;
+  int32_t s, g, t, T, L, Tq;
 };
 
-__device__ __forceinline__ void advance(Cursor& c, const int32_t* __restrict__ lens,
-                                        const DecodeDims& d, int32_t cap) {
+template <bool kCausal>
+__device__ __forceinline__ void advance(Cursor& c, const Ctx& cx, const DecodeDims& d,
+                                        int32_t cap) {
   if (++c.t < c.T) return;
   c.t = 0;
   if (++c.g < d.Hkv) return;
@@ -305,7 +420,14 @@ __device__ __forceinline__ void advance(Cursor& c, const int32_t* __restrict__ l
   c.start += static_cast<int64_t>(d.Hkv) * c.T;
   do {
     ++c.s;
-    c.L = c.s < d.S ? clamp_len(lens[c.s], cap) : 1;  // past the batch only at the very end
+    if (c.s < d.S) {
+      const SeqLen sl = seq_len<kCausal>(cx.lens, cx.qlens, d, cap, c.s);
+      c.L = sl.L;
+      c.Tq = sl.T;
+    } else {
+      c.L = 1;  // past the batch only at the very end
+      c.Tq = 1;
+    }
   } while (c.L == 0);
   c.T = tiles_of(c.L);
 }
@@ -325,50 +447,79 @@ __device__ __forceinline__ void load_at(TileRegs<D, B>& r, const Ctx& cx, const 
   load_tile<D, B>(r, pc, c.t, lane);
 }
 
-// Score MFMA B operand: lane holds q[head lane%16][c*32 + (lane/16)*8 .. +7].
-template <int D>
-__device__ __forceinline__ void load_q(bf16x8_t (&qop)[D / 32], const Ctx& cx, const DecodeDims& d,
-                                       const Cursor& c, int lane) {
-  const int32_t h = lane & 15;
-  if (h < d.G) {
-    const uint16_t* qr =
-        cx.q + (static_cast<int64_t>(c.s) * d.Hq + c.g * d.G + h) * D + (lane >> 4) * 8;
+// First q/out row of a (sequence, KV head) pair.
+template <bool kCausal>
+__device__ __forceinline__ int64_t pair_row(const DecodeDims& d, const Cursor& c) {
+  const int64_t seq_rows = kCausal ? static_cast<int64_t>(d.Qmax) * d.Hq : d.Hq;
+  return c.s * seq_rows + c.g * d.G;
+}
+
+// Rows of a pair (R = G in decode launches).
+template <bool kCausal>
+__device__ __forceinline__ int32_t pair_rows(const DecodeDims& d) {
+  return kCausal ? d.R : d.G;
+}
+
+// True when column j of this lane is a row the launch computes.
+template <int NC, bool kCausal>
+__device__ __forceinline__ bool live(const Cols<NC>& cl, int j, const Cursor& c) {
+  return cl.row[j] >= 0 && (!kCausal || cl.qi[j] < c.Tq);
+}
+
+// Score MFMA B operand: lane holds q[row of column j][c*32 + (lane/16)*8 .. +7];
+// zeros for columns the launch does not compute.
+template <int D, int NC, bool kCausal>
+__device__ __forceinline__ void load_q(bf16x8_t (&qop)[NC][D / 32], const Ctx& cx,
+                                       const DecodeDims& d, const Cursor& c, const Cols<NC>& cl,
+                                       int lane) {
+  const int64_t r0 = pair_row<kCausal>(d, c);
 #pragma unroll
-    for (int k = 0; k < D / 32; ++k)
-      qop[k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qr + k * 32));
-  } else {
+  for (int j = 0; j < NC; ++j) {
+    if (live<NC, kCausal>(cl, j, c)) {
+      const uint16_t* qr = cx.q + (r0 + cl.row[j]) * D + (lane >> 4) * 8;
 #pragma unroll
-    for (int k = 0; k < D / 32; ++k) qop[k] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+      for (int k = 0; k < D / 32; ++k)
+        qop[j][k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qr + k * 32));
+    } else {
+#pragma unroll
+      for (int k = 0; k < D / 32; ++k)
+        qop[j][k] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
+    }
   }
 }
 
 // End of a segment: the output rows when it covered the whole pair, else a partial
 // record (O, then m, then l) in slot `rec`.
-template <int D>
-__device__ void finish_segment(const Ctx& cx, const DecodeDims& d, const SegState<D>& st,
-                               const Cursor& c, bool whole, int64_t rec, int lane) {
-  const int32_t h = lane & 15;
-  if (h >= d.G) return;
-  const float l_tot = st.l[0];
-  if (whole) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* orow =
-        cx.out + (static_cast<int64_t>(c.s) * d.Hq + c.g * d.G + h) * D + (lane >> 4) * 4;
+template <int D, int NC, bool kCausal>
+__device__ void finish_segment(const Ctx& cx, const DecodeDims& d, const SegState<D> (&st)[NC],
+                               const Cursor& c, const Cols<NC>& cl, bool whole, int64_t rec,
+                               int lane) {
+  const int64_t r0 = pair_row<kCausal>(d, c);
+  const int32_t R = pair_rows<kCausal>(d);
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      bf16x4_t y;
+  for (int j = 0; j < NC; ++j) {
+    if (!live<NC, kCausal>(cl, j, c)) continue;
+    const float l_tot = st[j].l[0];
+    if (whole) {
+      const float inv = 1.0f / l_tot;
+      uint16_t* orow = cx.out + (r0 + cl.row[j]) * D + (lane >> 4) * 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = static_cast<__bf16>(st.o[mt][i] * inv);
-      *reinterpret_cast<u32x2_t*>(orow + mt * 16) = __builtin_bit_cast(u32x2_t, y);
-    }
-  } else {
-    float* base = cx.ws + rec * record_floats(d.G, D);
-    float* orow = base + h * D + (lane >> 4) * 4;
+      for (int mt = 0; mt < D / 16; ++mt) {
+        bf16x4_t y;
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<f32x4_t*>(orow + mt * 16) = st.o[mt];
-    if (lane < 16) {
-      base[d.G * D + h] = st.m;
-      base[d.G * D + d.G + h] = l_tot;
+        for (int i = 0; i < 4; ++i) y[i] = static_cast<__bf16>(st[j].o[mt][i] * inv);
+        *reinterpret_cast<u32x2_t*>(orow + mt * 16) = __builtin_bit_cast(u32x2_t, y);
+      }
+    } else {
+      const int32_t n = j * 16 + (lane & 15);
+      float* base = cx.ws + rec * record_floats(R, D);
+      float* orow = base + n * D + (lane >> 4) * 4;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<f32x4_t*>(orow + mt * 16) = st[j].o[mt];
+      if (lane < 16) {
+        base[R * D + n] = st[j].m;
+        base[R * D + R + n] = l_tot;
+      }
     }
   }
 }
@@ -377,56 +528,79 @@ __device__ void finish_segment(const Ctx& cx, const DecodeDims& d, const SegStat
 // tiles ahead of the arithmetic across (sequence, head) boundaries; the query of a
 // pair is fetched with the pair's first tile.  Returns the descriptor of the split
 // pair this worker opens (s = -1 if none).
-template <int D, int B>
+template <int D, int B, int NC, bool kCausal>
 __device__ int4 run_worker(const Ctx& cx, const DecodeDims& d, const WorkerPlan& pl, int64_t w,
                            int lane) {
   const int32_t cap = d.M * B;
   const int32_t n = static_cast<int32_t>(pl.u_end - pl.u);
+  const Cols<NC> cl = make_cols<NC, kCausal>(d, lane);
   Cursor lc;
   lc.start = pl.start;
   lc.s = pl.s;
-  lc.L = clamp_len(cx.lens[pl.s], cap);
+  {
+    const SeqLen sl = seq_len<kCausal>(cx.lens, cx.qlens, d, cap, pl.s);
+    lc.L = sl.L;
+    lc.Tq = sl.T;
+  }
   lc.T = tiles_of(lc.L);
   lc.g = static_cast<int32_t>((pl.u - pl.start) / lc.T);
   lc.t = static_cast<int32_t>((pl.u - pl.start) - static_cast<int64_t>(lc.g) * lc.T);
   Cursor cc = lc;
 
+  constexpr int kPipe = pipe_depth<D, NC>();
   TileRegs<D, B> r[kPipe];
-  bf16x8_t qb[kPipe][D / 32];
-  bf16x8_t qc[D / 32];
-  SegState<D> st;
+  bf16x8_t qb[kPipe][NC][D / 32];
+  bf16x8_t qc[NC][D / 32];
+  SegState<D> st[NC];
+  int32_t lim_abs[NC];  // last position column j sees (multi-token launches)
   int32_t seg_t0 = cc.t;
   int64_t rec = 2 * w;  // first segment -> slot 0, later ones -> slot 1
   int4 opened = {-1, 0, 0, 0};
 
   auto load_step = [&](int slot, int32_t li) {
-    if (lc.t == 0 || li == 0) load_q<D>(qb[slot], cx, d, lc, lane);
+    if (lc.t == 0 || li == 0) load_q<D, NC, kCausal>(qb[slot], cx, d, lc, cl, lane);
     load_at<D, B>(r[slot], cx, d, lc, lane);
-    advance(lc, cx.lens, d, cap);
+    advance<kCausal>(lc, cx, d, cap);
   };
   auto compute_step = [&](int slot, int32_t i) {
     if (cc.t == 0 || i == 0) {
 #pragma unroll
-      for (int k = 0; k < D / 32; ++k) qc[k] = qb[slot][k];
+      for (int j = 0; j < NC; ++j) {
 #pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt) st.o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      st.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      st.m = -INFINITY;
+        for (int k = 0; k < D / 32; ++k) qc[j][k] = qb[slot][j][k];
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) st[j].o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        st[j].l = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        st[j].m = -INFINITY;
+        // query token qi sits at position L - Tq + qi; other columns see the context
+        lim_abs[j] = live<NC, kCausal>(cl, j, cc) ? cc.L - cc.Tq + cl.qi[j] : cc.L - 1;
+      }
       seg_t0 = cc.t;
     }
-    compute_tile<D, B>(r[slot], qc, st, d.c, min(kTile, cc.L - cc.t * kTile), lane);
+    const int32_t valid = min(kTile, cc.L - cc.t * kTile);
+    if constexpr (kCausal) {
+      int32_t lim[NC];
+#pragma unroll
+      for (int j = 0; j < NC; ++j) lim[j] = lim_abs[j] - cc.t * kTile;
+      compute_tile<D, B, NC, true>(r[slot], qc, st, d.c, valid, cc.L - cc.Tq - cc.t * kTile, lim,
+                                   lane);
+    } else {
+      const int32_t lim[NC] = {valid - 1};
+      compute_tile<D, B, NC, false>(r[slot], qc, st, d.c, valid, valid - 1, lim, lane);
+    }
     if (cc.t == cc.T - 1 || i == n - 1) {
       const bool whole = seg_t0 == 0 && cc.t == cc.T - 1;
-      finish_segment<D>(cx, d, st, cc, whole, rec, lane);
+      finish_segment<D, NC, kCausal>(cx, d, st, cc, cl, whole, rec, lane);
       if (!whole && seg_t0 == 0) {
         // this worker holds the first share of a pair that later workers continue
         const int64_t u0 = cc.start + static_cast<int64_t>(cc.g) * cc.T;
+        const int32_t slot_tq = static_cast<int32_t>(rec - 2 * w) | (kCausal ? cc.Tq << 1 : 0);
         opened = int4{cc.s, cc.g, static_cast<int32_t>(worker_of(u0 + cc.T - 1, pl.U, pl.N)),
-                      static_cast<int32_t>(rec - 2 * w)};
+                      slot_tq};
       }
       rec = 2 * w + 1;
     }
-    advance(cc, cx.lens, d, cap);
+    advance<kCausal>(cc, cx, d, cap);
   };
 
 #pragma unroll
@@ -453,15 +627,17 @@ __device__ int4 run_worker(const Ctx& cx, const DecodeDims& d, const WorkerPlan&
   return opened;
 }
 
-// The decode kernel.  Workspace: partial records ([n_workers][2] of
-// record_floats), then one descriptor per worker: (s, g, wb, first_slot) of the
-// split pair whose first share this worker holds, or s = -1.
-template <int D, int B>
+// The decode kernel (NC = 1, no position mask) and the multi-token kernel.
+// Workspace: partial records ([n_workers][2] of record_floats), then one
+// descriptor per worker: (s, g, wb, first_slot | Tq << 1) of the split pair whose
+// first share this worker holds, or s = -1 (Tq only in multi-token launches).
+template <int D, int B, int NC, bool kCausal>
 __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
-    uint16_t* __restrict__ out, float* __restrict__ ws, int4* __restrict__ desc, DecodeDims d) {
-  const Ctx cx{q, k, v, tables, lens, out, ws};
+    const int32_t* __restrict__ qlens, uint16_t* __restrict__ out, float* __restrict__ ws,
+    int4* __restrict__ desc, DecodeDims d) {
+  const Ctx cx{q, k, v, tables, lens, qlens, out, ws};
   const int lane = __lane_id();
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
   if (w >= d.n_workers) return;
@@ -469,14 +645,25 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void decode_kernel(
 
   int4 opened = {-1, 0, 0, 0};
   WorkerPlan pl;
-  if (plan_worker(lens, d, cap, w, lane, pl)) opened = run_worker<D, B>(cx, d, pl, w, lane);
+  if (plan_worker<kCausal>(lens, qlens, d, cap, w, lane, pl))
+    opened = run_worker<D, B, NC, kCausal>(cx, d, pl, w, lane);
 
-  // Rows of empty sequences are zeros (done last: off the path to the first loads).
+  // Rows no tile reaches are zeros: every row of an empty sequence, and in a
+  // multi-token launch the rows past a sequence's query tokens (done last: off
+  // the path to the first loads).
+  const int32_t row_elems = d.Hq * D;
   for (int64_t se = w; se < d.S; se += d.n_workers) {
-    if (clamp_len(lens[se], cap) == 0) {
-      uint16_t* row = out + se * d.Hq * D;
-      for (int32_t i = lane * 8; i < d.Hq * D; i += kWave * 8)
-        *reinterpret_cast<u32x4_t*>(row + i) = u32x4_t{0, 0, 0, 0};
+    int32_t first = 0;
+    if constexpr (kCausal) {
+      first = seq_len<true>(lens, qlens, d, cap, static_cast<int32_t>(se)).T;
+    } else {
+      if (clamp_len(lens[se], cap) != 0) continue;
+    }
+    const int32_t rows = kCausal ? d.Qc : 1;
+    for (int32_t qi = first; qi < rows; ++qi) {
+      uint16_t* row = out + (kCausal ? se * d.Qmax + qi : se) * row_elems;
+      for (int32_t e = lane * 8; e < row_elems; e += kWave * 8)
+        *reinterpret_cast<u32x4_t*>(row + e) = u32x4_t{0, 0, 0, 0};
     }
   }
   if (lane == 0) desc[w] = opened;
@@ -488,13 +675,14 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void decode_kernel(
 // pairs are spread over the threads, kMergeItems per thread at a time; an item
 // folds the records of wa..wb in worker order with a running max, kMergeChunk
 // records per batch, and the loads of all of a thread's items are issued together.
-// The order is fixed, so the result does not depend on timing.
+// The order is fixed, so the result does not depend on timing.  In multi-token
+// launches the rows past the pair's query tokens are left to the decode kernel.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeChunk = 8;
 constexpr int kMergeItems = 2;
 constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
 
-template <int D>
+template <int D, bool kCausal>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __restrict__ desc,
                                                               uint16_t* __restrict__ out,
                                                               const float* __restrict__ ws,
@@ -517,24 +705,27 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
     }
   }
   __syncthreads();
-  const int64_t rf = record_floats(d.G, D);
-  const int32_t GD = d.G * D;
-  const int32_t total = s_count * GD;
+  const int64_t rf = record_floats(d.R, D);
+  const int32_t RD = d.R * D;
+  const int32_t total = s_count * RD;
   for (int32_t base = tid; base < total; base += kMergeThreads * kMergeItems) {
     float run_m[kMergeItems], run_l[kMergeItems], acc[kMergeItems];
     int64_t wa[kMergeItems], wb[kMergeItems], first[kMergeItems];
     int32_t pi[kMergeItems], oi[kMergeItems];
+    bool act[kMergeItems];
 #pragma unroll
     for (int it = 0; it < kMergeItems; ++it) {
       const int32_t item = base + it * kMergeThreads;
       run_m[it] = -INFINITY;
       run_l[it] = 0.f;
       acc[it] = 0.f;
-      pi[it] = item < total ? item / GD : 0;
-      oi[it] = item < total ? item - pi[it] * GD : 0;
+      pi[it] = item < total ? item / RD : 0;
+      oi[it] = item < total ? item - pi[it] * RD : 0;
+      act[it] = item < total;
+      if constexpr (kCausal) act[it] = act[it] && (oi[it] / D) / d.G < (s_desc[pi[it]].w >> 1);
       wa[it] = s_wa[pi[it]];
-      wb[it] = item < total ? static_cast<int64_t>(s_desc[pi[it]].z) : wa[it] - 1;  // none
-      first[it] = (2 * wa[it] + s_desc[pi[it]].w) * rf;
+      wb[it] = act[it] ? static_cast<int64_t>(s_desc[pi[it]].z) : wa[it] - 1;  // none
+      first[it] = (2 * wa[it] + (s_desc[pi[it]].w & 1)) * rf;
     }
     int64_t kmax = 0;
 #pragma unroll
@@ -549,8 +740,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
           const int64_t wk = wa[it] + c + k;
           if (wk <= wb[it]) {
             const float* rec = ws + (c + k == 0 ? first[it] : 2 * wk * rf);
-            m[it][k] = rec[GD + h];
-            l[it][k] = rec[GD + d.G + h];
+            m[it][k] = rec[RD + h];
+            l[it][k] = rec[RD + d.R + h];
             o[it][k] = rec[oi[it]];
           } else {
             m[it][k] = -INFINITY;
@@ -579,43 +770,64 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
     }
 #pragma unroll
     for (int it = 0; it < kMergeItems; ++it) {
-      if (base + it * kMergeThreads < total) {
+      if (act[it]) {
         const int4 ds = s_desc[pi[it]];
-        out[(static_cast<int64_t>(ds.x) * d.Hq + ds.y * d.G) * D + oi[it]] =
-            __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[it] / run_l[it]));
+        int64_t idx;
+        if constexpr (kCausal) {
+          const int32_t row = oi[it] / D;  // row = qi * G + head
+          const int32_t qi = row / d.G;
+          idx = ((static_cast<int64_t>(ds.x) * d.Qmax + qi) * d.Hq + ds.y * d.G + (row - qi * d.G)) *
+                    D + (oi[it] - row * D);
+        } else {
+          idx = (static_cast<int64_t>(ds.x) * d.Hq + ds.y * d.G) * D + oi[it];
+        }
+        out[idx] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[it] / run_l[it]));
       }
     }
   }
 }
 
-template <int D, int B>
+template <int D, int B, int NC, bool kCausal>
 hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
                     hipStream_t stream) {
   const int groups = (d.n_workers + kWavesPerGroup - 1) / kWavesPerGroup;
   if (groups <= 0) return hipSuccess;
   int4* desc = reinterpret_cast<int4*>(reinterpret_cast<char*>(b.ws) +
-                                       records_bytes(d.n_workers, d.G, D));
-  hipLaunchKernelGGL((decode_kernel<D, B>), dim3(groups), dim3(kWave * kWavesPerGroup), 0, stream,
-                     b.q, b.k, b.v, b.tables, b.lens, b.out, b.ws, desc, d);
+                                       records_bytes(d.n_workers, d.R, D));
+  hipLaunchKernelGGL((decode_kernel<D, B, NC, kCausal>), dim3(groups), dim3(kWave * kWavesPerGroup),
+                     0, stream, b.q, b.k, b.v, b.tables, b.lens, b.qlens, b.out, b.ws, desc, d);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(merge_groups), dim3(kMergeThreads), 0, stream, desc,
-                     b.out, b.ws, d);
+  hipLaunchKernelGGL((merge_kernel<D, kCausal>), dim3(merge_groups), dim3(kMergeThreads), 0, stream,
+                     desc, b.out, b.ws, d);
   return hipGetLastError();
+}
+
+template <int NC, bool kCausal>
+hipError_t dispatch(const DecodeBuffers& b, const DecodeDims& d, int D, int B, int merge_groups,
+                    hipStream_t stream) {
+  if (D == 128) {
+    if (B == 16) return launch_t<128, 16, NC, kCausal>(b, d, merge_groups, stream);
+    if (B == 32) return launch_t<128, 32, NC, kCausal>(b, d, merge_groups, stream);
+    if (B == 8) return launch_t<128, 8, NC, kCausal>(b, d, merge_groups, stream);
+  } else if (D == 64) {
+    if (B == 16) return launch_t<64, 16, NC, kCausal>(b, d, merge_groups, stream);
+    if (B == 32) return launch_t<64, 32, NC, kCausal>(b, d, merge_groups, stream);
+    if (B == 8) return launch_t<64, 8, NC, kCausal>(b, d, merge_groups, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                          int merge_groups, hipStream_t stream) {
-  if (D == 128) {
-    if (B == 16) return launch_t<128, 16>(b, d, merge_groups, stream);
-    if (B == 32) return launch_t<128, 32>(b, d, merge_groups, stream);
-    if (B == 8) return launch_t<128, 8>(b, d, merge_groups, stream);
-  } else if (D == 64) {
-    if (B == 16) return launch_t<64, 16>(b, d, merge_groups, stream);
-    if (B == 32) return launch_t<64, 32>(b, d, merge_groups, stream);
-    if (B == 8) return launch_t<64, 8>(b, d, merge_groups, stream);
-  }
+  return dispatch<1, false>(b, d, D, B, merge_groups, stream);
+}
+
+hipError_t launch_multi(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                        int merge_groups, hipStream_t stream) {
+  if (d.R <= 16) return dispatch<1, true>(b, d, D, B, merge_groups, stream);
+  if (d.R <= kMaxRows) return dispatch<2, true>(b, d, D, B, merge_groups, stream);
   return hipErrorInvalidValue;
 }
 

@@ -16,42 +16,55 @@ constexpr int kMaxLayers = 128; // copy_blocks pool pointers travel as kernel ar
 // Buffers of one decode call.  The kernels take them as separate __restrict__
 // parameters so that reads of the block table and lengths become scalar loads.
 struct DecodeBuffers {
-  const uint16_t* q;        // bf16 [S][Hq][D]
+  const uint16_t* q;        // bf16 [S][Qmax][Hq][D], offset to the launch's first query token
   const uint16_t* k;        // K pool
   const uint16_t* v;        // V pool
   const int32_t* tables;    // int32 [S][M]
   const int32_t* lens;      // int32 [S]
-  uint16_t* out;            // bf16 [S][Hq][D]
+  const int32_t* qlens;     // int32 [S] query tokens per sequence (multi-token launches only)
+  uint16_t* out;            // bf16, same layout and offset as q
   float* ws;                // workspace: partial records, then per-worker descriptors
 };
 
-// Sizes of one decode call (passed by value).
+// Sizes of one launch (passed by value).  A decode launch has one query token
+// per sequence (Qmax = Qc = 1, q_off = 0, R = G).  A multi-token launch covers
+// query tokens [q_off, q_off + Qc) of every sequence; each (sequence, KV head)
+// pair then has R = G * Qc rows, row n being query token n / G of head n % G.
 struct DecodeDims {
   int32_t S, Hq, Hkv, G, M;
   int32_t n_workers;        // workers launched; the kernels use min(n_workers, units)
   int64_t NB;
   float c;                  // scale * log2(e): scores are kept in the log2 domain
+  int32_t Qmax;             // query-token stride of q and out
+  int32_t Qc;               // query tokens of this launch
+  int32_t q_off;            // first query token of this launch
+  int32_t R;                // rows of a (sequence, KV head) pair: G * Qc
 };
 
-// Floats in one partial record: O[G][D], then m[G], then l[G], padded to a
+// Floats in one partial record: O[R][D], then m[R], then l[R], padded to a
 // multiple of four floats so every record starts 16-byte aligned.
-__host__ __device__ inline int64_t record_floats(int G, int D) {
-  return static_cast<int64_t>(G) * D + ((2 * G + 3) / 4) * 4;
+__host__ __device__ inline int64_t record_floats(int R, int D) {
+  return static_cast<int64_t>(R) * D + ((2 * R + 3) / 4) * 4;
 }
 
-// Workspace of a decode call: partial records ([n_workers][2][record_floats]),
-// then one 16-byte descriptor per worker.
-__host__ __device__ inline int64_t records_bytes(int64_t workers, int G, int D) {
-  return workers * 2 * record_floats(G, D) * static_cast<int64_t>(sizeof(float));
+// Workspace of a launch: partial records ([n_workers][2][record_floats]), then
+// one 16-byte descriptor per worker.
+__host__ __device__ inline int64_t records_bytes(int64_t workers, int R, int D) {
+  return workers * 2 * record_floats(R, D) * static_cast<int64_t>(sizeof(float));
 }
-inline int64_t workspace_bytes_for(int64_t workers, int G, int D) {
-  return records_bytes(workers, G, D) + workers * 16;
+inline int64_t workspace_bytes_for(int64_t workers, int R, int D) {
+  return records_bytes(workers, R, D) + workers * 16;
 }
 
-// Launches the decode kernel and the merge kernel (pkv_decode.hip).  Returns a
-// hipError_t.
+// Rows one multi-token launch can hold: two 16-column MFMA tiles per wave.
+constexpr int kMaxRows = 32;
+
+// Launch the decode kernel and the merge kernel (pkv_decode.hip).  Return a
+// hipError_t.  launch_multi takes a multi-token launch (d.R <= kMaxRows).
 hipError_t launch_decode(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                          int merge_groups, hipStream_t stream);
+hipError_t launch_multi(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                        int merge_groups, hipStream_t stream);
 
 // KV append (pkv_append.hip).
 struct AppendBuffers {

@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["pkv_abi_version", "pkv_status_string",
                             "paged_attn_decode_workspace_bytes", "paged_attn_decode",
+                            "paged_attn_multi_workspace_bytes", "paged_attn_multi",
                             "kv_append", "copy_blocks"])
 
 
@@ -84,6 +85,34 @@ def test_decode_rejects_bad_arguments_on_the_host(lib, over, code):
 
 def test_decode_with_no_sequences_is_a_no_op(lib):
     assert _decode_call(lib, S=0, q=None, out=None) == 0
+
+
+def _multi_call(lib, **over):
+    """Call paged_attn_multi with fake (never dereferenced) pointers."""
+    a = dict(q=0x1000, k=0x2000, v=0x3000, tables=0x4000, lens=0x5000, qlens=0x5800, Q=4,
+             block_size=16, scale=0.125, out=0x6000, S=2, Hq=8, Hkv=2, D=128, M=4, NB=10,
+             max_ctx=64, ws=0x7000, ws_bytes=1 << 20, stream=None)
+    a.update(over)
+    return lib.paged_attn_multi(a["q"], a["k"], a["v"], a["tables"], a["lens"], a["qlens"], a["Q"],
+                                a["block_size"], a["scale"], a["out"], a["S"], a["Hq"], a["Hkv"],
+                                a["D"], a["M"], a["NB"], a["max_ctx"], a["ws"], a["ws_bytes"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(Q=-1), -2),                   # negative max_query_len
+    (dict(max_ctx=65), -2),
+    (dict(D=96), -3),
+    (dict(Hq=34, Hkv=1), -3),
+    (dict(qlens=None), -1),
+    (dict(q=None), -1),
+    (dict(q=0x1008), -5),
+    (dict(S=0, q=None, out=None, qlens=None), 0),   # nothing to do
+    (dict(Q=0, q=None, out=None), 0),
+])
+def test_multi_rejects_bad_arguments_on_the_host(lib, over, code):
+    assert _multi_call(lib, **over) == code
 
 
 def test_copy_blocks_host_checks(lib):
