@@ -12,7 +12,12 @@ Prints one JSON line: decode tokens/s (value), KV GB/s, the roofline of the main
 decode kernel (HIP events around every launch in the timed region) and the CPU
 oracle timed on a bounded sample of the same workload.
 
-Other workloads (--workload chat|mix) are for measurements beside the headline.
+Other workloads (--workload chat|mix|prefix|tiny) are for measurements beside the
+headline; prefix also times the copy-on-write copy_blocks call, and counts the
+shared prefix's bytes once (unique positions read) beside the logical bytes.
+--query-tokens T > 1 times multi-token attention instead of decode: every
+sequence verifies T query tokens (its last T positions, causal), as a
+speculative decoding step does; value is then query tokens/s.
 """
 
 from __future__ import annotations
@@ -31,6 +36,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "paged decode: achieved KV GB/s (% of HBM peak) + decode tokens/s, 1 GPU"
+METRIC_MULTI = ("paged multi-token attention (T causal query tokens per sequence): achieved KV "
+                "GB/s (% of HBM peak) + query tokens/s, 1 GPU")
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 CSRC = os.path.join(ROOT, "paged_kv_cache_280_amd", "csrc")
 
@@ -40,11 +47,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long", choices=["long", "chat", "mix", "append"])
+    ap.add_argument("--workload", default="long",
+                    choices=["long", "chat", "mix", "prefix", "tiny", "append"])
     ap.add_argument("--with-append", action="store_true",
                     help="each layer call first appends the new token's K/V (kv_append), "
                          "then decodes: the full per-layer decode step")
     ap.add_argument("--block-size", type=int, default=16)
+    ap.add_argument("--query-tokens", type=int, default=1,
+                    help="T > 1: multi-token attention, T causal query tokens per sequence")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -92,11 +102,42 @@ def measured_traffic(workload_key):
     return t.get("hbm_bytes_per_call")
 
 
+def prefix_case(args):
+    """Shared-prefix parallel sampling: 16 prompts x 8 samples, a 1020-token prefix
+    stored once per prompt, tails U_int[0, 256], built by the block manager (which
+    queues the copy-on-write pairs).  Returns (case, pairs, unique positions)."""
+    import workloads as wl
+    from paged_kv_cache_280_amd.block_manager import BlockManager
+
+    sc = wl.prefix_script(args.seed, prefix_len=1020, block_size=args.block_size)
+    bm = BlockManager(sc.num_blocks, sc.block_size, sc.free_order)
+    seqs = []
+    for p in range(sc.num_prompts):
+        bm.add(("prompt", p), sc.prefix_len)
+        for k in range(sc.num_samples):
+            bm.fork(("prompt", p), (p, k))
+            seqs.append((p, k))
+        bm.free(("prompt", p))
+    for (p, k) in seqs:
+        bm.append((p, k), int(sc.tails[p, k]))
+    pairs = bm.take_copies()
+    pad = int(bm.free_ids()[0]) if bm.num_free else 0
+    tables, lens = bm.batch(seqs, pad_block=pad)
+    B = sc.block_size
+    pos = np.concatenate([tables[i, np.arange(L) // B].astype(np.int64) * B + np.arange(L) % B
+                          for i, L in enumerate(lens)])
+    case = wl.Case("prefix", len(seqs), sc.num_q_heads, sc.num_kv_heads, sc.head_dim, B,
+                   sc.num_blocks, lens, tables, sc.scale, num_layers=16, poison_block=pad,
+                   seed=args.seed)
+    return case, pairs, int(np.unique(pos).size)
+
+
 def build_workload(args, dev):
     import torch
 
     import workloads as wl
 
+    extra = {}
     if args.workload == "long":
         case = wl.case_long(args.seed, block_size=args.block_size)
         layers = case.num_layers
@@ -110,6 +151,18 @@ def build_workload(args, dev):
         layers = 16
         desc = ("chat-batch decode: 64 seqs, 16 layers, 32 q / 8 KV heads, head_dim 128, "
                 "block %d" % case.block_size)
+    elif args.workload == "prefix":
+        # 16 layers with their own pools (2.2 GB), so the unique 134 MB of a layer
+        # is not served from the last-level cache by the previous step
+        case, pairs, unique = prefix_case(args)
+        layers = case.num_layers
+        extra = {"pairs": pairs, "unique_tokens": unique}
+        desc = ("shared-prefix sampling: 16 prompts x 8 samples, prefix 1020 stored once, tails "
+                "U[0,256], 16 layers, 32 q / 8 KV heads, head_dim 128, block %d" % case.block_size)
+    elif args.workload == "tiny":
+        case = wl.case_tiny(args.seed)
+        layers = 1
+        desc = "tiny decode: 1 seq x 100 tokens, 4 q / 4 KV heads, head_dim 64, block 16"
     else:
         case = wl.case_mix(args.seed, args.block_size)
         layers = 1
@@ -120,13 +173,14 @@ def build_workload(args, dev):
         q, k, v, tabs, lens = wl.device_tensors(case, dev, layer=layer)
         pools.append((q, k, v))
     torch.cuda.synchronize()
-    return case, layers, desc, pools, tabs, lens
+    return case, layers, desc, pools, tabs, lens, extra
 
 
 def cpu_baseline(case, pools, layers, args):
     """The oracle on the host cores over a bounded sample of the same workload:
     whole (layer, sequence) pairs in order until about ``--cpu-seconds`` of oracle
-    time, scaled by context tokens to the full step."""
+    time, scaled by context tokens to the full step.  With several query tokens the
+    oracle's multi-token attention runs on the same q rows the GPU reads."""
     import torch
 
     import oracle
@@ -146,8 +200,13 @@ def cpu_baseline(case, pools, layers, args):
             qh = q[s:s + 1].view(torch.int16).cpu().numpy().view(np.uint16)
             tab = np.arange(nb, dtype=np.int32)[None, :]
             t0 = time.perf_counter()
-            oracle.paged_decode(qh, kh, vh, tab, np.array([L], np.int32), case.block_size,
-                                case.scale, case.num_kv_heads, threads=threads)
+            if args.query_tokens > 1:
+                oracle.paged_attn_multi(qh, kh, vh, tab, np.array([L], np.int32),
+                                        np.array([args.query_tokens], np.int32), case.block_size,
+                                        case.scale, case.num_kv_heads, threads=threads)
+            else:
+                oracle.paged_decode(qh, kh, vh, tab, np.array([L], np.int32), case.block_size,
+                                    case.scale, case.num_kv_heads, threads=threads)
             elapsed += time.perf_counter() - t0
             done_tokens += L
             pairs_done += 1
@@ -157,15 +216,94 @@ def cpu_baseline(case, pools, layers, args):
             break
     total_tokens = int(case.context_lens.sum()) * layers
     step_seconds = elapsed * total_tokens / max(done_tokens, 1)
+    # one core: the last sampled pair again, single-threaded
+    t0 = time.perf_counter()
+    if args.query_tokens > 1:
+        oracle.paged_attn_multi(qh, kh, vh, tab, np.array([L], np.int32),
+                                np.array([args.query_tokens], np.int32), case.block_size,
+                                case.scale, case.num_kv_heads, threads=1)
+    else:
+        oracle.paged_decode(qh, kh, vh, tab, np.array([L], np.int32), case.block_size,
+                            case.scale, case.num_kv_heads, threads=1)
+    one_core_step = (time.perf_counter() - t0) * total_tokens / max(L, 1)
     return {
-        "value": round(case.num_seqs / step_seconds, 4),
+        "value": round(case.num_seqs * args.query_tokens / step_seconds, 4),
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
         "sample": "%d of %d (layer, sequence) pairs, %d context tokens, %.1f s of oracle time on "
                   "%d threads, scaled by context tokens to the full step"
                   % (pairs_done, case.num_seqs * layers, done_tokens, elapsed, threads),
+        "one_core_value": round(case.num_seqs * args.query_tokens / one_core_step, 4),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
     }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def copy_blocks_timing(pools, pairs, args):
+    """The copy-on-write copy_blocks call of the shared-prefix workload (every
+    layer's K and V pool in one call), timed with HIP events.  Copying again is
+    harmless: sources are never destinations."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    dev = pools[0][1].device
+    pd = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).to(dev)
+    ks, vs = [p[1] for p in pools], [p[2] for p in pools]
+    for _ in range(3):
+        pkv.copy_blocks(ks, vs, pd)
+    torch.cuda.synchronize()
+    reps = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        pkv.copy_blocks(ks, vs, pd)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    block_bytes = ks[0][0].numel() * ks[0].element_size()
+    moved = 2 * 2 * len(pairs) * len(ks) * block_bytes  # K and V: read src, write dst
+    return {"pairs": int(len(pairs)), "layers": len(ks), "us_per_call": round(us, 2),
+            "bytes_per_call": int(moved), "gbs": round(moved / us / 1e3, 1)}
+
+
+def attainable_bandwidth(nbytes=4 << 30, reps=10):
+    """Plain device streams on the same GPU in the same run: a 4 GiB read (torch
+    column sums of a [4096][n] float32 view: one pass over the bytes, 1 MB written)
+    and a 4 GiB copy (bytes read + written)."""
+    import torch
+
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn, moved in (("read", lambda: x.view(4096, -1).sum(0), nbytes),
+                            ("copy", lambda: y.copy_(x), 2 * nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name + "_gbs"] = round(moved * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    res["kernels"] = ("torch column sums over a 4 GiB float32 [4096][n] view (read); torch copy "
+                      "of 4 GiB (read + write)")
+    return res
 
 
 def append_bench(args):
@@ -224,30 +362,48 @@ def main():
     pkv.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    case, layers, desc, pools, tabs, lens = build_workload(args, dev)
+    case, layers, desc, pools, tabs, lens, extra = build_workload(args, dev)
     S, Hq, Hkv, D, B = (case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
                         case.block_size)
     max_ctx = case.max_context_len
-    ws = pkv.new_workspace(S, Hq, Hkv, D, B, max_ctx, dev)
+    T = args.query_tokens
+    multi = T > 1
+    if multi:
+        # q of every layer becomes [S][T][Hq][D]; each sequence's last T positions
+        # are its query tokens
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed + 29)
+        pools = [(torch.randn((S, T, Hq, D), generator=gen, device=dev).to(torch.bfloat16), k, v)
+                 for (_, k, v) in pools]
+        qlens = torch.full((S,), T, dtype=torch.int32, device=dev)
+        desc += ", %d causal query tokens per sequence" % T
+        ws = pkv.new_multi_workspace(S, Hq, Hkv, D, B, max_ctx, T, dev)
+    else:
+        ws = pkv.new_workspace(S, Hq, Hkv, D, B, max_ctx, dev)
     outs = [torch.empty_like(p[0]) for p in pools]
-    per_call_bytes = decode_algorithmic_bytes(case.context_lens, Hq, Hkv, D, B)
+    per_call_bytes = decode_algorithmic_bytes(case.context_lens, Hq, Hkv, D, B, query_tokens=T,
+                                              unique_tokens=extra.get("unique_tokens"))
+    logical_bytes = decode_algorithmic_bytes(case.context_lens, Hq, Hkv, D, B, query_tokens=T)
 
     stream = torch.cuda.current_stream(dev)
     n_ev = args.steps * layers
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n_ev)]
 
-    # --with-append: the new token of every sequence (position L-1) is written
-    # into its slot before the layer's decode
+    # --with-append: the K/V of every sequence's newest T positions (T = 1: the
+    # token being decoded, position L-1) are written into their slots before the
+    # layer's attention
     if args.with_append:
         gen = torch.Generator(device=dev)
         gen.manual_seed(args.seed + 17)
-        new_k = [torch.randn((S, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+        new_k = [torch.randn((S * T, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
                  for _ in range(layers)]
-        new_v = [torch.randn((S, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+        new_v = [torch.randn((S * T, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
                  for _ in range(layers)]
-        tok_seq = torch.arange(S, device=dev, dtype=torch.int32)
-        tok_pos = (lens - 1).to(torch.int32)
+        # the T newest positions of every sequence (T = 1: the token being decoded)
+        tok_seq = torch.arange(S, device=dev, dtype=torch.int32).repeat_interleave(T)
+        tok_pos = (lens.repeat_interleave(T) - T +
+                   torch.arange(T, device=dev, dtype=torch.int32).repeat(S)).to(torch.int32)
 
     def step(timed_events=None):
         for layer in range(layers):
@@ -257,8 +413,12 @@ def main():
             e = timed_events[layer] if timed_events is not None else None
             if e is not None:
                 e[0].record(stream)
-            pkv.paged_attn_decode(q, k, v, tabs, lens, B, case.scale, outs[layer],
-                                  workspace=ws, max_context_len=max_ctx)
+            if multi:
+                pkv.paged_attn_multi(q, k, v, tabs, lens, qlens, B, case.scale, outs[layer],
+                                     workspace=ws, max_context_len=max_ctx)
+            else:
+                pkv.paged_attn_decode(q, k, v, tabs, lens, B, case.scale, outs[layer],
+                                      workspace=ws, max_context_len=max_ctx)
             if e is not None:
                 e[1].record(stream)
 
@@ -304,14 +464,17 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     kern_ms = [a.elapsed_time(b) for a, b in ev]
     kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    p10, p50, p90 = (float(x) * 1e3 for x in np.percentile(kern_ms, [10, 50, 90]))
+    copy_line = copy_blocks_timing(pools, extra["pairs"], args) if "pairs" in extra else None
+    attain = attainable_bandwidth()
     step_bytes = per_call_bytes * layers
-    tokens_per_s = S / (ms_per_step / 1e3)
+    tokens_per_s = S * T / (ms_per_step / 1e3)
     kv_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
     achieved = per_call_bytes / kern_avg_s / 1e9
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload if not multi else "%s_q%d" % (args.workload, T))
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC_MULTI if multi else METRIC,
         "value": round(tokens_per_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -325,19 +488,29 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "num_seqs": S, "context_len": int(case.context_lens.max()),
                    "layers": layers, "block_size": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
-                   "head_dim": D},
+                   "head_dim": D, "query_tokens": T},
         "graph": graph is not None,
         "with_append": bool(args.with_append),
         "kv_gbs": round(kv_gbs, 1),
         "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "paged_attn_decode (decode_kernel + merge_kernel)",
+        "us_per_call": {"mean": round(kern_avg_s * 1e6, 2), "p10": round(p10, 2),
+                        "median": round(p50, 2), "p90": round(p90, 2),
+                        "calls": len(kern_ms)},
+        "attainable": attain,
+        "roofline": {"bound": "hbm",
+                     "kernel": ("paged_attn_multi" if multi else "paged_attn_decode") +
+                               " (decode_kernel + merge_kernel)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "frac_of_attainable": round(achieved / attain["read_gbs"], 4),
                      "algorithmic_bytes_per_launch": int(per_call_bytes),
                      "avg_launch_us": round(kern_avg_s * 1e6, 2)},
         "cpu_baseline": None,
     }
+    if "unique_tokens" in extra:
+        line["logical_kv_gbs"] = round(logical_bytes * layers / (ms_per_step / 1e3) / 1e9, 1)
+        line["copy_blocks"] = copy_line
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, pools, layers, args)
     print(json.dumps(line), flush=True)

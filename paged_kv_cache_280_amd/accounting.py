@@ -5,9 +5,11 @@
   layers times tokens times KV heads times head size times bytes per element.
 * ``blocks_needed``: a sequence of L tokens holds ceil(L/B) blocks
   ("PagedAttention (vLLM)", troisinh.com, section "Cơ chế Block Table").
-* ``decode_algorithmic_bytes``: the bytes one decode call must move at least --
-  K and V of every valid token once, q, out, the table entries in use and the
-  lengths.  Split-K scratch traffic is overhead and is not counted.
+* ``decode_algorithmic_bytes``: the bytes one decode (or multi-token) call must
+  move at least -- K and V of every valid token once, q, out, the table entries
+  in use and the lengths.  Split-K scratch traffic, and the K/V re-read by a
+  multi-token call that needs several runs of query tokens, are overhead and are
+  not counted.
 """
 
 from __future__ import annotations
@@ -26,14 +28,17 @@ def blocks_needed(tokens, block_size: int):
 
 
 def decode_algorithmic_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                             block_size: int, elem_bytes: int = 2, unique_tokens=None) -> int:
-    """Algorithmic bytes of one decode call.  ``unique_tokens`` replaces the sum of
-    context lengths when sequences share physical blocks (count each stored slot
-    once)."""
+                             block_size: int, elem_bytes: int = 2, unique_tokens=None,
+                             query_tokens: int = 1) -> int:
+    """Algorithmic bytes of one decode call (``query_tokens`` > 1: one multi-token
+    call with that many query rows per sequence, plus its query lengths).
+    ``unique_tokens`` replaces the sum of context lengths when sequences share
+    physical blocks (count each stored slot once)."""
     lens = np.asarray(context_lens, dtype=np.int64)
     S = lens.size
     tokens = int(lens.sum()) if unique_tokens is None else int(unique_tokens)
     kv = tokens * num_kv_heads * head_dim * elem_bytes * 2
-    qo = 2 * S * num_q_heads * head_dim * elem_bytes
+    qo = 2 * S * int(query_tokens) * num_q_heads * head_dim * elem_bytes
     tables = int(blocks_needed(lens, block_size).sum()) * 4
-    return kv + qo + tables + 4 * S
+    qlens = 4 * S if query_tokens > 1 else 0
+    return kv + qo + tables + 4 * S + qlens
