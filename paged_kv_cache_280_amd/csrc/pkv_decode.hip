@@ -678,7 +678,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void decode_kernel(
 // The order is fixed, so the result does not depend on timing.  In multi-token
 // launches the rows past the pair's query tokens are left to the decode kernel.
 constexpr int kMergeThreads = 512;
-constexpr int kMergeChunk = 8;
+constexpr int kMergeChunk = 16;
 constexpr int kMergeItems = 2;
 constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
 
