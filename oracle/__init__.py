@@ -5,7 +5,8 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 library (``paged_kv_cache_280_amd``) never imports it, and the two share no code.
 
 ``oracle.cpp`` holds the plain loops (fp32 oracle, fp64 twin, per-row debug form
-with the softmax weights, byte copy of blocks).  This module compiles it with
+with the softmax weights, multi-token causal attention, decode over fp8 blocks and
+the E4M3FN decoding, KV append, byte copy of blocks).  This module compiles it with
 ``g++ -O2 -fopenmp`` (no fast-math) and exposes numpy-level wrappers.
 
 Parity pins (what fixes the oracle other than itself) live in
@@ -52,6 +53,12 @@ def _bind(lib):
     lib.oracle_paged_attn_multi_f32.argtypes = [p, p, p, p, p, p, i32, i32, ctypes.c_float, p,
                                                  i32, i32, i32, i32, i32, i64, i32]
     lib.oracle_paged_attn_multi_f32.restype = ctypes.c_int
+    lib.oracle_paged_decode_fp8_f32.argtypes = [p, p, p, p, p, i32, ctypes.c_float,
+                                                ctypes.c_float, ctypes.c_float, p, i32, i32, i32,
+                                                i32, i32, i64, i32]
+    lib.oracle_paged_decode_fp8_f32.restype = ctypes.c_int
+    lib.oracle_fp8_e4m3_to_f32.argtypes = [p, p, i64]
+    lib.oracle_fp8_e4m3_to_f32.restype = None
     lib.oracle_kv_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64]
     lib.oracle_kv_append.restype = ctypes.c_int
     lib.oracle_copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32]
@@ -156,6 +163,38 @@ def paged_decode_probs(q, k_pool, v_pool, block_tables, context_lens, block_size
     return out, probs[:L]
 
 
+def paged_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, block_size, scale, k_scale,
+                     v_scale, num_kv_heads, threads=0, lib=None):
+    """Reference decode over fp8 pools: q bf16 bits [S][Hq][D]; k_pool uint8
+    [NB][Hkv][D/16][B][16]; v_pool uint8 [NB][Hkv][16][B/4][D/16][4]; each code is
+    an E4M3FN number, times k_scale (keys) or v_scale (values).  Returns float32
+    [S][Hq][D]."""
+    q = _u16(q)
+    kp = np.ascontiguousarray(k_pool, dtype=np.uint8)
+    vp = np.ascontiguousarray(v_pool, dtype=np.uint8)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S, Hq, D = q.shape
+    NB, B = kp.shape[0], int(block_size)
+    if kp.size != NB * num_kv_heads * D * B or vp.size != kp.size:
+        raise OracleError("pool size does not match [NB][Hkv][..] with D=%d B=%d" % (D, B))
+    out = np.zeros((S, Hq, D), np.float32)
+    rc = (lib or _load()).oracle_paged_decode_fp8_f32(
+        _ptr(q), _ptr(kp), _ptr(vp), _ptr(tables), _ptr(lens), B, float(scale), float(k_scale),
+        float(v_scale), _ptr(out), S, Hq, num_kv_heads, D, tables.shape[1], NB, int(threads))
+    if rc != 0:
+        raise OracleError("oracle_paged_decode_fp8 returned %d" % rc)
+    return out
+
+
+def fp8_e4m3_to_f32(codes, lib=None):
+    """The oracle's E4M3FN decoding of uint8 codes (float32, same shape)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.zeros(c.shape, np.float32)
+    (lib or _load()).oracle_fp8_e4m3_to_f32(_ptr(c), _ptr(out), c.size)
+    return out
+
+
 def kv_append(k_new, v_new, k_pool, v_pool, block_tables, token_seq, token_pos, block_size,
               lib=None):
     """Write new tokens' rows (bf16 bits [T][Hkv][D]) into host pools in place."""
@@ -219,3 +258,9 @@ class Variant:
 
     def paged_attn_multi(self, *args, **kwargs):
         return paged_attn_multi(*args, lib=self._lib, **kwargs)
+
+    def paged_decode_fp8(self, *args, **kwargs):
+        return paged_decode_fp8(*args, lib=self._lib, **kwargs)
+
+    def fp8_e4m3_to_f32(self, *args, **kwargs):
+        return fp8_e4m3_to_f32(*args, lib=self._lib, **kwargs)

@@ -32,6 +32,17 @@
 //   * block_tables is int32 [S][M] row-major; only the first ceil(L/B) entries of
 //     row s are read.  Tail slots of the last block, padding entries of a table
 //     row and unreferenced blocks are never read.
+//   * fp8 KV blocks ("KV cache, PagedAttention" (aiwiki.vn), paragraph on cache
+//     quantisation: fewer bytes per stored key/value): each element is an OCP
+//     E4M3FN code (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+//     infinities; S.1111.111 is NaN) times a per-call scale (one for K, one for
+//     V).  Layouts:
+//       K  [num_blocks][Hkv][D/16][B][16] element (b,g,o,d) at
+//          (((b*Hkv + g)*(D/16) + d/16)*B + o)*16 + d%16
+//       V  [num_blocks][Hkv][16][B/4][D/16][4] element (b,g,o,d) at
+//          ((((b*Hkv + g)*16 + d%16)*(B/4) + o/4)*(D/16) + d/16)*4 + o%4
+//     A stored code is decoded exactly, then multiplied by its scale in the
+//     accumulator type.
 //
 // Precision: the accumulator type is a template parameter.  The fp32
 // instantiation is the oracle the GPU is compared against; the fp64 one measures
@@ -72,12 +83,57 @@ inline int64_t v_index(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t
   return ((b * sh.Hkv + g) * sh.D + d) * sh.B + o;
 }
 
+inline int64_t k8_index(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t d) {
+  return (((b * sh.Hkv + g) * (sh.D / 16) + d / 16) * sh.B + o) * 16 + d % 16;
+}
+
+inline int64_t v8_index(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t d) {
+  return ((((b * sh.Hkv + g) * 16 + d % 16) * (sh.B / 4) + o / 4) * (sh.D / 16) + d / 16) * 4 + o % 4;
+}
+
+// OCP E4M3FN: normal codes are (1 + m/8) * 2^(e-7), subnormal codes (e = 0) are
+// (m/8) * 2^-6, and exponent 15 with mantissa 7 is NaN.
+inline float e4m3_to_float(uint8_t code) {
+  const int e = (code >> 3) & 15, m = code & 7;
+  float v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = std::ldexp(static_cast<float>(m), -9);
+  else
+    v = std::ldexp(static_cast<float>(8 + m), e - 10);
+  return (code & 0x80) ? -v : v;
+}
+
+// Where the keys and values are read: bf16 pools, or fp8 pools with their scales.
+struct Bf16Kv {
+  const uint16_t* kp;
+  const uint16_t* vp;
+  float k(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t d) const {
+    return bf16_bits_to_float(kp[k_index(sh, b, g, o, d)]);
+  }
+  float v(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t d) const {
+    return bf16_bits_to_float(vp[v_index(sh, b, g, o, d)]);
+  }
+};
+
+struct Fp8Kv {
+  const uint8_t* kp;
+  const uint8_t* vp;
+  float k_scale, v_scale;
+  float k(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t d) const {
+    return e4m3_to_float(kp[k8_index(sh, b, g, o, d)]) * k_scale;
+  }
+  float v(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t d) const {
+    return e4m3_to_float(vp[v8_index(sh, b, g, o, d)]) * v_scale;
+  }
+};
+
 // One query row attending to positions 0 .. L-1 of sequence s through its table
 // row, with KV head g.  Returns 0, or -1 when a table entry lies outside the pool.
-template <typename Acc>
-int attend(const Shape& sh, const uint16_t* qrow, const uint16_t* kp, const uint16_t* vp,
-           const int32_t* trow, int g, int L, Acc scale, Acc* out_row,
-           Acc* probs_row /* may be null; length >= L */) {
+template <typename Acc, typename Kv>
+int attend(const Shape& sh, const uint16_t* qrow, const Kv& kv, const int32_t* trow, int g, int L,
+           Acc scale, Acc* out_row, Acc* probs_row /* may be null; length >= L */) {
   for (int d = 0; d < sh.D; ++d) out_row[d] = Acc(0);
   if (L == 0) return 0;
   std::vector<Acc> x(L);
@@ -90,7 +146,7 @@ int attend(const Shape& sh, const uint16_t* qrow, const uint16_t* kp, const uint
     const int o = t % sh.B;
     Acc dot = Acc(0);
     for (int d = 0; d < sh.D; ++d)
-      dot += Acc(bf16_bits_to_float(qrow[d])) * Acc(bf16_bits_to_float(kp[k_index(sh, b, g, o, d)]));
+      dot += Acc(bf16_bits_to_float(qrow[d])) * Acc(kv.k(sh, b, g, o, d));
     x[t] = scale * dot;
   }
   Acc m = x[0];
@@ -107,7 +163,7 @@ int attend(const Shape& sh, const uint16_t* qrow, const uint16_t* kp, const uint
   for (int d = 0; d < sh.D; ++d) {
     Acc acc = Acc(0);
     for (int t = 0; t < L; ++t)
-      acc += x[t] * Acc(bf16_bits_to_float(vp[v_index(sh, blk[t], g, t % sh.B, d)]));
+      acc += x[t] * Acc(kv.v(sh, blk[t], g, t % sh.B, d));
     out_row[d] = acc;
   }
   return 0;
@@ -115,21 +171,20 @@ int attend(const Shape& sh, const uint16_t* qrow, const uint16_t* kp, const uint
 
 // One (sequence, query head) pair of a decode step: the query attends to all
 // context_lens[s] cached positions.
-template <typename Acc>
-int decode_one(const Shape& sh, const uint16_t* q, const uint16_t* kp, const uint16_t* vp,
-               const int32_t* tables, const int32_t* lens, Acc scale, int s, int h,
-               Acc* out_row, Acc* probs_row) {
+template <typename Acc, typename Kv>
+int decode_one(const Shape& sh, const uint16_t* q, const Kv& kv, const int32_t* tables,
+               const int32_t* lens, Acc scale, int s, int h, Acc* out_row, Acc* probs_row) {
   const int G = sh.Hq / sh.Hkv;
   const uint16_t* qrow = q + (static_cast<int64_t>(s) * sh.Hq + h) * sh.D;
-  return attend<Acc>(sh, qrow, kp, vp, tables + static_cast<int64_t>(s) * sh.M, h / G, lens[s],
+  return attend<Acc>(sh, qrow, kv, tables + static_cast<int64_t>(s) * sh.M, h / G, lens[s],
                      scale, out_row, probs_row);
 }
 
-template <typename Acc>
-int decode_all(const uint16_t* q, const uint16_t* kp, const uint16_t* vp, const int32_t* tables,
-               const int32_t* lens, int32_t B, double scale, Acc* out, int32_t S, int32_t Hq,
-               int32_t Hkv, int32_t D, int32_t M, int64_t NB, int32_t threads) {
-  if (!q || !kp || !vp || !tables || !lens || !out) return -2;
+template <typename Acc, typename Kv>
+int decode_all(const uint16_t* q, const Kv& kv, const int32_t* tables, const int32_t* lens,
+               int32_t B, double scale, Acc* out, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+               int32_t M, int64_t NB, int32_t threads) {
+  if (!q || !kv.kp || !kv.vp || !tables || !lens || !out) return -2;
   if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || M < 0 || NB < 0) return -3;
   if (Hq % Hkv != 0 || D % 8 != 0) return -3;
   for (int s = 0; s < S; ++s)
@@ -143,7 +198,7 @@ int decode_all(const uint16_t* q, const uint16_t* kp, const uint16_t* vp, const 
 #endif
   for (int64_t i = 0; i < pairs; ++i) {
     const int s = static_cast<int>(i / Hq), h = static_cast<int>(i % Hq);
-    const int rc = decode_one<Acc>(sh, q, kp, vp, tables, lens, static_cast<Acc>(scale), s, h,
+    const int rc = decode_one<Acc>(sh, q, kv, tables, lens, static_cast<Acc>(scale), s, h,
                                    out + i * D, nullptr);
     if (rc < status) status = rc;
   }
@@ -163,9 +218,9 @@ int oracle_paged_decode_f32(const uint16_t* q, const uint16_t* k_pool, const uin
                             int32_t block_size, float scale, float* out, int32_t num_seqs,
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t max_blocks_per_seq, int64_t num_blocks, int32_t threads) {
-  return decode_all<float>(q, k_pool, v_pool, block_tables, context_lens, block_size, scale, out,
-                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                           num_blocks, threads);
+  return decode_all<float>(q, Bf16Kv{k_pool, v_pool}, block_tables, context_lens, block_size,
+                           scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                           max_blocks_per_seq, num_blocks, threads);
 }
 
 // The same computation with a double accumulator and double output.
@@ -174,9 +229,29 @@ int oracle_paged_decode_f64(const uint16_t* q, const uint16_t* k_pool, const uin
                             int32_t block_size, double scale, double* out, int32_t num_seqs,
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t max_blocks_per_seq, int64_t num_blocks, int32_t threads) {
-  return decode_all<double>(q, k_pool, v_pool, block_tables, context_lens, block_size, scale, out,
-                            num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                            num_blocks, threads);
+  return decode_all<double>(q, Bf16Kv{k_pool, v_pool}, block_tables, context_lens, block_size,
+                            scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            max_blocks_per_seq, num_blocks, threads);
+}
+
+// Decode over fp8 pools (layouts and decoding in the header comment): keys are
+// code(K) * k_scale, values code(V) * v_scale; everything else as
+// oracle_paged_decode_f32.  Also needs head_dim % 16 == 0 and block_size % 4 == 0.
+int oracle_paged_decode_fp8_f32(const uint16_t* q, const uint8_t* k_pool, const uint8_t* v_pool,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t block_size, float scale, float k_scale, float v_scale,
+                                float* out, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                                int64_t num_blocks, int32_t threads) {
+  if (head_dim % 16 != 0 || block_size % 4 != 0) return -3;
+  return decode_all<float>(q, Fp8Kv{k_pool, v_pool, k_scale, v_scale}, block_tables, context_lens,
+                           block_size, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                           max_blocks_per_seq, num_blocks, threads);
+}
+
+// The E4M3FN decoding itself, for n codes.
+void oracle_fp8_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_to_float(codes[i]);
 }
 
 // Several query tokens per sequence (speculative verification, chunked prefill):
@@ -220,7 +295,7 @@ int oracle_paged_attn_multi_f32(const uint16_t* q, const uint16_t* k_pool, const
       continue;
     }
     const int p = context_lens[s] - query_lens[s] + i;
-    const int rc = attend<float>(sh, q + r * head_dim, k_pool, v_pool,
+    const int rc = attend<float>(sh, q + r * head_dim, Bf16Kv{k_pool, v_pool},
                                  block_tables + static_cast<int64_t>(s) * max_blocks_per_seq,
                                  h / G, p + 1, scale, orow, nullptr);
     if (rc < status) status = rc;
@@ -242,8 +317,8 @@ int oracle_paged_decode_probs_f32(const uint16_t* q, const uint16_t* k_pool,
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim % 8 != 0) return -3;
   const Shape sh{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                  num_blocks};
-  return decode_one<float>(sh, q, k_pool, v_pool, block_tables, context_lens, scale, seq, head,
-                           out_row, probs);
+  return decode_one<float>(sh, q, Bf16Kv{k_pool, v_pool}, block_tables, context_lens, scale, seq,
+                           head, out_row, probs);
 }
 
 // KV append ("Cơ chế Block Table", troisinh.com): token i of sequence seq[i] at

@@ -29,8 +29,20 @@ MUTATIONS = {
     "no_scale": ("    x[t] = scale * dot;", "    x[t] = dot;"),
     "scale_twice": ("    x[t] = scale * dot;", "    x[t] = scale * scale * dot * 8;"),
     "unnormalised": ("x[t] = x[t] / z;", "x[t] = x[t] / (z + Acc(1e-3));"),
-    "value_from_key_slot": ("vp[v_index(sh, blk[t], g, t % sh.B, d)]",
-                            "vp[v_index(sh, blk[t], g, (t + 1) % sh.B, d)]"),
+    "value_from_key_slot": ("kv.v(sh, blk[t], g, t % sh.B, d)",
+                            "kv.v(sh, blk[t], g, (t + 1) % sh.B, d)"),
+    "fp8_subnormal_exponent": ("v = std::ldexp(static_cast<float>(m), -9);",
+                               "v = std::ldexp(static_cast<float>(m), -10);"),
+    "fp8_exponent_bias": ("v = std::ldexp(static_cast<float>(8 + m), e - 10);",
+                          "v = std::ldexp(static_cast<float>(8 + m), e - 9);"),
+    "fp8_k_layout_token_major": (
+        "return (((b * sh.Hkv + g) * (sh.D / 16) + d / 16) * sh.B + o) * 16 + d % 16;",
+        "return (((b * sh.Hkv + g) * sh.B + o) * (sh.D / 16) + d / 16) * 16 + d % 16;"),
+    "fp8_v_layout_swapped": (
+        "(sh.B / 4) + o / 4) * (sh.D / 16) + d / 16) * 4 + o % 4;",
+        "(sh.D / 16) + d / 16) * (sh.B / 4) + o / 4) * 4 + o % 4;"),
+    "fp8_v_scale_dropped": ("return e4m3_to_float(vp[v8_index(sh, b, g, o, d)]) * v_scale;",
+                            "return e4m3_to_float(vp[v8_index(sh, b, g, o, d)]);"),
     "append_wrong_offset": ("const int o = p % block_size;", "const int o = (p + 1) % block_size;"),
     "causal_off_by_one": ("h / G, p + 1, scale, orow, nullptr);", "h / G, p, scale, orow, nullptr);"),
     "q_head_offset": ("q + (static_cast<int64_t>(s) * sh.Hq + h) * sh.D",

@@ -385,3 +385,78 @@ def test_multi_query_with_one_token_is_decode(oracle_lib):
     multi = oracle_lib.paged_attn_multi(q[:, None], kp, vp, case.block_tables, case.context_lens,
                                         np.ones(3, np.int32), 16, case.scale, 2)
     assert np.array_equal(multi[:, 0].view(np.uint32), dec.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3FN) KV blocks
+# ---------------------------------------------------------------------------
+
+def test_fp8_decoding_of_every_code_matches_torch_float8(oracle_lib):
+    """All 256 E4M3FN codes decode as torch's float8_e4m3fn does (NaN where it gives NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle_lib.fp8_e4m3_to_f32(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok].view(np.uint32), ref[ok].view(np.uint32))   # -0.0 included
+    # landmarks of the format: 1.0, the largest finite, smallest normal and subnormal
+    assert ours[0x38] == 1.0 and ours[0x7E] == 448.0 and ours[0x08] == 2.0 ** -6
+    assert ours[0x01] == 2.0 ** -9 and np.isnan(ours[0x7F]) and np.isnan(ours[0xFF])
+
+
+def brute_force_fp8(case, q, kp8, vp8, k_scale, v_scale):
+    """fp8 pools decoded by torch (float8_e4m3fn -> float64, times the scale),
+    gathered into contiguous rows with einops, attended by torch's fp64 SDPA."""
+    def dec(a, scale):
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(
+            torch.float64).numpy() * scale
+    kl = rearrange(dec(kp8, k_scale), "n h c b e -> n h b (c e)")
+    vl = rearrange(dec(vp8, v_scale), "n h dl bq dc f -> n h (bq f) (dc dl)")
+    qf = wl.f32_from_bf16(q).astype(np.float64)
+    S, Hq, D = q.shape
+    G = Hq // case.num_kv_heads
+    out = np.zeros((S, Hq, D))
+    for s in range(S):
+        L = int(case.context_lens[s])
+        if L == 0:
+            continue
+        ids = case.block_tables[s, :-(-L // case.block_size)]
+        for h in range(Hq):
+            K = kl[ids, h // G].reshape(-1, D)[:L]
+            V = vl[ids, h // G].reshape(-1, D)[:L]
+            o = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(qf[s, h]).view(1, 1, 1, D), torch.from_numpy(K).view(1, 1, L, D),
+                torch.from_numpy(V).view(1, 1, L, D), scale=case.scale)
+            out[s, h] = o.view(D).numpy()
+    return out
+
+
+@pytest.mark.parametrize("B,D,G,scales", [(16, 128, 4, (0.037, 0.051)), (8, 64, 1, (1 / 16, 1 / 8)),
+                                          (32, 128, 8, (0.02, 0.09))])
+def test_fp8_oracle_matches_fp64_library_attention(oracle_lib, B, D, G, scales):
+    Hkv = 2
+    case = wl.case_random(B + D + G, 4, G * Hkv, Hkv, D, B, [3 * B + 5, 1, 0, 200])
+    kp8, vp8 = wl.host_pools_fp8(case, *scales)           # NaN codes in every unread slot
+    q = wl.randn_bf16(np.random.default_rng(B), (case.num_seqs, case.num_q_heads, D))
+    got = oracle_lib.paged_decode_fp8(q, kp8, vp8, case.block_tables, case.context_lens, B,
+                                      case.scale, scales[0], scales[1], Hkv)
+    ref = brute_force_fp8(case, q, kp8, vp8, *scales)
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= 2e-5
+
+
+def test_fp8_oracle_equals_bf16_oracle_on_the_same_values(oracle_lib):
+    """With power-of-two scales every decoded value is a bf16 number; the fp8 oracle
+    then performs exactly the bf16 oracle's arithmetic, bit for bit."""
+    case = wl.case_random(21, 3, 8, 2, 128, 16, [70, 16, 5])
+    ks, vs = 2.0 ** -4, 2.0 ** -3
+    kp8, vp8 = wl.host_pools_fp8(case, ks, vs, poison=False)
+    to_bf16 = lambda a, s: wl.bf16_from_f32(
+        torch.from_numpy(a).view(torch.float8_e4m3fn).to(torch.float32).numpy() * np.float32(s))
+    kp = wl.k_to_pool(to_bf16(wl.k8_from_pool(kp8), ks))
+    vp = wl.v_to_pool(to_bf16(wl.v8_from_pool(vp8), vs))
+    q = wl.randn_bf16(np.random.default_rng(4), (3, 8, 128))
+    a = oracle_lib.paged_decode_fp8(q, kp8, vp8, case.block_tables, case.context_lens, 16,
+                                    case.scale, ks, vs, 2)
+    b = run(oracle_lib, case, q, kp, vp)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -376,3 +376,107 @@ def fill_device_pools(case: Case, k, v, g, poison=True) -> None:
         for b, first in case.tail_slots():
             kk[b, :, :, first:, :] = -1
             vv[b, :, :, first:] = -1
+
+
+# ---------------------------------------------------------------------------
+# fp8 (OCP E4M3FN) pools: one byte per element, a scale per pool
+# ---------------------------------------------------------------------------
+# Layouts (the library's documented fp8 format, restated so that inputs can be
+# written into it):  K [NB][Hkv][D/16][B][16] and V [NB][Hkv][16][B/4][D/16][4],
+# element (b, g, o, d) of V at [b][g][d%16][o/4][d/16][o%4].  Codes come from
+# torch's float8_e4m3fn conversion of N(0,1)/scale (input generation only).
+
+E4M3_NAN = 0x7F
+
+
+def k8_pool_shape(nb, hkv, d, b):
+    return (nb, hkv, d // 16, b, 16)
+
+
+def v8_pool_shape(nb, hkv, d, b):
+    return (nb, hkv, 16, b // 4, d // 16, 4)
+
+
+def k8_to_pool(k_logical: np.ndarray) -> np.ndarray:
+    nb, hkv, b, d = k_logical.shape
+    return np.ascontiguousarray(k_logical.reshape(nb, hkv, b, d // 16, 16).transpose(0, 1, 3, 2, 4))
+
+
+def v8_to_pool(v_logical: np.ndarray) -> np.ndarray:
+    nb, hkv, b, d = v_logical.shape
+    x = v_logical.reshape(nb, hkv, b // 4, 4, d // 16, 16)      # [o/4][o%4][d/16][d%16]
+    return np.ascontiguousarray(x.transpose(0, 1, 5, 2, 4, 3))   # [d%16][o/4][d/16][o%4]
+
+
+def k8_from_pool(k_pool: np.ndarray) -> np.ndarray:
+    nb, hkv, dc, b, sixteen = k_pool.shape
+    return np.ascontiguousarray(k_pool.transpose(0, 1, 3, 2, 4).reshape(nb, hkv, b, dc * sixteen))
+
+
+def v8_from_pool(v_pool: np.ndarray) -> np.ndarray:
+    nb, hkv, sixteen, bq, dc, four = v_pool.shape
+    x = v_pool.transpose(0, 1, 3, 5, 4, 2)                       # [o/4][o%4][d/16][d%16]
+    return np.ascontiguousarray(x.reshape(nb, hkv, bq * four, dc * sixteen))
+
+
+def e4m3_codes(x: np.ndarray, scale: float) -> np.ndarray:
+    """uint8 E4M3FN codes of x / scale (torch's conversion; values clipped to the
+    format's range first)."""
+    import torch
+
+    y = np.clip(np.asarray(x, dtype=np.float32) / np.float32(scale), -448.0, 448.0)
+    return torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def host_pools_fp8(case: Case, k_scale: float, v_scale: float, layer=0, poison=True):
+    """(k_pool, v_pool) as uint8 numpy arrays in the fp8 layouts: codes of bf16-free
+    N(0,1) draws divided by the scales; with ``poison`` every slot that must not be
+    read holds the NaN code."""
+    rng = np.random.default_rng([case.seed, 5, layer])
+    NB, H, D, B = case.num_blocks, case.num_kv_heads, case.head_dim, case.block_size
+    k = e4m3_codes(rng.standard_normal((NB, H, B, D), dtype=np.float32), k_scale)
+    v = e4m3_codes(rng.standard_normal((NB, H, B, D), dtype=np.float32), v_scale)
+    if poison:
+        used = np.zeros(NB, bool)
+        used[case.used_blocks()] = True
+        for a in (k, v):
+            a[~used] = E4M3_NAN
+            for b, first in case.tail_slots():
+                a[b, :, first:, :] = E4M3_NAN
+    return k8_to_pool(k), v8_to_pool(v)
+
+
+def device_pools_fp8(case: Case, device, k_scale: float, v_scale: float, layer=0, poison=True):
+    """fp8 K and V pools (uint8 torch tensors in the fp8 layouts) on ``device``,
+    filled for the referenced blocks from a seeded device generator; with
+    ``poison`` everything else (and each last block's unused tail) is the NaN code."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(case.seed) * 1000003 + 7919 + int(layer))
+    NB, H, D, B = case.num_blocks, case.num_kv_heads, case.head_dim, case.block_size
+    k = torch.full(k8_pool_shape(NB, H, D, B), E4M3_NAN if poison else 0, dtype=torch.uint8,
+                   device=device)
+    v = torch.full(v8_pool_shape(NB, H, D, B), E4M3_NAN if poison else 0, dtype=torch.uint8,
+                   device=device)
+    used = torch.from_numpy(case.used_blocks().astype(np.int64)).to(device)
+    tails = {b: first for b, first in case.tail_slots()} if poison else {}
+
+    def codes(n, scale):
+        x = torch.randn((n, H, B, D), generator=g, device=device, dtype=torch.float32) / scale
+        return x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    chunk = 1 << 13
+    for i in range(0, used.numel(), chunk):
+        ids = used[i:i + chunk]
+        kl, vl = codes(ids.numel(), k_scale), codes(ids.numel(), v_scale)
+        if tails:
+            for j, b in enumerate(ids.tolist()):
+                if b in tails:
+                    kl[j, :, tails[b]:, :] = E4M3_NAN
+                    vl[j, :, tails[b]:, :] = E4M3_NAN
+        n = ids.numel()
+        k[ids] = kl.reshape(n, H, B, D // 16, 16).permute(0, 1, 3, 2, 4).contiguous()
+        v[ids] = vl.reshape(n, H, B // 4, 4, D // 16, 16).permute(0, 1, 5, 2, 4, 3).contiguous()
+    return k, v
