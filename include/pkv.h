@@ -123,6 +123,33 @@ int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           void* stream);
 
 /*
+ * Paged decode attention over fp8 KV blocks ("KV cache, PagedAttention",
+ * aiwiki.vn, paragraph on cache quantisation: keys and values stored with fewer
+ * bytes).  Each pool element is one OCP E4M3FN code (sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; no infinities; S.1111.111 is NaN); the key it stands
+ * for is code * k_scale, the value code * v_scale.  The computation is
+ * paged_attn_decode's on those keys and values.  fp8 pool layouts (B =
+ * block_size, D = head_dim):
+ *   K  [NB][Hkv][D/16][B][16]        : element (b, g, o, d) at
+ *                                      (((b*Hkv + g)*(D/16) + d/16)*B + o)*16 + d%16
+ *   V  [NB][Hkv][16][B/4][D/16][4]   : element (b, g, o, d) at
+ *                                      ((((b*Hkv + g)*16 + d%16)*(B/4) + o/4)*(D/16)
+ *                                       + d/16)*4 + o%4
+ * A (block, head) tile is B*D contiguous bytes and a whole block Hkv*B*D bytes
+ * (copy_blocks takes block_bytes = Hkv*B*D for these pools).  q and out are bf16 as
+ * in paged_attn_decode.  k_scale and v_scale must be finite (else PKV_ERR_SHAPE);
+ * the workspace is sized by paged_attn_decode_workspace_bytes.  All other
+ * arguments, checks and guarantees are paged_attn_decode's.
+ */
+int32_t paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t block_size, float scale, float k_scale, float v_scale,
+                              void* out, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int32_t max_context_len, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device scratch paged_attn_multi needs for these sizes on the current
  * device (the same role as paged_attn_decode_workspace_bytes).  Returns 0 for
  * sizes paged_attn_multi would reject.

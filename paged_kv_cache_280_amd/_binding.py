@@ -22,7 +22,8 @@ STATUS_NAMES = {
 }
 
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "paged_attn_decode_workspace_bytes",
-           "paged_attn_decode", "paged_attn_multi_workspace_bytes", "paged_attn_multi",
+           "paged_attn_decode", "paged_attn_decode_fp8", "paged_attn_multi_workspace_bytes",
+           "paged_attn_multi",
            "kv_append", "copy_blocks")
 
 
@@ -54,6 +55,10 @@ def load_library(path: str = LIB_PATH):
                    sz, p]
     lib.paged_attn_decode.argtypes = decode_args
     lib.paged_attn_decode.restype = i32
+    f32 = ctypes.c_float
+    lib.paged_attn_decode_fp8.argtypes = [p, p, p, p, p, i32, f32, f32, f32, p, i32, i32, i32, i32,
+                                          i32, i64, i32, p, sz, p]
+    lib.paged_attn_decode_fp8.restype = i32
     lib.paged_attn_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.paged_attn_multi_workspace_bytes.restype = sz
     lib.paged_attn_multi.argtypes = [p, p, p, p, p, p, i32, i32, ctypes.c_float, p, i32, i32, i32,
@@ -161,6 +166,58 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
                                    _stream_handle(q, stream))
     if rc != 0:
         raise PkvError(rc, "paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
+                          k_scale, v_scale, out=None, *, max_context_len=None, workspace=None,
+                          stream=None):
+    """Paged decode attention over fp8 (E4M3FN) pools (see ``include/pkv.h``).
+    ``k_cache`` uint8 [num_blocks][Hkv][D/16][block_size][16], ``v_cache`` uint8
+    [num_blocks][Hkv][16][block_size/4][D/16][4]; keys are code * k_scale, values
+    code * v_scale.  Workspace as for paged_attn_decode.  Returns ``out``."""
+    import torch
+
+    lib = load_library()
+    _check(q.dim() == 3, "q must be [num_seqs][num_q_heads][head_dim]")
+    S, Hq, D = q.shape
+    B = int(block_size)
+    _check(k_cache.dim() == 5 and k_cache.shape[2] * 16 == D and k_cache.shape[3] == B
+           and k_cache.shape[4] == 16, "k_cache must be [num_blocks][Hkv][D/16][block_size][16]")
+    NB, Hkv = int(k_cache.shape[0]), int(k_cache.shape[1])
+    _check(tuple(v_cache.shape) == (NB, Hkv, 16, B // 4, D // 16, 4),
+           "v_cache must be [num_blocks][Hkv][16][block_size/4][D/16][4]")
+    _check(q.dtype == torch.bfloat16 and q.is_contiguous(), "q: contiguous bf16")
+    for t in (k_cache, v_cache):
+        _check(t.dtype == torch.uint8 and t.is_contiguous(), "fp8 pools: contiguous uint8 codes")
+    _check(block_tables.dim() == 2 and block_tables.shape[0] == S,
+           "block_tables must be [num_seqs][max_blocks_per_seq]")
+    _check(context_lens.dim() == 1 and context_lens.shape[0] == S, "context_lens must be [num_seqs]")
+    for t in (block_tables, context_lens):
+        _check(t.dtype == torch.int32 and t.is_contiguous(), "tables/lengths: contiguous int32")
+    devs = {t.device for t in (q, k_cache, v_cache, block_tables, context_lens)}
+    _check(len(devs) == 1 and q.is_cuda, "all tensors must be on one GPU")
+    M = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = M * B
+    with torch.cuda.device(q.device):
+        if out is None:
+            out = torch.empty_like(q)
+        _check(out.shape == q.shape and out.dtype == torch.bfloat16 and out.is_contiguous()
+               and out.device == q.device, "out must match q")
+        if workspace is None:
+            workspace = new_workspace(S, Hq, Hkv, D, B, max_context_len, q.device)
+        _check(workspace.is_cuda and workspace.device == q.device and workspace.is_contiguous(),
+               "workspace must be a contiguous tensor on q's device")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        rc = lib.paged_attn_decode_fp8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                       block_tables.data_ptr(), context_lens.data_ptr(), B,
+                                       float(scale), float(k_scale), float(v_scale),
+                                       out.data_ptr(), S, Hq, Hkv, D, M, NB,
+                                       int(max_context_len), workspace.data_ptr(), ws_bytes,
+                                       _stream_handle(q, stream))
+    if rc != 0:
+        raise PkvError(rc, "paged_attn_decode_fp8")
     return out
 
 

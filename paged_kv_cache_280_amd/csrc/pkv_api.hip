@@ -84,15 +84,18 @@ int32_t check_shapes(int32_t block_size, float scale, int32_t num_seqs, int32_t 
   return PKV_OK;
 }
 
+// fp8: the pools hold E4M3FN codes; keys are code * k_scale, values code * v_scale.
 int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, int32_t block_size,
                     float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
                     int64_t num_blocks, int32_t max_context_len, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, void* stream, bool fp8, float k_scale,
+                    float v_scale) {
   const int32_t st = check_shapes(block_size, scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                   max_blocks_per_seq, num_blocks, max_context_len);
   if (st != PKV_OK) return st;
+  if (!isfinite(k_scale) || !isfinite(v_scale)) return PKV_ERR_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !workspace)
     return PKV_ERR_NULL;
@@ -107,8 +110,8 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
 
   DecodeBuffers b;
   b.q = static_cast<const uint16_t*>(q);
-  b.k = static_cast<const uint16_t*>(k_cache);
-  b.v = static_cast<const uint16_t*>(v_cache);
+  b.k = k_cache;
+  b.v = v_cache;
   b.tables = block_tables;
   b.lens = context_lens;
   b.qlens = nullptr;
@@ -122,14 +125,19 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
   d.M = max_blocks_per_seq;
   d.n_workers = static_cast<int32_t>(workers);
   d.NB = num_blocks;
-  d.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+  // scores in the log2 domain; an fp8 K pool's scale folds into the same factor
+  d.c = static_cast<float>(static_cast<double>(scale) * static_cast<double>(k_scale) *
+                           1.4426950408889634);  // log2(e)
   d.Qmax = 1;
   d.Qc = 1;
   d.q_off = 0;
   d.R = group;
+  d.v_scale = v_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_decode(b, d, head_dim, block_size, merge_groups_for(workers, cu), s) != hipSuccess)
-    return PKV_ERR_LAUNCH;
+  const int mg = merge_groups_for(workers, cu);
+  const hipError_t e = fp8 ? launch_decode_fp8(b, d, head_dim, block_size, mg, s)
+                           : launch_decode(b, d, head_dim, block_size, mg, s);
+  if (e != hipSuccess) return PKV_ERR_LAUNCH;
   return PKV_OK;
 }
 
@@ -180,6 +188,7 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   d.NB = num_blocks;
   d.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
   d.Qmax = max_query_len;
+  d.v_scale = 1.0f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t per = tokens_per_launch(group, max_query_len);
   const int64_t token_elems = static_cast<int64_t>(num_q_heads) * head_dim;
@@ -191,8 +200,8 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
     d.R = group * d.Qc;
     DecodeBuffers b;
     b.q = static_cast<const uint16_t*>(q) + off * token_elems;
-    b.k = static_cast<const uint16_t*>(k_cache);
-    b.v = static_cast<const uint16_t*>(v_cache);
+    b.k = k_cache;
+    b.v = v_cache;
     b.tables = block_tables;
     b.lens = context_lens;
     b.qlens = query_lens;
@@ -247,7 +256,21 @@ int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           void* stream) {
   return pkv::decode_impl(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, out,
                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                          num_blocks, max_context_len, workspace, workspace_bytes, stream);
+                          num_blocks, max_context_len, workspace, workspace_bytes, stream, false,
+                          1.0f, 1.0f);
+}
+
+int32_t paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t block_size, float scale, float k_scale, float v_scale,
+                              void* out, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, int32_t max_context_len, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return pkv::decode_impl(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, out,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          num_blocks, max_context_len, workspace, workspace_bytes, stream, true,
+                          k_scale, v_scale);
 }
 
 size_t paged_attn_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

@@ -46,6 +46,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -58,10 +60,14 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Tile buffers in registers (kPipe-1 loads in flight).  Two column tiles of
-// 128-dim rows leave room for two buffers only.
-template <int D, int NC>
+// 128-dim rows leave room for two buffers only; fp8 tiles are half the bytes, so
+// they keep more of them in flight.
+#ifndef PKV_FP8_PIPE
+#define PKV_FP8_PIPE 5
+#endif
+template <int D, int NC, bool kFp8>
 constexpr int pipe_depth() {
-  return (NC == 2 && D == 128) ? 2 : 3;
+  return kFp8 ? PKV_FP8_PIPE : ((NC == 2 && D == 128) ? 2 : 3);
 }
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: weights stay below 2^8
 
@@ -205,16 +211,11 @@ __device__ bool plan_worker(const int32_t* __restrict__ lens, const int32_t* __r
   return true;
 }
 
-template <int D, int B>
-struct TileRegs {
-  u32x4_t k[D / 32];  // score MFMA A operand: token lane%16, dims c*32 + (lane/16)*8 .. +7
-  u32x2_t v[D / 16];  // value MFMA A operand: dim mt*16 + lane%16, tokens (lane/16)*4 .. +3
-};
-
-// Where one (sequence, KV head) pair's tiles come from.
+// Where one (sequence, KV head) pair's tiles come from (T: pool element type).
+template <typename T>
 struct PairCursor {
-  const uint16_t* k;        // K pool
-  const uint16_t* v;        // V pool
+  const T* k;               // K pool
+  const T* v;               // V pool
   const int32_t* trow;      // block-table row of the sequence
   int64_t head_off;         // g * (elements of one (block, head) tile)
   int64_t block_stride;     // elements of one block (all heads)
@@ -222,44 +223,129 @@ struct PairCursor {
   int32_t nblk;             // ceil(L / B)
 };
 
-// Issue the loads of tile t.
+// A tile of bf16 K/V in registers: every lane's MFMA operands, as loaded.
 template <int D, int B>
-__device__ __forceinline__ void load_tile(TileRegs<D, B>& r, const PairCursor& pc, int32_t t,
-                                          int lane) {
-  const int32_t tok0 = t * kTile;
-  if constexpr (B >= kTile) {
-    const int32_t b = clamp_block(pc.trow[tok0 / B], pc.nb);
-    const int32_t ob = tok0 % B;
-    const int64_t base = static_cast<int64_t>(b) * pc.block_stride + pc.head_off;
-    const uint16_t* kt = pc.k + base;
-    const uint16_t* vt = pc.v + base;
-    const uint32_t koff = static_cast<uint32_t>(((lane >> 4) * B + ob + (lane & 15)) * 8);
-    const uint32_t voff = static_cast<uint32_t>((lane & 15) * B + ob + (lane >> 4) * 4);
+struct Bf16Tile {
+  using Elem = uint16_t;
+  u32x4_t k[D / 32];  // score MFMA A operand: token lane%16, dims c*32 + (lane/16)*8 .. +7
+  u32x2_t v[D / 16];  // value MFMA A operand: dim mt*16 + lane%16, tokens (lane/16)*4 .. +3
+
+  // Issue the loads of tile t.
+  __device__ __forceinline__ void load(const PairCursor<Elem>& pc, int32_t t, int lane) {
+    const int32_t tok0 = t * kTile;
+    if constexpr (B >= kTile) {
+      const int32_t b = clamp_block(pc.trow[tok0 / B], pc.nb);
+      const int32_t ob = tok0 % B;
+      const int64_t base = static_cast<int64_t>(b) * pc.block_stride + pc.head_off;
+      const uint16_t* kt = pc.k + base;
+      const uint16_t* vt = pc.v + base;
+      const uint32_t koff = static_cast<uint32_t>(((lane >> 4) * B + ob + (lane & 15)) * 8);
+      const uint32_t voff = static_cast<uint32_t>((lane & 15) * B + ob + (lane >> 4) * 4);
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      r.k[c] = *reinterpret_cast<const u32x4_t*>(kt + koff + c * 4 * B * 8);
+      for (int c = 0; c < D / 32; ++c)
+        k[c] = *reinterpret_cast<const u32x4_t*>(kt + koff + c * 4 * B * 8);
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt)
-      r.v[mt] = *reinterpret_cast<const u32x2_t*>(vt + voff + mt * 16 * B);
-  } else {
-    // B == 8: the tile spans logical blocks 2t and 2t+1 (the second clamped to the
-    // sequence's last block; its lanes are masked when it lies past the context).
-    static_assert(B == 8, "block sizes below 16 other than 8 are not built");
-    const int32_t j0 = tok0 / B;
-    const int32_t j1 = j0 + 1 < pc.nblk ? j0 + 1 : pc.nblk - 1;
-    const int64_t base0 = static_cast<int64_t>(clamp_block(pc.trow[j0], pc.nb)) * pc.block_stride;
-    const int64_t base1 = static_cast<int64_t>(clamp_block(pc.trow[j1], pc.nb)) * pc.block_stride;
-    const int64_t kb = ((lane & 15) < 8 ? base0 : base1) + pc.head_off;
-    const int64_t vb = ((lane >> 4) < 2 ? base0 : base1) + pc.head_off;
-    const uint16_t* kt = pc.k + kb + ((lane >> 4) * B + (lane & 7)) * 8;
-    const uint16_t* vt = pc.v + vb + (lane & 15) * B + ((lane >> 4) & 1) * 4;
+      for (int mt = 0; mt < D / 16; ++mt)
+        v[mt] = *reinterpret_cast<const u32x2_t*>(vt + voff + mt * 16 * B);
+    } else {
+      // B == 8: the tile spans logical blocks 2t and 2t+1 (the second clamped to
+      // the sequence's last block; its lanes are masked when it lies past the
+      // context).
+      static_assert(B == 8, "block sizes below 16 other than 8 are not built");
+      const int32_t j0 = tok0 / B;
+      const int32_t j1 = j0 + 1 < pc.nblk ? j0 + 1 : pc.nblk - 1;
+      const int64_t base0 = static_cast<int64_t>(clamp_block(pc.trow[j0], pc.nb)) * pc.block_stride;
+      const int64_t base1 = static_cast<int64_t>(clamp_block(pc.trow[j1], pc.nb)) * pc.block_stride;
+      const int64_t kb = ((lane & 15) < 8 ? base0 : base1) + pc.head_off;
+      const int64_t vb = ((lane >> 4) < 2 ? base0 : base1) + pc.head_off;
+      const uint16_t* kt = pc.k + kb + ((lane >> 4) * B + (lane & 7)) * 8;
+      const uint16_t* vt = pc.v + vb + (lane & 15) * B + ((lane >> 4) & 1) * 4;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) r.k[c] = *reinterpret_cast<const u32x4_t*>(kt + c * 4 * B * 8);
+      for (int c = 0; c < D / 32; ++c) k[c] = *reinterpret_cast<const u32x4_t*>(kt + c * 4 * B * 8);
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt)
-      r.v[mt] = *reinterpret_cast<const u32x2_t*>(vt + mt * 16 * B);
+      for (int mt = 0; mt < D / 16; ++mt)
+        v[mt] = *reinterpret_cast<const u32x2_t*>(vt + mt * 16 * B);
+    }
   }
+  __device__ __forceinline__ bf16x8_t kop(int cc) const { return __builtin_bit_cast(bf16x8_t, k[cc]); }
+  __device__ __forceinline__ u32x2_t vop(int mt) const { return v[mt]; }
+  // Keep the first n of this lane's four tokens (the others lie past the context).
+  __device__ __forceinline__ void mask_v(int32_t n) {
+    const uint64_t keep = n >= 4 ? ~0ull : (n <= 0 ? 0ull : ((1ull << (16 * n)) - 1));
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      v[mt].x &= static_cast<uint32_t>(keep);
+      v[mt].y &= static_cast<uint32_t>(keep >> 32);
+    }
+  }
+};
+
+// Two E4M3FN codes (word kHi of x) as two bf16 numbers, exactly: every E4M3
+// value is a bf16 value, and the conversion's scale is 1.
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, kHi));
 }
+
+// A tile of fp8 K/V in registers (one byte per element, 16-byte loads); the
+// operands are widened to bf16 when the MFMAs need them.  The score MFMA's
+// reduction runs over a permutation of the head dimension: MFMA cc at lane group
+// gq = lane/16 takes dims (cc/2)*64 + gq*16 + (cc%2)*8 .. +7 (the query uses the
+// same permutation).
+template <int D, int B>
+struct Fp8Tile {
+  using Elem = uint8_t;
+  u32x4_t k[D / 64];  // token lane%16, dims c*64 + (lane/16)*16 .. +15
+  u32x4_t v[D / 64];  // dims (4i + jj)*16 + lane%16 (dword jj), tokens (lane/16)*4 .. +3
+
+  __device__ __forceinline__ void load(const PairCursor<Elem>& pc, int32_t t, int lane) {
+    const int32_t tok0 = t * kTile;
+    const uint8_t* kt;
+    const uint8_t* vt;
+    if constexpr (B >= kTile) {
+      const int32_t b = clamp_block(pc.trow[tok0 / B], pc.nb);
+      const int32_t ob = tok0 % B;
+      const int64_t base = static_cast<int64_t>(b) * pc.block_stride + pc.head_off;
+      kt = pc.k + base + ((lane >> 4) * B + ob + (lane & 15)) * 16;
+      vt = pc.v + base + ((lane & 15) * (B / 4) + ob / 4 + (lane >> 4)) * (D / 16) * 4;
+    } else {
+      static_assert(B == 8, "block sizes below 16 other than 8 are not built");
+      const int32_t j0 = tok0 / B;
+      const int32_t j1 = j0 + 1 < pc.nblk ? j0 + 1 : pc.nblk - 1;
+      const int64_t base0 = static_cast<int64_t>(clamp_block(pc.trow[j0], pc.nb)) * pc.block_stride;
+      const int64_t base1 = static_cast<int64_t>(clamp_block(pc.trow[j1], pc.nb)) * pc.block_stride;
+      const int64_t kb = ((lane & 15) < 8 ? base0 : base1) + pc.head_off;
+      const int64_t vb = ((lane >> 4) < 2 ? base0 : base1) + pc.head_off;
+      kt = pc.k + kb + ((lane >> 4) * B + (lane & 7)) * 16;
+      vt = pc.v + vb + ((lane & 15) * (B / 4) + ((lane >> 4) & 1)) * (D / 16) * 4;
+    }
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) k[c] = *reinterpret_cast<const u32x4_t*>(kt + c * 4 * B * 16);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(vt + i * 16);
+  }
+  __device__ __forceinline__ bf16x8_t kop(int cc) const {
+    const u32x4_t w = k[cc / 2];
+    const uint32_t a = (cc & 1) ? w.z : w.x;
+    const uint32_t b = (cc & 1) ? w.w : w.y;
+    const u32x4_t r = {e4m3x2_to_bf16x2<false>(a), e4m3x2_to_bf16x2<true>(a),
+                       e4m3x2_to_bf16x2<false>(b), e4m3x2_to_bf16x2<true>(b)};
+    return __builtin_bit_cast(bf16x8_t, r);
+  }
+  __device__ __forceinline__ u32x2_t vop(int mt) const {
+    const uint32_t w = v[mt / 4][mt % 4];
+    return u32x2_t{e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
+  }
+  // Keep the first n of this lane's four tokens: code 0 is +0.
+  __device__ __forceinline__ void mask_v(int32_t n) {
+    const uint32_t keep = n >= 4 ? ~0u : (n <= 0 ? 0u : ((1u << (8 * n)) - 1));
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) v[i] &= keep;
+  }
+};
+
+template <int D, int B, bool kFp8>
+using TileOf = typename std::conditional<kFp8, Fp8Tile<D, B>, Bf16Tile<D, B>>::type;
 
 // Softmax state of one wave's column tile over one segment.
 template <int D>
@@ -301,8 +387,8 @@ __device__ __forceinline__ Cols<NC> make_cols(const DecodeDims& d, int lane) {
 // (16 except in the last tile).  Multi-token launches also mask by position:
 // column j of this lane sees the tile's tokens 0 .. lim[j], and lim_lo is the
 // smallest lim of the wave (nothing is masked by position when lim_lo >= 15).
-template <int D, int B, int NC, bool kCausal>
-__device__ __forceinline__ void compute_tile(TileRegs<D, B>& r, const bf16x8_t (&qop)[NC][D / 32],
+template <int D, int NC, bool kCausal, typename Tile>
+__device__ __forceinline__ void compute_tile(Tile& r, const bf16x8_t (&qop)[NC][D / 32],
                                              SegState<D> (&st)[NC], float c, int32_t valid,
                                              int32_t lim_lo, const int32_t (&lim)[NC], int lane) {
   f32x4_t sc[NC];
@@ -311,8 +397,7 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, B>& r, const bf16x8_t (
     sc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < D / 32; ++cc)
-      sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[cc]),
-                                                      qop[j][cc], sc[j], 0, 0, 0);
+      sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.kop(cc), qop[j][cc], sc[j], 0, 0, 0);
   }
   const int32_t tq = (lane >> 4) * 4;  // first of the four tokens this lane scores
   float x[NC][4];
@@ -335,16 +420,8 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, B>& r, const bf16x8_t (
         if (tq + i >= valid) x[0][i] = -INFINITY;
     }
   }
-  if (valid < kTile) {
-    // V rows past the context are zeroed: their slots may hold anything
-    const int32_t n = valid - tq;
-    const uint64_t keep = n >= 4 ? ~0ull : (n <= 0 ? 0ull : ((1ull << (16 * n)) - 1));
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      r.v[mt].x &= static_cast<uint32_t>(keep);
-      r.v[mt].y &= static_cast<uint32_t>(keep >> 32);
-    }
-  }
+  // V rows past the context are zeroed: their slots may hold anything
+  if (valid < kTile) r.mask_v(valid - tq);
   bool over = false;
 #pragma unroll
   for (int j = 0; j < NC; ++j)
@@ -386,15 +463,16 @@ __device__ __forceinline__ void compute_tile(TileRegs<D, B>& r, const bf16x8_t (
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt)
       st[j].o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-          __builtin_bit_cast(bf16x4_t, r.v[mt]), pb, st[j].o[mt], 0, 0, 0);
+          __builtin_bit_cast(bf16x4_t, r.vop(mt)), pb, st[j].o[mt], 0, 0, 0);
     st[j].l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, st[j].l, 0, 0, 0);
   }
 }
 
+template <typename T>
 struct Ctx {
   const uint16_t* __restrict__ q;
-  const uint16_t* __restrict__ k;
-  const uint16_t* __restrict__ v;
+  const T* __restrict__ k;
+  const T* __restrict__ v;
   const int32_t* __restrict__ tables;
   const int32_t* __restrict__ lens;
   const int32_t* __restrict__ qlens;
@@ -410,8 +488,8 @@ struct Cursor {
   int32_t s, g, t, T, L, Tq;
 };
 
-template <bool kCausal>
-__device__ __forceinline__ void advance(Cursor& c, const Ctx& cx, const DecodeDims& d,
+template <bool kCausal, typename Cx>
+__device__ __forceinline__ void advance(Cursor& c, const Cx& cx, const DecodeDims& d,
                                         int32_t cap) {
   if (++c.t < c.T) return;
   c.t = 0;
@@ -432,11 +510,11 @@ __device__ __forceinline__ void advance(Cursor& c, const Ctx& cx, const DecodeDi
   c.T = tiles_of(c.L);
 }
 
-template <int D, int B>
-__device__ __forceinline__ void load_at(TileRegs<D, B>& r, const Ctx& cx, const DecodeDims& d,
+template <int D, int B, typename Tile, typename Cx>
+__device__ __forceinline__ void load_at(Tile& r, const Cx& cx, const DecodeDims& d,
                                         const Cursor& c, int lane) {
   constexpr int64_t kTileElems = static_cast<int64_t>(D) * B;
-  PairCursor pc;
+  PairCursor<typename Tile::Elem> pc;
   pc.k = cx.k;
   pc.v = cx.v;
   pc.trow = cx.tables + static_cast<int64_t>(c.s) * d.M;
@@ -444,7 +522,7 @@ __device__ __forceinline__ void load_at(TileRegs<D, B>& r, const Ctx& cx, const 
   pc.head_off = kTileElems * c.g;
   pc.nb = d.NB;
   pc.nblk = (c.L + B - 1) / B;
-  load_tile<D, B>(r, pc, c.t, lane);
+  r.load(pc, c.t, lane);
 }
 
 // First q/out row of a (sequence, KV head) pair.
@@ -466,20 +544,29 @@ __device__ __forceinline__ bool live(const Cols<NC>& cl, int j, const Cursor& c)
   return cl.row[j] >= 0 && (!kCausal || cl.qi[j] < c.Tq);
 }
 
-// Score MFMA B operand: lane holds q[row of column j][c*32 + (lane/16)*8 .. +7];
-// zeros for columns the launch does not compute.
-template <int D, int NC, bool kCausal>
-__device__ __forceinline__ void load_q(bf16x8_t (&qop)[NC][D / 32], const Ctx& cx,
+// Score MFMA B operand: lane holds q[row of column j][c*32 + (lane/16)*8 .. +7]
+// (with fp8 K, the permuted dims (c/2)*64 + (lane/16)*16 + (c%2)*8 .. +7); zeros
+// for columns the launch does not compute.
+template <int D, int NC, bool kCausal, bool kFp8, typename Cx>
+__device__ __forceinline__ void load_q(bf16x8_t (&qop)[NC][D / 32], const Cx& cx,
                                        const DecodeDims& d, const Cursor& c, const Cols<NC>& cl,
                                        int lane) {
   const int64_t r0 = pair_row<kCausal>(d, c);
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     if (live<NC, kCausal>(cl, j, c)) {
-      const uint16_t* qr = cx.q + (r0 + cl.row[j]) * D + (lane >> 4) * 8;
+      if constexpr (kFp8) {
+        const uint16_t* qr = cx.q + (r0 + cl.row[j]) * D + (lane >> 4) * 16;
 #pragma unroll
-      for (int k = 0; k < D / 32; ++k)
-        qop[j][k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qr + k * 32));
+        for (int k = 0; k < D / 32; ++k)
+          qop[j][k] = __builtin_bit_cast(
+              bf16x8_t, *reinterpret_cast<const u32x4_t*>(qr + (k / 2) * 64 + (k % 2) * 8));
+      } else {
+        const uint16_t* qr = cx.q + (r0 + cl.row[j]) * D + (lane >> 4) * 8;
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k)
+          qop[j][k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qr + k * 32));
+      }
     } else {
 #pragma unroll
       for (int k = 0; k < D / 32; ++k)
@@ -490,8 +577,8 @@ __device__ __forceinline__ void load_q(bf16x8_t (&qop)[NC][D / 32], const Ctx& c
 
 // End of a segment: the output rows when it covered the whole pair, else a partial
 // record (O, then m, then l) in slot `rec`.
-template <int D, int NC, bool kCausal>
-__device__ void finish_segment(const Ctx& cx, const DecodeDims& d, const SegState<D> (&st)[NC],
+template <int D, int NC, bool kCausal, typename Cx>
+__device__ void finish_segment(const Cx& cx, const DecodeDims& d, const SegState<D> (&st)[NC],
                                const Cursor& c, const Cols<NC>& cl, bool whole, int64_t rec,
                                int lane) {
   const int64_t r0 = pair_row<kCausal>(d, c);
@@ -501,7 +588,7 @@ __device__ void finish_segment(const Ctx& cx, const DecodeDims& d, const SegStat
     if (!live<NC, kCausal>(cl, j, c)) continue;
     const float l_tot = st[j].l[0];
     if (whole) {
-      const float inv = 1.0f / l_tot;
+      const float inv = d.v_scale / l_tot;
       uint16_t* orow = cx.out + (r0 + cl.row[j]) * D + (lane >> 4) * 4;
 #pragma unroll
       for (int mt = 0; mt < D / 16; ++mt) {
@@ -528,8 +615,8 @@ __device__ void finish_segment(const Ctx& cx, const DecodeDims& d, const SegStat
 // tiles ahead of the arithmetic across (sequence, head) boundaries; the query of a
 // pair is fetched with the pair's first tile.  Returns the descriptor of the split
 // pair this worker opens (s = -1 if none).
-template <int D, int B, int NC, bool kCausal>
-__device__ int4 run_worker(const Ctx& cx, const DecodeDims& d, const WorkerPlan& pl, int64_t w,
+template <int D, int B, int NC, bool kCausal, bool kFp8, typename Cx>
+__device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& pl, int64_t w,
                            int lane) {
   const int32_t cap = d.M * B;
   const int32_t n = static_cast<int32_t>(pl.u_end - pl.u);
@@ -547,8 +634,8 @@ __device__ int4 run_worker(const Ctx& cx, const DecodeDims& d, const WorkerPlan&
   lc.t = static_cast<int32_t>((pl.u - pl.start) - static_cast<int64_t>(lc.g) * lc.T);
   Cursor cc = lc;
 
-  constexpr int kPipe = pipe_depth<D, NC>();
-  TileRegs<D, B> r[kPipe];
+  constexpr int kPipe = pipe_depth<D, NC, kFp8>();
+  TileOf<D, B, kFp8> r[kPipe];
   bf16x8_t qb[kPipe][NC][D / 32];
   bf16x8_t qc[NC][D / 32];
   SegState<D> st[NC];
@@ -558,7 +645,7 @@ __device__ int4 run_worker(const Ctx& cx, const DecodeDims& d, const WorkerPlan&
   int4 opened = {-1, 0, 0, 0};
 
   auto load_step = [&](int slot, int32_t li) {
-    if (lc.t == 0 || li == 0) load_q<D, NC, kCausal>(qb[slot], cx, d, lc, cl, lane);
+    if (lc.t == 0 || li == 0) load_q<D, NC, kCausal, kFp8>(qb[slot], cx, d, lc, cl, lane);
     load_at<D, B>(r[slot], cx, d, lc, lane);
     advance<kCausal>(lc, cx, d, cap);
   };
@@ -582,11 +669,11 @@ __device__ int4 run_worker(const Ctx& cx, const DecodeDims& d, const WorkerPlan&
       int32_t lim[NC];
 #pragma unroll
       for (int j = 0; j < NC; ++j) lim[j] = lim_abs[j] - cc.t * kTile;
-      compute_tile<D, B, NC, true>(r[slot], qc, st, d.c, valid, cc.L - cc.Tq - cc.t * kTile, lim,
-                                   lane);
+      compute_tile<D, NC, true>(r[slot], qc, st, d.c, valid, cc.L - cc.Tq - cc.t * kTile, lim,
+                                lane);
     } else {
       const int32_t lim[NC] = {valid - 1};
-      compute_tile<D, B, NC, false>(r[slot], qc, st, d.c, valid, valid - 1, lim, lane);
+      compute_tile<D, NC, false>(r[slot], qc, st, d.c, valid, valid - 1, lim, lane);
     }
     if (cc.t == cc.T - 1 || i == n - 1) {
       const bool whole = seg_t0 == 0 && cc.t == cc.T - 1;
@@ -631,13 +718,14 @@ __device__ int4 run_worker(const Ctx& cx, const DecodeDims& d, const WorkerPlan&
 // Workspace: partial records ([n_workers][2] of record_floats), then one
 // descriptor per worker: (s, g, wb, first_slot | Tq << 1) of the split pair whose
 // first share this worker holds, or s = -1 (Tq only in multi-token launches).
-template <int D, int B, int NC, bool kCausal>
+template <int D, int B, int NC, bool kCausal, bool kFp8>
 __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void decode_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ q, const typename TileOf<D, B, kFp8>::Elem* __restrict__ k,
+    const typename TileOf<D, B, kFp8>::Elem* __restrict__ v,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ qlens, uint16_t* __restrict__ out, float* __restrict__ ws,
     int4* __restrict__ desc, DecodeDims d) {
-  const Ctx cx{q, k, v, tables, lens, qlens, out, ws};
+  const Ctx<typename TileOf<D, B, kFp8>::Elem> cx{q, k, v, tables, lens, qlens, out, ws};
   const int lane = __lane_id();
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
   if (w >= d.n_workers) return;
@@ -646,7 +734,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void decode_kernel(
   int4 opened = {-1, 0, 0, 0};
   WorkerPlan pl;
   if (plan_worker<kCausal>(lens, qlens, d, cap, w, lane, pl))
-    opened = run_worker<D, B, NC, kCausal>(cx, d, pl, w, lane);
+    opened = run_worker<D, B, NC, kCausal, kFp8>(cx, d, pl, w, lane);
 
   // Rows no tile reaches are zeros: every row of an empty sequence, and in a
   // multi-token launch the rows past a sequence's query tokens (done last: off
@@ -679,7 +767,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void decode_kernel(
 // launches the rows past the pair's query tokens are left to the decode kernel.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeChunk = 16;
-constexpr int kMergeItems = 2;
+constexpr int kMergeItems = 1;
 constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
 
 template <int D, bool kCausal>
@@ -781,38 +869,42 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
         } else {
           idx = (static_cast<int64_t>(ds.x) * d.Hq + ds.y * d.G) * D + oi[it];
         }
-        out[idx] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[it] / run_l[it]));
+        out[idx] = __builtin_bit_cast(uint16_t,
+                                      static_cast<__bf16>(acc[it] / run_l[it] * d.v_scale));
       }
     }
   }
 }
 
-template <int D, int B, int NC, bool kCausal>
+template <int D, int B, int NC, bool kCausal, bool kFp8>
 hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
                     hipStream_t stream) {
+  using Elem = typename TileOf<D, B, kFp8>::Elem;
   const int groups = (d.n_workers + kWavesPerGroup - 1) / kWavesPerGroup;
   if (groups <= 0) return hipSuccess;
   int4* desc = reinterpret_cast<int4*>(reinterpret_cast<char*>(b.ws) +
                                        records_bytes(d.n_workers, d.R, D));
-  hipLaunchKernelGGL((decode_kernel<D, B, NC, kCausal>), dim3(groups), dim3(kWave * kWavesPerGroup),
-                     0, stream, b.q, b.k, b.v, b.tables, b.lens, b.qlens, b.out, b.ws, desc, d);
+  hipLaunchKernelGGL((decode_kernel<D, B, NC, kCausal, kFp8>), dim3(groups),
+                     dim3(kWave * kWavesPerGroup), 0, stream, b.q, static_cast<const Elem*>(b.k),
+                     static_cast<const Elem*>(b.v), b.tables, b.lens, b.qlens, b.out, b.ws, desc,
+                     d);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((merge_kernel<D, kCausal>), dim3(merge_groups), dim3(kMergeThreads), 0, stream,
                      desc, b.out, b.ws, d);
   return hipGetLastError();
 }
 
-template <int NC, bool kCausal>
+template <int NC, bool kCausal, bool kFp8>
 hipError_t dispatch(const DecodeBuffers& b, const DecodeDims& d, int D, int B, int merge_groups,
                     hipStream_t stream) {
   if (D == 128) {
-    if (B == 16) return launch_t<128, 16, NC, kCausal>(b, d, merge_groups, stream);
-    if (B == 32) return launch_t<128, 32, NC, kCausal>(b, d, merge_groups, stream);
-    if (B == 8) return launch_t<128, 8, NC, kCausal>(b, d, merge_groups, stream);
+    if (B == 16) return launch_t<128, 16, NC, kCausal, kFp8>(b, d, merge_groups, stream);
+    if (B == 32) return launch_t<128, 32, NC, kCausal, kFp8>(b, d, merge_groups, stream);
+    if (B == 8) return launch_t<128, 8, NC, kCausal, kFp8>(b, d, merge_groups, stream);
   } else if (D == 64) {
-    if (B == 16) return launch_t<64, 16, NC, kCausal>(b, d, merge_groups, stream);
-    if (B == 32) return launch_t<64, 32, NC, kCausal>(b, d, merge_groups, stream);
-    if (B == 8) return launch_t<64, 8, NC, kCausal>(b, d, merge_groups, stream);
+    if (B == 16) return launch_t<64, 16, NC, kCausal, kFp8>(b, d, merge_groups, stream);
+    if (B == 32) return launch_t<64, 32, NC, kCausal, kFp8>(b, d, merge_groups, stream);
+    if (B == 8) return launch_t<64, 8, NC, kCausal, kFp8>(b, d, merge_groups, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -821,13 +913,18 @@ hipError_t dispatch(const DecodeBuffers& b, const DecodeDims& d, int D, int B, i
 
 hipError_t launch_decode(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                          int merge_groups, hipStream_t stream) {
-  return dispatch<1, false>(b, d, D, B, merge_groups, stream);
+  return dispatch<1, false, false>(b, d, D, B, merge_groups, stream);
+}
+
+hipError_t launch_decode_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                             int merge_groups, hipStream_t stream) {
+  return dispatch<1, false, true>(b, d, D, B, merge_groups, stream);
 }
 
 hipError_t launch_multi(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                         int merge_groups, hipStream_t stream) {
-  if (d.R <= 16) return dispatch<1, true>(b, d, D, B, merge_groups, stream);
-  if (d.R <= kMaxRows) return dispatch<2, true>(b, d, D, B, merge_groups, stream);
+  if (d.R <= 16) return dispatch<1, true, false>(b, d, D, B, merge_groups, stream);
+  if (d.R <= kMaxRows) return dispatch<2, true, false>(b, d, D, B, merge_groups, stream);
   return hipErrorInvalidValue;
 }
 

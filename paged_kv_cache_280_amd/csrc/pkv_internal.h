@@ -17,8 +17,8 @@ constexpr int kMaxLayers = 128; // copy_blocks pool pointers travel as kernel ar
 // parameters so that reads of the block table and lengths become scalar loads.
 struct DecodeBuffers {
   const uint16_t* q;        // bf16 [S][Qmax][Hq][D], offset to the launch's first query token
-  const uint16_t* k;        // K pool
-  const uint16_t* v;        // V pool
+  const void* k;            // K pool (bf16, or fp8 codes)
+  const void* v;            // V pool
   const int32_t* tables;    // int32 [S][M]
   const int32_t* lens;      // int32 [S]
   const int32_t* qlens;     // int32 [S] query tokens per sequence (multi-token launches only)
@@ -39,6 +39,7 @@ struct DecodeDims {
   int32_t Qc;               // query tokens of this launch
   int32_t q_off;            // first query token of this launch
   int32_t R;                // rows of a (sequence, KV head) pair: G * Qc
+  float v_scale;            // multiplies the outputs (fp8 V pools; 1 for bf16)
 };
 
 // Floats in one partial record: O[R][D], then m[R], then l[R], padded to a
@@ -65,6 +66,10 @@ hipError_t launch_decode(const DecodeBuffers& b, const DecodeDims& d, int D, int
                          int merge_groups, hipStream_t stream);
 hipError_t launch_multi(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                         int merge_groups, hipStream_t stream);
+// Decode over fp8 (E4M3FN) pools: d.c carries scale * k_scale * log2(e), d.v_scale
+// the V pool's scale.
+hipError_t launch_decode_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                             int merge_groups, hipStream_t stream);
 
 // KV append (pkv_append.hip).
 struct AppendBuffers {

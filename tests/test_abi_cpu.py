@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["pkv_abi_version", "pkv_status_string",
                             "paged_attn_decode_workspace_bytes", "paged_attn_decode",
+                            "paged_attn_decode_fp8",
                             "paged_attn_multi_workspace_bytes", "paged_attn_multi",
                             "kv_append", "copy_blocks"])
 
@@ -113,6 +114,20 @@ def _multi_call(lib, **over):
 ])
 def test_multi_rejects_bad_arguments_on_the_host(lib, over, code):
     assert _multi_call(lib, **over) == code
+
+
+def test_fp8_decode_host_checks(lib):
+    call = lambda **o: lib.paged_attn_decode_fp8(
+        o.get("q", 0x1000), 0x2000, 0x3000, 0x4000, 0x5000, o.get("B", 16), 0.125,
+        o.get("ks", 0.05), o.get("vs", 0.05), o.get("out", 0x6000), o.get("S", 2), 8, 2,
+        o.get("D", 128), 4, 10, 64, 0x7000, 1 << 20, None)
+    assert call(ks=float("inf")) == -2
+    assert call(vs=float("nan")) == -2
+    assert call(D=96) == -3
+    assert call(B=40) == -3
+    assert call(q=None) == -1
+    assert call(out=0x6008) == -5
+    assert call(S=0, q=None, out=None) == 0
 
 
 def test_copy_blocks_host_checks(lib):
