@@ -39,6 +39,7 @@ METRIC = "paged decode: achieved KV GB/s (% of HBM peak) + decode tokens/s, 1 GP
 METRIC_MULTI = ("paged multi-token attention (T causal query tokens per sequence): achieved KV "
                 "GB/s (% of HBM peak) + query tokens/s, 1 GPU")
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+FP8_SCALE = 1.0 / 16   # K and V pool scales of the fp8 runs (N(0,1) values * 16 fit E4M3)
 CSRC = os.path.join(ROOT, "paged_kv_cache_280_amd", "csrc")
 
 
@@ -53,6 +54,8 @@ def parse():
                     help="each layer call first appends the new token's K/V (kv_append), "
                          "then decodes: the full per-layer decode step")
     ap.add_argument("--block-size", type=int, default=16)
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="fp8: K/V pools of E4M3FN codes with a scale of 1/16 each")
     ap.add_argument("--query-tokens", type=int, default=1,
                     help="T > 1: multi-token attention, T causal query tokens per sequence")
     ap.add_argument("--seed", type=int, default=0)
@@ -171,8 +174,13 @@ def build_workload(args, dev):
     pools = []
     for layer in range(layers):
         q, k, v, tabs, lens = wl.device_tensors(case, dev, layer=layer)
+        if args.kv_dtype == "fp8":
+            del k, v
+            k, v = wl.device_pools_fp8(case, dev, FP8_SCALE, FP8_SCALE, layer=layer)
         pools.append((q, k, v))
     torch.cuda.synchronize()
+    if args.kv_dtype == "fp8":
+        desc += ", fp8 E4M3 K/V"
     return case, layers, desc, pools, tabs, lens, extra
 
 
@@ -180,10 +188,25 @@ def cpu_baseline(case, pools, layers, args):
     """The oracle on the host cores over a bounded sample of the same workload:
     whole (layer, sequence) pairs in order until about ``--cpu-seconds`` of oracle
     time, scaled by context tokens to the full step.  With several query tokens the
-    oracle's multi-token attention runs on the same q rows the GPU reads."""
+    oracle's multi-token attention runs on the same q rows the GPU reads; with fp8
+    pools, the oracle's fp8 decode."""
     import torch
 
     import oracle
+
+    fp8 = args.kv_dtype == "fp8"
+
+    def run_oracle(qh, kh, vh, tab, L, threads):
+        lens = np.array([L], np.int32)
+        if args.query_tokens > 1:
+            oracle.paged_attn_multi(qh, kh, vh, tab, lens, np.array([args.query_tokens], np.int32),
+                                    case.block_size, case.scale, case.num_kv_heads, threads=threads)
+        elif fp8:
+            oracle.paged_decode_fp8(qh, kh, vh, tab, lens, case.block_size, case.scale, FP8_SCALE,
+                                    FP8_SCALE, case.num_kv_heads, threads=threads)
+        else:
+            oracle.paged_decode(qh, kh, vh, tab, lens, case.block_size, case.scale,
+                                case.num_kv_heads, threads=threads)
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     done_tokens = 0
@@ -195,18 +218,15 @@ def cpu_baseline(case, pools, layers, args):
             L = int(case.context_lens[s])
             nb = -(-L // case.block_size)
             idx = torch.from_numpy(case.block_tables[s, :nb].astype(np.int64)).to(kd.device)
-            kh = kd[idx].view(torch.int16).cpu().numpy().view(np.uint16)
-            vh = vd[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+            if fp8:
+                kh, vh = kd[idx].cpu().numpy(), vd[idx].cpu().numpy()
+            else:
+                kh = kd[idx].view(torch.int16).cpu().numpy().view(np.uint16)
+                vh = vd[idx].view(torch.int16).cpu().numpy().view(np.uint16)
             qh = q[s:s + 1].view(torch.int16).cpu().numpy().view(np.uint16)
             tab = np.arange(nb, dtype=np.int32)[None, :]
             t0 = time.perf_counter()
-            if args.query_tokens > 1:
-                oracle.paged_attn_multi(qh, kh, vh, tab, np.array([L], np.int32),
-                                        np.array([args.query_tokens], np.int32), case.block_size,
-                                        case.scale, case.num_kv_heads, threads=threads)
-            else:
-                oracle.paged_decode(qh, kh, vh, tab, np.array([L], np.int32), case.block_size,
-                                    case.scale, case.num_kv_heads, threads=threads)
+            run_oracle(qh, kh, vh, tab, L, threads)
             elapsed += time.perf_counter() - t0
             done_tokens += L
             pairs_done += 1
@@ -218,13 +238,7 @@ def cpu_baseline(case, pools, layers, args):
     step_seconds = elapsed * total_tokens / max(done_tokens, 1)
     # one core: the last sampled pair again, single-threaded
     t0 = time.perf_counter()
-    if args.query_tokens > 1:
-        oracle.paged_attn_multi(qh, kh, vh, tab, np.array([L], np.int32),
-                                np.array([args.query_tokens], np.int32), case.block_size,
-                                case.scale, case.num_kv_heads, threads=1)
-    else:
-        oracle.paged_decode(qh, kh, vh, tab, np.array([L], np.int32), case.block_size,
-                            case.scale, case.num_kv_heads, threads=1)
+    run_oracle(qh, kh, vh, tab, L, 1)
     one_core_step = (time.perf_counter() - t0) * total_tokens / max(L, 1)
     return {
         "value": round(case.num_seqs * args.query_tokens / step_seconds, 4),
@@ -368,6 +382,10 @@ def main():
     max_ctx = case.max_context_len
     T = args.query_tokens
     multi = T > 1
+    fp8 = args.kv_dtype == "fp8"
+    if fp8 and multi:
+        print("--kv-dtype fp8 is built for decode (one query token) only", file=sys.stderr)
+        sys.exit(2)
     if multi:
         # q of every layer becomes [S][T][Hq][D]; each sequence's last T positions
         # are its query tokens
@@ -381,9 +399,12 @@ def main():
     else:
         ws = pkv.new_workspace(S, Hq, Hkv, D, B, max_ctx, dev)
     outs = [torch.empty_like(p[0]) for p in pools]
+    kv_elem = 1 if fp8 else 2
     per_call_bytes = decode_algorithmic_bytes(case.context_lens, Hq, Hkv, D, B, query_tokens=T,
-                                              unique_tokens=extra.get("unique_tokens"))
-    logical_bytes = decode_algorithmic_bytes(case.context_lens, Hq, Hkv, D, B, query_tokens=T)
+                                              unique_tokens=extra.get("unique_tokens"),
+                                              kv_elem_bytes=kv_elem)
+    logical_bytes = decode_algorithmic_bytes(case.context_lens, Hq, Hkv, D, B, query_tokens=T,
+                                             kv_elem_bytes=kv_elem)
 
     stream = torch.cuda.current_stream(dev)
     n_ev = args.steps * layers
@@ -416,6 +437,9 @@ def main():
             if multi:
                 pkv.paged_attn_multi(q, k, v, tabs, lens, qlens, B, case.scale, outs[layer],
                                      workspace=ws, max_context_len=max_ctx)
+            elif fp8:
+                pkv.paged_attn_decode_fp8(q, k, v, tabs, lens, B, case.scale, FP8_SCALE, FP8_SCALE,
+                                          outs[layer], workspace=ws, max_context_len=max_ctx)
             else:
                 pkv.paged_attn_decode(q, k, v, tabs, lens, B, case.scale, outs[layer],
                                       workspace=ws, max_context_len=max_ctx)
@@ -471,7 +495,7 @@ def main():
     tokens_per_s = S * T / (ms_per_step / 1e3)
     kv_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
     achieved = per_call_bytes / kern_avg_s / 1e9
-    traffic = measured_traffic(args.workload if not multi else "%s_q%d" % (args.workload, T))
+    traffic = measured_traffic(args.workload + ("_q%d" % T if multi else "") + ("_fp8" if fp8 else ""))
 
     line = {
         "metric": METRIC_MULTI if multi else METRIC,
@@ -484,7 +508,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 q/out, fp8 e4m3 K/V" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": desc, "num_seqs": S, "context_len": int(case.context_lens.max()),
                    "layers": layers, "block_size": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
@@ -498,7 +522,8 @@ def main():
                         "calls": len(kern_ms)},
         "attainable": attain,
         "roofline": {"bound": "hbm",
-                     "kernel": ("paged_attn_multi" if multi else "paged_attn_decode") +
+                     "kernel": ("paged_attn_multi" if multi else
+                                "paged_attn_decode_fp8" if fp8 else "paged_attn_decode") +
                                " (decode_kernel + merge_kernel)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

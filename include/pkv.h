@@ -65,11 +65,11 @@ int32_t pkv_abi_version(void);
 const char* pkv_status_string(int32_t status);
 
 /*
- * Bytes of device scratch paged_attn_decode needs for these sizes on the
- * current device.  The scratch holds the partial softmax states of (sequence,
- * KV head) pairs whose context is split across workers (split-K) and which
- * worker opens each split pair.  Returns 0 for sizes paged_attn_decode would
- * reject.
+ * Bytes of device scratch paged_attn_decode and paged_attn_decode_fp8 need for
+ * these sizes on the current device (one figure covers both).  The scratch holds
+ * the partial softmax states of (sequence, KV head) pairs whose context is split
+ * across workers (split-K) and which worker opens each split pair.  Returns 0 for
+ * sizes paged_attn_decode would reject.
  */
 size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim,

@@ -29,15 +29,16 @@ def blocks_needed(tokens, block_size: int):
 
 def decode_algorithmic_bytes(context_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
                              block_size: int, elem_bytes: int = 2, unique_tokens=None,
-                             query_tokens: int = 1) -> int:
+                             query_tokens: int = 1, kv_elem_bytes=None) -> int:
     """Algorithmic bytes of one decode call (``query_tokens`` > 1: one multi-token
     call with that many query rows per sequence, plus its query lengths).
     ``unique_tokens`` replaces the sum of context lengths when sequences share
-    physical blocks (count each stored slot once)."""
+    physical blocks (count each stored slot once); ``kv_elem_bytes`` is the size of
+    one stored K/V element when it differs from q's (1 for fp8 pools)."""
     lens = np.asarray(context_lens, dtype=np.int64)
     S = lens.size
     tokens = int(lens.sum()) if unique_tokens is None else int(unique_tokens)
-    kv = tokens * num_kv_heads * head_dim * elem_bytes * 2
+    kv = tokens * num_kv_heads * head_dim * (kv_elem_bytes or elem_bytes) * 2
     qo = 2 * S * int(query_tokens) * num_q_heads * head_dim * elem_bytes
     tables = int(blocks_needed(lens, block_size).sum()) * 4
     qlens = 4 * S if query_tokens > 1 else 0

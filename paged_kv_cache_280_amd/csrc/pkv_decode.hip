@@ -60,14 +60,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Tile buffers in registers (kPipe-1 loads in flight).  Two column tiles of
-// 128-dim rows leave room for two buffers only; fp8 tiles are half the bytes, so
-// they keep more of them in flight.
-#ifndef PKV_FP8_PIPE
-#define PKV_FP8_PIPE 5
-#endif
+// 128-dim rows leave room for two buffers only.  fp8 tiles run best with two
+// buffers too (measured: fewer registers, 200 VGPRs at D = 128, beat deeper
+// pipelines on every workload).
 template <int D, int NC, bool kFp8>
 constexpr int pipe_depth() {
-  return kFp8 ? PKV_FP8_PIPE : ((NC == 2 && D == 128) ? 2 : 3);
+  return (kFp8 || (NC == 2 && D == 128)) ? 2 : 3;
 }
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: weights stay below 2^8
 
@@ -719,7 +717,7 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
 // descriptor per worker: (s, g, wb, first_slot | Tq << 1) of the split pair whose
 // first share this worker holds, or s = -1 (Tq only in multi-token launches).
 template <int D, int B, int NC, bool kCausal, bool kFp8>
-__global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void decode_kernel(
+__global__ __launch_bounds__(kWave* kWavesPerGroup, kFp8 ? 2 : 1) void decode_kernel(
     const uint16_t* __restrict__ q, const typename TileOf<D, B, kFp8>::Elem* __restrict__ k,
     const typename TileOf<D, B, kFp8>::Elem* __restrict__ v,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
