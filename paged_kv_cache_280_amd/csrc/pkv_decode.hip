@@ -758,17 +758,20 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, kFp8 ? 2 : 1) void decode_ke
 // Merge of split pairs.  Work-group b reads the descriptors of its slice of
 // workers in one parallel pass and keeps the valid ones in LDS (each names a split
 // pair opened by worker wa and closed by wb).  The (pair, output) items of those
-// pairs are spread over the threads, kMergeItems per thread at a time; an item
-// folds the records of wa..wb in worker order with a running max, kMergeChunk
-// records per batch, and the loads of all of a thread's items are issued together.
-// The order is fixed, so the result does not depend on timing.  In multi-token
-// launches the rows past the pair's query tokens are left to the decode kernel.
+// pairs are spread over the threads, kItems per thread at a time; an item folds
+// the records of wa..wb in worker order with a running max, kChunk records per
+// batch, and the loads of all of a thread's items are issued together.  The order
+// is fixed, so the result does not depend on timing.  In multi-token launches the
+// rows past the pair's query tokens are left to the decode kernel.
+//
+// Two shapes (measured): pairs split over more than 12 workers take one item of
+// 16 records per batch (one round trip for a 16-way split); otherwise two items of
+// 12 records each, so that more independent loads are in flight.
 constexpr int kMergeThreads = 512;
-constexpr int kMergeChunk = 16;
-constexpr int kMergeItems = 1;
 constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
+constexpr int kMergeWideSplit = 12;
 
-template <int D, bool kCausal>
+template <int D, bool kCausal, int kChunk, int kItems>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __restrict__ desc,
                                                               uint16_t* __restrict__ out,
                                                               const float* __restrict__ ws,
@@ -794,13 +797,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
   const int64_t rf = record_floats(d.R, D);
   const int32_t RD = d.R * D;
   const int32_t total = s_count * RD;
-  for (int32_t base = tid; base < total; base += kMergeThreads * kMergeItems) {
-    float run_m[kMergeItems], run_l[kMergeItems], acc[kMergeItems];
-    int64_t wa[kMergeItems], wb[kMergeItems], first[kMergeItems];
-    int32_t pi[kMergeItems], oi[kMergeItems];
-    bool act[kMergeItems];
+  for (int32_t base = tid; base < total; base += kMergeThreads * kItems) {
+    float run_m[kItems], run_l[kItems], acc[kItems];
+    int64_t wa[kItems], wb[kItems], first[kItems];
+    int32_t pi[kItems], oi[kItems];
+    bool act[kItems];
 #pragma unroll
-    for (int it = 0; it < kMergeItems; ++it) {
+    for (int it = 0; it < kItems; ++it) {
       const int32_t item = base + it * kMergeThreads;
       run_m[it] = -INFINITY;
       run_l[it] = 0.f;
@@ -815,14 +818,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
     }
     int64_t kmax = 0;
 #pragma unroll
-    for (int it = 0; it < kMergeItems; ++it) kmax = max(kmax, wb[it] - wa[it] + 1);
-    for (int64_t c = 0; c < kmax; c += kMergeChunk) {
-      float m[kMergeItems][kMergeChunk], l[kMergeItems][kMergeChunk], o[kMergeItems][kMergeChunk];
+    for (int it = 0; it < kItems; ++it) kmax = max(kmax, wb[it] - wa[it] + 1);
+    for (int64_t c = 0; c < kmax; c += kChunk) {
+      float m[kItems][kChunk], l[kItems][kChunk], o[kItems][kChunk];
 #pragma unroll
-      for (int it = 0; it < kMergeItems; ++it) {
+      for (int it = 0; it < kItems; ++it) {
         const int32_t h = oi[it] / D;
 #pragma unroll
-        for (int k = 0; k < kMergeChunk; ++k) {
+        for (int k = 0; k < kChunk; ++k) {
           const int64_t wk = wa[it] + c + k;
           if (wk <= wb[it]) {
             const float* rec = ws + (c + k == 0 ? first[it] : 2 * wk * rf);
@@ -837,17 +840,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
         }
       }
 #pragma unroll
-      for (int it = 0; it < kMergeItems; ++it) {
+      for (int it = 0; it < kItems; ++it) {
         float cm = run_m[it];
 #pragma unroll
-        for (int k = 0; k < kMergeChunk; ++k) cm = fmaxf(cm, m[it][k]);
+        for (int k = 0; k < kChunk; ++k) cm = fmaxf(cm, m[it][k]);
         if (cm == -INFINITY) continue;  // item past the end, or no record in this chunk
         const float scale = __builtin_amdgcn_exp2f(run_m[it] - cm);
         run_l[it] *= scale;
         acc[it] *= scale;
         run_m[it] = cm;
 #pragma unroll
-        for (int k = 0; k < kMergeChunk; ++k) {
+        for (int k = 0; k < kChunk; ++k) {
           const float e = __builtin_amdgcn_exp2f(m[it][k] - cm);
           run_l[it] += e * l[it][k];
           acc[it] += e * o[it][k];
@@ -855,7 +858,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
       }
     }
 #pragma unroll
-    for (int it = 0; it < kMergeItems; ++it) {
+    for (int it = 0; it < kItems; ++it) {
       if (act[it]) {
         const int4 ds = s_desc[pi[it]];
         int64_t idx;
@@ -887,8 +890,14 @@ hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_group
                      static_cast<const Elem*>(b.v), b.tables, b.lens, b.qlens, b.out, b.ws, desc,
                      d);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL((merge_kernel<D, kCausal>), dim3(merge_groups), dim3(kMergeThreads), 0, stream,
-                     desc, b.out, b.ws, d);
+  // records per split pair: about the workers per (sequence, KV head) pair
+  const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
+  if (pairs > 0 && d.n_workers > kMergeWideSplit * pairs)
+    hipLaunchKernelGGL((merge_kernel<D, kCausal, 16, 1>), dim3(merge_groups), dim3(kMergeThreads), 0,
+                       stream, desc, b.out, b.ws, d);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, kCausal, 12, 2>), dim3(merge_groups), dim3(kMergeThreads), 0,
+                       stream, desc, b.out, b.ws, d);
   return hipGetLastError();
 }
 
