@@ -15,10 +15,24 @@ rule against the pages:
   in the last, partly filled block of each sequence; branches with a common
   prefix share blocks instead of duplicating them.
 
+* "vLLM PagedAttention: Bước đột phá về thông lượng suy luận LLM"
+  (vi.news.hada.io), list of advanced features, prefix caching: requests whose
+  prompts begin alike share the KV cache of that common beginning instead of
+  computing it again.
+
 Readings where the pages are silent: the free list is LIFO (the most recently
 freed block is handed out first) and starts in the order the caller gives; a
 request that cannot be met leaves every piece of state untouched; a write into
 a block whose reference count is 1 happens in place.
+
+Prefix caching (readings): only full blocks of a prompt are shared, and a block
+is identified by every token from position 0 to its end (its K/V depend on all
+of them); a new prompt reuses cached blocks from its start up to its first block
+that is not cached, its other blocks are taken, and then its new full blocks
+join the cache (each unless its key is already there); a cached block whose last user leaves keeps its contents and
+stays findable, and is handed out for new contents only when the free list is
+empty, least recently released first (its cache entry is then dropped); a
+finished sequence releases its blocks last to first.
 """
 
 from __future__ import annotations
@@ -41,31 +55,77 @@ class BlockModel:
         self.tables = {}   # seq id -> list of physical block ids
         self.lens = {}     # seq id -> number of tokens
         self.copies = []   # (src, dst) pairs emitted by copy-on-write, in order
+        self.cached = {}     # tuple of tokens 0 .. end of block -> block id
+        self.key_of = {}     # block id -> its key in self.cached
+        self.evictable = []  # cached blocks nobody holds, least recently released first
 
     # -- helpers ---------------------------------------------------------------
     def _take(self) -> int:
-        b = self.free.pop()
+        if self.free:
+            b = self.free.pop()
+        else:
+            b = self.evictable.pop(0)
+            del self.cached[self.key_of.pop(b)]
         self.refcount[b] = 1
         return b
 
     def _release(self, b: int) -> None:
         self.refcount[b] -= 1
         if self.refcount[b] == 0:
-            self.free.append(b)
+            if b in self.key_of:
+                self.evictable.append(b)
+            else:
+                self.free.append(b)
+
+    def available(self) -> int:
+        return len(self.free) + len(self.evictable)
 
     def blocks_for(self, n_tokens: int) -> int:
         return -(-int(n_tokens) // self.block_size)
 
     # -- operations --------------------------------------------------------------
-    def add(self, seq, n_tokens: int) -> None:
-        """A new sequence holding n_tokens (its prompt)."""
+    def add(self, seq, n_tokens: int, tokens=None) -> int:
+        """A new sequence holding n_tokens (its prompt).  With the prompt's token
+        ids, its leading full blocks come from the prefix cache where they can;
+        returns how many of its tokens were found there (their K/V need not be
+        written again)."""
         if seq in self.tables:
             raise KeyError(seq)
+        n_tokens = int(n_tokens)
         need = self.blocks_for(n_tokens)
-        if need > len(self.free):
-            raise PoolExhausted("need %d blocks, %d free" % (need, len(self.free)))
-        self.tables[seq] = [self._take() for _ in range(need)]
-        self.lens[seq] = int(n_tokens)
+        B = self.block_size
+        hits = []
+        if tokens is not None:
+            tokens = [int(t) for t in tokens]
+            if len(tokens) != n_tokens:
+                raise ValueError("one token id per prompt position")
+            for j in range(n_tokens // B):
+                key = tuple(tokens[:(j + 1) * B])
+                if key not in self.cached:
+                    break
+                hits.append(self.cached[key])
+        revived = sum(1 for b in hits if self.refcount[b] == 0)
+        if need - len(hits) > self.available() - revived:
+            raise PoolExhausted("need %d blocks, %d free" % (need - len(hits),
+                                                            self.available() - revived))
+        table = []
+        for b in hits:
+            if self.refcount[b] == 0:
+                self.evictable.remove(b)
+            self.refcount[b] += 1
+            table.append(b)
+        for j in range(len(hits), need):
+            table.append(self._take())
+        # then the new full blocks join the cache, each unless its key is there
+        for j in range(len(hits), need):
+            if tokens is not None and (j + 1) * B <= n_tokens:
+                key = tuple(tokens[:(j + 1) * B])
+                if key not in self.cached:
+                    self.cached[key] = table[j]
+                    self.key_of[table[j]] = key
+        self.tables[seq] = table
+        self.lens[seq] = n_tokens
+        return len(hits) * B
 
     def append(self, seq, n_tokens: int = 1) -> None:
         """Write n_tokens more tokens at the end of seq."""
@@ -76,8 +136,8 @@ class BlockModel:
         last_shared = (n_tokens > 0 and L % self.block_size != 0
                        and self.refcount[table[-1]] > 1)
         need = new_blocks + (1 if last_shared else 0)
-        if need > len(self.free):
-            raise PoolExhausted("need %d blocks, %d free" % (need, len(self.free)))
+        if need > self.available():
+            raise PoolExhausted("need %d blocks, %d free" % (need, self.available()))
         if last_shared:
             src = table[-1]
             dst = self._take()
@@ -98,7 +158,9 @@ class BlockModel:
             self.refcount[b] += 1
 
     def free_seq(self, seq) -> None:
-        for b in self.tables.pop(seq):
+        """Release the blocks last to first: a prompt's first blocks, the ones other
+        prompts can share, become the most recently released and are evicted last."""
+        for b in reversed(self.tables.pop(seq)):
             self._release(b)
         del self.lens[seq]
 
@@ -110,8 +172,13 @@ class BlockModel:
                 counted[b] += 1
         assert counted == self.refcount, "refcounts disagree with the tables"
         live = sum(1 for c in self.refcount if c > 0)
-        assert live + len(self.free) == self.num_blocks, "free + live != pool"
-        assert len(set(self.free)) == len(self.free), "a block is free twice"
-        assert all(self.refcount[b] == 0 for b in self.free), "a free block is referenced"
+        assert live + len(self.free) + len(self.evictable) == self.num_blocks, \
+            "free + evictable + live != pool"
+        idle = self.free + self.evictable
+        assert len(set(idle)) == len(idle), "a block is free twice"
+        assert all(self.refcount[b] == 0 for b in idle), "a free block is referenced"
+        assert all(b in self.key_of for b in self.evictable), "an evictable block has no key"
+        assert all(b not in self.key_of for b in self.free), "a free block is still cached"
+        assert all(self.cached[k] == b for b, k in self.key_of.items()), "cache maps disagree"
         for seq, table in self.tables.items():
             assert len(table) == self.blocks_for(self.lens[seq])

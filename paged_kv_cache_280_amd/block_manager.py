@@ -8,7 +8,21 @@ What it does, after "PagedAttention (vLLM)" (troisinh.com):
 * section "Copy-on-Write cho Beam Search": sequences forked from one another
   (parallel sampling, beam search) share the physical blocks of their common
   prefix; a shared block is copied the moment one sharer writes into it;
-* section "Vấn đề": a request that the pool cannot hold is refused.
+* section "Vấn đề": a request that the pool cannot hold is refused;
+* prefix caching ("vLLM PagedAttention: Bước đột phá về thông lượng suy luận
+  LLM", vi.news.hada.io, list of advanced features): a prompt that begins like
+  an earlier one reuses the blocks holding that beginning instead of computing
+  its K/V again.
+
+Prefix cache: a full prompt block is keyed by a SHA-256 chain over the token ids
+of every block up to and including it (the key of block j hashes the key of
+block j-1 and block j's ids), so equal keys mean equal token prefixes.  A new
+prompt takes cached blocks from its start up to its first block that is not
+cached; its other full blocks join the cache (unless their key is already
+there).  A cached block whose last holder leaves keeps its contents and stays
+findable (evictable); such blocks are handed out for new contents only once the
+free stack is empty, least recently released first, and lose their key then.  A
+finished sequence releases its blocks last to first.
 
 Design: reference counts and the free list live in numpy arrays; the free list is
 a stack (the most recently freed block is reused first, so a sequence that
@@ -19,6 +33,9 @@ nothing.
 """
 
 from __future__ import annotations
+
+import hashlib
+from collections import OrderedDict
 
 import numpy as np
 
@@ -44,15 +61,31 @@ class BlockManager:
         self._tables: dict = {}
         self._lens: dict = {}
         self._copies: list = []
+        self._cache: dict = {}                  # chain key -> block id
+        self._key_of: dict = {}                 # block id -> chain key
+        self._evictable: OrderedDict = OrderedDict()  # released cached blocks, oldest first
 
     # -- pool ------------------------------------------------------------------
     @property
     def num_free(self) -> int:
-        return self._top
+        """Blocks a request can be given: the free stack plus evictable cached blocks."""
+        return self._top + len(self._evictable)
+
+    @property
+    def num_cached(self) -> int:
+        return len(self._cache)
 
     def _take(self, n: int) -> np.ndarray:
-        ids = self._stack[self._top - n:self._top][::-1].copy()
-        self._top -= n
+        k = min(n, self._top)
+        ids = self._stack[self._top - k:self._top][::-1].copy()
+        self._top -= k
+        if k < n:   # the stack ran dry: evict the least recently released cached blocks
+            more = []
+            for _ in range(n - k):
+                b, _ = self._evictable.popitem(last=False)
+                del self._cache[self._key_of.pop(b)]
+                more.append(b)
+            ids = np.concatenate([ids, np.asarray(more, dtype=np.int32)])
         self.refcount[ids] = 1
         return ids
 
@@ -60,22 +93,60 @@ class BlockManager:
         for b in ids:
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
-                self._stack[self._top] = b
-                self._top += 1
+                if b in self._key_of:
+                    self._evictable[int(b)] = None
+                else:
+                    self._stack[self._top] = b
+                    self._top += 1
+
+    @staticmethod
+    def _chain(prev: bytes, block_tokens) -> bytes:
+        return hashlib.sha256(prev + np.asarray(block_tokens, dtype="<i8").tobytes()).digest()
 
     def blocks_for(self, n_tokens: int) -> int:
         return -(-int(n_tokens) // self.block_size)
 
     # -- sequences ----------------------------------------------------------------
-    def add(self, seq, n_tokens: int) -> None:
-        """Admit a sequence whose first n_tokens (its prompt) are about to be written."""
+    def add(self, seq, n_tokens: int, tokens=None) -> int:
+        """Admit a sequence whose first n_tokens (its prompt) are about to be written.
+        With the prompt's token ids the prefix cache is used: returns the number of
+        leading prompt tokens found there (their K/V are already in the pool; only
+        the rest must be written)."""
         if seq in self._tables:
             raise KeyError("sequence %r exists" % (seq,))
+        n_tokens = int(n_tokens)
         need = self.blocks_for(n_tokens)
-        if need > self._top:
-            raise PoolExhausted("need %d blocks, %d free" % (need, self._top))
-        self._tables[seq] = list(self._take(need))
-        self._lens[seq] = int(n_tokens)
+        B = self.block_size
+        hits, keys = [], []
+        if tokens is not None:
+            tokens = np.asarray(tokens, dtype=np.int64)
+            if tokens.shape != (n_tokens,):
+                raise ValueError("one token id per prompt position")
+            prev = b""
+            for j in range(n_tokens // B):
+                prev = self._chain(prev, tokens[j * B:(j + 1) * B])
+                keys.append(prev)
+            for key in keys:
+                b = self._cache.get(key)
+                if b is None:
+                    break
+                hits.append(b)
+        revived = sum(1 for b in hits if self.refcount[b] == 0)
+        if need - len(hits) > self.num_free - revived:
+            raise PoolExhausted("need %d blocks, %d free" % (need - len(hits),
+                                                            self.num_free - revived))
+        for b in hits:
+            if self.refcount[b] == 0:
+                del self._evictable[b]
+            self.refcount[b] += 1
+        new = list(self._take(need - len(hits)))
+        for j, b in enumerate(new, start=len(hits)):
+            if j < len(keys) and keys[j] not in self._cache:
+                self._cache[keys[j]] = int(b)
+                self._key_of[int(b)] = keys[j]
+        self._tables[seq] = [int(b) for b in hits] + [int(b) for b in new]
+        self._lens[seq] = n_tokens
+        return len(hits) * B
 
     def append(self, seq, n_tokens: int = 1):
         """Make room for n_tokens more tokens at the end of seq.  Returns the slots
@@ -87,8 +158,8 @@ class BlockManager:
         B = self.block_size
         grow = self.blocks_for(L + n_tokens) - len(table)
         cow = n_tokens > 0 and L % B != 0 and self.refcount[table[-1]] > 1
-        if grow + cow > self._top:
-            raise PoolExhausted("need %d blocks, %d free" % (grow + cow, self._top))
+        if grow + cow > self.num_free:
+            raise PoolExhausted("need %d blocks, %d free" % (grow + cow, self.num_free))
         if cow:
             src = table[-1]
             dst = int(self._take(1)[0])
@@ -111,7 +182,9 @@ class BlockManager:
         np.add.at(self.refcount, np.asarray(table, dtype=np.int64), 1)
 
     def free(self, seq) -> None:
-        self._give_back(self._tables.pop(seq))
+        """Release seq's blocks last to first, so that the first blocks of a prompt
+        (the ones others can share) are the last to be evicted."""
+        self._give_back(self._tables.pop(seq)[::-1])
         del self._lens[seq]
 
     # -- views handed to the GPU calls --------------------------------------------
@@ -151,4 +224,9 @@ class BlockManager:
         return 0.0 if held == 0 else (held - used) / held
 
     def free_ids(self) -> np.ndarray:
+        """Blocks on the free stack (holding nothing anyone can find)."""
         return self._stack[:self._top].copy()
+
+    def evictable_ids(self) -> np.ndarray:
+        """Cached blocks nobody holds, least recently released first."""
+        return np.asarray(list(self._evictable), dtype=np.int32)

@@ -15,8 +15,10 @@ def same_state(bm: BlockManager, model: BlockModel):
         assert bm.table(s) == model.tables[s], s
         assert bm.context_len(s) == model.lens[s]
     assert bm.refcount.tolist() == model.refcount
-    # same free blocks in the same LIFO order
+    # same free blocks in the same LIFO order, same evictable cached blocks in order
     assert bm.free_ids().tolist() == model.free
+    assert bm.evictable_ids().tolist() == model.evictable
+    assert bm.num_cached == len(model.cached)
     model.check_conservation()
 
 
@@ -130,3 +132,133 @@ def test_batch_view():
     assert tabs.shape == (3, 3) and tabs.dtype == np.int32
     assert tabs[0, :2].tolist() == bm.table("a") and tabs[0, 2] == 49
     assert (tabs[1] == 49).all()
+
+
+# ---------------------------------------------------------------------------
+# Prefix caching and beam search
+# ---------------------------------------------------------------------------
+
+def test_second_request_with_the_same_system_prompt_reuses_its_full_blocks():
+    B = 16
+    bm = BlockManager(100, B, np.arange(100))
+    system = list(range(1000, 1000 + 100))          # 6 full blocks + 4 tokens
+    a = system + [1, 2, 3]
+    b = system + [7, 8]
+    assert bm.add("a", len(a), a) == 0                # nothing cached yet
+    assert bm.add("b", len(b), b) == 6 * B            # the 6 full blocks of the prompt
+    assert bm.table("b")[:6] == bm.table("a")[:6]
+    assert bm.table("b")[6] != bm.table("a")[6]       # the partly filled block is private
+    assert all(bm.refcount[x] == 2 for x in bm.table("a")[:6])
+    # a prompt that differs inside block 2 shares only blocks 0 and 1
+    c = system[:40] + [5] + system[41:]
+    assert bm.add("c", len(c), c) == 2 * B
+    assert bm.table("c")[:2] == bm.table("a")[:2] and bm.table("c")[2] not in bm.table("a")
+
+
+def test_cached_blocks_outlive_their_requests_and_are_evicted_oldest_first():
+    B = 8
+    bm = BlockManager(10, B, np.arange(10))
+    p = list(range(16))                              # two full blocks
+    bm.add("a", 16, p)
+    blocks = bm.table("a")
+    bm.free("a")
+    assert bm.num_free == 10 and bm.evictable_ids().tolist() == blocks[::-1]   # last first
+    assert bm.add("again", 16, p) == 16              # found although nobody held them
+    assert bm.table("again") == blocks
+    bm.free("again")
+    q = [100 + i for i in range(64)]                 # 8 blocks: the whole free stack
+    assert bm.add("q", 64, q) == 0
+    q_blocks = bm.table("q")
+    bm.add("r", 8, [7] * 8)                          # the stack is empty: the oldest released
+    assert bm.table("r") == [blocks[1]]              # cached block goes first: p's second block
+    bm.free("q")                                     # q's full blocks become evictable (last first)
+    assert bm.add("again2", 16, p) == B              # p's first block is still found
+    assert bm.table("again2") == [blocks[0], q_blocks[-1]]
+    # a refused request changes nothing
+    before = (bm.evictable_ids().tolist(), bm.num_cached, bm.refcount.tolist())
+    with pytest.raises(PoolExhausted):
+        bm.add("too_big", 11 * B, list(range(11 * B)))
+    assert (bm.evictable_ids().tolist(), bm.num_cached, bm.refcount.tolist()) == before
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefix_cache_matches_the_oracle_model_on_random_scripts(seed):
+    rng = np.random.default_rng(100 + seed)
+    nb, B = 120, int(rng.choice([8, 16, 32]))
+    order = rng.permutation(nb)
+    bm = BlockManager(nb, B, order)
+    model = BlockModel(nb, B, order)
+    systems = [list(rng.integers(0, 50, size=int(rng.integers(B, 6 * B)))) for _ in range(3)]
+    live, next_id = [], 0
+    for _ in range(300):
+        op = rng.choice(["add", "append", "fork", "free"], p=[0.35, 0.3, 0.15, 0.2])
+        try:
+            if op == "add" or not live:
+                base = systems[int(rng.integers(3))] if rng.random() < 0.8 else []
+                toks = base + list(rng.integers(0, 50, size=int(rng.integers(0, 2 * B))))
+                got_m = model.add(next_id, len(toks), toks)
+                got_b = bm.add(next_id, len(toks), toks)
+                assert got_b == got_m
+                live.append(next_id)
+                next_id += 1
+            elif op == "append":
+                s = live[int(rng.integers(len(live)))]
+                n = int(rng.integers(0, 3 * B))
+                model.append(s, n)
+                bm.append(s, n)
+            elif op == "fork":
+                s = live[int(rng.integers(len(live)))]
+                model.fork(s, next_id)
+                bm.fork(s, next_id)
+                live.append(next_id)
+                next_id += 1
+            else:
+                s = live.pop(int(rng.integers(len(live))))
+                model.free_seq(s)
+                bm.free(s)
+        except ModelExhausted:
+            with pytest.raises(PoolExhausted):
+                if op == "add" or not live:
+                    bm.add(next_id, len(toks), toks)
+                else:
+                    bm.append(s, n)
+        same_state(bm, model)
+        assert bm.take_copies().tolist() == [list(p) for p in model.copies]
+        model.copies = []
+
+
+def test_beam_search_forks_and_frees_keep_the_pool_exact():
+    """Beam search with 4 beams for 40 steps: every step each beam proposes two
+    continuations, the 4 best (random scores here) survive as forks of their parent
+    beams, the old beams are freed, and each survivor appends its token (copying a
+    shared last block first).  Host state stays identical to the oracle's model and
+    every block is accounted for."""
+    rng = np.random.default_rng(7)
+    B, nb = 16, 200
+    order = rng.permutation(nb)
+    bm, model = BlockManager(nb, B, order), BlockModel(nb, B, order)
+    prompt = list(range(37))
+    for m in (bm, model):
+        m.add(("beam", 0, 0), 37, prompt)
+    beams = [("beam", 0, 0)]
+    for step in range(1, 41):
+        cands = [(float(rng.random()), p, c) for p in beams for c in range(2)]
+        cands.sort(reverse=True)
+        survivors = []
+        for i, (_, parent, c) in enumerate(cands[:4]):
+            child = ("beam", step, i)
+            for m in (bm, model):
+                m.fork(parent, child)
+            survivors.append(child)
+        for parent in beams:
+            bm.free(parent)
+            model.free_seq(parent)
+        for child in survivors:
+            bm.append(child, 1)
+            model.append(child, 1)
+        beams = survivors
+        same_state(bm, model)
+        assert bm.take_copies().tolist() == [list(p) for p in model.copies]
+        model.copies = []
+    # beams share every full block of the prompt; their last blocks are private
+    assert len({bm.table(b)[-1] for b in beams}) == 4

@@ -480,3 +480,43 @@ def device_pools_fp8(case: Case, device, k_scale: float, v_scale: float, layer=0
         k[ids] = kl.reshape(n, H, B, D // 16, 16).permute(0, 1, 3, 2, 4).contiguous()
         v[ids] = vl.reshape(n, H, B // 4, 4, D // 16, 16).permute(0, 1, 5, 2, 4, 3).contiguous()
     return k, v
+
+
+# ---------------------------------------------------------------------------
+# K/V rows that depend on a token history (prefix caching and beam search tests)
+# ---------------------------------------------------------------------------
+
+def history_kv(tokens, num_kv_heads, head_dim):
+    """bf16 K and V rows [Hkv][D] of the last position of ``tokens``, drawn from a
+    generator seeded by the whole history (as a model's K/V depend on every
+    earlier token): equal histories give equal rows."""
+    import hashlib
+
+    digest = hashlib.sha256(np.asarray(tokens, dtype="<i8").tobytes()).digest()
+    rng = np.random.default_rng(np.frombuffer(digest[:16], dtype=np.uint32).tolist())
+    return (randn_bf16(rng, (num_kv_heads, head_dim)), randn_bf16(rng, (num_kv_heads, head_dim)))
+
+
+def private_layout(histories, num_kv_heads, head_dim, block_size):
+    """Every sequence's K/V (rows from history_kv) in blocks of its own, numbered in
+    order; returns (k_pool, v_pool, block_tables, context_lens) with NaN in the
+    unused tail slots and in one extra block that table padding points at."""
+    B = block_size
+    nblk = [-(-len(h) // B) for h in histories]
+    NB = sum(nblk) + 1
+    kp = np.full(k_pool_shape(NB, num_kv_heads, head_dim, B), BF16_NAN, np.uint16)
+    vp = np.full(v_pool_shape(NB, num_kv_heads, head_dim, B), BF16_NAN, np.uint16)
+    tables = np.full((len(histories), max(nblk + [1]) + 1), NB - 1, np.int32)
+    nxt = 0
+    for i, h in enumerate(histories):
+        slots = []
+        for j in range(nblk[i]):
+            tables[i, j] = nxt + j
+        for p in range(len(h)):
+            slots.append((nxt + p // B, p % B))
+        rows = [history_kv(h[:p + 1], num_kv_heads, head_dim) for p in range(len(h))]
+        if rows:
+            write_tokens(kp, vp, slots, np.stack([r[0] for r in rows]), np.stack([r[1] for r in rows]))
+        nxt += nblk[i]
+    lens = np.array([len(h) for h in histories], np.int32)
+    return kp, vp, tables, lens
