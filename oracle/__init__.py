@@ -59,6 +59,11 @@ def _bind(lib):
     lib.oracle_paged_decode_fp8_f32.restype = ctypes.c_int
     lib.oracle_fp8_e4m3_to_f32.argtypes = [p, p, i64]
     lib.oracle_fp8_e4m3_to_f32.restype = None
+    lib.oracle_fp8_e4m3_from_f32.argtypes = [p, p, i64]
+    lib.oracle_fp8_e4m3_from_f32.restype = None
+    lib.oracle_kv_append_fp8.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64,
+                                         ctypes.c_float, ctypes.c_float]
+    lib.oracle_kv_append_fp8.restype = ctypes.c_int
     lib.oracle_kv_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64]
     lib.oracle_kv_append.restype = ctypes.c_int
     lib.oracle_copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32]
@@ -195,6 +200,34 @@ def fp8_e4m3_to_f32(codes, lib=None):
     return out
 
 
+def fp8_e4m3_from_f32(x, lib=None):
+    """The oracle's E4M3FN encoding (nearest, ties to even, saturating at 448) of
+    float32 values: uint8 codes, same shape."""
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(a.shape, np.uint8)
+    (lib or _load()).oracle_fp8_e4m3_from_f32(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def kv_append_fp8(k_new, v_new, k_pool, v_pool, block_tables, token_seq, token_pos, block_size,
+                  k_scale, v_scale, lib=None):
+    """Quantise new tokens' rows (bf16 bits [T][Hkv][D]) into uint8 fp8 pools in place."""
+    kn, vn = _u16(k_new), _u16(v_new)
+    for a in (k_pool, v_pool):
+        if a.dtype != np.uint8 or not a.flags["C_CONTIGUOUS"]:
+            raise OracleError("fp8 pools must be contiguous uint8 arrays (written in place)")
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    seq = np.ascontiguousarray(token_seq, dtype=np.int32)
+    pos = np.ascontiguousarray(token_pos, dtype=np.int32)
+    T, H, D = kn.shape
+    rc = (lib or _load()).oracle_kv_append_fp8(
+        _ptr(kn), _ptr(vn), _ptr(k_pool), _ptr(v_pool), _ptr(tables), _ptr(seq), _ptr(pos), T,
+        tables.shape[0], H, D, int(block_size), tables.shape[1], k_pool.shape[0], float(k_scale),
+        float(v_scale))
+    if rc != 0:
+        raise OracleError("oracle_kv_append_fp8 returned %d" % rc)
+
+
 def kv_append(k_new, v_new, k_pool, v_pool, block_tables, token_seq, token_pos, block_size,
               lib=None):
     """Write new tokens' rows (bf16 bits [T][Hkv][D]) into host pools in place."""
@@ -264,3 +297,9 @@ class Variant:
 
     def fp8_e4m3_to_f32(self, *args, **kwargs):
         return fp8_e4m3_to_f32(*args, lib=self._lib, **kwargs)
+
+    def fp8_e4m3_from_f32(self, *args, **kwargs):
+        return fp8_e4m3_from_f32(*args, lib=self._lib, **kwargs)
+
+    def kv_append_fp8(self, *args, **kwargs):
+        return kv_append_fp8(*args, lib=self._lib, **kwargs)

@@ -105,6 +105,31 @@ inline float e4m3_to_float(uint8_t code) {
   return (code & 0x80) ? -v : v;
 }
 
+// The E4M3FN code nearest to y (ties to the even mantissa), saturating at
+// +-448 (the largest finite magnitude; S.1111.111 is NaN, not a number to round
+// to); NaN gives 0x7F.  Written from the format's definition: magnitudes below
+// 2^-6 are multiples of 2^-9 (subnormal codes), the others (1 + m/8) * 2^e.
+inline uint8_t e4m3_from_float(float y) {
+  if (std::isnan(y)) return 0x7F;
+  const uint8_t sign = std::signbit(y) ? 0x80 : 0x00;
+  const double a = std::fabs(static_cast<double>(y));
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < std::ldexp(1.0, -6)) {
+    const int m = static_cast<int>(std::nearbyint(std::ldexp(a, 9)));  // 0 .. 8
+    return sign | static_cast<uint8_t>(m);  // m = 8 is the smallest normal, code 0x08
+  }
+  int e = 0;
+  const double f = std::frexp(a, &e);  // a = f * 2^e, f in [0.5, 1)
+  int exp = e - 1;                     // a = (2f) * 2^exp, 2f in [1, 2)
+  int m = static_cast<int>(std::nearbyint((2.0 * f - 1.0) * 8.0));
+  if (m == 8) {
+    m = 0;
+    ++exp;
+  }
+  if (exp + 7 > 15 || (exp + 7 == 15 && m == 7)) return sign | 0x7E;
+  return sign | static_cast<uint8_t>(((exp + 7) << 3) | m);
+}
+
 // Where the keys and values are read: bf16 pools, or fp8 pools with their scales.
 struct Bf16Kv {
   const uint16_t* kp;
@@ -252,6 +277,44 @@ int oracle_paged_decode_fp8_f32(const uint16_t* q, const uint8_t* k_pool, const 
 // The E4M3FN decoding itself, for n codes.
 void oracle_fp8_e4m3_to_f32(const uint8_t* codes, float* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = e4m3_to_float(codes[i]);
+}
+
+// The E4M3FN encoding itself (nearest, ties to even, saturating), for n floats.
+void oracle_fp8_e4m3_from_f32(const float* in, uint8_t* codes, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) codes[i] = e4m3_from_float(in[i]);
+}
+
+// KV append into fp8 pools: as oracle_kv_append, each element x (bf16) stored as
+// the code of x / k_scale (keys) or x / v_scale (values), the division in fp32.
+int oracle_kv_append_fp8(const uint16_t* k_new, const uint16_t* v_new, uint8_t* k_pool,
+                         uint8_t* v_pool, const int32_t* block_tables, const int32_t* seq,
+                         const int32_t* pos, int32_t num_tokens, int32_t num_seqs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t max_blocks_per_seq, int64_t num_blocks, float k_scale,
+                         float v_scale) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim % 16 != 0 || block_size % 4 != 0 ||
+      block_size <= 0)
+    return -3;
+  if (num_tokens == 0) return 0;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !seq || !pos) return -2;
+  const Shape sh{num_seqs, num_kv_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                 num_blocks};
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int32_t s = seq[i], p = pos[i];
+    if (s < 0 || s >= num_seqs || p < 0 ||
+        static_cast<int64_t>(p) >= static_cast<int64_t>(max_blocks_per_seq) * block_size)
+      continue;
+    const int64_t b = block_tables[static_cast<int64_t>(s) * max_blocks_per_seq + p / block_size];
+    if (b < 0 || b >= num_blocks) continue;
+    const int o = p % block_size;
+    for (int g = 0; g < num_kv_heads; ++g)
+      for (int d = 0; d < head_dim; ++d) {
+        const int64_t src = (static_cast<int64_t>(i) * num_kv_heads + g) * head_dim + d;
+        k_pool[k8_index(sh, b, g, o, d)] = e4m3_from_float(bf16_bits_to_float(k_new[src]) / k_scale);
+        v_pool[v8_index(sh, b, g, o, d)] = e4m3_from_float(bf16_bits_to_float(v_new[src]) / v_scale);
+      }
+  }
+  return 0;
 }
 
 // Several query tokens per sequence (speculative verification, chunked prefill):

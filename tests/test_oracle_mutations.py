@@ -41,9 +41,19 @@ MUTATIONS = {
     "fp8_v_layout_swapped": (
         "(sh.B / 4) + o / 4) * (sh.D / 16) + d / 16) * 4 + o % 4;",
         "(sh.D / 16) + d / 16) * (sh.B / 4) + o / 4) * 4 + o % 4;"),
+    "fp8_encode_ties_away": ("int m = static_cast<int>(std::nearbyint((2.0 * f - 1.0) * 8.0));",
+                             "int m = static_cast<int>(std::round((2.0 * f - 1.0) * 8.0));"),
+    "fp8_encode_bias": ("return sign | static_cast<uint8_t>(((exp + 7) << 3) | m);",
+                        "return sign | static_cast<uint8_t>(((exp + 8) << 3) | m);"),
+    "fp8_encode_no_saturation": ("  if (a >= 448.0) return sign | 0x7E;\n", ""),
+    "fp8_append_scale_multiplied": ("e4m3_from_float(bf16_bits_to_float(k_new[src]) / k_scale);",
+                                    "e4m3_from_float(bf16_bits_to_float(k_new[src]) * k_scale);"),
     "fp8_v_scale_dropped": ("return e4m3_to_float(vp[v8_index(sh, b, g, o, d)]) * v_scale;",
                             "return e4m3_to_float(vp[v8_index(sh, b, g, o, d)]);"),
-    "append_wrong_offset": ("const int o = p % block_size;", "const int o = (p + 1) % block_size;"),
+    "append_wrong_offset": ("k_pool[k_index(sh, b, g, o, d)] = k_new[src];",
+                            "k_pool[k_index(sh, b, g, (o + 1) % block_size, d)] = k_new[src];"),
+    "fp8_append_wrong_offset": ("v_pool[v8_index(sh, b, g, o, d)] = e4m3_from_float(",
+                                "v_pool[v8_index(sh, b, g, (o + 1) % block_size, d)] = e4m3_from_float("),
     "causal_off_by_one": ("h / G, p + 1, scale, orow, nullptr);", "h / G, p, scale, orow, nullptr);"),
     "q_head_offset": ("q + (static_cast<int64_t>(s) * sh.Hq + h) * sh.D",
                       "q + (static_cast<int64_t>(s) * sh.Hq + h / G) * sh.D"),

@@ -460,3 +460,55 @@ def test_fp8_oracle_equals_bf16_oracle_on_the_same_values(oracle_lib):
                                     case.scale, ks, vs, 2)
     b = run(oracle_lib, case, q, kp, vp)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def _torch_e4m3(y):
+    return torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_encoding_matches_torch_float8_in_range(oracle_lib):
+    """Nearest with ties to even, against torch's float32 -> float8_e4m3fn cast: random
+    magnitudes over the whole range, every representable value, and every midpoint
+    between neighbours (the ties)."""
+    rng = np.random.default_rng(0)
+    mags = np.exp2(rng.uniform(-12, np.log2(448.0), size=200000)).astype(np.float32)
+    vals = oracle_lib.fp8_e4m3_to_f32(np.arange(0x7F, dtype=np.uint8))   # +0 .. 448
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
+    y = np.concatenate([mags, -mags, vals, -vals, mids, -mids])
+    y = y[np.abs(y) <= 448.0]
+    assert np.array_equal(oracle_lib.fp8_e4m3_from_f32(y), _torch_e4m3(y))
+
+
+def test_fp8_encoding_saturates_and_round_trips(oracle_lib):
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle_lib.fp8_e4m3_to_f32(codes)
+    ok = ~np.isnan(vals)
+    assert np.array_equal(oracle_lib.fp8_e4m3_from_f32(vals[ok]), codes[ok])   # -0 -> 0x80
+    big = np.array([448.0, 460.0, 464.0, 1e6, np.inf, -500.0, -np.inf], np.float32)
+    assert oracle_lib.fp8_e4m3_from_f32(big).tolist() == [0x7E] * 5 + [0xFE] * 2
+    assert oracle_lib.fp8_e4m3_from_f32(np.array([np.nan], np.float32)).tolist() == [0x7F]
+
+
+def test_oracle_kv_append_fp8_quantises_into_the_right_slots(oracle_lib):
+    """Rows land at (table[s][p/B], p%B) as the codes of x/scale: checked against a
+    logical-layout rebuild with torch's cast (values kept inside the format's range)."""
+    rng = np.random.default_rng(3)
+    case = wl.case_random(5, 3, 8, 4, 64, 16, [40, 17, 3])
+    ks, vs = 0.05, 0.03
+    kp = np.full(wl.k8_pool_shape(case.num_blocks, 4, 64, 16), 0x7F, np.uint8)
+    vp = np.full(wl.v8_pool_shape(case.num_blocks, 4, 64, 16), 0x7F, np.uint8)
+    seq = np.array([0, 0, 1, 2, 2, 0], np.int32)
+    pos = np.array([0, 39, 16, 2, 0, 17], np.int32)
+    kn = wl.randn_bf16(rng, (6, 4, 64))
+    vn = wl.randn_bf16(rng, (6, 4, 64))
+    oracle_lib.kv_append_fp8(kn, vn, kp, vp, case.block_tables, seq, pos, 16, ks, vs)
+    kl, vl = wl.k8_from_pool(kp), wl.v8_from_pool(vp)
+    for i in range(6):
+        b = case.block_tables[seq[i], pos[i] // 16]
+        o = pos[i] % 16
+        want_k = _torch_e4m3(wl.f32_from_bf16(kn[i]) / np.float32(ks))
+        want_v = _torch_e4m3(wl.f32_from_bf16(vn[i]) / np.float32(vs))
+        assert np.array_equal(kl[b, :, o, :], want_k) and np.array_equal(vl[b, :, o, :], want_v)
+    written = sum(1 for _ in seq) * 4 * 64
+    assert (kl != 0x7F).sum() == written and (vl != 0x7F).sum() == written
