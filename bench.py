@@ -429,7 +429,10 @@ def main():
     def step(timed_events=None):
         for layer in range(layers):
             q, k, v = pools[layer]
-            if args.with_append:
+            if args.with_append and fp8:
+                pkv.kv_append_fp8(new_k[layer], new_v[layer], k, v, tabs, tok_seq, tok_pos, B,
+                                  FP8_SCALE, FP8_SCALE)
+            elif args.with_append:
                 pkv.kv_append(new_k[layer], new_v[layer], k, v, tabs, tok_seq, tok_pos, B)
             e = timed_events[layer] if timed_events is not None else None
             if e is not None:

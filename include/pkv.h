@@ -224,6 +224,23 @@ int32_t kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
                   int32_t max_blocks_per_seq, int64_t num_blocks, void* stream);
 
 /*
+ * KV append into fp8 pools (layouts under paged_attn_decode_fp8): as kv_append,
+ * each element x of the new rows (bf16) is stored as the E4M3FN code nearest to
+ * x / k_scale (keys) or x / v_scale (values), the division in IEEE fp32, ties to
+ * the even code, magnitudes beyond 448 saturating to +-448 and NaN stored as 0x7F
+ * ("KV cache, PagedAttention", aiwiki.vn, paragraph on cache quantisation).  The
+ * written bytes equal that rule's codes exactly.  k_scale and v_scale must be
+ * finite and nonzero (else PKV_ERR_SHAPE); block_size and head_dim as for
+ * paged_attn_decode_fp8.  Other arguments, checks and skips are kv_append's.
+ */
+int32_t kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* block_tables, const int32_t* token_seq,
+                      const int32_t* token_pos, int32_t num_tokens, int32_t num_seqs,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t max_blocks_per_seq, int64_t num_blocks, float k_scale,
+                      float v_scale, void* stream);
+
+/*
  * Copy-on-write block copy: for every pair i and every layer l,
  *   K_l[dst_i] := K_l[src_i]  and  V_l[dst_i] := V_l[src_i]   (whole blocks, bytes).
  *

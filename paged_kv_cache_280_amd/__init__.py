@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     abi_version,
     copy_blocks,
     kv_append,
+    kv_append_fp8,
     load_library,
     new_multi_workspace,
     new_workspace,

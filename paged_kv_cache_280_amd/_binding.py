@@ -24,7 +24,7 @@ STATUS_NAMES = {
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "paged_attn_decode_workspace_bytes",
            "paged_attn_decode", "paged_attn_decode_fp8", "paged_attn_multi_workspace_bytes",
            "paged_attn_multi",
-           "kv_append", "copy_blocks")
+           "kv_append", "kv_append_fp8", "copy_blocks")
 
 
 class PkvError(RuntimeError):
@@ -66,6 +66,9 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_multi.restype = i32
     lib.kv_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, p]
     lib.kv_append.restype = i32
+    lib.kv_append_fp8.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, f32, f32,
+                                  p]
+    lib.kv_append_fp8.restype = i32
     lib.copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32, p]
     lib.copy_blocks.restype = i32
     _lib = lib
@@ -308,6 +311,42 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos
                            int(block_tables.shape[1]), NB, _stream_handle(k_cache, stream))
     if rc != 0:
         raise PkvError(rc, "kv_append")
+
+
+def kv_append_fp8(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos, block_size,
+                  k_scale, v_scale, stream=None):
+    """Quantise new tokens' K/V rows ([T][Hkv][D] bf16) into fp8 pools through the
+    block table (see ``include/pkv.h``): code = E4M3(x / scale), nearest even,
+    saturating.  token_seq/token_pos: int32 [T]."""
+    import torch
+
+    lib = load_library()
+    _check(k_new.dim() == 3 and v_new.shape == k_new.shape, "k_new/v_new must be [T][Hkv][D]")
+    T, Hkv, D = k_new.shape
+    B = int(block_size)
+    _check(k_cache.dim() == 5 and tuple(k_cache.shape[1:]) == (Hkv, D // 16, B, 16),
+           "k_cache must be [num_blocks][Hkv][D/16][block_size][16]")
+    NB = int(k_cache.shape[0])
+    _check(tuple(v_cache.shape) == (NB, Hkv, 16, B // 4, D // 16, 4),
+           "v_cache must be [num_blocks][Hkv][16][block_size/4][D/16][4]")
+    for t in (k_new, v_new):
+        _check(t.dtype == torch.bfloat16 and t.is_contiguous(), "k_new/v_new: contiguous bf16")
+    for t in (k_cache, v_cache):
+        _check(t.dtype == torch.uint8 and t.is_contiguous(), "fp8 pools: contiguous uint8 codes")
+    for t in (block_tables, token_seq, token_pos):
+        _check(t.dtype == torch.int32 and t.is_contiguous(), "int32 contiguous tensors")
+    _check(token_seq.numel() == T and token_pos.numel() == T, "one sequence id and position per token")
+    _check(block_tables.dim() == 2, "block_tables must be [num_seqs][max_blocks_per_seq]")
+    devs = {t.device for t in (k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos)}
+    _check(len(devs) == 1 and k_cache.is_cuda, "all tensors must be on one GPU")
+    with torch.cuda.device(k_cache.device):
+        rc = lib.kv_append_fp8(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                               v_cache.data_ptr(), block_tables.data_ptr(), token_seq.data_ptr(),
+                               token_pos.data_ptr(), T, int(block_tables.shape[0]), Hkv, D, B,
+                               int(block_tables.shape[1]), NB, float(k_scale), float(v_scale),
+                               _stream_handle(k_cache, stream))
+    if rc != 0:
+        raise PkvError(rc, "kv_append_fp8")
 
 
 def copy_blocks(k_caches, v_caches, src_dst_pairs, stream=None):

@@ -218,6 +218,47 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   return PKV_OK;
 }
 
+int32_t append_impl(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* block_tables, const int32_t* token_seq,
+                    const int32_t* token_pos, int32_t num_tokens, int32_t num_seqs,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t max_blocks_per_seq, int64_t num_blocks, void* stream, bool fp8,
+                    float k_scale, float v_scale) {
+  if (num_tokens < 0 || num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return PKV_ERR_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > 0x7fffffffLL) return PKV_ERR_SHAPE;
+  if (!isfinite(k_scale) || !isfinite(v_scale) || k_scale == 0.0f || v_scale == 0.0f)
+    return PKV_ERR_SHAPE;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size))
+    return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !token_seq || !token_pos)
+    return PKV_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_ALIGNMENT;
+  AppendBuffers b;
+  b.k_new = static_cast<const uint16_t*>(k_new);
+  b.v_new = static_cast<const uint16_t*>(v_new);
+  b.k_cache = k_cache;
+  b.v_cache = v_cache;
+  b.tables = block_tables;
+  b.token_seq = token_seq;
+  b.token_pos = token_pos;
+  AppendDims a;
+  a.T = num_tokens;
+  a.S = num_seqs;
+  a.Hkv = num_kv_heads;
+  a.B = block_size;
+  a.M = max_blocks_per_seq;
+  a.NB = num_blocks;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = fp8 ? launch_append_fp8(b, a, head_dim, s) : launch_append(b, a, head_dim, s);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -314,36 +355,20 @@ int32_t kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
                   const int32_t* token_pos, int32_t num_tokens, int32_t num_seqs,
                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                   int32_t max_blocks_per_seq, int64_t num_blocks, void* stream) {
-  if (num_tokens < 0 || num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
-      max_blocks_per_seq <= 0 || num_blocks <= 0)
-    return PKV_ERR_SHAPE;
-  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > 0x7fffffffLL) return PKV_ERR_SHAPE;
-  if (!pkv::supported_head_dim(head_dim) || !pkv::supported_block_size(block_size))
-    return PKV_ERR_UNSUPPORTED;
-  if (num_tokens == 0) return PKV_OK;
-  if (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !token_seq || !token_pos)
-    return PKV_ERR_NULL;
-  if (!pkv::aligned16(k_new) || !pkv::aligned16(v_new) || !pkv::aligned16(k_cache) ||
-      !pkv::aligned16(v_cache))
-    return PKV_ERR_ALIGNMENT;
-  pkv::AppendBuffers b;
-  b.k_new = static_cast<const uint16_t*>(k_new);
-  b.v_new = static_cast<const uint16_t*>(v_new);
-  b.k_cache = static_cast<uint16_t*>(k_cache);
-  b.v_cache = static_cast<uint16_t*>(v_cache);
-  b.tables = block_tables;
-  b.token_seq = token_seq;
-  b.token_pos = token_pos;
-  pkv::AppendDims a;
-  a.T = num_tokens;
-  a.S = num_seqs;
-  a.Hkv = num_kv_heads;
-  a.B = block_size;
-  a.M = max_blocks_per_seq;
-  a.NB = num_blocks;
-  if (pkv::launch_append(b, a, head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
-    return PKV_ERR_LAUNCH;
-  return PKV_OK;
+  return pkv::append_impl(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos,
+                          num_tokens, num_seqs, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, num_blocks, stream, false, 1.0f, 1.0f);
+}
+
+int32_t kv_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* block_tables, const int32_t* token_seq,
+                      const int32_t* token_pos, int32_t num_tokens, int32_t num_seqs,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t max_blocks_per_seq, int64_t num_blocks, float k_scale,
+                      float v_scale, void* stream) {
+  return pkv::append_impl(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos,
+                          num_tokens, num_seqs, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, num_blocks, stream, true, k_scale, v_scale);
 }
 
 int32_t copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,

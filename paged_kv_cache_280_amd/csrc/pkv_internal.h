@@ -75,8 +75,8 @@ hipError_t launch_decode_fp8(const DecodeBuffers& b, const DecodeDims& d, int D,
 struct AppendBuffers {
   const uint16_t* k_new;      // bf16 [T][Hkv][D]
   const uint16_t* v_new;      // bf16 [T][Hkv][D]
-  uint16_t* k_cache;          // K pool
-  uint16_t* v_cache;          // V pool
+  void* k_cache;              // K pool (bf16, or fp8 codes)
+  void* v_cache;              // V pool
   const int32_t* tables;      // int32 [S][M]
   const int32_t* token_seq;   // int32 [T]
   const int32_t* token_pos;   // int32 [T]
@@ -85,9 +85,12 @@ struct AppendBuffers {
 struct AppendDims {
   int32_t T, S, Hkv, B, M;
   int64_t NB;
+  float k_scale, v_scale;     // fp8 pools: stored code = E4M3(x / scale)
 };
 
 hipError_t launch_append(const AppendBuffers& b, const AppendDims& a, int D, hipStream_t stream);
+hipError_t launch_append_fp8(const AppendBuffers& b, const AppendDims& a, int D,
+                             hipStream_t stream);
 
 // Launcher (pkv_copy.hip).
 hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,

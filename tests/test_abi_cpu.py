@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
                             "paged_attn_decode_workspace_bytes", "paged_attn_decode",
                             "paged_attn_decode_fp8",
                             "paged_attn_multi_workspace_bytes", "paged_attn_multi",
-                            "kv_append", "copy_blocks"])
+                            "kv_append", "kv_append_fp8", "copy_blocks"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -173,3 +173,15 @@ def test_kv_append_host_checks(lib):
     assert ap(B=12) == -3
     assert ap(tp=None) == -1
     assert ap(kc=0x3008) == -5
+
+
+def test_kv_append_fp8_host_checks(lib):
+    ap = lambda **o: lib.kv_append_fp8(o.get("kn", 0x1000), 0x2000, 0x3000, 0x4000, 0x5000, 0x6000,
+                                       0x7000, o.get("T", 4), 2, 8, o.get("D", 128), 16, 4, 10,
+                                       o.get("ks", 0.05), o.get("vs", 0.05), None)
+    assert ap(T=0, kn=None) == 0
+    assert ap(ks=0.0) == -2
+    assert ap(vs=float("inf")) == -2
+    assert ap(D=96) == -3
+    assert ap(kn=None) == -1
+    assert ap(kn=0x1008) == -5

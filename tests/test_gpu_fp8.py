@@ -127,3 +127,93 @@ def test_fp8_quantisation_error_against_bf16_attention():
     mx, mean, rel = errors(got, ref)
     print("fp8 vs bf16 attention: max_abs=%.3g mean_abs=%.3g rel_rms=%.3g" % (mx, mean, rel))
     assert rel < 0.08 and mean < 0.02
+
+
+def _specials_bf16(rng, shape, scale):
+    """bf16 rows mixing N(0,1), exact ties of the E4M3 grid (at a power-of-two scale),
+    values past the saturation point, signed zeros and NaN."""
+    x = rng.standard_normal(shape).astype(np.float32) * np.float32(rng.choice([0.01, 1.0, 30.0]))
+    vals = oracle.fp8_e4m3_to_f32(np.arange(0x7F, dtype=np.uint8))
+    ties = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32) * np.float32(scale)
+    flat = x.reshape(-1)
+    k = min(len(ties), flat.size // 4)
+    flat[:k] = ties[:k] * np.where(np.arange(k) % 2, 1, -1)
+    flat[k:k + 6] = [0.0, -0.0, np.nan, 1e6, -1e6, 500.0 * scale]
+    return wl.bf16_from_f32(np.nan_to_num(flat, nan=0.0)).reshape(shape) | \
+        np.where(np.isnan(flat), np.uint16(0x7FC0), np.uint16(0)).reshape(shape)
+
+
+@pytest.mark.parametrize("D,B,scales", [(128, 16, (1 / 16, 1 / 8)), (64, 8, (0.037, 0.0029)),
+                                        (128, 32, (0.5, 2.0))])
+def test_kv_append_fp8_matches_the_oracle_byte_for_byte(D, B, scales):
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    rng = np.random.default_rng(D + B)
+    H = 4
+    lens = [3 * B + 5, B, 2, 5 * B]
+    case = wl.case_random(D + B + 1, len(lens), H, H, D, B, lens)
+    kp, vp = wl.host_pools_fp8(case, *scales, poison=False)
+    seq, pos = [], []
+    for s, L in enumerate(lens):
+        seq += [s] * L
+        pos += list(range(L))
+    order = rng.permutation(len(seq))
+    seq = np.array(list(np.array(seq)[order]) + [len(lens), 0], np.int32)   # two to skip
+    pos = np.array(list(np.array(pos)[order]) + [0, -1], np.int32)
+    kn = _specials_bf16(rng, (len(seq), H, D), scales[0])
+    vn = _specials_bf16(rng, (len(seq), H, D), scales[1])
+    kd, vd = _dev_u8(kp), _dev_u8(vp)
+    pkv.kv_append_fp8(to_dev_bf16(kn), to_dev_bf16(vn), kd, vd, to_dev_i32(case.block_tables),
+                      to_dev_i32(seq), to_dev_i32(pos), B, *scales)
+    torch.cuda.synchronize()
+    oracle.kv_append_fp8(kn, vn, kp, vp, case.block_tables, seq, pos, B, *scales)
+    assert np.array_equal(kd.cpu().numpy(), kp) and np.array_equal(vd.cpu().numpy(), vp)
+
+
+def test_fp8_decode_step_with_append():
+    """A full fp8 decode step: the block manager makes room (copy-on-write of a shared
+    last block), kv_append_fp8 quantises the new token into its slot, decode reads it."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+    from paged_kv_cache_280_amd.block_manager import BlockManager
+
+    rng = np.random.default_rng(11)
+    H, Hq, D, B, nb = 8, 32, 128, 16, 300
+    ks, vs = 1 / 16, 1 / 16
+    bm = BlockManager(nb, B, rng.permutation(nb))
+    for s, L in enumerate([3 * B, 3 * B - 1, 1, 200]):
+        bm.add(s, L)
+    bm.fork(3, 4)
+    seqs = list(range(5))
+    kp = np.full(wl.k8_pool_shape(nb, H, D, B), wl.E4M3_NAN, np.uint8)
+    vp = np.full(wl.v8_pool_shape(nb, H, D, B), wl.E4M3_NAN, np.uint8)
+    tables0, lens0 = bm.batch(seqs)
+    kq = wl.randn_bf16(rng, (int(lens0.sum()), H, D))
+    vq = wl.randn_bf16(rng, (int(lens0.sum()), H, D))
+    tok_s = np.repeat(np.arange(5), lens0).astype(np.int32)
+    tok_p = np.concatenate([np.arange(L) for L in lens0]).astype(np.int32)
+    oracle.kv_append_fp8(kq, vq, kp, vp, tables0, tok_s, tok_p, B, ks, vs)   # the existing context
+    for s in seqs:
+        bm.append(s, 1)
+    pairs = bm.take_copies()
+    assert len(pairs) == 1
+    kd, vd = _dev_u8(kp), _dev_u8(vp)
+    pkv.copy_blocks([kd], [vd], to_dev_i32(pairs))
+    oracle.copy_blocks([kp], [vp], pairs)
+    tables, lens = bm.batch(seqs)
+    kn, vn = wl.randn_bf16(rng, (5, H, D)), wl.randn_bf16(rng, (5, H, D))
+    ts, tp = np.arange(5, dtype=np.int32), (lens - 1).astype(np.int32)
+    pkv.kv_append_fp8(to_dev_bf16(kn), to_dev_bf16(vn), kd, vd, to_dev_i32(tables), to_dev_i32(ts),
+                      to_dev_i32(tp), B, ks, vs)
+    oracle.kv_append_fp8(kn, vn, kp, vp, tables, ts, tp, B, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(kd.cpu().numpy(), kp) and np.array_equal(vd.cpu().numpy(), vp)
+    q = wl.randn_bf16(rng, (5, Hq, D))
+    out = pkv.paged_attn_decode_fp8(to_dev_bf16(q), kd, vd, to_dev_i32(tables), to_dev_i32(lens), B,
+                                    1 / np.sqrt(D), ks, vs, max_context_len=int(lens.max()))
+    torch.cuda.synchronize()
+    ref = oracle.paged_decode_fp8(q, kp, vp, tables, lens, B, 1 / np.sqrt(D), ks, vs, H)
+    assert_parity(bf16_to_f32(out), ref, "fp8 decode step with append")
