@@ -64,6 +64,10 @@ def _bind(lib):
     lib.oracle_kv_append_fp8.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64,
                                          ctypes.c_float, ctypes.c_float]
     lib.oracle_kv_append_fp8.restype = ctypes.c_int
+    lib.oracle_paged_attn_multi_fp8_f32.argtypes = [p, p, p, p, p, p, i32, i32, ctypes.c_float,
+                                                    ctypes.c_float, ctypes.c_float, p, i32, i32,
+                                                    i32, i32, i32, i64, i32]
+    lib.oracle_paged_attn_multi_fp8_f32.restype = ctypes.c_int
     lib.oracle_kv_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64]
     lib.oracle_kv_append.restype = ctypes.c_int
     lib.oracle_copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32]
@@ -145,6 +149,27 @@ def paged_attn_multi(q, k_pool, v_pool, block_tables, context_lens, query_lens, 
         kp.shape[0], int(threads))
     if rc != 0:
         raise OracleError("oracle_paged_attn_multi returned %d" % rc)
+    return out
+
+
+def paged_attn_multi_fp8(q, k_pool, v_pool, block_tables, context_lens, query_lens, block_size,
+                         scale, k_scale, v_scale, num_kv_heads, threads=0, lib=None):
+    """Reference multi-token attention over fp8 pools (layouts as paged_decode_fp8;
+    q bf16 bits [S][Qmax][Hq][D]).  Returns float32 [S][Qmax][Hq][D]."""
+    q = _u16(q)
+    kp = np.ascontiguousarray(k_pool, dtype=np.uint8)
+    vp = np.ascontiguousarray(v_pool, dtype=np.uint8)
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qlens = np.ascontiguousarray(query_lens, dtype=np.int32)
+    S, Qmax, Hq, D = q.shape
+    out = np.zeros((S, Qmax, Hq, D), np.float32)
+    rc = (lib or _load()).oracle_paged_attn_multi_fp8_f32(
+        _ptr(q), _ptr(kp), _ptr(vp), _ptr(tables), _ptr(lens), _ptr(qlens), Qmax,
+        int(block_size), float(scale), float(k_scale), float(v_scale), _ptr(out), S, Hq,
+        num_kv_heads, D, tables.shape[1], kp.shape[0], int(threads))
+    if rc != 0:
+        raise OracleError("oracle_paged_attn_multi_fp8 returned %d" % rc)
     return out
 
 
@@ -291,6 +316,9 @@ class Variant:
 
     def paged_attn_multi(self, *args, **kwargs):
         return paged_attn_multi(*args, lib=self._lib, **kwargs)
+
+    def paged_attn_multi_fp8(self, *args, **kwargs):
+        return paged_attn_multi_fp8(*args, lib=self._lib, **kwargs)
 
     def paged_decode_fp8(self, *args, **kwargs):
         return paged_decode_fp8(*args, lib=self._lib, **kwargs)

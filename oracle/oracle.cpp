@@ -230,6 +230,51 @@ int decode_all(const uint16_t* q, const Kv& kv, const int32_t* tables, const int
   return status;
 }
 
+// Several query tokens per sequence over either pool format (see the extern
+// functions below for the contract).
+template <typename Kv>
+int multi_all(const uint16_t* q, const Kv& kv, const int32_t* block_tables,
+              const int32_t* context_lens, const int32_t* query_lens, int32_t max_query_len,
+              int32_t block_size, float scale, float* out, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+              int64_t num_blocks, int32_t threads) {
+  if (!q || !kv.kp || !kv.vp || !block_tables || !context_lens || !query_lens || !out) return -2;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim % 8 != 0 ||
+      num_q_heads % num_kv_heads != 0 || max_query_len < 0 || block_size <= 0)
+    return -3;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int L = context_lens[s], T = query_lens[s];
+    if (L < 0 || static_cast<int64_t>(L) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+      return -4;
+    if (T < 0 || T > L || T > max_query_len) return -5;
+  }
+  const Shape sh{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                 num_blocks};
+  const int G = num_q_heads / num_kv_heads;
+  const int64_t rows = static_cast<int64_t>(num_seqs) * max_query_len * num_q_heads;
+  int status = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : status)
+#endif
+  for (int64_t r = 0; r < rows; ++r) {
+    const int s = static_cast<int>(r / (static_cast<int64_t>(max_query_len) * num_q_heads));
+    const int i = static_cast<int>((r / num_q_heads) % max_query_len);
+    const int h = static_cast<int>(r % num_q_heads);
+    float* orow = out + r * head_dim;
+    if (i >= query_lens[s]) {
+      for (int d = 0; d < head_dim; ++d) orow[d] = 0.f;
+      continue;
+    }
+    const int p = context_lens[s] - query_lens[s] + i;
+    const int rc = attend<float>(sh, q + r * head_dim, kv,
+                                 block_tables + static_cast<int64_t>(s) * max_blocks_per_seq,
+                                 h / G, p + 1, scale, orow, nullptr);
+    if (rc < status) status = rc;
+  }
+  return status;
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,41 +374,24 @@ int oracle_paged_attn_multi_f32(const uint16_t* q, const uint16_t* k_pool, const
                                 int32_t block_size, float scale, float* out, int32_t num_seqs,
                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_blocks_per_seq, int64_t num_blocks, int32_t threads) {
-  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !query_lens || !out) return -2;
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim % 8 != 0 ||
-      num_q_heads % num_kv_heads != 0 || max_query_len < 0 || block_size <= 0)
-    return -3;
-  for (int s = 0; s < num_seqs; ++s) {
-    const int L = context_lens[s], T = query_lens[s];
-    if (L < 0 || static_cast<int64_t>(L) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
-      return -4;
-    if (T < 0 || T > L || T > max_query_len) return -5;
-  }
-  const Shape sh{num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                 num_blocks};
-  const int G = num_q_heads / num_kv_heads;
-  const int64_t rows = static_cast<int64_t>(num_seqs) * max_query_len * num_q_heads;
-  int status = 0;
-#ifdef _OPENMP
-  if (threads > 0) omp_set_num_threads(threads);
-#pragma omp parallel for schedule(dynamic, 1) reduction(min : status)
-#endif
-  for (int64_t r = 0; r < rows; ++r) {
-    const int s = static_cast<int>(r / (static_cast<int64_t>(max_query_len) * num_q_heads));
-    const int i = static_cast<int>((r / num_q_heads) % max_query_len);
-    const int h = static_cast<int>(r % num_q_heads);
-    float* orow = out + r * head_dim;
-    if (i >= query_lens[s]) {
-      for (int d = 0; d < head_dim; ++d) orow[d] = 0.f;
-      continue;
-    }
-    const int p = context_lens[s] - query_lens[s] + i;
-    const int rc = attend<float>(sh, q + r * head_dim, Bf16Kv{k_pool, v_pool},
-                                 block_tables + static_cast<int64_t>(s) * max_blocks_per_seq,
-                                 h / G, p + 1, scale, orow, nullptr);
-    if (rc < status) status = rc;
-  }
-  return status;
+  return multi_all(q, Bf16Kv{k_pool, v_pool}, block_tables, context_lens, query_lens,
+                   max_query_len, block_size, scale, out, num_seqs, num_q_heads, num_kv_heads,
+                   head_dim, max_blocks_per_seq, num_blocks, threads);
+}
+
+// The same over fp8 pools (keys code * k_scale, values code * v_scale).
+int oracle_paged_attn_multi_fp8_f32(const uint16_t* q, const uint8_t* k_pool,
+                                    const uint8_t* v_pool, const int32_t* block_tables,
+                                    const int32_t* context_lens, const int32_t* query_lens,
+                                    int32_t max_query_len, int32_t block_size, float scale,
+                                    float k_scale, float v_scale, float* out, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_blocks_per_seq, int64_t num_blocks,
+                                    int32_t threads) {
+  if (head_dim % 16 != 0 || block_size % 4 != 0) return -3;
+  return multi_all(q, Fp8Kv{k_pool, v_pool, k_scale, v_scale}, block_tables, context_lens,
+                   query_lens, max_query_len, block_size, scale, out, num_seqs, num_q_heads,
+                   num_kv_heads, head_dim, max_blocks_per_seq, num_blocks, threads);
 }
 
 // Debug form for one (sequence, query head): writes the D outputs and the L

@@ -512,3 +512,31 @@ def test_oracle_kv_append_fp8_quantises_into_the_right_slots(oracle_lib):
         assert np.array_equal(kl[b, :, o, :], want_k) and np.array_equal(vl[b, :, o, :], want_v)
     written = sum(1 for _ in seq) * 4 * 64
     assert (kl != 0x7F).sum() == written and (vl != 0x7F).sum() == written
+
+
+def test_fp8_multi_query_reduces_to_pinned_functions(oracle_lib):
+    """Multi-token attention over fp8 pools: one query token is the fp8 decode bit for
+    bit, and at power-of-two scales it is the bf16 multi-token oracle on the same
+    (exactly representable) values bit for bit."""
+    case = wl.case_random(31, 4, 16, 4, 128, 16, [45, 16, 7, 100])
+    ks, vs = 2.0 ** -4, 2.0 ** -5
+    kp8, vp8 = wl.host_pools_fp8(case, ks, vs, poison=False)
+    rng = np.random.default_rng(6)
+    q1 = wl.randn_bf16(rng, (4, 16, 128))
+    one = oracle_lib.paged_attn_multi_fp8(q1[:, None], kp8, vp8, case.block_tables,
+                                          case.context_lens, np.ones(4, np.int32), 16,
+                                          case.scale, ks, vs, 4)
+    dec = oracle_lib.paged_decode_fp8(q1, kp8, vp8, case.block_tables, case.context_lens, 16,
+                                      case.scale, ks, vs, 4)
+    assert np.array_equal(one[:, 0].view(np.uint32), dec.view(np.uint32))
+    to_bf16 = lambda a, s: wl.bf16_from_f32(
+        torch.from_numpy(a).view(torch.float8_e4m3fn).to(torch.float32).numpy() * np.float32(s))
+    kp = wl.k_to_pool(to_bf16(wl.k8_from_pool(kp8), ks))
+    vp = wl.v_to_pool(to_bf16(wl.v8_from_pool(vp8), vs))
+    q = wl.randn_bf16(rng, (4, 5, 16, 128))
+    qlens = np.array([5, 3, 0, 5], np.int32)
+    a = oracle_lib.paged_attn_multi_fp8(q, kp8, vp8, case.block_tables, case.context_lens, qlens,
+                                        16, case.scale, ks, vs, 4)
+    b = oracle_lib.paged_attn_multi(q, kp, vp, case.block_tables, case.context_lens, qlens, 16,
+                                    case.scale, 4)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
