@@ -198,7 +198,12 @@ def cpu_baseline(case, pools, layers, args):
 
     def run_oracle(qh, kh, vh, tab, L, threads):
         lens = np.array([L], np.int32)
-        if args.query_tokens > 1:
+        if args.query_tokens > 1 and fp8:
+            oracle.paged_attn_multi_fp8(qh, kh, vh, tab, lens,
+                                        np.array([args.query_tokens], np.int32), case.block_size,
+                                        case.scale, FP8_SCALE, FP8_SCALE, case.num_kv_heads,
+                                        threads=threads)
+        elif args.query_tokens > 1:
             oracle.paged_attn_multi(qh, kh, vh, tab, lens, np.array([args.query_tokens], np.int32),
                                     case.block_size, case.scale, case.num_kv_heads, threads=threads)
         elif fp8:
@@ -383,9 +388,6 @@ def main():
     T = args.query_tokens
     multi = T > 1
     fp8 = args.kv_dtype == "fp8"
-    if fp8 and multi:
-        print("--kv-dtype fp8 is built for decode (one query token) only", file=sys.stderr)
-        sys.exit(2)
     if multi:
         # q of every layer becomes [S][T][Hq][D]; each sequence's last T positions
         # are its query tokens
@@ -438,8 +440,9 @@ def main():
             if e is not None:
                 e[0].record(stream)
             if multi:
+                sc = dict(k_scale=FP8_SCALE, v_scale=FP8_SCALE) if fp8 else {}
                 pkv.paged_attn_multi(q, k, v, tabs, lens, qlens, B, case.scale, outs[layer],
-                                     workspace=ws, max_context_len=max_ctx)
+                                     workspace=ws, max_context_len=max_ctx, **sc)
             elif fp8:
                 pkv.paged_attn_decode_fp8(q, k, v, tabs, lens, B, case.scale, FP8_SCALE, FP8_SCALE,
                                           outs[layer], workspace=ws, max_context_len=max_ctx)

@@ -150,8 +150,8 @@ int32_t paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_
                               size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device scratch paged_attn_multi needs for these sizes on the current
- * device (the same role as paged_attn_decode_workspace_bytes).  Returns 0 for
+ * Bytes of device scratch paged_attn_multi and paged_attn_multi_fp8 need for these
+ * sizes on the current device (the same role as paged_attn_decode_workspace_bytes).  Returns 0 for
  * sizes paged_attn_multi would reject.
  */
 size_t paged_attn_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -196,6 +196,24 @@ int32_t paged_attn_multi(const void* q, const void* k_cache, const void* v_cache
                          int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
                          int64_t num_blocks, int32_t max_context_len, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * Multi-token paged attention over fp8 pools: paged_attn_multi's computation on
+ * the keys code * k_scale and values code * v_scale of pools in the fp8 layouts
+ * (see paged_attn_decode_fp8).  Workspace from paged_attn_multi_workspace_bytes,
+ * which covers both pool formats.  k_scale and v_scale must be finite (else
+ * PKV_ERR_SHAPE); everything else as paged_attn_multi.  With max_query_len = 1 and
+ * one query token per non-empty sequence the result equals paged_attn_decode_fp8's
+ * bit for bit.
+ */
+int32_t paged_attn_multi_fp8(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const int32_t* query_lens, int32_t max_query_len, int32_t block_size,
+                             float scale, float k_scale, float v_scale, void* out,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * KV append: write the key and value rows of num_tokens new tokens into their

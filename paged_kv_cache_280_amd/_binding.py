@@ -23,7 +23,7 @@ STATUS_NAMES = {
 
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "paged_attn_decode_workspace_bytes",
            "paged_attn_decode", "paged_attn_decode_fp8", "paged_attn_multi_workspace_bytes",
-           "paged_attn_multi",
+           "paged_attn_multi", "paged_attn_multi_fp8",
            "kv_append", "kv_append_fp8", "copy_blocks")
 
 
@@ -64,6 +64,10 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_multi.argtypes = [p, p, p, p, p, p, i32, i32, ctypes.c_float, p, i32, i32, i32,
                                      i32, i32, i64, i32, p, sz, p]
     lib.paged_attn_multi.restype = i32
+    lib.paged_attn_multi_fp8.argtypes = [p, p, p, p, p, p, i32, i32, ctypes.c_float, ctypes.c_float,
+                                         ctypes.c_float, p, i32, i32, i32, i32, i32, i64, i32, p,
+                                         sz, p]
+    lib.paged_attn_multi_fp8.restype = i32
     lib.kv_append.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, p]
     lib.kv_append.restype = i32
     lib.kv_append_fp8.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, f32, f32,
@@ -242,21 +246,53 @@ def new_multi_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, block_siz
         return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
 
 
+def _fp8_pool_shapes(q3, k_cache, v_cache, block_tables, context_lens, block_size):
+    """(Hkv, NB, M) of fp8 pools after host-side checks (q3: q seen as [S][rows][D])."""
+    import torch
+
+    S, _, D = q3.shape
+    B = int(block_size)
+    _check(k_cache.dim() == 5 and k_cache.shape[2] * 16 == D and k_cache.shape[3] == B
+           and k_cache.shape[4] == 16, "k_cache must be [num_blocks][Hkv][D/16][block_size][16]")
+    NB, Hkv = int(k_cache.shape[0]), int(k_cache.shape[1])
+    _check(tuple(v_cache.shape) == (NB, Hkv, 16, B // 4, D // 16, 4),
+           "v_cache must be [num_blocks][Hkv][16][block_size/4][D/16][4]")
+    _check(q3.dtype == torch.bfloat16 and q3.is_contiguous(), "q: contiguous bf16")
+    for t in (k_cache, v_cache):
+        _check(t.dtype == torch.uint8 and t.is_contiguous(), "fp8 pools: contiguous uint8 codes")
+    _check(block_tables.dim() == 2 and block_tables.shape[0] == S,
+           "block_tables must be [num_seqs][max_blocks_per_seq]")
+    _check(context_lens.dim() == 1 and context_lens.shape[0] == S, "context_lens must be [num_seqs]")
+    for t in (block_tables, context_lens):
+        _check(t.dtype == torch.int32 and t.is_contiguous(), "tables/lengths: contiguous int32")
+    devs = {t.device for t in (q3, k_cache, v_cache, block_tables, context_lens)}
+    _check(len(devs) == 1 and q3.is_cuda, "all tensors must be on one GPU")
+    return Hkv, NB, int(block_tables.shape[1])
+
+
 def paged_attn_multi(q, k_cache, v_cache, block_tables, context_lens, query_lens, block_size,
-                     scale, out=None, *, max_context_len=None, workspace=None, stream=None):
+                     scale, out=None, *, max_context_len=None, workspace=None, stream=None,
+                     k_scale=None, v_scale=None):
     """Multi-token paged attention with a causal mask (see ``include/pkv.h``).
     ``q`` is [num_seqs][max_query_len][num_q_heads][head_dim] bf16, ``query_lens``
     int32 [num_seqs].  Returns ``out`` (same shape as q; rows past a sequence's
-    query tokens are zero)."""
+    query tokens are zero).  With ``k_scale``/``v_scale`` given, the pools are fp8
+    (E4M3FN codes in the fp8 layouts) and ``paged_attn_multi_fp8`` runs."""
     import torch
 
     lib = load_library()
     _check(q.dim() == 4, "q must be [num_seqs][max_query_len][num_q_heads][head_dim]")
     S, Q, Hq, D = q.shape
     _check(q.is_contiguous(), "q must be contiguous")
+    fp8 = k_scale is not None or v_scale is not None
+    _check(not fp8 or (k_scale is not None and v_scale is not None), "give both k_scale and v_scale")
     # the pools, tables and lengths are checked as for decode, on q seen as [S][Q*Hq][D]
-    _, _, Hkv, _, NB, M = decode_shapes(q.view(S, Q * Hq, D), k_cache, v_cache, block_tables,
-                                        context_lens, block_size)
+    if fp8:
+        Hkv, NB, M = _fp8_pool_shapes(q.view(S, Q * Hq, D), k_cache, v_cache, block_tables,
+                                      context_lens, block_size)
+    else:
+        _, _, Hkv, _, NB, M = decode_shapes(q.view(S, Q * Hq, D), k_cache, v_cache, block_tables,
+                                            context_lens, block_size)
     _check(query_lens.dim() == 1 and query_lens.shape[0] == S and query_lens.dtype == torch.int32
            and query_lens.is_contiguous() and query_lens.device == q.device,
            "query_lens must be contiguous int32 [num_seqs] on q's device")
@@ -272,13 +308,16 @@ def paged_attn_multi(q, k_cache, v_cache, block_tables, context_lens, query_lens
         _check(workspace.is_cuda and workspace.device == q.device and workspace.is_contiguous(),
                "workspace must be a contiguous tensor on q's device")
         ws_bytes = workspace.numel() * workspace.element_size()
-        rc = lib.paged_attn_multi(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                  block_tables.data_ptr(), context_lens.data_ptr(),
-                                  query_lens.data_ptr(), Q, int(block_size), float(scale),
-                                  out.data_ptr(), S, Hq, Hkv, D, M, NB, int(max_context_len),
-                                  workspace.data_ptr(), ws_bytes, _stream_handle(q, stream))
+        ptrs = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                context_lens.data_ptr(), query_lens.data_ptr(), Q, int(block_size), float(scale))
+        rest = (out.data_ptr(), S, Hq, Hkv, D, M, NB, int(max_context_len), workspace.data_ptr(),
+                ws_bytes, _stream_handle(q, stream))
+        if fp8:
+            rc = lib.paged_attn_multi_fp8(*ptrs, float(k_scale), float(v_scale), *rest)
+        else:
+            rc = lib.paged_attn_multi(*ptrs, *rest)
     if rc != 0:
-        raise PkvError(rc, "paged_attn_multi")
+        raise PkvError(rc, "paged_attn_multi_fp8" if fp8 else "paged_attn_multi")
     return out
 
 

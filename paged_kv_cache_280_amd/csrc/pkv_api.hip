@@ -164,11 +164,13 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
                    float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
                    int64_t num_blocks, int32_t max_context_len, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   size_t workspace_bytes, void* stream, bool fp8, float k_scale,
+                   float v_scale) {
   const int32_t st = check_shapes(block_size, scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                   max_blocks_per_seq, num_blocks, max_context_len);
   if (st != PKV_OK) return st;
   if (max_query_len < 0) return PKV_ERR_SHAPE;
+  if (!isfinite(k_scale) || !isfinite(v_scale)) return PKV_ERR_SHAPE;
   if (num_seqs == 0 || max_query_len == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_lens || !out ||
       !workspace)
@@ -179,7 +181,7 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   const int cu = current_cu_count();
   if (cu <= 0) return PKV_ERR_DEVICE;
   const int32_t group = num_q_heads / num_kv_heads;
-  const int64_t workers = worker_count(cu, num_seqs, num_kv_heads, max_context_len);
+  const int64_t workers = worker_count(cu, num_seqs, num_kv_heads, max_context_len, fp8);
   if (workspace_bytes < multi_workspace_for(workers, group, head_dim, max_query_len))
     return PKV_ERR_WORKSPACE;
 
@@ -191,9 +193,10 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   d.M = max_blocks_per_seq;
   d.n_workers = static_cast<int32_t>(workers);
   d.NB = num_blocks;
-  d.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+  d.c = static_cast<float>(static_cast<double>(scale) * static_cast<double>(k_scale) *
+                           1.4426950408889634);  // log2(e); an fp8 K scale folds in
   d.Qmax = max_query_len;
-  d.v_scale = 1.0f;
+  d.v_scale = v_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t per = tokens_per_launch(group, max_query_len);
   const int64_t token_elems = static_cast<int64_t>(num_q_heads) * head_dim;
@@ -212,7 +215,8 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
     b.qlens = query_lens;
     b.out = static_cast<uint16_t*>(out) + off * token_elems;
     b.ws = static_cast<float*>(workspace);
-    if (launch_multi(b, d, head_dim, block_size, merge_groups_for(workers, cu), s) != hipSuccess)
+    if (launch_multi(b, d, head_dim, block_size, merge_groups_for(workers, cu), s, fp8) !=
+        hipSuccess)
       return PKV_ERR_LAUNCH;
   }
   return PKV_OK;
@@ -332,7 +336,10 @@ size_t paged_attn_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
     return 0;
   const int cu = pkv::current_cu_count();
   if (cu <= 0) return 0;
-  const int64_t workers = pkv::worker_count(cu, num_seqs, num_kv_heads, max_context_len);
+  // enough for either pool format (fp8 launches more workers)
+  const int64_t workers =
+      std::max(pkv::worker_count(cu, num_seqs, num_kv_heads, max_context_len, false),
+               pkv::worker_count(cu, num_seqs, num_kv_heads, max_context_len, true));
   return pkv::multi_workspace_for(workers, num_q_heads / num_kv_heads, head_dim,
                                   max_query_len > 0 ? max_query_len : 1);
 }
@@ -347,7 +354,21 @@ int32_t paged_attn_multi(const void* q, const void* k_cache, const void* v_cache
   return pkv::multi_impl(q, k_cache, v_cache, block_tables, context_lens, query_lens,
                          max_query_len, block_size, scale, out, num_seqs, num_q_heads,
                          num_kv_heads, head_dim, max_blocks_per_seq, num_blocks, max_context_len,
-                         workspace, workspace_bytes, stream);
+                         workspace, workspace_bytes, stream, false, 1.0f, 1.0f);
+}
+
+int32_t paged_attn_multi_fp8(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const int32_t* query_lens, int32_t max_query_len, int32_t block_size,
+                             float scale, float k_scale, float v_scale, void* out,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t max_blocks_per_seq, int64_t num_blocks,
+                             int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return pkv::multi_impl(q, k_cache, v_cache, block_tables, context_lens, query_lens,
+                         max_query_len, block_size, scale, out, num_seqs, num_q_heads,
+                         num_kv_heads, head_dim, max_blocks_per_seq, num_blocks, max_context_len,
+                         workspace, workspace_bytes, stream, true, k_scale, v_scale);
 }
 
 int32_t kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

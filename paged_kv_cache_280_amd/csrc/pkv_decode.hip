@@ -717,7 +717,7 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
 // descriptor per worker: (s, g, wb, first_slot | Tq << 1) of the split pair whose
 // first share this worker holds, or s = -1 (Tq only in multi-token launches).
 template <int D, int B, int NC, bool kCausal, bool kFp8>
-__global__ __launch_bounds__(kWave* kWavesPerGroup, kFp8 ? 2 : 1) void decode_kernel(
+__global__ __launch_bounds__(kWave* kWavesPerGroup, (kFp8 && NC == 1) ? 2 : 1) void decode_kernel(
     const uint16_t* __restrict__ q, const typename TileOf<D, B, kFp8>::Elem* __restrict__ k,
     const typename TileOf<D, B, kFp8>::Elem* __restrict__ v,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
@@ -929,7 +929,12 @@ hipError_t launch_decode_fp8(const DecodeBuffers& b, const DecodeDims& d, int D,
 }
 
 hipError_t launch_multi(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                        int merge_groups, hipStream_t stream) {
+                        int merge_groups, hipStream_t stream, bool fp8) {
+  if (fp8) {
+    if (d.R <= 16) return dispatch<1, true, true>(b, d, D, B, merge_groups, stream);
+    if (d.R <= kMaxRows) return dispatch<2, true, true>(b, d, D, B, merge_groups, stream);
+    return hipErrorInvalidValue;
+  }
   if (d.R <= 16) return dispatch<1, true, false>(b, d, D, B, merge_groups, stream);
   if (d.R <= kMaxRows) return dispatch<2, true, false>(b, d, D, B, merge_groups, stream);
   return hipErrorInvalidValue;

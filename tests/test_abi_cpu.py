@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
                             "paged_attn_decode_workspace_bytes", "paged_attn_decode",
                             "paged_attn_decode_fp8",
                             "paged_attn_multi_workspace_bytes", "paged_attn_multi",
+                            "paged_attn_multi_fp8",
                             "kv_append", "kv_append_fp8", "copy_blocks"])
 
 

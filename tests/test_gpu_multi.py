@@ -151,3 +151,55 @@ def test_multi_verify_at_long_context_sampled():
     ref = oracle.paged_attn_multi(q, kp, vp, case.block_tables, case.context_lens, qlens,
                                   case.block_size, case.scale, case.num_kv_heads)
     assert_parity(got, ref, "verify 8x16000 Q=4")
+
+
+# (head_dim, block_size, q heads, kv heads, max query tokens) over fp8 pools
+FP8_SHAPES = [(128, 16, 32, 8, 4), (128, 16, 32, 8, 8), (64, 8, 8, 8, 40), (128, 32, 16, 2, 3)]
+
+
+@pytest.mark.parametrize("D,B,Hq,Hkv,Q", FP8_SHAPES)
+def test_multi_over_fp8_pools_matches_the_oracle(D, B, Hq, Hkv, Q):
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    rng = np.random.default_rng(D + B + Q + 100)
+    lens = np.array([Q + 3, 5 * B + 1, Q, 0, 700, 2000], np.int32)
+    qlens = np.minimum(np.array([Q, 1, Q, 0, Q // 2, Q - 1], np.int32), lens)
+    case = wl.case_random(D + Q + 7, len(lens), Hq, Hkv, D, B, lens)
+    ks, vs = 0.043, 0.057
+    kp8, vp8 = wl.host_pools_fp8(case, ks, vs)
+    q = _q_with_nan_padding(rng, len(lens), Q, Hq, D, qlens)
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    out = pkv.paged_attn_multi(to_dev_bf16(q), u8(kp8), u8(vp8), to_dev_i32(case.block_tables),
+                               to_dev_i32(lens), to_dev_i32(qlens), B, case.scale,
+                               max_context_len=int(lens.max()), k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    got = bf16_to_f32(out)
+    ref = oracle.paged_attn_multi_fp8(q, kp8, vp8, case.block_tables, lens, qlens, B, case.scale,
+                                      ks, vs, Hkv)
+    for s, T in enumerate(qlens):
+        assert not got[s, T:].any()
+    assert_parity(got, ref, "multi fp8 D=%d B=%d G=%d Q=%d" % (D, B, Hq // Hkv, Q))
+
+
+def test_multi_over_fp8_pools_with_one_token_is_fp8_decode_bit_for_bit():
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    case = wl.case_chat(seed=12, num_seqs=20)
+    ks, vs = 1 / 16, 1 / 16
+    kp8, vp8 = wl.host_pools_fp8(case, ks, vs)
+    q = wl.host_q(case)
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    kd, vd = u8(kp8), u8(vp8)
+    tabs, lens = to_dev_i32(case.block_tables), to_dev_i32(case.context_lens)
+    mx = int(case.context_lens.max())
+    dec = pkv.paged_attn_decode_fp8(to_dev_bf16(q), kd, vd, tabs, lens, 16, case.scale, ks, vs,
+                                    max_context_len=mx)
+    multi = pkv.paged_attn_multi(to_dev_bf16(q[:, None]), kd, vd, tabs, lens,
+                                 to_dev_i32(np.ones(case.num_seqs, np.int32)), 16, case.scale,
+                                 max_context_len=mx, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert torch.equal(dec.view(torch.int16), multi[:, 0].contiguous().view(torch.int16))
