@@ -47,6 +47,25 @@ int waves_per_cu(bool fp8) {
   return v ? v : (fp8 ? kDefaultWavesPerCuFp8 : kDefaultWavesPerCu);
 }
 
+// Pair mode (one worker per (sequence, KV head) pair, no split, no merge kernel)
+// for batches of short contexts: at most kPairModeTiles tiles per pair and no more
+// pairs than resident worker slots.  PKV_PAIR_MODE=0 or 1 forces it off or on
+// (when legal) for measurements.
+constexpr int64_t kPairModeTiles = 16;
+
+bool use_pair_mode(int cu, int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                   bool fp8) {
+  static const int forced = [] {
+    const char* e = getenv("PKV_PAIR_MODE");
+    return e ? atoi(e) : -1;
+  }();
+  const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  const int64_t tiles = (static_cast<int64_t>(max_context_len) + kTile - 1) / kTile;
+  const bool legal = pairs <= static_cast<int64_t>(cu) * waves_per_cu(fp8) * 2;
+  if (forced >= 0) return forced == 1 && legal;
+  return legal && tiles <= kPairModeTiles && pairs <= static_cast<int64_t>(cu) * waves_per_cu(fp8);
+}
+
 bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
 bool supported_block_size(int32_t b) { return b == 8 || b == 16 || b == 32; }
 
@@ -128,7 +147,8 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
   d.Hkv = num_kv_heads;
   d.G = group;
   d.M = max_blocks_per_seq;
-  d.n_workers = static_cast<int32_t>(workers);
+  d.pair_mode = use_pair_mode(cu, num_seqs, num_kv_heads, max_context_len, fp8) ? 1 : 0;
+  d.n_workers = d.pair_mode ? num_seqs * num_kv_heads : static_cast<int32_t>(workers);
   d.NB = num_blocks;
   // scores in the log2 domain; an fp8 K pool's scale folds into the same factor
   d.c = static_cast<float>(static_cast<double>(scale) * static_cast<double>(k_scale) *
@@ -191,7 +211,8 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   d.Hkv = num_kv_heads;
   d.G = group;
   d.M = max_blocks_per_seq;
-  d.n_workers = static_cast<int32_t>(workers);
+  d.pair_mode = use_pair_mode(cu, num_seqs, num_kv_heads, max_context_len, fp8) ? 1 : 0;
+  d.n_workers = d.pair_mode ? num_seqs * num_kv_heads : static_cast<int32_t>(workers);
   d.NB = num_blocks;
   d.c = static_cast<float>(static_cast<double>(scale) * static_cast<double>(k_scale) *
                            1.4426950408889634);  // log2(e); an fp8 K scale folds in

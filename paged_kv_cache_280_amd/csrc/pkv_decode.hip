@@ -222,6 +222,25 @@ struct PairCursor {
 };
 
 // A tile of bf16 K/V in registers: every lane's MFMA operands, as loaded.
+// Pair mode: worker w takes (sequence w / Hkv, KV head w % Hkv) whole.  Returns
+// false for workers past the pairs and for empty sequences.
+template <bool kCausal>
+__device__ bool plan_pair(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
+                          const DecodeDims& d, int32_t cap, int64_t w, WorkerPlan& p) {
+  if (w >= static_cast<int64_t>(d.S) * d.Hkv) return false;
+  const int32_t s = static_cast<int32_t>(w / d.Hkv);
+  const int32_t g = static_cast<int32_t>(w - static_cast<int64_t>(s) * d.Hkv);
+  const int32_t T = tiles_of(seq_len<kCausal>(lens, qlens, d, cap, s).L);
+  if (T == 0) return false;
+  p.U = 1;  // only used to find the workers of split pairs, and none is split
+  p.N = 1;
+  p.s = s;
+  p.start = 0;
+  p.u = static_cast<int64_t>(g) * T;
+  p.u_end = p.u + T;
+  return true;
+}
+
 template <int D, int B>
 struct Bf16Tile {
   using Elem = uint16_t;
@@ -731,8 +750,9 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, (kFp8 && NC == 1) ? 2 : 1) v
 
   int4 opened = {-1, 0, 0, 0};
   WorkerPlan pl;
-  if (plan_worker<kCausal>(lens, qlens, d, cap, w, lane, pl))
-    opened = run_worker<D, B, NC, kCausal, kFp8>(cx, d, pl, w, lane);
+  const bool has = d.pair_mode ? plan_pair<kCausal>(lens, qlens, d, cap, w, pl)
+                               : plan_worker<kCausal>(lens, qlens, d, cap, w, lane, pl);
+  if (has) opened = run_worker<D, B, NC, kCausal, kFp8>(cx, d, pl, w, lane);
 
   // Rows no tile reaches are zeros: every row of an empty sequence, and in a
   // multi-token launch the rows past a sequence's query tokens (done last: off
@@ -752,7 +772,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, (kFp8 && NC == 1) ? 2 : 1) v
         *reinterpret_cast<u32x4_t*>(row + e) = u32x4_t{0, 0, 0, 0};
     }
   }
-  if (lane == 0) desc[w] = opened;
+  if (!d.pair_mode && lane == 0) desc[w] = opened;
 }
 
 // Merge of split pairs.  Work-group b reads the descriptors of its slice of
@@ -890,6 +910,7 @@ hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_group
                      static_cast<const Elem*>(b.v), b.tables, b.lens, b.qlens, b.out, b.ws, desc,
                      d);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if (d.pair_mode) return hipSuccess;  // nothing is split: no merge
   // records per split pair: about the workers per (sequence, KV head) pair
   const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
   if (pairs > 0 && d.n_workers > kMergeWideSplit * pairs)

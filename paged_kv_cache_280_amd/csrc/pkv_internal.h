@@ -40,6 +40,8 @@ struct DecodeDims {
   int32_t q_off;            // first query token of this launch
   int32_t R;                // rows of a (sequence, KV head) pair: G * Qc
   float v_scale;            // multiplies the outputs (fp8 V pools; 1 for bf16)
+  int32_t pair_mode;        // 1: worker w takes (sequence, KV head) pair w whole (no split,
+                            // no records, no merge); n_workers = S * Hkv
 };
 
 // Floats in one partial record: O[R][D], then m[R], then l[R], padded to a
