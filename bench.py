@@ -326,18 +326,27 @@ def attainable_bandwidth(nbytes=4 << 30, reps=10):
 
 
 def append_bench(args):
-    """kv_append of a prefill-sized chunk: 8 sequences x 2048 new tokens into a pool
-    with random block placement (GQA 8 KV heads, head_dim 128, block 16).  Prints
-    one JSON line with the call time and the bytes moved (rows read + slots written)."""
+    """kv_append (or kv_append_fp8 with --kv-dtype fp8) of a prefill-sized chunk:
+    8 sequences x 2048 new tokens into a pool with random block placement (GQA 8 KV
+    heads, head_dim 128).  Prints one JSON line with the call time and the bytes
+    moved (bf16 rows read + slots written)."""
     import torch
 
     import paged_kv_cache_280_amd as pkv
     import workloads as wl
 
     dev = torch.device("cuda:0")
+    fp8 = args.kv_dtype == "fp8"
     S, chunk, H, D, B = 8, 2048, 8, 128, args.block_size
     case = wl.case_random(args.seed, S, 32, H, D, B, [chunk] * S)
-    _, kd, vd, tabs, _ = wl.device_tensors(case, dev, poison=False)
+    if fp8:
+        kd, vd = wl.device_pools_fp8(case, dev, FP8_SCALE, FP8_SCALE, poison=False)
+        tabs = torch.from_numpy(case.block_tables).to(dev)
+        call = lambda: pkv.kv_append_fp8(k_new, v_new, kd, vd, tabs, seq, pos, B, FP8_SCALE,
+                                         FP8_SCALE)
+    else:
+        _, kd, vd, tabs, _ = wl.device_tensors(case, dev, poison=False)
+        call = lambda: pkv.kv_append(k_new, v_new, kd, vd, tabs, seq, pos, B)
     g = torch.Generator(device=dev)
     g.manual_seed(args.seed)
     T = S * chunk
@@ -346,19 +355,20 @@ def append_bench(args):
     seq = torch.arange(S, device=dev, dtype=torch.int32).repeat_interleave(chunk)
     pos = torch.arange(chunk, device=dev, dtype=torch.int32).repeat(S)
     for _ in range(args.warmup):
-        pkv.kv_append(k_new, v_new, kd, vd, tabs, seq, pos, B)
+        call()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        pkv.kv_append(k_new, v_new, kd, vd, tabs, seq, pos, B)
+        call()
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / args.steps
-    moved = 2 * 2 * T * H * D * 2   # K and V rows: read once, written once
-    print(json.dumps({"workload": "kv_append %d tokens (8 seqs x %d), 8 KV heads, head_dim 128, "
-                      "block %d" % (T, chunk, B), "us_per_call": round(us, 2),
-                      "bytes_per_call": moved, "gbs": round(moved / us / 1e3, 1)}), flush=True)
+    moved = 2 * T * H * D * (2 + (1 if fp8 else 2))   # K and V: bf16 rows read, slots written
+    print(json.dumps({"workload": "kv_append%s %d tokens (8 seqs x %d), 8 KV heads, head_dim 128, "
+                      "block %d" % ("_fp8" if fp8 else "", T, chunk, B),
+                      "us_per_call": round(us, 2), "bytes_per_call": moved,
+                      "gbs": round(moved / us / 1e3, 1)}), flush=True)
 
 
 def main():

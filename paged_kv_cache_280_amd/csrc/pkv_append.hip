@@ -5,9 +5,12 @@
 // blocks are taken only when a token needs them, so the caller's block manager
 // has already made room (and resolved copy-on-write) before this runs.
 //
-// One wave per (token, group of four KV heads).  K rows land as 16-byte chunks
-// (the K pool keeps 8 consecutive dims together); V rows are dim-major in the pool,
-// so each dim of a token is one 2-byte store.
+// One wave per (16 consecutive input tokens, group of four KV heads); lane
+// (j, h) writes token t0 + j's row of head h.  K rows land as 16-byte chunks (the
+// K pool keeps 8 consecutive dims together).  V rows are dim-major in the pool, so
+// each dim of a token is one 2-byte store; when the 16 tokens are consecutive
+// positions of one sequence (a prefill chunk), the stores of one dim from the 16
+// lanes of a head fall on consecutive slots and coalesce.
 //
 // fp8 pools ("KV cache, PagedAttention", aiwiki.vn, paragraph on cache
 // quantisation): each element is stored as the E4M3FN code nearest to x / scale
@@ -22,6 +25,40 @@ namespace {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kAppendHeadsPerWave = 4;
+constexpr int kAppendTokensPerWave = kWave / kAppendHeadsPerWave;  // 16
+
+// Slot of token t's row of head g: its (block, head) tile (elements of the pool
+// before it) and offset o in the block.  False when the token names no slot of this
+// pool: sequence or position out of range, or a table entry outside the pool.
+template <int D>
+__device__ __forceinline__ bool token_slot(int64_t t, int32_t g, const int32_t* __restrict__ tables,
+                                           const int32_t* __restrict__ token_seq,
+                                           const int32_t* __restrict__ token_pos,
+                                           const AppendDims& a, int64_t& tile, int32_t& o) {
+  if (t >= a.T || g >= a.Hkv) return false;
+  const int32_t s = token_seq[t];
+  const int32_t p = token_pos[t];
+  if (s < 0 || s >= a.S || p < 0 || p >= a.M * a.B) return false;
+  const int32_t b = tables[static_cast<int64_t>(s) * a.M + p / a.B];
+  if (b < 0 || b >= a.NB) return false;  // never write outside the pool
+  tile = (static_cast<int64_t>(b) * a.Hkv + g) * D * a.B;
+  o = p % a.B;
+  return true;
+}
+
+// Index of this lane's wave among all waves of the launch, and the wave's group
+// of four KV heads and first token.
+struct AppendWave {
+  int32_t g0;   // first KV head of the group
+  int64_t t0;   // first of the wave's 16 tokens
+};
+
+__device__ __forceinline__ AppendWave append_wave(const AppendDims& a) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + threadIdx.x / kWave;
+  const int32_t head_groups = (a.Hkv + kAppendHeadsPerWave - 1) / kAppendHeadsPerWave;
+  return {static_cast<int32_t>(item % head_groups) * kAppendHeadsPerWave,
+          (item / head_groups) * kAppendTokensPerWave};
+}
 
 template <int D>
 __global__ __launch_bounds__(kWave* kWavesPerGroup) void append_kernel(
@@ -29,31 +66,27 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void append_kernel(
     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ token_seq,
     const int32_t* __restrict__ token_pos, AppendDims a) {
-  constexpr int kChunks = D / 8;                        // 16-byte K chunks per head row
-  constexpr int kLanesPerHead = kWave / kAppendHeadsPerWave;  // 16
   const int lane = __lane_id();
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + threadIdx.x / kWave;
-  const int32_t head_groups = (a.Hkv + kAppendHeadsPerWave - 1) / kAppendHeadsPerWave;
-  if (item >= static_cast<int64_t>(a.T) * head_groups) return;
-  const int32_t t = static_cast<int32_t>(item / head_groups);
-  const int32_t g = static_cast<int32_t>(item % head_groups) * kAppendHeadsPerWave +
-                    lane / kLanesPerHead;
-  if (g >= a.Hkv) return;
-  const int32_t s = token_seq[t];
-  const int32_t p = token_pos[t];
-  if (s < 0 || s >= a.S || p < 0 || p >= a.M * a.B) return;  // not a slot of this pool
-  const int32_t b = tables[static_cast<int64_t>(s) * a.M + p / a.B];
-  if (b < 0 || b >= a.NB) return;                            // never write outside the pool
-  const int32_t o = p % a.B;
-  const int64_t tile = (static_cast<int64_t>(b) * a.Hkv + g) * D * a.B;  // (block, head) tile
-  const uint16_t* kr = k_new + (static_cast<int64_t>(t) * a.Hkv + g) * D;
-  const uint16_t* vr = v_new + (static_cast<int64_t>(t) * a.Hkv + g) * D;
-  const int sub = lane % kLanesPerHead;
-  for (int c = sub; c < kChunks; c += kLanesPerHead)
+  const AppendWave w = append_wave(a);
+  const int64_t t = w.t0 + lane % kAppendTokensPerWave;
+  const int32_t g = w.g0 + lane / kAppendTokensPerWave;
+  int64_t tile;
+  int32_t o;
+  if (!token_slot<D>(t, g, tables, token_seq, token_pos, a, tile, o)) return;
+  const uint16_t* kr = k_new + (t * a.Hkv + g) * D;
+  const uint16_t* vr = v_new + (t * a.Hkv + g) * D;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c)
     *reinterpret_cast<u32x4_t*>(k_cache + tile + (static_cast<int64_t>(c) * a.B + o) * 8) =
         *reinterpret_cast<const u32x4_t*>(kr + c * 8);
-  for (int dd = sub; dd < D; dd += kLanesPerHead)
-    v_cache[tile + static_cast<int64_t>(dd) * a.B + o] = vr[dd];
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vr + c * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      v_cache[tile + static_cast<int64_t>(c * 8 + i) * a.B + o] =
+          static_cast<uint16_t>(x[i / 2] >> (16 * (i % 2)));
+  }
 }
 
 // E4M3FN code of y: NaN -> 0x7F; otherwise y clamped to +-448 and converted by
@@ -77,50 +110,92 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return w;
 }
 
-__device__ __forceinline__ float widen_bf16(uint16_t x) {
-  return __builtin_bit_cast(float, static_cast<uint32_t>(x) << 16);
+// The two bf16 values of a dword as floats (first element in the low half).
+__device__ __forceinline__ float lo_bf16(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t x) {
+  return __builtin_bit_cast(float, x & 0xFFFF0000u);
 }
 
+// Codes of 8 consecutive bf16 values (one 16-byte load) divided by scale.
+__device__ __forceinline__ void e4m3x8(const uint16_t* src, float scale, uint32_t& lo,
+                                       uint32_t& hi) {
+  const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src);
+  lo = e4m3x4(lo_bf16(x[0]) / scale, hi_bf16(x[0]) / scale, lo_bf16(x[1]) / scale,
+              hi_bf16(x[1]) / scale);
+  hi = e4m3x4(lo_bf16(x[2]) / scale, hi_bf16(x[2]) / scale, lo_bf16(x[3]) / scale,
+              hi_bf16(x[3]) / scale);
+}
+
+// fp8: lane (j, k) of a head's 16 lanes takes tokens t0 + 4j .. t0 + 4j + 3 and
+// dims k*D/4 .. (k+1)*D/4 - 1.  The V pool keeps the codes of 4 consecutive
+// positions of one dim in one dword, so when the lane's 4 tokens are such a
+// position quad (same block, offsets 4m .. 4m+3: a prefill chunk in order) each
+// dim is one dword store; otherwise each token's codes are byte stores.
 template <int D>
 __global__ __launch_bounds__(kWave* kWavesPerGroup) void append_fp8_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ token_seq,
     const int32_t* __restrict__ token_pos, AppendDims a) {
-  constexpr int kChunks = D / 16;                       // 16-byte K chunks per head row
-  constexpr int kLanesPerHead = kWave / kAppendHeadsPerWave;  // 16
+  constexpr int kDims = D / 4;  // dims per lane: 32 or 16
   const int lane = __lane_id();
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + threadIdx.x / kWave;
-  const int32_t head_groups = (a.Hkv + kAppendHeadsPerWave - 1) / kAppendHeadsPerWave;
-  if (item >= static_cast<int64_t>(a.T) * head_groups) return;
-  const int32_t t = static_cast<int32_t>(item / head_groups);
-  const int32_t g = static_cast<int32_t>(item % head_groups) * kAppendHeadsPerWave +
-                    lane / kLanesPerHead;
-  if (g >= a.Hkv) return;
-  const int32_t s = token_seq[t];
-  const int32_t p = token_pos[t];
-  if (s < 0 || s >= a.S || p < 0 || p >= a.M * a.B) return;  // not a slot of this pool
-  const int32_t b = tables[static_cast<int64_t>(s) * a.M + p / a.B];
-  if (b < 0 || b >= a.NB) return;                            // never write outside the pool
-  const int32_t o = p % a.B;
-  const int64_t tile = (static_cast<int64_t>(b) * a.Hkv + g) * D * a.B;  // bytes
-  const uint16_t* kr = k_new + (static_cast<int64_t>(t) * a.Hkv + g) * D;
-  const uint16_t* vr = v_new + (static_cast<int64_t>(t) * a.Hkv + g) * D;
-  const int sub = lane % kLanesPerHead;
-  for (int c = sub; c < kChunks; c += kLanesPerHead) {
-    float x[16];
+  const AppendWave w = append_wave(a);
+  const int32_t g = w.g0 + lane / kAppendTokensPerWave;
+  const int64_t t0 = w.t0 + (lane % kAppendTokensPerWave) / 4 * 4;
+  const int d0 = (lane % 4) * kDims;
+  int64_t tile[4];  // in bytes for fp8 pools
+  int32_t o[4];
+  bool ok[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = widen_bf16(kr[c * 16 + i]) / a.k_scale;
-    const u32x4_t w = {e4m3x4(x[0], x[1], x[2], x[3]), e4m3x4(x[4], x[5], x[6], x[7]),
-                       e4m3x4(x[8], x[9], x[10], x[11]), e4m3x4(x[12], x[13], x[14], x[15])};
-    *reinterpret_cast<u32x4_t*>(k_cache + tile + (static_cast<int64_t>(c) * a.B + o) * 16) = w;
+  for (int u = 0; u < 4; ++u)
+    ok[u] = token_slot<D>(t0 + u, g, tables, token_seq, token_pos, a, tile[u], o[u]);
+  bool quad = ok[0] && ok[1] && ok[2] && ok[3] && o[0] % 4 == 0;
+#pragma unroll
+  for (int u = 1; u < 4; ++u) quad = quad && tile[u] == tile[0] && o[u] == o[0] + u;
+
+  uint32_t cv[4][kDims / 4];  // V codes, dword i of token u = dims d0 + 4i .. 4i+3
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (!ok[u]) continue;
+    const int64_t row = ((t0 + u) * a.Hkv + g) * D + d0;
+#pragma unroll
+    for (int c = 0; c < kDims / 16; ++c) {  // one 16-byte K chunk per 16 dims
+      uint32_t k0, k1, k2, k3;
+      e4m3x8(k_new + row + c * 16, a.k_scale, k0, k1);
+      e4m3x8(k_new + row + c * 16 + 8, a.k_scale, k2, k3);
+      *reinterpret_cast<u32x4_t*>(
+          k_cache + tile[u] + (static_cast<int64_t>(d0 / 16 + c) * a.B + o[u]) * 16) =
+          u32x4_t{k0, k1, k2, k3};
+    }
+#pragma unroll
+    for (int c = 0; c < kDims / 8; ++c) e4m3x8(v_new + row + c * 8, a.v_scale, cv[u][2 * c],
+                                               cv[u][2 * c + 1]);
   }
   // V element (o, d) at [d%16][o/4][d/16][o%4] of the tile
-  for (int dd = sub; dd < D; dd += kLanesPerHead) {
-    const float y = widen_bf16(vr[dd]) / a.v_scale;
-    const uint32_t code = e4m3x4(y, 0.f, 0.f, 0.f) & 0xFFu;
-    v_cache[tile + ((static_cast<int64_t>(dd % 16) * (a.B / 4) + o / 4) * (D / 16) + dd / 16) * 4 +
-            o % 4] = static_cast<uint8_t>(code);
+  const int64_t row_bytes = (D / 16) * 4;  // one [d%16][o/4] row
+  if (quad) {
+#pragma unroll
+    for (int i = 0; i < kDims; ++i) {
+      const int d = d0 + i;
+      const int sh = 8 * (i % 4);
+      const uint32_t word = ((cv[0][i / 4] >> sh) & 0xFFu) | (((cv[1][i / 4] >> sh) & 0xFFu) << 8) |
+                            (((cv[2][i / 4] >> sh) & 0xFFu) << 16) |
+                            (((cv[3][i / 4] >> sh) & 0xFFu) << 24);
+      *reinterpret_cast<uint32_t*>(
+          v_cache + tile[0] + (static_cast<int64_t>(d % 16) * (a.B / 4) + o[0] / 4) * row_bytes +
+          (d / 16) * 4) = word;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!ok[u]) continue;
+#pragma unroll
+      for (int i = 0; i < kDims; ++i) {
+        const int d = d0 + i;
+        v_cache[tile[u] + (static_cast<int64_t>(d % 16) * (a.B / 4) + o[u] / 4) * row_bytes +
+                (d / 16) * 4 + o[u] % 4] = static_cast<uint8_t>(cv[u][i / 4] >> (8 * (i % 4)));
+      }
+    }
   }
 }
 
@@ -128,7 +203,8 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void append_fp8_kernel(
 
 hipError_t launch_append(const AppendBuffers& b, const AppendDims& a, int D, hipStream_t stream) {
   const int64_t head_groups = (a.Hkv + kAppendHeadsPerWave - 1) / kAppendHeadsPerWave;
-  const int64_t waves = static_cast<int64_t>(a.T) * head_groups;
+  const int64_t waves =
+      (static_cast<int64_t>(a.T) + kAppendTokensPerWave - 1) / kAppendTokensPerWave * head_groups;
   const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
   if (groups <= 0) return hipSuccess;
   if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -150,7 +226,8 @@ hipError_t launch_append(const AppendBuffers& b, const AppendDims& a, int D, hip
 hipError_t launch_append_fp8(const AppendBuffers& b, const AppendDims& a, int D,
                              hipStream_t stream) {
   const int64_t head_groups = (a.Hkv + kAppendHeadsPerWave - 1) / kAppendHeadsPerWave;
-  const int64_t waves = static_cast<int64_t>(a.T) * head_groups;
+  const int64_t waves =
+      (static_cast<int64_t>(a.T) + kAppendTokensPerWave - 1) / kAppendTokensPerWave * head_groups;
   const int64_t groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
   if (groups <= 0) return hipSuccess;
   if (groups > 0x7fffffffLL) return hipErrorInvalidValue;

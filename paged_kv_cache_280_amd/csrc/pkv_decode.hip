@@ -43,6 +43,14 @@
 // pair, one or two 16-column tiles per wave, each column with its own position
 // limit; every K/V tile is loaded once for all of them.  A pair's tiles stop at
 // the last position its last query token sees.
+//
+// fp8 pools ("KV cache, PagedAttention", aiwiki.vn, paragraph on cache
+// quantisation): one-byte E4M3FN codes, loaded 16 bytes per lane and widened
+// exactly to bf16 for the same MFMAs; the K pool's scale folds into the score
+// factor and the V pool's into the output, so nothing is scaled per element.
+//
+// Pair mode (short contexts): worker w takes pair w whole, so nothing is split and
+// no merge runs.
 
 #include <math.h>
 

@@ -49,6 +49,32 @@ def test_kv_append_matches_the_oracle_byte_for_byte(D, B, H):
     assert np.array_equal(_host(kd), kp) and np.array_equal(_host(vd), vp)
 
 
+@pytest.mark.parametrize("D,B,H,start,T", [(128, 16, 8, 7, 37), (64, 8, 5, 0, 64),
+                                          (128, 32, 3, 30, 100)])
+def test_kv_append_of_a_prefill_chunk_in_order(D, B, H, start, T):
+    """A chunk of T consecutive positions of one sequence, starting mid-block (the
+    prefill layout: consecutive tokens land on consecutive slots), plus a second
+    sequence's single token after it; T is not a multiple of 16."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    rng = np.random.default_rng(D + H + T)
+    lens = [start + T, 3 * B]
+    case = wl.case_random(D + T, len(lens), H, H, D, B, lens)
+    kp, vp = wl.host_pools(case, poison=False)
+    seq = np.array([0] * T + [1], np.int32)
+    pos = np.array(list(range(start, start + T)) + [3 * B - 1], np.int32)
+    kn = wl.randn_bf16(rng, (len(seq), H, D))
+    vn = wl.randn_bf16(rng, (len(seq), H, D))
+    kd, vd = to_dev_bf16(kp), to_dev_bf16(vp)
+    pkv.kv_append(to_dev_bf16(kn), to_dev_bf16(vn), kd, vd, to_dev_i32(case.block_tables),
+                  to_dev_i32(seq), to_dev_i32(pos), B)
+    torch.cuda.synchronize()
+    oracle.kv_append(kn, vn, kp, vp, case.block_tables, seq, pos, B)
+    assert np.array_equal(_host(kd), kp) and np.array_equal(_host(vd), vp)
+
+
 def test_kv_append_with_no_tokens_is_a_no_op():
     import torch
 

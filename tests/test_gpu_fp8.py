@@ -172,6 +172,34 @@ def test_kv_append_fp8_matches_the_oracle_byte_for_byte(D, B, scales):
     assert np.array_equal(kd.cpu().numpy(), kp) and np.array_equal(vd.cpu().numpy(), vp)
 
 
+# start 7 never forms an aligned position quad (byte stores throughout); the others
+# do, with ragged ends
+@pytest.mark.parametrize("D,B,H,start,T", [(128, 16, 8, 7, 37), (128, 16, 8, 4, 61),
+                                          (64, 32, 5, 0, 70), (128, 8, 3, 0, 33),
+                                          (64, 16, 4, 2, 300)])
+def test_kv_append_fp8_of_a_prefill_chunk_in_order(D, B, H, start, T):
+    """T consecutive positions of one sequence from mid-block, quantised in place."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    rng = np.random.default_rng(D + T)
+    scales = (0.041, 0.023)
+    lens = [start + T, B + 1]
+    case = wl.case_random(D + B + T, len(lens), H, H, D, B, lens)
+    kp, vp = wl.host_pools_fp8(case, *scales, poison=False)
+    seq = np.array([0] * T + [1], np.int32)
+    pos = np.array(list(range(start, start + T)) + [B], np.int32)
+    kn = _specials_bf16(rng, (len(seq), H, D), scales[0])
+    vn = _specials_bf16(rng, (len(seq), H, D), scales[1])
+    kd, vd = _dev_u8(kp), _dev_u8(vp)
+    pkv.kv_append_fp8(to_dev_bf16(kn), to_dev_bf16(vn), kd, vd, to_dev_i32(case.block_tables),
+                      to_dev_i32(seq), to_dev_i32(pos), B, *scales)
+    torch.cuda.synchronize()
+    oracle.kv_append_fp8(kn, vn, kp, vp, case.block_tables, seq, pos, B, *scales)
+    assert np.array_equal(kd.cpu().numpy(), kp) and np.array_equal(vd.cpu().numpy(), vp)
+
+
 def test_fp8_decode_step_with_append():
     """A full fp8 decode step: the block manager makes room (copy-on-write of a shared
     last block), kv_append_fp8 quantises the new token into its slot, decode reads it."""
