@@ -277,6 +277,33 @@ int32_t copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_la
                     int64_t num_blocks, int64_t block_bytes, const int32_t* src_dst_pairs,
                     int32_t num_pairs, void* stream);
 
+/*
+ * Check of the table contract the attention entry points assume (they clamp
+ * block ids and lengths into range instead of checking them, so a caller that
+ * breaks the contract gets meaningless rows for that sequence and no error).
+ * The block-table walk is that of troisinh.com, section "Cơ chế Block Table":
+ * position t of sequence s lives in the block block_tables[s][t / block_size].
+ * For every sequence s, with L = context_lens[s]:
+ *   kind 1: L < 0 or L > max_blocks_per_seq*block_size;
+ *   kind 2: one of the first ceil(L'/block_size) entries of row s lies outside
+ *           [0, num_blocks), L' being L clamped into [0, max_blocks_per_seq*block_size];
+ *   kind 3: query_lens is not NULL and query_lens[s] < 0, > L' or > max_query_len.
+ *
+ *   block_tables, context_lens, query_lens (may be NULL): as in the attention calls
+ *   max_query_len  rows per sequence of the multi-token q (ignored without query_lens)
+ *   result        DEVICE int32, 4-byte aligned.  After the enqueued work finishes it
+ *                 holds -1 when every sequence meets the contract, else 4*s + kind
+ *                 for the smallest such s and the smallest kind it breaks.
+ *   num_seqs      below 2^29 (0 writes -1)
+ * Enqueues two kernels (a one-thread reset of *result, then one wave per sequence
+ * with an atomic minimum); no memset, so the pair may be captured in a graph.
+ * Reading *result is the caller's (it needs the stream to have finished).
+ */
+int32_t pkv_check_batch(const int32_t* block_tables, const int32_t* context_lens,
+                        const int32_t* query_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                        int64_t num_blocks, int32_t block_size, int32_t max_query_len,
+                        int32_t* result, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

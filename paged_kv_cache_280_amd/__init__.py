@@ -9,7 +9,9 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     PkvError,
+    CHECK_KINDS,
     abi_version,
+    check_batch,
     copy_blocks,
     kv_append,
     kv_append_fp8,

@@ -24,7 +24,7 @@ STATUS_NAMES = {
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "paged_attn_decode_workspace_bytes",
            "paged_attn_decode", "paged_attn_decode_fp8", "paged_attn_multi_workspace_bytes",
            "paged_attn_multi", "paged_attn_multi_fp8",
-           "kv_append", "kv_append_fp8", "copy_blocks")
+           "kv_append", "kv_append_fp8", "copy_blocks", "pkv_check_batch")
 
 
 class PkvError(RuntimeError):
@@ -75,6 +75,8 @@ def load_library(path: str = LIB_PATH):
     lib.kv_append_fp8.restype = i32
     lib.copy_blocks.argtypes = [p, p, i32, i64, i64, p, i32, p]
     lib.copy_blocks.restype = i32
+    lib.pkv_check_batch.argtypes = [p, p, p, i32, i32, i64, i32, i32, p, p]
+    lib.pkv_check_batch.restype = i32
     _lib = lib
     return lib
 
@@ -419,3 +421,39 @@ def copy_blocks(k_caches, v_caches, src_dst_pairs, stream=None):
                              _stream_handle(ref, stream))
     if rc != 0:
         raise PkvError(rc, "copy_blocks")
+
+
+CHECK_KINDS = {1: "context length outside [0, max_blocks_per_seq*block_size]",
+               2: "block-table entry outside [0, num_blocks)",
+               3: "query length outside [0, min(context length, max_query_len)]"}
+
+
+def check_batch(block_tables, context_lens, block_size, num_blocks, query_lens=None,
+                max_query_len=0, stream=None):
+    """Check the table contract on the device (see ``pkv_check_batch`` in
+    ``include/pkv.h``).  Waits for the stream and returns None when every sequence
+    meets it, else ``(sequence, kind, text)`` for the first one that does not."""
+    import torch
+
+    lib = load_library()
+    for t in (block_tables, context_lens) + ((query_lens,) if query_lens is not None else ()):
+        _check(t.dtype == torch.int32 and t.is_contiguous() and t.is_cuda, "int32 contiguous GPU tensors")
+    _check(block_tables.dim() == 2 and context_lens.numel() == block_tables.shape[0],
+           "block_tables [num_seqs][max_blocks_per_seq] and context_lens [num_seqs]")
+    S, M = int(block_tables.shape[0]), int(block_tables.shape[1])
+    if query_lens is not None:
+        _check(query_lens.numel() == S, "query_lens [num_seqs]")
+    result = torch.empty(1, dtype=torch.int32, device=block_tables.device)
+    with torch.cuda.device(block_tables.device):
+        st = stream if stream is not None else torch.cuda.current_stream(block_tables.device)
+        rc = lib.pkv_check_batch(block_tables.data_ptr(), context_lens.data_ptr(),
+                                 query_lens.data_ptr() if query_lens is not None else None, S, M,
+                                 int(num_blocks), int(block_size), int(max_query_len),
+                                 result.data_ptr(), ctypes.c_void_p(st.cuda_stream))
+        if rc != 0:
+            raise PkvError(rc, "pkv_check_batch")
+        st.synchronize()
+    code = int(result.item())
+    if code < 0:
+        return None
+    return code // 4, code % 4, CHECK_KINDS.get(code % 4, "unknown")

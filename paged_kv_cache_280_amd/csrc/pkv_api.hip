@@ -432,4 +432,26 @@ int32_t copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_la
   return PKV_OK;
 }
 
+int32_t pkv_check_batch(const int32_t* block_tables, const int32_t* context_lens,
+                        const int32_t* query_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                        int64_t num_blocks, int32_t block_size, int32_t max_query_len,
+                        int32_t* result, void* stream) {
+  if (num_seqs < 0 || num_seqs >= (1 << 29) || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      block_size <= 0 || max_query_len < 0)
+    return PKV_ERR_SHAPE;
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX) return PKV_ERR_SHAPE;
+  if (!result || (num_seqs > 0 && (!block_tables || !context_lens))) return PKV_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(result) & 3u) != 0) return PKV_ERR_ALIGNMENT;
+  pkv::CheckDims c;
+  c.S = num_seqs;
+  c.M = max_blocks_per_seq;
+  c.B = block_size;
+  c.Qmax = max_query_len;
+  c.NB = num_blocks;
+  if (pkv::launch_check(block_tables, context_lens, query_lens, result, c,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PKV_ERR_LAUNCH;
+  return PKV_OK;
+}
+
 }  // extern "C"

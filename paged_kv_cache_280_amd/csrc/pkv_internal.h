@@ -95,6 +95,16 @@ hipError_t launch_append(const AppendBuffers& b, const AppendDims& a, int D, hip
 hipError_t launch_append_fp8(const AppendBuffers& b, const AppendDims& a, int D,
                              hipStream_t stream);
 
+// Table-contract check (pkv_check.hip): S sequences, M entries per table row,
+// block size B, NB pool blocks, Qmax query rows per sequence (multi-token).
+struct CheckDims {
+  int32_t S, M, B, Qmax;
+  int64_t NB;
+};
+
+hipError_t launch_check(const int32_t* tables, const int32_t* lens, const int32_t* qlens,
+                        int32_t* result, const CheckDims& c, hipStream_t stream);
+
 // Launcher (pkv_copy.hip).
 hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                               int64_t num_blocks, int64_t block_bytes, const int32_t* pairs,

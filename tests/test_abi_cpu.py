@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
                             "paged_attn_decode_fp8",
                             "paged_attn_multi_workspace_bytes", "paged_attn_multi",
                             "paged_attn_multi_fp8",
-                            "kv_append", "kv_append_fp8", "copy_blocks"])
+                            "kv_append", "kv_append_fp8", "copy_blocks", "pkv_check_batch"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -186,3 +186,21 @@ def test_kv_append_fp8_host_checks(lib):
     assert ap(D=96) == -3
     assert ap(kn=None) == -1
     assert ap(kn=0x1008) == -5
+
+
+def test_check_batch_rejects_bad_arguments_on_the_host(lib):
+    """pkv_check_batch: shape and pointer errors come back before anything is enqueued."""
+    def call(tables=0x1000, lens=0x2000, qlens=None, S=4, M=8, NB=64, B=16, Qmax=0, result=0x3000):
+        return lib.pkv_check_batch(tables, lens, qlens, S, M, NB, B, Qmax, result, None)
+
+    assert call(S=-1) == -2
+    assert call(S=1 << 29) == -2
+    assert call(M=0) == -2
+    assert call(NB=0) == -2
+    assert call(B=0) == -2
+    assert call(Qmax=-1) == -2
+    assert call(M=1 << 28, B=32) == -2          # a row would address more than 2^31 positions
+    assert call(result=None) == -1
+    assert call(tables=None) == -1
+    assert call(lens=None) == -1
+    assert call(result=0x3002) == -5            # result must be 4-byte aligned
