@@ -32,7 +32,10 @@
  * D = head_dim, Hkv = num_kv_heads, NB = num_blocks), bf16:
  *   K  [NB][Hkv][D/8][B][8] : element (block b, head g, slot o, dim d) at
  *                             (((b*Hkv + g)*(D/8) + d/8)*B + o)*8 + d%8
- *   V  [NB][Hkv][D][B]      : element (b, g, o, d) at ((b*Hkv + g)*D + d)*B + o
+ *   V  [NB][Hkv][B/Bt][D][Bt], Bt = min(B, 16) : element (b, g, o, d) at
+ *                             (((b*Hkv + g)*(B/Bt) + o/Bt)*D + d)*Bt + o%Bt
+ *                             (B <= 16: [NB][Hkv][D][B]; B = 32: each 16-position
+ *                             half of a block is its own [D][16] run)
  * Each (block, head) tile is one contiguous run of B*D*2 bytes, and a whole block
  * (all heads) is one contiguous run of Hkv*B*D*2 bytes.
  */

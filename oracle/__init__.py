@@ -103,7 +103,8 @@ def paged_decode(q, k_pool, v_pool, block_tables, context_lens, block_size, scal
                  num_kv_heads, precision="f32", threads=0, lib=None):
     """Reference decode.  Arrays are numpy; q/k_pool/v_pool hold bf16 bit patterns
     (uint16 or int16).  Shapes: q [S][Hq][D]; k_pool [NB][Hkv][D/8][B][8];
-    v_pool [NB][Hkv][D][B]; block_tables [S][M] int32; context_lens [S] int32.
+    v_pool [NB][Hkv][B/Bt][D][Bt], Bt = min(B, 16); block_tables [S][M] int32;
+    context_lens [S] int32.
     Returns float32 (or float64) [S][Hq][D]."""
     q, kp, vp = _u16(q), _u16(k_pool), _u16(v_pool)
     tables = np.ascontiguousarray(block_tables, dtype=np.int32)

@@ -27,8 +27,9 @@
 //   * pool layout (one pool per layer, per K and per V):
 //       K  [num_blocks][Hkv][D/8][B][8]   element (b,g,o,d) at
 //          (((b*Hkv + g)*(D/8) + d/8)*B + o)*8 + d%8
-//       V  [num_blocks][Hkv][D][B]        element (b,g,o,d) at
-//          ((b*Hkv + g)*D + d)*B + o
+//       V  [num_blocks][Hkv][B/Bt][D][Bt] with Bt = min(B, 16): element (b,g,o,d)
+//          at (((b*Hkv + g)*(B/Bt) + o/Bt)*D + d)*Bt + o%Bt (each 16-position
+//          half of a block is its own [D][16] run; the whole block when B <= 16)
 //   * block_tables is int32 [S][M] row-major; only the first ceil(L/B) entries of
 //     row s are read.  Tail slots of the last block, padding entries of a table
 //     row and unreferenced blocks are never read.
@@ -80,7 +81,8 @@ inline int64_t k_index(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t
 }
 
 inline int64_t v_index(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t d) {
-  return ((b * sh.Hkv + g) * sh.D + d) * sh.B + o;
+  const int64_t bt = sh.B < 16 ? sh.B : 16;
+  return (((b * sh.Hkv + g) * (sh.B / bt) + o / bt) * sh.D + d) * bt + o % bt;
 }
 
 inline int64_t k8_index(const Shape& sh, int64_t b, int64_t g, int64_t o, int64_t d) {

@@ -102,6 +102,17 @@ def _check(cond, msg):
         raise ValueError(msg)
 
 
+def _v_pool_ok(v_cache, NB, Hkv, D, B):
+    """bf16 V pool [NB][Hkv][B/Bt][D][Bt], Bt = min(B, 16); for B <= 16 the same
+    memory may also come as [NB][Hkv][D][B]."""
+    bt = min(B, 16)
+    shape = tuple(v_cache.shape)
+    return shape == (NB, Hkv, B // bt, D, bt) or (B <= 16 and shape == (NB, Hkv, D, B))
+
+
+V_POOL_TEXT = "v_cache must be [num_blocks][Hkv][block_size/Bt][D][Bt], Bt = min(block_size, 16)"
+
+
 def decode_shapes(q, k_cache, v_cache, block_tables, context_lens, block_size):
     """(S, Hq, Hkv, D, NB, M) of a decode call, after host-side checks of the tensors."""
     import torch
@@ -112,7 +123,7 @@ def decode_shapes(q, k_cache, v_cache, block_tables, context_lens, block_size):
     _check(k_cache.dim() == 5 and k_cache.shape[2] * 8 == D and k_cache.shape[3] == B
            and k_cache.shape[4] == 8, "k_cache must be [num_blocks][Hkv][D/8][block_size][8]")
     NB, Hkv = int(k_cache.shape[0]), int(k_cache.shape[1])
-    _check(tuple(v_cache.shape) == (NB, Hkv, D, B), "v_cache must be [num_blocks][Hkv][D][block_size]")
+    _check(_v_pool_ok(v_cache, NB, Hkv, D, B), V_POOL_TEXT)
     _check(block_tables.dim() == 2 and block_tables.shape[0] == S,
            "block_tables must be [num_seqs][max_blocks_per_seq]")
     _check(context_lens.dim() == 1 and context_lens.shape[0] == S, "context_lens must be [num_seqs]")
@@ -336,7 +347,7 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos
     _check(k_cache.dim() == 5 and tuple(k_cache.shape[1:]) == (Hkv, D // 8, B, 8),
            "k_cache must be [num_blocks][Hkv][D/8][block_size][8]")
     NB = int(k_cache.shape[0])
-    _check(tuple(v_cache.shape) == (NB, Hkv, D, B), "v_cache must be [num_blocks][Hkv][D][block_size]")
+    _check(_v_pool_ok(v_cache, NB, Hkv, D, B), V_POOL_TEXT)
     for t in (k_new, v_new, k_cache, v_cache):
         _check(t.dtype == torch.bfloat16 and t.is_contiguous(), "bf16 contiguous tensors")
     for t in (block_tables, token_seq, token_pos):

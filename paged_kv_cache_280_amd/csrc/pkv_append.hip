@@ -7,10 +7,11 @@
 //
 // One wave per (16 consecutive input tokens, group of four KV heads); lane
 // (j, h) writes token t0 + j's row of head h.  K rows land as 16-byte chunks (the
-// K pool keeps 8 consecutive dims together).  V rows are dim-major in the pool, so
-// each dim of a token is one 2-byte store; when the 16 tokens are consecutive
-// positions of one sequence (a prefill chunk), the stores of one dim from the 16
-// lanes of a head fall on consecutive slots and coalesce.
+// K pool keeps 8 consecutive dims together).  V rows are dim-major in the pool
+// (each 16-position half of a block its own [D][16] run), so each dim of a token is
+// one 2-byte store; when the 16 tokens are consecutive positions of one sequence (a
+// prefill chunk), the stores of one dim from the 16 lanes of a head fall on
+// consecutive slots and coalesce.
 //
 // fp8 pools ("KV cache, PagedAttention", aiwiki.vn, paragraph on cache
 // quantisation): each element is stored as the E4M3FN code nearest to x / scale
@@ -79,13 +80,14 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void append_kernel(
   for (int c = 0; c < D / 8; ++c)
     *reinterpret_cast<u32x4_t*>(k_cache + tile + (static_cast<int64_t>(c) * a.B + o) * 8) =
         *reinterpret_cast<const u32x4_t*>(kr + c * 8);
+  const int32_t bt = a.B < 16 ? a.B : 16;  // positions of one V run
+  uint16_t* vrun = v_cache + tile + static_cast<int64_t>(o / bt) * D * bt + o % bt;
 #pragma unroll
   for (int c = 0; c < D / 8; ++c) {
     const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vr + c * 8);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      v_cache[tile + static_cast<int64_t>(c * 8 + i) * a.B + o] =
-          static_cast<uint16_t>(x[i / 2] >> (16 * (i % 2)));
+      vrun[static_cast<int64_t>(c * 8 + i) * bt] = static_cast<uint16_t>(x[i / 2] >> (16 * (i % 2)));
   }
 }
 

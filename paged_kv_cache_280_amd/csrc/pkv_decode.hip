@@ -263,15 +263,16 @@ struct Bf16Tile {
       const int32_t ob = tok0 % B;
       const int64_t base = static_cast<int64_t>(b) * pc.block_stride + pc.head_off;
       const uint16_t* kt = pc.k + base;
-      const uint16_t* vt = pc.v + base;
+      // V keeps each 16-position half of a block as its own [D][16] run
+      const uint16_t* vt = pc.v + base + (ob / kTile) * D * kTile;
       const uint32_t koff = static_cast<uint32_t>(((lane >> 4) * B + ob + (lane & 15)) * 8);
-      const uint32_t voff = static_cast<uint32_t>((lane & 15) * B + ob + (lane >> 4) * 4);
+      const uint32_t voff = static_cast<uint32_t>((lane & 15) * kTile + (lane >> 4) * 4);
 #pragma unroll
       for (int c = 0; c < D / 32; ++c)
         k[c] = *reinterpret_cast<const u32x4_t*>(kt + koff + c * 4 * B * 8);
 #pragma unroll
       for (int mt = 0; mt < D / 16; ++mt)
-        v[mt] = *reinterpret_cast<const u32x2_t*>(vt + voff + mt * 16 * B);
+        v[mt] = *reinterpret_cast<const u32x2_t*>(vt + voff + mt * 16 * kTile);
     } else {
       // B == 8: the tile spans logical blocks 2t and 2t+1 (the second clamped to
       // the sequence's last block; its lanes are masked when it lies past the

@@ -158,7 +158,7 @@ def test_shared_prefix_sampling_end_to_end(prefix, expect_copies):
     for i, L in enumerate(lens):      # the tail slots of private last blocks are never read
         if L % B:
             kp2[priv_tables[i, (L - 1) // B], :, :, L % B:, :] = wl.BF16_NAN
-            vp2[priv_tables[i, (L - 1) // B], :, :, L % B:] = wl.BF16_NAN
+            wl.poison_v_tail(vp2, priv_tables[i, (L - 1) // B], L % B, wl.BF16_NAN)
     out2 = pkv.paged_attn_decode(to_dev_bf16(q), to_dev_bf16(kp2), to_dev_bf16(vp2),
                                  to_dev_i32(priv_tables), to_dev_i32(lens), B, sc.scale,
                                  max_context_len=int(lens.max()))

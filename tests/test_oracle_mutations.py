@@ -19,7 +19,7 @@ MUTATIONS = {
         "return (((b * sh.Hkv + g) * (sh.D / 8) + d / 8) * sh.B + o) * 8 + d % 8;",
         "return (((b * sh.Hkv + g) * sh.B + o) * (sh.D / 8) + d / 8) * 8 + d % 8;"),
     "v_layout_dim_minor": (
-        "return ((b * sh.Hkv + g) * sh.D + d) * sh.B + o;",
+        "return (((b * sh.Hkv + g) * (sh.B / bt) + o / bt) * sh.D + d) * bt + o % bt;",
         "return ((b * sh.Hkv + g) * sh.B + o) * sh.D + d;"),
     "group_by_modulo": ("h / G, lens[s],", "h % sh.Hkv, lens[s],"),
     "drop_last_token": ("for (int t = 0; t < L; ++t) {\n    const int j",

@@ -32,7 +32,7 @@ def brute_force(case, q, kp, vp):
     """Gather every (seq, kv head) into contiguous [L][D] rows with einops and
     run the library routine in float64.  Returns float64 [S][Hq][D]."""
     kl = rearrange(wl.f32_from_bf16(kp).astype(np.float64), "n h c b e -> n h b (c e)")
-    vl = rearrange(wl.f32_from_bf16(vp).astype(np.float64), "n h d b -> n h b d")
+    vl = rearrange(wl.f32_from_bf16(vp).astype(np.float64), "n h t d b -> n h (t b) d")
     qf = wl.f32_from_bf16(q).astype(np.float64)
     S, Hq, D = q.shape
     G = Hq // case.num_kv_heads
@@ -162,7 +162,7 @@ def test_q_zero_gives_mean_of_values(oracle_lib):
     q = np.zeros((2, 4, 64), np.uint16)  # +0.0
     kp, vp = wl.host_pools(case)
     got = run(oracle_lib, case, q, kp, vp, "f64")
-    vl = rearrange(wl.f32_from_bf16(vp).astype(np.float64), "n h d b -> n h b d")
+    vl = rearrange(wl.f32_from_bf16(vp).astype(np.float64), "n h t d b -> n h (t b) d")
     for s in range(2):
         L = int(case.context_lens[s])
         ids = case.block_tables[s, : -(-L // 8)]
@@ -176,7 +176,7 @@ def test_single_token_returns_its_value_exactly(oracle_lib):
     q = wl.host_q(case)
     kp, vp = wl.host_pools(case)
     got = run(oracle_lib, case, q, kp, vp)
-    vl = rearrange(wl.f32_from_bf16(vp), "n h d b -> n h b d")
+    vl = rearrange(wl.f32_from_bf16(vp), "n h t d b -> n h (t b) d")
     for s in range(3):
         b = case.block_tables[s, 0]
         for h in range(4):
@@ -197,7 +197,7 @@ def test_argmax_limit(oracle_lib):
     case = wl.case_random(6, 1, 1, 1, 64, 16, [50])
     kp, vp = wl.host_pools(case)
     kl = rearrange(wl.f32_from_bf16(kp), "n h c b e -> n h b (c e)")
-    vl = rearrange(wl.f32_from_bf16(vp), "n h d b -> n h b d")
+    vl = rearrange(wl.f32_from_bf16(vp), "n h t d b -> n h (t b) d")
     j = 23
     b, o = case.block_tables[0, j // 16], j % 16
     q = wl.bf16_from_f32(kl[b, 0, o] * 4.0).reshape(1, 1, 64)
@@ -336,9 +336,9 @@ def test_oracle_kv_append_places_rows_by_the_table(oracle_lib):
         vn = wl.randn_bf16(rng, (8, 2, D))
         oracle_lib.kv_append(kn, vn, kp, vp, case.block_tables, seq, pos, B)
         kl = rearrange(kp, "n h c b e -> n h b (c e)")
-        vl = rearrange(vp, "n h d b -> n h b d")
+        vl = rearrange(vp, "n h t d b -> n h (t b) d")
         kl0 = rearrange(kp0, "n h c b e -> n h b (c e)")
-        vl0 = rearrange(vp0, "n h d b -> n h b d")
+        vl0 = rearrange(vp0, "n h t d b -> n h (t b) d")
         touched = np.zeros(kl.shape[:3], bool)
         for i in range(6):                       # the last two tokens are out of range
             b, o = case.block_tables[seq[i], pos[i] // B], pos[i] % B
@@ -360,7 +360,7 @@ def test_multi_query_oracle_matches_causal_library_attention(oracle_lib, B, D, G
     got = oracle_lib.paged_attn_multi(q, kp, vp, case.block_tables, case.context_lens, qlens,
                                       B, case.scale, 2)
     kl = rearrange(wl.f32_from_bf16(kp).astype(np.float64), "n h c b e -> n h b (c e)")
-    vl = rearrange(wl.f32_from_bf16(vp).astype(np.float64), "n h d b -> n h b d")
+    vl = rearrange(wl.f32_from_bf16(vp).astype(np.float64), "n h t d b -> n h (t b) d")
     for s, (L, T) in enumerate(zip(lens, qlens)):
         ids = case.block_tables[s, : -(-L // B)]
         assert (got[s, T:] == 0).all()

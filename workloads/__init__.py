@@ -17,7 +17,8 @@ Workload shapes follow the pages:
   scattered (troisinh.com, sections "Vấn đề" and "Tại sao nó hoạt động").
 
 Pool layout (the library's documented format, restated here so that inputs can
-be written into it):  K [NB][Hkv][D/8][B][8] and V [NB][Hkv][D][B], bf16.
+be written into it):  K [NB][Hkv][D/8][B][8] and V [NB][Hkv][B/Bt][D][Bt] with
+Bt = min(B, 16), bf16.
 Every slot that must never be read (unreferenced blocks, the unused tail of each
 sequence's last block) holds a NaN; padding entries of a block-table row point
 at a block that is entirely NaN.
@@ -56,8 +57,14 @@ def k_pool_shape(nb, hkv, d, b):
     return (nb, hkv, d // 8, b, 8)
 
 
+def v_half(b):
+    """Positions of one V run: the pool keeps each 16-position half of a block as
+    its own [D][16] run (the whole block when B <= 16)."""
+    return min(int(b), 16)
+
+
 def v_pool_shape(nb, hkv, d, b):
-    return (nb, hkv, d, b)
+    return (nb, hkv, b // v_half(b), d, v_half(b))
 
 
 def k_to_pool(k_logical: np.ndarray) -> np.ndarray:
@@ -66,7 +73,9 @@ def k_to_pool(k_logical: np.ndarray) -> np.ndarray:
 
 
 def v_to_pool(v_logical: np.ndarray) -> np.ndarray:
-    return np.ascontiguousarray(v_logical.transpose(0, 1, 3, 2))
+    nb, hkv, b, d = v_logical.shape
+    bt = v_half(b)
+    return np.ascontiguousarray(v_logical.reshape(nb, hkv, b // bt, bt, d).transpose(0, 1, 2, 4, 3))
 
 
 def k_from_pool(k_pool: np.ndarray) -> np.ndarray:
@@ -75,7 +84,17 @@ def k_from_pool(k_pool: np.ndarray) -> np.ndarray:
 
 
 def v_from_pool(v_pool: np.ndarray) -> np.ndarray:
-    return np.ascontiguousarray(v_pool.transpose(0, 1, 3, 2))
+    nb, hkv, nh, d, bt = v_pool.shape
+    return np.ascontiguousarray(v_pool.transpose(0, 1, 2, 4, 3).reshape(nb, hkv, nh * bt, d))
+
+
+def poison_v_tail(v, b, first, nan):
+    """Set V positions first.. of block b (all heads, all dims) to ``nan``."""
+    bt = v.shape[-1]
+    for h in range(v.shape[2]):
+        lo = max(first - h * bt, 0)
+        if lo < bt:
+            v[b, :, h, :, lo:] = nan
 
 
 # ---------------------------------------------------------------------------
@@ -298,9 +317,10 @@ def write_tokens(k_pool, v_pool, slots, k_rows, v_rows):
     # K [NB][Hkv][D/8][B][8]: element (b, g, o, d) at [b, g, d // 8, o, d % 8]
     k_pool[b[:, None, None], np.arange(hkv)[None, :, None], (np.arange(d) // 8)[None, None, :],
            o[:, None, None], (np.arange(d) % 8)[None, None, :]] = k_rows
-    # V [NB][Hkv][D][B]
-    v_pool[b[:, None, None], np.arange(hkv)[None, :, None], np.arange(d)[None, None, :],
-           o[:, None, None]] = v_rows
+    # V [NB][Hkv][B/Bt][D][Bt]: element (b, g, o, d) at [b, g, o // Bt, d, o % Bt]
+    bt = v_pool.shape[-1]
+    v_pool[b[:, None, None], np.arange(hkv)[None, :, None], (o // bt)[:, None, None],
+           np.arange(d)[None, None, :], (o % bt)[:, None, None]] = v_rows
 
 
 # ---------------------------------------------------------------------------
@@ -331,7 +351,7 @@ def poison_host_pools(case: Case, k: np.ndarray, v: np.ndarray) -> None:
     v[~used] = BF16_NAN
     for b, first in case.tail_slots():
         k[b, :, :, first:, :] = BF16_NAN
-        v[b, :, :, first:] = BF16_NAN
+        poison_v_tail(v, b, first, BF16_NAN)
 
 
 # ---------------------------------------------------------------------------
@@ -375,7 +395,7 @@ def fill_device_pools(case: Case, k, v, g, poison=True) -> None:
         kk, vv = k.view(torch.int16), v.view(torch.int16)
         for b, first in case.tail_slots():
             kk[b, :, :, first:, :] = -1
-            vv[b, :, :, first:] = -1
+            poison_v_tail(vv, b, first, -1)
 
 
 # ---------------------------------------------------------------------------
