@@ -55,7 +55,8 @@ extern "C" {
 #define PKV_OK 0
 #define PKV_ERR_NULL -1        /* a required pointer is NULL */
 #define PKV_ERR_SHAPE -2       /* inconsistent sizes (e.g. num_q_heads % num_kv_heads != 0) */
-#define PKV_ERR_UNSUPPORTED -3 /* head_dim, block_size or group size outside the built set */
+#define PKV_ERR_UNSUPPORTED -3 /* head_dim, block_size or group size outside the built set,
+                                  or max_blocks_per_seq*block_size above 2^26 */
 #define PKV_ERR_WORKSPACE -4   /* workspace smaller than paged_attn_decode_workspace_bytes() */
 #define PKV_ERR_ALIGNMENT -5   /* q, k_cache, v_cache, out or workspace not 16-byte aligned */
 #define PKV_ERR_DEVICE -6      /* the HIP runtime could not report the current device */
@@ -90,7 +91,8 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   q             bf16 [num_seqs][num_q_heads][head_dim]
  *   k_cache       bf16 K pool, layout above, num_blocks blocks
  *   v_cache       bf16 V pool, layout above
- *   block_tables  int32 [num_seqs][max_blocks_per_seq], row-major; only the first
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq], row-major (a row addresses at
+ *                 most 2^26 positions: max_blocks_per_seq*block_size <= 2^26); only the first
  *                 ceil(L/block_size) entries of row s are read, and each must lie
  *                 in [0, num_blocks).  Entries outside that range are clamped into
  *                 it (no memory outside the pool is read; that sequence's output

@@ -105,7 +105,22 @@ int32_t check_shapes(int32_t block_size, float scale, int32_t num_seqs, int32_t 
   if (static_cast<int64_t>(max_blocks_per_seq) * block_size > 0x7fffffffLL) return PKV_ERR_SHAPE;
   if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
   if (num_q_heads / num_kv_heads > kMaxGroup) return PKV_ERR_UNSUPPORTED;
+  // the work plan counts a row's units in 32-bit lane scans
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > kMaxRowPositions)
+    return PKV_ERR_UNSUPPORTED;
   return PKV_OK;
+}
+
+// Work units of a tile and of a pair's query and output rows (rows * head_dim * 2
+// bytes each way).  Batches of more than 64 sequences weigh pairs: a tile is 4
+// units and the rows count in quarters of a tile's K/V bytes (16 positions *
+// head_dim * 2 bytes, bf16; half that for fp8).  Smaller batches count tiles only
+// (measured: the weighting moves nothing there and the lighter plan starts the
+// first loads sooner).
+void set_units(DecodeDims& d, int32_t rows, bool fp8) {
+  const bool weigh = d.S > kWave;
+  d.unit = weigh ? 4 : 1;
+  d.hdr = weigh ? (fp8 ? (rows + 1) / 2 : (rows + 2) / 4) : 0;
 }
 
 // fp8: the pools hold E4M3FN codes; keys are code * k_scale, values code * v_scale.
@@ -157,6 +172,7 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
   d.Qc = 1;
   d.q_off = 0;
   d.R = group;
+  set_units(d, group, fp8);
   d.v_scale = v_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int mg = merge_groups_for(workers, cu);
@@ -227,6 +243,7 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
     d.q_off = off;
     d.Qc = per < max_query_len - off ? per : max_query_len - off;
     d.R = group * d.Qc;
+    set_units(d, d.R, fp8);
     DecodeBuffers b;
     b.q = static_cast<const uint16_t*>(q) + off * token_elems;
     b.k = k_cache;

@@ -89,18 +89,18 @@ __device__ __forceinline__ int32_t clamp_block(int32_t b, int64_t nb) {
   return b < 0 ? 0 : (b >= nb ? static_cast<int32_t>(nb - 1) : b);
 }
 
-__device__ __forceinline__ int32_t wave_sum(int32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+// Inclusive prefix sum over the wave's 64 lanes with DPP moves (no LDS traffic):
+// doubling shifts within each row of 16 lanes, then each row's running total
+// broadcast into the rows after it (lane 15 into rows 1 and 3, lane 31 into rows
+// 2 and 3).  Out-of-row sources of the shifts read 0.
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 1, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 2, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 4, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 8, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowBcast15, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowBcast31, 0xC, 0xF, false);
   return x;
 }
 
@@ -134,86 +134,220 @@ __device__ __forceinline__ int32_t seq_tiles(const int32_t* __restrict__ lens,
   return s < d.S ? tiles_of(seq_len<kCausal>(lens, qlens, d, cap, s).L) : 0;
 }
 
-// Work units (tiles) of sequences [0, s_end): Hkv * sum ceil(L_s / 16).
-template <bool kCausal>
-__device__ int64_t units_before(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
-                                const DecodeDims& d, int32_t cap, int32_t s_end, int lane) {
-  int64_t tot = 0;
-  for (int32_t base = 0; base < s_end; base += kWave) {
-    const int32_t s = base + lane;
-    const int32_t T = s < s_end ? seq_tiles<kCausal>(lens, qlens, d, cap, s) : 0;
-    tot += uniform(wave_sum(T));
-  }
-  return tot * d.Hkv;
+// Work units.  A tile of a (sequence, KV head) pair counts d.unit units and each
+// pair d.hdr more (its query and output rows; with d.unit = 4, in quarters of a
+// tile's K/V bytes), so ranges of equal units carry about equal bytes however
+// many pairs they hold.  The pairs of sequence s follow each other in head order:
+// pair (s, g) spans units [start_s + g*P_s, start_s + (g+1)*P_s), P_s =
+// unit*T_s + hdr, and its tile t sits at unit start_s + g*P_s + hdr + unit*t.
+// Empty sequences hold no units.  A worker owns the tiles whose unit lies in its
+// range.  Launches over at most 64 sequences use unit 1 and hdr 0 (units are
+// tiles), which keeps the plan to one scan and one lookup.
+__device__ __forceinline__ int32_t pair_units(int32_t T, const DecodeDims& d) {
+  return T > 0 ? d.unit * T + d.hdr : 0;
 }
 
-// The sequence whose unit range contains unit u, and the first unit of that range.
-template <bool kCausal>
-__device__ void locate(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
-                       const DecodeDims& d, int32_t cap, int64_t u, int lane, int32_t& s_out,
-                       int64_t& start_out) {
-  int64_t acc = 0;
-  for (int32_t base = 0; base < d.S; base += kWave) {
-    const int32_t s = base + lane;
-    const int32_t T = seq_tiles<kCausal>(lens, qlens, d, cap, s);
-    const int32_t incl = wave_inclusive_scan(T, lane);
-    const int64_t chunk_units =
-        static_cast<int64_t>(__builtin_amdgcn_readlane(incl, kWave - 1)) * d.Hkv;
-    if (u < acc + chunk_units) {
-      const uint64_t hit = __ballot(acc + static_cast<int64_t>(incl) * d.Hkv > u);
-      const int32_t first = uniform(__builtin_ctzll(hit));
-      s_out = base + first;
-      start_out = acc + static_cast<int64_t>(__builtin_amdgcn_readlane(incl - T, first)) * d.Hkv;
-      return;
-    }
-    acc += chunk_units;
-  }
-  s_out = d.S;
-  start_out = acc;
-}
-
-// Range of worker w: units [w*U/N, (w+1)*U/N).  worker_of(u) is the largest w
-// whose range starts at or before u.
-__device__ __forceinline__ int64_t range_begin(int64_t w, int64_t U, int64_t N) {
-  return w * U / N;
-}
-
+// Range of worker w: units [w*U/N, (w+1)*U/N) (range_of below).  worker_of(u) is
+// the largest w whose range starts at or before u.
 __device__ __forceinline__ int64_t worker_of(int64_t u, int64_t U, int64_t N) {
   return ((u + 1) * N - 1) / U;
 }
 
-// A worker's share of the batch: total units U, active workers N, its range
-// [u, u_end), the sequence s holding unit u and the first unit `start` of s.
-struct WorkerPlan {
-  int64_t U, N, u, u_end, start;
-  int32_t s;
+// Per-lane view of 64 consecutive sequences base + lane: their SeqLen (L, Tq),
+// tiles T, pair units P, and inclusive scans of T and P (zeros past the batch).
+struct Chunk {
+  int32_t base, L, Tq, T, P, incT, incP;
 };
 
-// Returns false when worker w has no range.  With at most kWave sequences the
-// lengths are read once and scanned in registers; otherwise in two passes.
+template <bool kCausal>
+__device__ __forceinline__ SeqLen lane_len(const int32_t* __restrict__ lens,
+                                           const int32_t* __restrict__ qlens, const DecodeDims& d,
+                                           int32_t cap, int32_t base, int lane) {
+  return base + lane < d.S ? seq_len<kCausal>(lens, qlens, d, cap, base + lane) : SeqLen{0, 0};
+}
+
+// One shuffle scan: the unit scan follows from the tile scan and the count of
+// non-empty sequences up to this lane.
+__device__ __forceinline__ Chunk make_chunk(int32_t base, SeqLen sl, const DecodeDims& d,
+                                            int lane) {
+  Chunk c;
+  c.base = base;
+  c.L = sl.L;
+  c.Tq = sl.T;
+  const int32_t T = tiles_of(sl.L);
+  c.T = T;
+  c.P = pair_units(T, d);
+  c.incT = wave_inclusive_scan(c.T);
+  const uint64_t upto = lane == kWave - 1 ? ~0ull : ((1ull << (lane + 1)) - 1);
+  c.incP = d.unit * c.incT + d.hdr * __builtin_popcountll(__ballot(T > 0) & upto);
+  return c;
+}
+
+// Where unit x falls (x at or past the chunk's first unit acc_u): false when x
+// lies past the chunk.  Otherwise the sequence s holding x, the first unit and
+// the first tile (index over the whole batch) of s, the tiles of s, and the first
+// tile of s at or after x as (g, t), g = Hkv when x lies past the last tile of s.
+struct UnitLoc {
+  int32_t s, g, t, T, P, L, Tq;
+  int64_t start, tstart;
+};
+
+__device__ __forceinline__ bool locate_in(const Chunk& c, const DecodeDims& d, int64_t acc_u,
+                                          int64_t acc_t, int64_t x, UnitLoc& r) {
+  const int64_t chunk_u = static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, kWave - 1)) * d.Hkv;
+  if (x >= acc_u + chunk_u) return false;
+  const uint64_t hit = __ballot(acc_u + static_cast<int64_t>(c.incP) * d.Hkv > x);
+  const int32_t i = uniform(__builtin_ctzll(hit));
+  r.s = c.base + i;
+  r.L = __builtin_amdgcn_readlane(c.L, i);
+  r.Tq = __builtin_amdgcn_readlane(c.Tq, i);
+  r.T = __builtin_amdgcn_readlane(c.T, i);
+  r.P = __builtin_amdgcn_readlane(c.P, i);
+  r.start = acc_u + static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, i) - r.P) * d.Hkv;
+  r.tstart = acc_t + static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, i) - r.T) * d.Hkv;
+  const int64_t rel = x - r.start;
+  r.g = rel < (int64_t(1) << 31) ? static_cast<int32_t>(rel) / r.P : static_cast<int32_t>(rel / r.P);
+  const int32_t off = static_cast<int32_t>(rel - static_cast<int64_t>(r.g) * r.P);
+  r.t = off <= d.hdr ? 0 : (off - d.hdr + d.unit - 1) / d.unit;
+  if (r.t >= r.T) {
+    ++r.g;
+    r.t = 0;
+  }
+  return true;
+}
+
+// Index over the whole batch of the first tile at or after the located unit.
+__device__ __forceinline__ int64_t first_tile(const UnitLoc& r) {
+  return r.tstart + static_cast<int64_t>(r.g) * r.T + r.t;
+}
+
+// A worker's share of the batch: total units U, active workers N, the first tile
+// (s, g, t) of its range, the first unit `start` and the SeqLen (L, Tq) of s, and
+// its tile count n.
+struct WorkerPlan {
+  int64_t U, N, start;
+  int32_t s, g, t, n, L, Tq;
+};
+
+// Chunks of the batch's sequences held in registers (the rest are read again on
+// every pass): one read of the lengths and one scan serve every pass up to 256
+// sequences.
+constexpr int kPlanChunks = 4;
+
+// Passes over the chunks in order: f(chunk, acc_u, acc_t) returns true to stop.
+template <bool kCausal, typename F>
+__device__ __forceinline__ void for_chunks(const int32_t* __restrict__ lens,
+                                           const int32_t* __restrict__ qlens,
+                                           const DecodeDims& d, int32_t cap,
+                                           const Chunk (&ch)[kPlanChunks], int lane, F&& f) {
+  int64_t acc_u = 0, acc_t = 0;
+#pragma unroll
+  for (int k = 0; k < kPlanChunks; ++k) {
+    if (k * kWave >= d.S) return;
+    const Chunk& c = ch[k];
+    if (f(c, acc_u, acc_t)) return;
+    acc_u += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, kWave - 1)) * d.Hkv;
+    acc_t += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, kWave - 1)) * d.Hkv;
+  }
+  for (int32_t base = kPlanChunks * kWave; base < d.S; base += kWave) {
+    const Chunk c = make_chunk(base, lane_len<kCausal>(lens, qlens, d, cap, base, lane), d, lane);
+    if (f(c, acc_u, acc_t)) return;
+    acc_u += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, kWave - 1)) * d.Hkv;
+    acc_t += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, kWave - 1)) * d.Hkv;
+  }
+}
+
+// Ends of worker w's range, [w*U/N, (w+1)*U/N), with 32-bit divisions whenever
+// the operands fit (U = q*N + r, so w*U/N = w*q + r*w/N).
+__device__ __forceinline__ void range_of(int64_t w, int64_t U, int64_t N, int64_t& u, int64_t& ue) {
+  const bool small = U < (int64_t(1) << 32) && N < (int64_t(1) << 16);
+  const int64_t q = small ? static_cast<uint32_t>(U) / static_cast<uint32_t>(N) : U / N;
+  const int64_t r = U - q * N;  // < N
+  if (small) {
+    u = w * q + static_cast<uint32_t>(r * w) / static_cast<uint32_t>(N);
+    ue = (w + 1) * q + static_cast<uint32_t>(r * (w + 1)) / static_cast<uint32_t>(N);
+  } else {
+    u = w * q + r * w / N;
+    ue = (w + 1) * q + r * (w + 1) / N;
+  }
+}
+
+// Returns false when worker w has no tile.
 template <bool kCausal>
 __device__ bool plan_worker(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
                             const DecodeDims& d, int32_t cap, int64_t w, int lane, WorkerPlan& p) {
-  if (d.S <= kWave) {
-    const int32_t T = seq_tiles<kCausal>(lens, qlens, d, cap, lane);
-    const int32_t incl = wave_inclusive_scan(T, lane);
+  if (d.S <= kWave) {  // units are tiles: one scan, one lookup
+    const SeqLen sl = lane_len<kCausal>(lens, qlens, d, cap, 0, lane);
+    const int32_t T = tiles_of(sl.L);
+    const int32_t incl = wave_inclusive_scan(T);
     p.U = static_cast<int64_t>(__builtin_amdgcn_readlane(incl, kWave - 1)) * d.Hkv;
     p.N = min(static_cast<int64_t>(d.n_workers), p.U);
     if (w >= p.N) return false;
-    p.u = range_begin(w, p.U, p.N);
-    p.u_end = range_begin(w + 1, p.U, p.N);
-    const uint64_t hit = __ballot(static_cast<int64_t>(incl) * d.Hkv > p.u);
-    const int32_t first = uniform(__builtin_ctzll(hit));
-    p.s = first;
-    p.start = static_cast<int64_t>(__builtin_amdgcn_readlane(incl - T, first)) * d.Hkv;
+    int64_t u, ue;
+    range_of(w, p.U, p.N, u, ue);
+    const uint64_t hit = __ballot(static_cast<int64_t>(incl) * d.Hkv > u);
+    const int32_t i = uniform(__builtin_ctzll(hit));
+    p.s = i;
+    p.L = __builtin_amdgcn_readlane(sl.L, i);
+    p.Tq = __builtin_amdgcn_readlane(sl.T, i);
+    const int32_t Ts = __builtin_amdgcn_readlane(T, i);
+    p.start = static_cast<int64_t>(__builtin_amdgcn_readlane(incl, i) - Ts) * d.Hkv;
+    const int64_t rel = u - p.start;
+    p.g = rel < (int64_t(1) << 31) ? static_cast<int32_t>(rel) / Ts : static_cast<int32_t>(rel / Ts);
+    p.t = static_cast<int32_t>(rel - static_cast<int64_t>(p.g) * Ts);
+    p.n = static_cast<int32_t>(ue - u);
     return true;
   }
-  p.U = units_before<kCausal>(lens, qlens, d, cap, d.S, lane);
-  p.N = min(static_cast<int64_t>(d.n_workers), p.U);
+  SeqLen T0[kPlanChunks];  // all lengths read first: one round trip
+#pragma unroll
+  for (int k = 0; k < kPlanChunks; ++k) T0[k] = lane_len<kCausal>(lens, qlens, d, cap, k * kWave, lane);
+  Chunk Tc[kPlanChunks];
+#pragma unroll
+  for (int k = 0; k < kPlanChunks; ++k)
+    if (k * kWave < d.S) Tc[k] = make_chunk(k * kWave, T0[k], d, lane);
+  // pass 1: total units and tiles
+  int64_t U = 0, tiles = 0;
+  for_chunks<kCausal>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t, int64_t) {
+    U += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, kWave - 1)) * d.Hkv;
+    tiles += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, kWave - 1)) * d.Hkv;
+    return false;
+  });
+  p.U = U;
+  p.N = min(static_cast<int64_t>(d.n_workers), tiles);  // every range >= d.unit units
   if (w >= p.N) return false;
-  p.u = range_begin(w, p.U, p.N);
-  p.u_end = range_begin(w + 1, p.U, p.N);
-  locate<kCausal>(lens, qlens, d, cap, p.u, lane, p.s, p.start);
+  int64_t u, ue;
+  range_of(w, p.U, p.N, u, ue);
+  // pass 2: where the range starts and ends
+  UnitLoc lu, le;
+  bool found_u = false, found_e = ue >= U;
+  int64_t first = 0, last = tiles;
+  for_chunks<kCausal>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t au, int64_t at) {
+    if (!found_u && locate_in(c, d, au, at, u, lu)) {
+      found_u = true;
+      first = first_tile(lu);
+    }
+    if (!found_e && locate_in(c, d, au, at, ue, le)) {
+      found_e = true;
+      last = first_tile(le);
+    }
+    return found_u && found_e;
+  });
+  if (!found_u || last <= first) return false;
+  p.n = static_cast<int32_t>(last - first);
+  if (lu.g >= d.Hkv) {
+    // u lies past the last tile of its sequence: the range starts at the next
+    // sequence that holds units
+    const int64_t next = lu.start + static_cast<int64_t>(lu.P) * d.Hkv;
+    for_chunks<kCausal>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t au, int64_t at) {
+      return locate_in(c, d, au, at, next, lu);
+    });
+  }
+  p.s = lu.s;
+  p.g = lu.g;
+  p.t = lu.t;
+  p.L = lu.L;
+  p.Tq = lu.Tq;
+  p.start = lu.start;
   return true;
 }
 
@@ -229,7 +363,6 @@ struct PairCursor {
   int32_t nblk;             // ceil(L / B)
 };
 
-// A tile of bf16 K/V in registers: every lane's MFMA operands, as loaded.
 // Pair mode: worker w takes (sequence w / Hkv, KV head w % Hkv) whole.  Returns
 // false for workers past the pairs and for empty sequences.
 template <bool kCausal>
@@ -238,17 +371,22 @@ __device__ bool plan_pair(const int32_t* __restrict__ lens, const int32_t* __res
   if (w >= static_cast<int64_t>(d.S) * d.Hkv) return false;
   const int32_t s = static_cast<int32_t>(w / d.Hkv);
   const int32_t g = static_cast<int32_t>(w - static_cast<int64_t>(s) * d.Hkv);
-  const int32_t T = tiles_of(seq_len<kCausal>(lens, qlens, d, cap, s).L);
+  const SeqLen sl = seq_len<kCausal>(lens, qlens, d, cap, s);
+  const int32_t T = tiles_of(sl.L);
   if (T == 0) return false;
+  p.L = sl.L;
+  p.Tq = sl.T;
   p.U = 1;  // only used to find the workers of split pairs, and none is split
   p.N = 1;
-  p.s = s;
   p.start = 0;
-  p.u = static_cast<int64_t>(g) * T;
-  p.u_end = p.u + T;
+  p.s = s;
+  p.g = g;
+  p.t = 0;
+  p.n = T;
   return true;
 }
 
+// A tile of bf16 K/V in registers: every lane's MFMA operands, as loaded.
 template <int D, int B>
 struct Bf16Tile {
   using Elem = uint16_t;
@@ -521,7 +659,7 @@ __device__ __forceinline__ void advance(Cursor& c, const Cx& cx, const DecodeDim
   c.t = 0;
   if (++c.g < d.Hkv) return;
   c.g = 0;
-  c.start += static_cast<int64_t>(d.Hkv) * c.T;
+  c.start += static_cast<int64_t>(d.Hkv) * pair_units(c.T, d);
   do {
     ++c.s;
     if (c.s < d.S) {
@@ -637,7 +775,7 @@ __device__ void finish_segment(const Cx& cx, const DecodeDims& d, const SegState
   }
 }
 
-// One worker: the tiles of units [u, u_end) in order, with loads running kPipe-1
+// One worker: the n tiles of its range in order, with loads running kPipe-1
 // tiles ahead of the arithmetic across (sequence, head) boundaries; the query of a
 // pair is fetched with the pair's first tile.  Returns the descriptor of the split
 // pair this worker opens (s = -1 if none).
@@ -645,19 +783,16 @@ template <int D, int B, int NC, bool kCausal, bool kFp8, typename Cx>
 __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& pl, int64_t w,
                            int lane) {
   const int32_t cap = d.M * B;
-  const int32_t n = static_cast<int32_t>(pl.u_end - pl.u);
+  const int32_t n = pl.n;
   const Cols<NC> cl = make_cols<NC, kCausal>(d, lane);
   Cursor lc;
   lc.start = pl.start;
   lc.s = pl.s;
-  {
-    const SeqLen sl = seq_len<kCausal>(cx.lens, cx.qlens, d, cap, pl.s);
-    lc.L = sl.L;
-    lc.Tq = sl.T;
-  }
+  lc.L = pl.L;
+  lc.Tq = pl.Tq;
   lc.T = tiles_of(lc.L);
-  lc.g = static_cast<int32_t>((pl.u - pl.start) / lc.T);
-  lc.t = static_cast<int32_t>((pl.u - pl.start) - static_cast<int64_t>(lc.g) * lc.T);
+  lc.g = pl.g;
+  lc.t = pl.t;
   Cursor cc = lc;
 
   constexpr int kPipe = pipe_depth<D, NC, kFp8>();
@@ -705,11 +840,13 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
       const bool whole = seg_t0 == 0 && cc.t == cc.T - 1;
       finish_segment<D, NC, kCausal>(cx, d, st, cc, cl, whole, rec, lane);
       if (!whole && seg_t0 == 0) {
-        // this worker holds the first share of a pair that later workers continue
-        const int64_t u0 = cc.start + static_cast<int64_t>(cc.g) * cc.T;
+        // this worker holds the first share of a pair that later workers continue;
+        // the worker holding the pair's last tile closes it (worked out here, mid-
+        // stream, rather than after the last tile where it would lengthen the tail)
+        const int64_t last_unit = cc.start + static_cast<int64_t>(cc.g) * pair_units(cc.T, d) +
+                                  d.hdr + static_cast<int64_t>(d.unit) * (cc.T - 1);
         const int32_t slot_tq = static_cast<int32_t>(rec - 2 * w) | (kCausal ? cc.Tq << 1 : 0);
-        opened = int4{cc.s, cc.g, static_cast<int32_t>(worker_of(u0 + cc.T - 1, pl.U, pl.N)),
-                      slot_tq};
+        opened = int4{cc.s, cc.g, static_cast<int32_t>(worker_of(last_unit, pl.U, pl.N)), slot_tq};
       }
       rec = 2 * w + 1;
     }

@@ -12,6 +12,9 @@ constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 4;
 constexpr int kMaxGroup = 16;   // query heads per KV head served by one MFMA column tile
 constexpr int kMaxLayers = 128; // copy_blocks pool pointers travel as kernel arguments
+// Positions one block-table row may address (max_blocks_per_seq * block_size): the
+// work plan sums a row's work units in 32-bit lane scans.
+constexpr int64_t kMaxRowPositions = int64_t(1) << 26;
 
 // Buffers of one decode call.  The kernels take them as separate __restrict__
 // parameters so that reads of the block table and lengths become scalar loads.
@@ -42,6 +45,8 @@ struct DecodeDims {
   float v_scale;            // multiplies the outputs (fp8 V pools; 1 for bf16)
   int32_t pair_mode;        // 1: worker w takes (sequence, KV head) pair w whole (no split,
                             // no records, no merge); n_workers = S * Hkv
+  int32_t unit;             // work units of one tile (1, or 4 when pairs are weighted)
+  int32_t hdr;              // work units of a pair's query and output rows
 };
 
 // Floats in one partial record: O[R][D], then m[R], then l[R], padded to a

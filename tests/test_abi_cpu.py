@@ -76,6 +76,7 @@ def _decode_call(lib, **over):
     (dict(D=96), -3),                   # head_dim not built
     (dict(block_size=12, max_ctx=48), -3),
     (dict(Hq=34, Hkv=1), -3),           # group of 34 query heads per KV head
+    (dict(M=(1 << 22) + 1), -3),        # a table row addressing more than 2^26 positions
     (dict(q=None), -1),
     (dict(ws=None), -1),
     (dict(tables=None), -1),
