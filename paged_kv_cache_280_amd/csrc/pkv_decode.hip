@@ -127,13 +127,6 @@ __device__ __forceinline__ SeqLen seq_len(const int32_t* __restrict__ lens,
   }
 }
 
-template <bool kCausal>
-__device__ __forceinline__ int32_t seq_tiles(const int32_t* __restrict__ lens,
-                                             const int32_t* __restrict__ qlens, const DecodeDims& d,
-                                             int32_t cap, int32_t s) {
-  return s < d.S ? tiles_of(seq_len<kCausal>(lens, qlens, d, cap, s).L) : 0;
-}
-
 // Work units.  A tile of a (sequence, KV head) pair counts d.unit units and each
 // pair d.hdr more (its query and output rows; with d.unit = 4, in quarters of a
 // tile's K/V bytes), so ranges of equal units carry about equal bytes however
