@@ -51,8 +51,11 @@ def parse():
     ap.add_argument("--workload", default="long",
                     choices=["long", "chat", "mix", "prefix", "tiny", "append"])
     ap.add_argument("--with-append", action="store_true",
-                    help="each layer call first appends the new token's K/V (kv_append), "
-                         "then decodes: the full per-layer decode step")
+                    help="each layer call also appends the new token's K/V: the full "
+                         "per-layer decode step")
+    ap.add_argument("--append-mode", default="fused", choices=["fused", "separate"],
+                    help="with --with-append: one paged_attn_decode_append call (fused), or "
+                         "kv_append then the decode (separate; always so for --query-tokens > 1)")
     ap.add_argument("--block-size", type=int, default=16)
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="fp8: K/V pools of E4M3FN codes with a scale of 1/16 each")
@@ -438,9 +441,22 @@ def main():
         tok_pos = (lens.repeat_interleave(T) - T +
                    torch.arange(T, device=dev, dtype=torch.int32).repeat(S)).to(torch.int32)
 
+    fused_append = args.with_append and args.append_mode == "fused" and not multi
+
     def step(timed_events=None):
         for layer in range(layers):
             q, k, v = pools[layer]
+            if fused_append:
+                e = timed_events[layer] if timed_events is not None else None
+                if e is not None:
+                    e[0].record(stream)
+                sc = dict(k_scale=FP8_SCALE, v_scale=FP8_SCALE) if fp8 else {}
+                pkv.paged_attn_decode_append(q, new_k[layer], new_v[layer], k, v, tabs, lens, B,
+                                             case.scale, outs[layer], workspace=ws,
+                                             max_context_len=max_ctx, **sc)
+                if e is not None:
+                    e[1].record(stream)
+                continue
             if args.with_append and fp8:
                 pkv.kv_append_fp8(new_k[layer], new_v[layer], k, v, tabs, tok_seq, tok_pos, B,
                                   FP8_SCALE, FP8_SCALE)
@@ -530,7 +546,7 @@ def main():
                    "layers": layers, "block_size": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D, "query_tokens": T},
         "graph": graph is not None,
-        "with_append": bool(args.with_append),
+        "with_append": ("fused" if fused_append else "separate") if args.with_append else False,
         "kv_gbs": round(kv_gbs, 1),
         "hbm_frac": round(kv_gbs / HBM_PEAK_GBS, 4),
         "us_per_call": {"mean": round(kern_avg_s * 1e6, 2), "p10": round(p10, 2),

@@ -155,6 +155,51 @@ int32_t paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_
                               size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step with its KV append in one call: for every sequence s with
+ * L = context_lens[s] >= 1 positions (the newest included), the newest position's
+ * rows k_new[s] / v_new[s] are written into its slot (block_tables[s][(L-1)/B],
+ * offset (L-1) % B) -- "PagedAttention (vLLM)" (troisinh.com), section "Cơ chế
+ * Block Table": a position lives in logical block p / B at offset p % B -- and
+ * attention runs over all L positions.  The pools end up as kv_append of those
+ * rows leaves them, and the outputs equal paged_attn_decode's after it up to
+ * rounding: when there are no more (sequence, KV head) pairs than decode workers,
+ * the worker holding a pair's last tile folds the newest position in itself (its
+ * weight formed on the vector units, scores summed in another order); with more
+ * pairs the call enqueues the append and then the decode, and the outputs are
+ * bit-identical to the two calls.  L = 0 writes nothing and gives zero rows.
+ *
+ *   k_new, v_new  bf16 [num_seqs][num_kv_heads][head_dim], 16-byte aligned
+ *   k_cache, v_cache  written: only the newest position's slot of each sequence.
+ *                 The caller's block manager has made those blocks private
+ *                 (copy-on-write resolved) before the call.
+ * All other arguments, checks and guarantees are paged_attn_decode's; the workspace
+ * is sized by paged_attn_decode_workspace_bytes.
+ */
+int32_t paged_attn_decode_append(const void* q, const void* k_new, const void* v_new,
+                                 void* k_cache, void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, int32_t block_size, float scale,
+                                 void* out, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 int32_t max_context_len, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_decode_append over fp8 pools: the newest rows are stored as
+ * kv_append_fp8 stores them (code = E4M3(x / scale), nearest even, saturating,
+ * NaN -> 0x7F) and attended to as those codes, as paged_attn_decode_fp8 does.
+ * k_scale and v_scale must be finite and non-zero (else PKV_ERR_SHAPE).
+ */
+int32_t paged_attn_decode_append_fp8(const void* q, const void* k_new, const void* v_new,
+                                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t block_size, float scale,
+                                     float k_scale, float v_scale, void* out, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t max_blocks_per_seq, int64_t num_blocks,
+                                     int32_t max_context_len, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device scratch paged_attn_multi and paged_attn_multi_fp8 need for these
  * sizes on the current device (the same role as paged_attn_decode_workspace_bytes).  Returns 0 for
  * sizes paged_attn_multi would reject.

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     new_multi_workspace,
     new_workspace,
     paged_attn_decode,
+    paged_attn_decode_append,
     paged_attn_decode_fp8,
     paged_attn_decode_workspace_bytes,
     paged_attn_multi,

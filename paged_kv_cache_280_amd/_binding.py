@@ -24,7 +24,8 @@ STATUS_NAMES = {
 EXPORTS = ("pkv_abi_version", "pkv_status_string", "paged_attn_decode_workspace_bytes",
            "paged_attn_decode", "paged_attn_decode_fp8", "paged_attn_multi_workspace_bytes",
            "paged_attn_multi", "paged_attn_multi_fp8",
-           "kv_append", "kv_append_fp8", "copy_blocks", "pkv_check_batch")
+           "kv_append", "kv_append_fp8", "copy_blocks", "pkv_check_batch",
+           "paged_attn_decode_append", "paged_attn_decode_append_fp8")
 
 
 class PkvError(RuntimeError):
@@ -77,6 +78,12 @@ def load_library(path: str = LIB_PATH):
     lib.copy_blocks.restype = i32
     lib.pkv_check_batch.argtypes = [p, p, p, i32, i32, i64, i32, i32, p, p]
     lib.pkv_check_batch.restype = i32
+    lib.paged_attn_decode_append.argtypes = [p, p, p, p, p, p, p, i32, f32, p, i32, i32, i32, i32,
+                                             i32, i64, i32, p, sz, p]
+    lib.paged_attn_decode_append.restype = i32
+    lib.paged_attn_decode_append_fp8.argtypes = [p, p, p, p, p, p, p, i32, f32, f32, f32, p, i32,
+                                                 i32, i32, i32, i32, i64, i32, p, sz, p]
+    lib.paged_attn_decode_append_fp8.restype = i32
     _lib = lib
     return lib
 
@@ -238,6 +245,70 @@ def paged_attn_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, block
                                        _stream_handle(q, stream))
     if rc != 0:
         raise PkvError(rc, "paged_attn_decode_fp8")
+    return out
+
+
+def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                             block_size, scale, out=None, *, max_context_len=None, workspace=None,
+                             k_scale=None, v_scale=None, stream=None):
+    """One decode step with its KV append (see ``include/pkv.h``): the rows
+    k_new / v_new (bf16 [num_seqs][Hkv][D]) of each sequence's newest position
+    (context_lens[s] - 1) go into their slots, and attention runs over all
+    context_lens[s] positions.  With ``k_scale`` / ``v_scale`` the pools are fp8
+    (layouts as in paged_attn_decode_fp8).  Returns ``out``."""
+    import torch
+
+    lib = load_library()
+    fp8 = k_scale is not None or v_scale is not None
+    _check(q.dim() == 3, "q must be [num_seqs][num_q_heads][head_dim]")
+    S, Hq, D = q.shape
+    B = int(block_size)
+    if fp8:
+        _check(k_scale is not None and v_scale is not None, "fp8 pools need k_scale and v_scale")
+        _check(k_cache.dim() == 5 and k_cache.shape[2] * 16 == D and k_cache.shape[3] == B
+               and k_cache.shape[4] == 16, "k_cache must be [num_blocks][Hkv][D/16][block_size][16]")
+        NB, Hkv = int(k_cache.shape[0]), int(k_cache.shape[1])
+        _check(tuple(v_cache.shape) == (NB, Hkv, 16, B // 4, D // 16, 4),
+               "v_cache must be [num_blocks][Hkv][16][block_size/4][D/16][4]")
+        for t in (k_cache, v_cache):
+            _check(t.dtype == torch.uint8 and t.is_contiguous(), "fp8 pools: contiguous uint8 codes")
+        _check(q.dtype == torch.bfloat16 and q.is_contiguous(), "q: contiguous bf16")
+        _check(block_tables.dim() == 2 and block_tables.shape[0] == S
+               and context_lens.dim() == 1 and context_lens.shape[0] == S,
+               "block_tables [num_seqs][max_blocks_per_seq], context_lens [num_seqs]")
+        for t in (block_tables, context_lens):
+            _check(t.dtype == torch.int32 and t.is_contiguous(), "tables/lengths: contiguous int32")
+        M = int(block_tables.shape[1])
+    else:
+        S, Hq, Hkv, D, NB, M = decode_shapes(q, k_cache, v_cache, block_tables, context_lens, B)
+    for t in (k_new, v_new):
+        _check(tuple(t.shape) == (S, Hkv, D) and t.dtype == torch.bfloat16 and t.is_contiguous(),
+               "k_new/v_new must be contiguous bf16 [num_seqs][Hkv][D]")
+    devs = {t.device for t in (q, k_new, v_new, k_cache, v_cache, block_tables, context_lens)}
+    _check(len(devs) == 1 and q.is_cuda, "all tensors must be on one GPU")
+    if max_context_len is None:
+        max_context_len = M * B
+    with torch.cuda.device(q.device):
+        if out is None:
+            out = torch.empty_like(q)
+        _check(out.shape == q.shape and out.dtype == torch.bfloat16 and out.is_contiguous()
+               and out.device == q.device, "out must match q")
+        if workspace is None:
+            workspace = new_workspace(S, Hq, Hkv, D, B, max_context_len, q.device)
+        _check(workspace.is_cuda and workspace.device == q.device and workspace.is_contiguous(),
+               "workspace must be a contiguous tensor on q's device")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        head = (q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B,
+                float(scale))
+        tail = (out.data_ptr(), S, Hq, Hkv, D, M, NB, int(max_context_len), workspace.data_ptr(),
+                ws_bytes, _stream_handle(q, stream))
+        if fp8:
+            rc = lib.paged_attn_decode_append_fp8(*head, float(k_scale), float(v_scale), *tail)
+        else:
+            rc = lib.paged_attn_decode_append(*head, *tail)
+    if rc != 0:
+        raise PkvError(rc, "paged_attn_decode_append_fp8" if fp8 else "paged_attn_decode_append")
     return out
 
 

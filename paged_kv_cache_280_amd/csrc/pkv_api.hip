@@ -130,7 +130,8 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
                     int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
                     int64_t num_blocks, int32_t max_context_len, void* workspace,
                     size_t workspace_bytes, void* stream, bool fp8, float k_scale,
-                    float v_scale) {
+                    float v_scale, const void* k_new = nullptr, const void* v_new = nullptr) {
+  const bool append = k_new != nullptr || v_new != nullptr;
   const int32_t st = check_shapes(block_size, scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                   max_blocks_per_seq, num_blocks, max_context_len);
   if (st != PKV_OK) return st;
@@ -138,16 +139,18 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !workspace)
     return PKV_ERR_NULL;
+  if (append && (!k_new || !v_new)) return PKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       !aligned16(workspace))
     return PKV_ERR_ALIGNMENT;
+  if (append && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGNMENT;
   const int cu = current_cu_count();
   if (cu <= 0) return PKV_ERR_DEVICE;
   const int32_t group = num_q_heads / num_kv_heads;
   const int64_t workers = worker_count(cu, num_seqs, num_kv_heads, max_context_len, fp8);
   if (workspace_bytes < workspace_for(workers, group, head_dim)) return PKV_ERR_WORKSPACE;
 
-  DecodeBuffers b;
+  DecodeBuffers b{};
   b.q = static_cast<const uint16_t*>(q);
   b.k = k_cache;
   b.v = v_cache;
@@ -156,7 +159,13 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
   b.qlens = nullptr;
   b.out = static_cast<uint16_t*>(out);
   b.ws = static_cast<float*>(workspace);
-  DecodeDims d;
+  if (append) {
+    b.k_new = static_cast<const uint16_t*>(k_new);
+    b.v_new = static_cast<const uint16_t*>(v_new);
+    b.kw = const_cast<void*>(k_cache);
+    b.vw = const_cast<void*>(v_cache);
+  }
+  DecodeDims d{};
   d.S = num_seqs;
   d.Hq = num_q_heads;
   d.Hkv = num_kv_heads;
@@ -174,10 +183,42 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
   d.R = group;
   set_units(d, group, fp8);
   d.v_scale = v_scale;
+  d.k_scale = k_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // Decode with append folds each pair's newest position into the worker holding
+  // its last tile, which reads the new rows once per pair it closes.  When workers
+  // hold several pairs each that costs more than one more launch: then the rows are
+  // written by the append kernel first and a plain decode follows (same results up
+  // to rounding, same pools).
+  const bool fused = append && (d.pair_mode ||
+                                static_cast<int64_t>(num_seqs) * num_kv_heads <= d.n_workers);
+  if (append && !fused) {
+    AppendBuffers ab{};
+    ab.k_new = static_cast<const uint16_t*>(k_new);
+    ab.v_new = static_cast<const uint16_t*>(v_new);
+    ab.k_cache = const_cast<void*>(k_cache);
+    ab.v_cache = const_cast<void*>(v_cache);
+    ab.tables = block_tables;
+    ab.token_pos = context_lens;
+    AppendDims ad{};
+    ad.T = num_seqs;
+    ad.S = num_seqs;
+    ad.Hkv = num_kv_heads;
+    ad.B = block_size;
+    ad.M = max_blocks_per_seq;
+    ad.NB = num_blocks;
+    ad.k_scale = k_scale;
+    ad.v_scale = v_scale;
+    ad.newest = 1;
+    if ((fp8 ? launch_append_fp8(ab, ad, head_dim, s) : launch_append(ab, ad, head_dim, s)) !=
+        hipSuccess)
+      return PKV_ERR_LAUNCH;
+  }
+  d.len_off = fused ? 1 : 0;
   const int mg = merge_groups_for(workers, cu);
-  const hipError_t e = fp8 ? launch_decode_fp8(b, d, head_dim, block_size, mg, s)
-                           : launch_decode(b, d, head_dim, block_size, mg, s);
+  const hipError_t e = fused ? launch_decode_append(b, d, head_dim, block_size, mg, s, fp8)
+                       : fp8 ? launch_decode_fp8(b, d, head_dim, block_size, mg, s)
+                             : launch_decode(b, d, head_dim, block_size, mg, s);
   if (e != hipSuccess) return PKV_ERR_LAUNCH;
   return PKV_OK;
 }
@@ -221,7 +262,7 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   if (workspace_bytes < multi_workspace_for(workers, group, head_dim, max_query_len))
     return PKV_ERR_WORKSPACE;
 
-  DecodeDims d;
+  DecodeDims d{};
   d.S = num_seqs;
   d.Hq = num_q_heads;
   d.Hkv = num_kv_heads;
@@ -244,7 +285,7 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
     d.Qc = per < max_query_len - off ? per : max_query_len - off;
     d.R = group * d.Qc;
     set_units(d, d.R, fp8);
-    DecodeBuffers b;
+    DecodeBuffers b{};
     b.q = static_cast<const uint16_t*>(q) + off * token_elems;
     b.k = k_cache;
     b.v = v_cache;
@@ -279,7 +320,7 @@ int32_t append_impl(const void* k_new, const void* v_new, void* k_cache, void* v
     return PKV_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
     return PKV_ERR_ALIGNMENT;
-  AppendBuffers b;
+  AppendBuffers b{};
   b.k_new = static_cast<const uint16_t*>(k_new);
   b.v_new = static_cast<const uint16_t*>(v_new);
   b.k_cache = k_cache;
@@ -287,7 +328,7 @@ int32_t append_impl(const void* k_new, const void* v_new, void* k_cache, void* v
   b.tables = block_tables;
   b.token_seq = token_seq;
   b.token_pos = token_pos;
-  AppendDims a;
+  AppendDims a{};
   a.T = num_tokens;
   a.S = num_seqs;
   a.Hkv = num_kv_heads;
@@ -362,6 +403,37 @@ int32_t paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_
                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                           num_blocks, max_context_len, workspace, workspace_bytes, stream, true,
                           k_scale, v_scale);
+}
+
+int32_t paged_attn_decode_append(const void* q, const void* k_new, const void* v_new,
+                                 void* k_cache, void* v_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, int32_t block_size, float scale,
+                                 void* out, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 int32_t max_context_len, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_NULL;
+  return pkv::decode_impl(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, out,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          num_blocks, max_context_len, workspace, workspace_bytes, stream, false,
+                          1.0f, 1.0f, k_new, v_new);
+}
+
+int32_t paged_attn_decode_append_fp8(const void* q, const void* k_new, const void* v_new,
+                                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, int32_t block_size, float scale,
+                                     float k_scale, float v_scale, void* out, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t max_blocks_per_seq, int64_t num_blocks,
+                                     int32_t max_context_len, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_NULL;
+  if (k_scale == 0.0f || v_scale == 0.0f) return PKV_ERR_SHAPE;  // new rows are divided by them
+  return pkv::decode_impl(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, out,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          num_blocks, max_context_len, workspace, workspace_bytes, stream, true,
+                          k_scale, v_scale, k_new, v_new);
 }
 
 size_t paged_attn_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

@@ -18,6 +18,7 @@
 // (ties to even), saturating at +-448; NaN is stored as 0x7F.  K chunks of 16 dims
 // are one 16-byte store; V codes are one byte each.
 
+#include "pkv_fp8.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -37,9 +38,10 @@ __device__ __forceinline__ bool token_slot(int64_t t, int32_t g, const int32_t* 
                                            const int32_t* __restrict__ token_pos,
                                            const AppendDims& a, int64_t& tile, int32_t& o) {
   if (t >= a.T || g >= a.Hkv) return false;
-  const int32_t s = token_seq[t];
-  const int32_t p = token_pos[t];
-  if (s < 0 || s >= a.S || p < 0 || p >= a.M * a.B) return false;
+  const int32_t cap = a.M * a.B;
+  const int32_t s = a.newest ? static_cast<int32_t>(t) : token_seq[t];
+  const int32_t p = a.newest ? (token_pos[t] < 0 ? 0 : min(token_pos[t], cap)) - 1 : token_pos[t];
+  if (s < 0 || s >= a.S || p < 0 || p >= cap) return false;
   const int32_t b = tables[static_cast<int64_t>(s) * a.M + p / a.B];
   if (b < 0 || b >= a.NB) return false;  // never write outside the pool
   tile = (static_cast<int64_t>(b) * a.Hkv + g) * D * a.B;
@@ -89,33 +91,6 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void append_kernel(
     for (int i = 0; i < 8; ++i)
       vrun[static_cast<int64_t>(c * 8 + i) * bt] = static_cast<uint16_t>(x[i / 2] >> (16 * (i % 2)));
   }
-}
-
-// E4M3FN code of y: NaN -> 0x7F; otherwise y clamped to +-448 and converted by
-// the hardware (round to nearest even), which then never leaves the finite range.
-__device__ __forceinline__ float e4m3_ready(float y) {
-  return fminf(fmaxf(y, -448.0f), 448.0f);
-}
-
-// Four codes packed in one dword, first element in the low byte.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  const bool nan_a = __builtin_isnan(a), nan_b = __builtin_isnan(b);
-  const bool nan_c = __builtin_isnan(c), nan_d = __builtin_isnan(d);
-  uint32_t w = static_cast<uint32_t>(
-      __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_ready(a), e4m3_ready(b), 0, false));
-  w = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_ready(c), e4m3_ready(d),
-                                                            static_cast<int>(w), true));
-  if (nan_a) w = (w & 0xFFFFFF00u) | 0x7Fu;
-  if (nan_b) w = (w & 0xFFFF00FFu) | 0x7F00u;
-  if (nan_c) w = (w & 0xFF00FFFFu) | 0x7F0000u;
-  if (nan_d) w = (w & 0x00FFFFFFu) | 0x7F000000u;
-  return w;
-}
-
-// The two bf16 values of a dword as floats (first element in the low half).
-__device__ __forceinline__ float lo_bf16(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t x) {
-  return __builtin_bit_cast(float, x & 0xFFFF0000u);
 }
 
 // Codes of 8 consecutive bf16 values (one 16-byte load) divided by scale.

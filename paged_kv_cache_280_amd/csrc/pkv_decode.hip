@@ -56,6 +56,7 @@
 
 #include <type_traits>
 
+#include "pkv_fp8.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -117,7 +118,8 @@ template <bool kCausal>
 __device__ __forceinline__ SeqLen seq_len(const int32_t* __restrict__ lens,
                                           const int32_t* __restrict__ qlens, const DecodeDims& d,
                                           int32_t cap, int32_t s) {
-  const int32_t L = clamp_len(lens[s], cap);
+  // decode with append: the tiles cover all but the newest position
+  const int32_t L = max(clamp_len(lens[s], cap) - d.len_off, 0);
   if constexpr (!kCausal) {
     return SeqLen{L, 1};
   } else {
@@ -635,6 +637,10 @@ struct Ctx {
   const int32_t* __restrict__ qlens;
   uint16_t* __restrict__ out;
   float* __restrict__ ws;
+  const uint16_t* __restrict__ k_new;  // decode with append: the newest rows, bf16 [S][Hkv][D]
+  const uint16_t* __restrict__ v_new;
+  T* kw;                               // the pools, written (the newest rows)
+  T* vw;
 };
 
 // Position in a worker's stream of tiles: tile t of (sequence s, KV head g); L
@@ -768,11 +774,164 @@ __device__ void finish_segment(const Cx& cx, const DecodeDims& d, const SegState
   }
 }
 
+// Decode with append: the pair's newest position (the one past its tiles) joins
+// the segment holding the pair's last tile, from k_new / v_new, the way
+// compute_tile treats a position: score in the log2 domain, the same lazy
+// rescaling, the weight rounded to bf16 for the weighted sum of values.  The
+// worker also writes the new rows into their slot (the caller has made the block
+// private, so no other worker reads it).  fp8 pools: the row is stored, and
+// attended to, as E4M3(x / scale).
+// This lane's parts of a pair's newest rows: the key dims of its score operand
+// and the value dims of its O entries (read ahead by fetch_new).
+template <int D>
+struct NewRow {
+  u32x4_t k[D / 32];
+  u32x2_t v[D / 16];
+};
+
+template <int D, bool kFp8, typename Cx>
+__device__ __forceinline__ void fetch_new(NewRow<D>& nr, const Cx& cx, const DecodeDims& d,
+                                          const Cursor& c, int lane) {
+  const int64_t row = (static_cast<int64_t>(c.s) * d.Hkv + c.g) * D;
+  const int gq = lane >> 4;
+#pragma unroll
+  for (int k = 0; k < D / 32; ++k) {
+    const int d0 = kFp8 ? (k / 2) * 64 + gq * 16 + (k % 2) * 8 : k * 32 + gq * 8;
+    nr.k[k] = *reinterpret_cast<const u32x4_t*>(cx.k_new + row + d0);
+  }
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt)
+    nr.v[mt] = *reinterpret_cast<const u32x2_t*>(cx.v_new + row + mt * 16 + gq * 4);
+}
+
+template <int D, int B, bool kFp8, typename Cx>
+__device__ __forceinline__ void append_token(SegState<D>& st, const bf16x8_t (&qop)[D / 32],
+                                             const NewRow<D>& nr, const Cx& cx,
+                                             const DecodeDims& d, const Cursor& c, int lane) {
+  const int gq = lane >> 4;
+  const bool writer = (lane & 15) == 0;  // lanes 0, 16, 32, 48 cover every dim once
+  const int32_t p = c.L;                 // the tiles hold positions 0 .. p - 1
+  const int32_t b = clamp_block(cx.tables[static_cast<int64_t>(c.s) * d.M + p / B], d.NB);
+  const int32_t ob = p % B;
+  const int64_t tile = (static_cast<int64_t>(b) * d.Hkv + c.g) * D * B;  // elements
+  // score: this lane's query dims (the score MFMA operand layout) against the new key
+  float part = 0.f;
+#pragma unroll
+  for (int k = 0; k < D / 32; ++k) {
+    const int d0 = kFp8 ? (k / 2) * 64 + gq * 16 + (k % 2) * 8 : k * 32 + gq * 8;
+    const u32x4_t x = nr.k[k];
+    uint32_t w[4];
+    if constexpr (kFp8) {
+      const float ks = d.k_scale;
+      const uint32_t lo = e4m3x4(lo_bf16(x[0]) / ks, hi_bf16(x[0]) / ks, lo_bf16(x[1]) / ks,
+                                 hi_bf16(x[1]) / ks);
+      const uint32_t hi = e4m3x4(lo_bf16(x[2]) / ks, hi_bf16(x[2]) / ks, lo_bf16(x[3]) / ks,
+                                 hi_bf16(x[3]) / ks);
+      w[0] = e4m3x2_to_bf16x2<false>(lo);
+      w[1] = e4m3x2_to_bf16x2<true>(lo);
+      w[2] = e4m3x2_to_bf16x2<false>(hi);
+      w[3] = e4m3x2_to_bf16x2<true>(hi);
+      if (writer)
+        *reinterpret_cast<u32x2_t*>(cx.kw + tile + ((d0 / 16) * B + ob) * 16 + d0 % 16) =
+            u32x2_t{lo, hi};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = x[e];
+      if (writer) *reinterpret_cast<u32x4_t*>(cx.kw + tile + ((d0 / 8) * B + ob) * 8) = x;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      part = fmaf(static_cast<float>(qop[k][2 * e]), lo_bf16(w[e]), part);
+      part = fmaf(static_cast<float>(qop[k][2 * e + 1]), hi_bf16(w[e]), part);
+    }
+  }
+  part += __shfl_xor(part, 16);
+  part += __shfl_xor(part, 32);
+  const float sc = part * d.c;
+  float x = sc - st.m;
+  if (x > kRescaleThreshold) {  // also when nothing has been seen (m = -inf)
+    const float alpha = __builtin_amdgcn_exp2f(st.m - sc);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) st.o[mt] *= alpha;
+    st.l *= alpha;
+    st.m = sc;
+    x = 0.f;
+  }
+  const float wgt = static_cast<float>(static_cast<__bf16>(__builtin_amdgcn_exp2f(x)));
+  st.l += wgt;
+  constexpr int32_t kRun = B < kTile ? B : kTile;  // positions of one bf16 V run
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) {
+    const int d0 = mt * 16 + gq * 4;  // this lane's four dims of O
+    const u32x2_t vv = nr.v[mt];
+    uint32_t pair[2];
+    if constexpr (kFp8) {
+      const float vs = d.v_scale;
+      const uint32_t code = e4m3x4(lo_bf16(vv.x) / vs, hi_bf16(vv.x) / vs, lo_bf16(vv.y) / vs,
+                                   hi_bf16(vv.y) / vs);
+      pair[0] = e4m3x2_to_bf16x2<false>(code);
+      pair[1] = e4m3x2_to_bf16x2<true>(code);
+      if (writer) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dd = d0 + i;
+          cx.vw[tile + ((dd % 16) * (B / 4) + ob / 4) * (D / 16) * 4 + (dd / 16) * 4 + ob % 4] =
+              static_cast<uint8_t>(code >> (8 * i));
+        }
+      }
+    } else {
+      pair[0] = vv.x;
+      pair[1] = vv.y;
+      if (writer) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          cx.vw[tile + ((ob / kRun) * D + d0 + i) * kRun + ob % kRun] =
+              static_cast<uint16_t>(pair[i / 2] >> (16 * (i % 2)));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = (i % 2) ? hi_bf16(pair[i / 2]) : lo_bf16(pair[i / 2]);
+      st.o[mt][i] = fmaf(wgt, v, st.o[mt][i]);
+    }
+  }
+}
+
+// Decode with append, a sequence whose only position is the new one: every
+// query head's output is that position's value, and the rows go into slot 0.
+template <int D, int B, bool kFp8, typename Cx>
+__device__ void one_token(const Cx& cx, const DecodeDims& d, int64_t s, int lane) {
+  const int32_t b = clamp_block(cx.tables[s * d.M], d.NB);
+  constexpr int32_t kRun = B < kTile ? B : kTile;
+  for (int32_t e = lane; e < d.Hkv * D; e += kWave) {
+    const int32_t g = e / D, dd = e % D;
+    const int64_t tile = (static_cast<int64_t>(b) * d.Hkv + g) * D * B;
+    const uint16_t kx = cx.k_new[s * d.Hkv * D + e];
+    const uint16_t vx = cx.v_new[s * d.Hkv * D + e];
+    const float kf = __builtin_bit_cast(float, static_cast<uint32_t>(kx) << 16);
+    const float vf = __builtin_bit_cast(float, static_cast<uint32_t>(vx) << 16);
+    uint16_t outv = vx;
+    if constexpr (kFp8) {
+      const uint32_t kc = e4m3x4(kf / d.k_scale, 0.f, 0.f, 0.f) & 0xFFu;
+      const uint32_t vc = e4m3x4(vf / d.v_scale, 0.f, 0.f, 0.f) & 0xFFu;
+      cx.kw[tile + ((dd / 16) * B) * 16 + dd % 16] = static_cast<uint8_t>(kc);
+      cx.vw[tile + ((dd % 16) * (B / 4)) * (D / 16) * 4 + (dd / 16) * 4] = static_cast<uint8_t>(vc);
+      // softmax over one position: the output is the value, times the V scale
+      const float val = lo_bf16(e4m3x2_to_bf16x2<false>(vc)) * d.v_scale;
+      outv = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
+    } else {
+      cx.kw[tile + (dd / 8) * B * 8 + dd % 8] = kx;
+      cx.vw[tile + dd * kRun] = vx;
+    }
+    for (int32_t j = 0; j < d.G; ++j) cx.out[(s * d.Hq + g * d.G + j) * D + dd] = outv;
+  }
+}
+
 // One worker: the n tiles of its range in order, with loads running kPipe-1
 // tiles ahead of the arithmetic across (sequence, head) boundaries; the query of a
 // pair is fetched with the pair's first tile.  Returns the descriptor of the split
 // pair this worker opens (s = -1 if none).
-template <int D, int B, int NC, bool kCausal, bool kFp8, typename Cx>
+template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, typename Cx>
 __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& pl, int64_t w,
                            int lane) {
   const int32_t cap = d.M * B;
@@ -798,6 +957,15 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
   int64_t rec = 2 * w;  // first segment -> slot 0, later ones -> slot 1
   int4 opened = {-1, 0, 0, 0};
 
+  // Decode with append: the newest rows of the pair whose last tile the next
+  // compute step takes, read before that step's tile loads are issued, so that
+  // waiting for them does not wait for the tiles loaded after.
+  NewRow<D> nr;
+  auto fetch_step = [&]() {
+    if constexpr (kAppend) {
+      if (cc.t == cc.T - 1) fetch_new<D, kFp8>(nr, cx, d, cc, lane);
+    }
+  };
   auto load_step = [&](int slot, int32_t li) {
     if (lc.t == 0 || li == 0) load_q<D, NC, kCausal, kFp8>(qb[slot], cx, d, lc, cl, lane);
     load_at<D, B>(r[slot], cx, d, lc, lane);
@@ -828,6 +996,10 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
     } else {
       const int32_t lim[NC] = {valid - 1};
       compute_tile<D, NC, false>(r[slot], qc, st, d.c, valid, valid - 1, lim, lane);
+      if constexpr (kAppend) {
+        static_assert(NC == 1, "decode with append has one query row per head");
+        if (cc.t == cc.T - 1) append_token<D, B, kFp8>(st[0], qc[0], nr, cx, d, cc, lane);
+      }
     }
     if (cc.t == cc.T - 1 || i == n - 1) {
       const bool whole = seg_t0 == 0 && cc.t == cc.T - 1;
@@ -854,6 +1026,7 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
   while (i + 2 * kPipe - 1 <= n) {
 #pragma unroll
     for (int k = 0; k < kPipe; ++k) {
+      fetch_step();
       load_step((k + kPipe - 1) % kPipe, i + k + kPipe - 1);
       compute_step(k, i + k);
     }
@@ -863,6 +1036,7 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
 #pragma unroll
   for (int k = 0; k < 2 * kPipe - 2; ++k) {
     if (k < rem) {
+      fetch_step();
       if (k + kPipe - 1 < rem) load_step((k + kPipe - 1) % kPipe, i + k + kPipe - 1);
       compute_step(k % kPipe, i + k);
     }
@@ -874,14 +1048,20 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
 // Workspace: partial records ([n_workers][2] of record_floats), then one
 // descriptor per worker: (s, g, wb, first_slot | Tq << 1) of the split pair whose
 // first share this worker holds, or s = -1 (Tq only in multi-token launches).
-template <int D, int B, int NC, bool kCausal, bool kFp8>
-__global__ __launch_bounds__(kWave* kWavesPerGroup, (kFp8 && NC == 1) ? 2 : 1) void decode_kernel(
+// fp8 single-tile launches cap registers for two waves per SIMD; decode with append
+// keeps one (its new-row arithmetic needs the room).
+template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend>
+__global__ __launch_bounds__(kWave* kWavesPerGroup,
+                             (kFp8 && NC == 1 && !kAppend) ? 2 : 1) void decode_kernel(
     const uint16_t* __restrict__ q, const typename TileOf<D, B, kFp8>::Elem* __restrict__ k,
     const typename TileOf<D, B, kFp8>::Elem* __restrict__ v,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
     const int32_t* __restrict__ qlens, uint16_t* __restrict__ out, float* __restrict__ ws,
-    int4* __restrict__ desc, DecodeDims d) {
-  const Ctx<typename TileOf<D, B, kFp8>::Elem> cx{q, k, v, tables, lens, qlens, out, ws};
+    int4* __restrict__ desc, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, typename TileOf<D, B, kFp8>::Elem* kw,
+    typename TileOf<D, B, kFp8>::Elem* vw, DecodeDims d) {
+  const Ctx<typename TileOf<D, B, kFp8>::Elem> cx{q,  k,  v,     tables, lens, qlens, out,
+                                                  ws, k_new, v_new, kw,    vw};
   const int lane = __lane_id();
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
   if (w >= d.n_workers) return;
@@ -891,7 +1071,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, (kFp8 && NC == 1) ? 2 : 1) v
   WorkerPlan pl;
   const bool has = d.pair_mode ? plan_pair<kCausal>(lens, qlens, d, cap, w, pl)
                                : plan_worker<kCausal>(lens, qlens, d, cap, w, lane, pl);
-  if (has) opened = run_worker<D, B, NC, kCausal, kFp8>(cx, d, pl, w, lane);
+  if (has) opened = run_worker<D, B, NC, kCausal, kFp8, kAppend>(cx, d, pl, w, lane);
 
   // Rows no tile reaches are zeros: every row of an empty sequence, and in a
   // multi-token launch the rows past a sequence's query tokens (done last: off
@@ -902,7 +1082,11 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, (kFp8 && NC == 1) ? 2 : 1) v
     if constexpr (kCausal) {
       first = seq_len<true>(lens, qlens, d, cap, static_cast<int32_t>(se)).T;
     } else {
-      if (clamp_len(lens[se], cap) != 0) continue;
+      const int32_t Lt = clamp_len(lens[se], cap);
+      if constexpr (kAppend) {
+        if (Lt == 1) one_token<D, B, kFp8>(cx, d, se, lane);
+      }
+      if (Lt != 0) continue;
     }
     const int32_t rows = kCausal ? d.Qc : 1;
     for (int32_t qi = first; qi < rows; ++qi) {
@@ -1036,7 +1220,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
   }
 }
 
-template <int D, int B, int NC, bool kCausal, bool kFp8>
+template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend>
 hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
                     hipStream_t stream) {
   using Elem = typename TileOf<D, B, kFp8>::Elem;
@@ -1044,10 +1228,10 @@ hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_group
   if (groups <= 0) return hipSuccess;
   int4* desc = reinterpret_cast<int4*>(reinterpret_cast<char*>(b.ws) +
                                        records_bytes(d.n_workers, d.R, D));
-  hipLaunchKernelGGL((decode_kernel<D, B, NC, kCausal, kFp8>), dim3(groups),
+  hipLaunchKernelGGL((decode_kernel<D, B, NC, kCausal, kFp8, kAppend>), dim3(groups),
                      dim3(kWave * kWavesPerGroup), 0, stream, b.q, static_cast<const Elem*>(b.k),
                      static_cast<const Elem*>(b.v), b.tables, b.lens, b.qlens, b.out, b.ws, desc,
-                     d);
+                     b.k_new, b.v_new, static_cast<Elem*>(b.kw), static_cast<Elem*>(b.vw), d);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   if (d.pair_mode) return hipSuccess;  // nothing is split: no merge
   // records per split pair: about the workers per (sequence, KV head) pair
@@ -1061,17 +1245,17 @@ hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_group
   return hipGetLastError();
 }
 
-template <int NC, bool kCausal, bool kFp8>
+template <int NC, bool kCausal, bool kFp8, bool kAppend = false>
 hipError_t dispatch(const DecodeBuffers& b, const DecodeDims& d, int D, int B, int merge_groups,
                     hipStream_t stream) {
   if (D == 128) {
-    if (B == 16) return launch_t<128, 16, NC, kCausal, kFp8>(b, d, merge_groups, stream);
-    if (B == 32) return launch_t<128, 32, NC, kCausal, kFp8>(b, d, merge_groups, stream);
-    if (B == 8) return launch_t<128, 8, NC, kCausal, kFp8>(b, d, merge_groups, stream);
+    if (B == 16) return launch_t<128, 16, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
+    if (B == 32) return launch_t<128, 32, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
+    if (B == 8) return launch_t<128, 8, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
   } else if (D == 64) {
-    if (B == 16) return launch_t<64, 16, NC, kCausal, kFp8>(b, d, merge_groups, stream);
-    if (B == 32) return launch_t<64, 32, NC, kCausal, kFp8>(b, d, merge_groups, stream);
-    if (B == 8) return launch_t<64, 8, NC, kCausal, kFp8>(b, d, merge_groups, stream);
+    if (B == 16) return launch_t<64, 16, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
+    if (B == 32) return launch_t<64, 32, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
+    if (B == 8) return launch_t<64, 8, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -1086,6 +1270,12 @@ hipError_t launch_decode(const DecodeBuffers& b, const DecodeDims& d, int D, int
 hipError_t launch_decode_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                              int merge_groups, hipStream_t stream) {
   return dispatch<1, false, true>(b, d, D, B, merge_groups, stream);
+}
+
+hipError_t launch_decode_append(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                                int merge_groups, hipStream_t stream, bool fp8) {
+  return fp8 ? dispatch<1, false, true, true>(b, d, D, B, merge_groups, stream)
+             : dispatch<1, false, false, true>(b, d, D, B, merge_groups, stream);
 }
 
 hipError_t launch_multi(const DecodeBuffers& b, const DecodeDims& d, int D, int B,

@@ -27,6 +27,12 @@ struct DecodeBuffers {
   const int32_t* qlens;     // int32 [S] query tokens per sequence (multi-token launches only)
   uint16_t* out;            // bf16, same layout and offset as q
   float* ws;                // workspace: partial records, then per-worker descriptors
+  // decode-with-append launches only: each sequence's newest position, written into
+  // its slot and attended to in the same launch
+  const uint16_t* k_new;    // bf16 [S][Hkv][D]
+  const uint16_t* v_new;    // bf16 [S][Hkv][D]
+  void* kw;                 // the K pool (written: the new rows)
+  void* vw;                 // the V pool
 };
 
 // Sizes of one launch (passed by value).  A decode launch has one query token
@@ -47,6 +53,9 @@ struct DecodeDims {
                             // no records, no merge); n_workers = S * Hkv
   int32_t unit;             // work units of one tile (1, or 4 when pairs are weighted)
   int32_t hdr;              // work units of a pair's query and output rows
+  int32_t len_off;          // 1 in decode-with-append launches: the tiles cover the first
+                            // context_lens[s] - 1 positions, the newest comes from k_new/v_new
+  float k_scale;            // fp8 decode-with-append: new K rows are stored as E4M3(x / k_scale)
 };
 
 // Floats in one partial record: O[R][D], then m[R], then l[R], padded to a
@@ -78,6 +87,9 @@ hipError_t launch_multi(const DecodeBuffers& b, const DecodeDims& d, int D, int 
 // the V pool's scale.
 hipError_t launch_decode_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                              int merge_groups, hipStream_t stream);
+// Decode with append (d.len_off = 1; b.k_new, v_new, kw, vw set), bf16 or fp8 pools.
+hipError_t launch_decode_append(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                                int merge_groups, hipStream_t stream, bool fp8);
 
 // KV append (pkv_append.hip).
 struct AppendBuffers {
@@ -94,6 +106,8 @@ struct AppendDims {
   int32_t T, S, Hkv, B, M;
   int64_t NB;
   float k_scale, v_scale;     // fp8 pools: stored code = E4M3(x / scale)
+  int32_t newest;             // 1: token t is sequence t's newest position, and token_pos
+                              // holds the context lengths (position = length - 1)
 };
 
 hipError_t launch_append(const AppendBuffers& b, const AppendDims& a, int D, hipStream_t stream);

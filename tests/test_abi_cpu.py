@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
                             "paged_attn_decode_fp8",
                             "paged_attn_multi_workspace_bytes", "paged_attn_multi",
                             "paged_attn_multi_fp8",
-                            "kv_append", "kv_append_fp8", "copy_blocks", "pkv_check_batch"])
+                            "kv_append", "kv_append_fp8", "copy_blocks", "pkv_check_batch",
+                            "paged_attn_decode_append", "paged_attn_decode_append_fp8"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -205,3 +206,22 @@ def test_check_batch_rejects_bad_arguments_on_the_host(lib):
     assert call(tables=None) == -1
     assert call(lens=None) == -1
     assert call(result=0x3002) == -5            # result must be 4-byte aligned
+
+
+def test_decode_append_rejects_bad_arguments_on_the_host(lib):
+    """paged_attn_decode_append(_fp8): missing or misaligned new rows and unusable
+    scales come back before anything is enqueued."""
+    def call(fp8=False, kn=0x8000, vn=0x9000, ks=0.5, vs=0.5, S=2, out=0x6000):
+        head = (0x1000, kn, vn, 0x2000, 0x3000, 0x4000, 0x5000, 16, 0.125)
+        tail = (out, S, 8, 2, 128, 4, 10, 64, 0x7000, 1 << 20, None)
+        if fp8:
+            return lib.paged_attn_decode_append_fp8(*head, ks, vs, *tail)
+        return lib.paged_attn_decode_append(*head, *tail)
+
+    for fp8 in (False, True):
+        assert call(fp8, kn=None) == -1
+        assert call(fp8, vn=None) == -1
+        assert call(fp8, kn=0x8004) == -5
+        assert call(fp8, S=0, kn=None, vn=None, out=None) == 0
+    assert call(True, ks=0.0) == -2
+    assert call(True, vs=float("inf")) == -2
