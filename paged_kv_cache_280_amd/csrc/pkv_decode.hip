@@ -10,11 +10,12 @@
 // Block Table"); the kernel gathers the rows it needs by walking that table (same
 // page, section "Tại sao nó hoạt động").
 //
-// Work decomposition.  The unit of work is a 16-token tile of one (sequence, KV
-// head) pair.  Units are numbered sequence-major, then KV head, then tile, and the
-// N workers (one wave each) take equal contiguous ranges of that numbering, so
-// every worker streams the same number of K/V bytes whatever the mix of context
-// lengths.  A worker's range is cut into segments at (sequence, head) boundaries.
+// Work decomposition.  Work is counted over the 16-token tiles of the (sequence,
+// KV head) pairs, numbered sequence-major, then KV head, then tile, and the N
+// workers (one wave each) take equal contiguous ranges of that count, so every
+// worker streams about the same bytes whatever the mix of context lengths (batches
+// of more than 64 sequences also count each pair's query and output rows).  A
+// worker's range is cut into segments at (sequence, head) boundaries.
 // A segment that covers a whole pair writes the output directly; a segment that
 // covers part of a pair writes its softmax state (reference max m, sum l,
 // unnormalised accumulator O; fp32) to the workspace; a second kernel merges the
@@ -51,6 +52,10 @@
 //
 // Pair mode (short contexts): worker w takes pair w whole, so nothing is split and
 // no merge runs.
+//
+// Decode with append: the tiles cover all but each sequence's newest position,
+// which the worker holding the pair's last tile adds from the new rows and writes
+// into its slot (one launch for the append and the attention over it).
 
 #include <math.h>
 
