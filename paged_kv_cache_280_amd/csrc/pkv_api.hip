@@ -114,13 +114,22 @@ int32_t check_shapes(int32_t block_size, float scale, int32_t num_seqs, int32_t 
 // Work units of a tile and of a pair's query and output rows (rows * head_dim * 2
 // bytes each way).  Batches of more than 64 sequences weigh pairs: a tile is 4
 // units and the rows count in quarters of a tile's K/V bytes (16 positions *
-// head_dim * 2 bytes, bf16; half that for fp8).  Smaller batches count tiles only
-// (measured: the weighting moves nothing there and the lighter plan starts the
-// first loads sooner).
+// head_dim * 2 bytes, bf16; half that for fp8), plus kPairFixedUnits for what a
+// pair costs whatever its rows (switching the stream to it, its query fetch, the
+// rounding and store of its output).  Smaller batches count tiles only (measured:
+// the weighting moves nothing there and the lighter plan starts the first loads
+// sooner).
+//
+// kPairFixedUnits measured on the continuous-batching mix (256 sequences, 2,048
+// pairs): workers holding 20+ short pairs finished ~12 us after single-pair
+// workers with rows alone; 3 to 5 extra units level them (3 and 4 best): bf16
+// 384.8 -> 381 us (B = 16) and 392 -> 383 us (B = 32), fp8 222.8 -> 216 / 213 us.
+constexpr int32_t kPairFixedUnits = 3;
+
 void set_units(DecodeDims& d, int32_t rows, bool fp8) {
   const bool weigh = d.S > kWave;
   d.unit = weigh ? 4 : 1;
-  d.hdr = weigh ? (fp8 ? (rows + 1) / 2 : (rows + 2) / 4) : 0;
+  d.hdr = weigh ? (fp8 ? (rows + 1) / 2 : (rows + 2) / 4) + kPairFixedUnits : 0;
 }
 
 // fp8: the pools hold E4M3FN codes; keys are code * k_scale, values code * v_scale.

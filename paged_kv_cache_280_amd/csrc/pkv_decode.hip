@@ -1,1298 +1,14 @@
-// Paged decode attention for gfx950 (CDNA4): block-table walk, MFMA scores,
-// online softmax, MFMA value accumulation, split-K across persistent workers and a
-// deterministic merge of split (sequence, KV head) pairs.
-//
-// What is computed: "KV cache, PagedAttention" (aiwiki.vn), paragraph on query, key
-// and value -- the query of the current position scores every cached key, and the
-// softmax of the scores weights the cached values.  Where the K/V rows are: a
-// per-sequence block table maps logical block j to a physical block of B tokens
-// anywhere in the pool ("PagedAttention (vLLM)", troisinh.com, section "Cơ chế
-// Block Table"); the kernel gathers the rows it needs by walking that table (same
-// page, section "Tại sao nó hoạt động").
-//
-// Work decomposition.  Work is counted over the 16-token tiles of the (sequence,
-// KV head) pairs, numbered sequence-major, then KV head, then tile, and the N
-// workers (one wave each) take equal contiguous ranges of that count, so every
-// worker streams about the same bytes whatever the mix of context lengths (batches
-// of more than 64 sequences also count each pair's query and output rows).  A
-// worker's range is cut into segments at (sequence, head) boundaries.
-// A segment that covers a whole pair writes the output directly; a segment that
-// covers part of a pair writes its softmax state (reference max m, sum l,
-// unnormalised accumulator O; fp32) to the workspace; a second kernel merges the
-// states of each split pair in worker order (deterministic result).
-//
-// Per tile (one wave, 16 tokens x D dims, up to 16 query heads of one KV head):
-//   scores  S[token][head] = K_tile (16 x D) * q^T (D x 16)  -- D/32 MFMA 16x16x32 bf16
-//   weights p = exp2(S*scale*log2e - m), m a per-head reference max shared by the
-//           four lanes holding that head; m moves up (and O, l are rescaled) only
-//           when a score exceeds it by more than 2^8, so p <= 256 and the
-//           cross-lane max runs only on those rare tiles; p rounded to bf16
-//   values  O^T[dim][head] += V_tile^T (D x 16) * P^T (16 x 16) -- D/16 MFMA 16x16x16
-//   sum     l[head] += sum_t P[head][t] -- one more MFMA against a block of ones,
-//           so l adds exactly the bf16 weights that O used
-// The pool layouts put each lane's MFMA operand in 16 (K) or 8 (V) contiguous
-// bytes, so tiles go from HBM straight into operand registers with coalesced
-// loads, and the score MFMA's output registers are already the weight operand of
-// the value MFMA (no shuffles, no LDS).  Loads run kPipe-1 tiles ahead of the
-// arithmetic through the worker's whole range, across segment boundaries.
-//
-// Multi-token launches (a prefill chunk, or the draft tokens a speculative step
-// verifies: "vLLM PagedAttention: Bước đột phá về thông lượng suy luận LLM",
-// vi.news.hada.io, list of advanced features).  A sequence's query tokens are its
-// last T positions; query token i sits at position L - T + i and sees positions
-// 0 .. L - T + i.  The MFMA columns then hold (query token, head) rows of the
-// pair, one or two 16-column tiles per wave, each column with its own position
-// limit; every K/V tile is loaded once for all of them.  A pair's tiles stop at
-// the last position its last query token sees.
-//
-// fp8 pools ("KV cache, PagedAttention", aiwiki.vn, paragraph on cache
-// quantisation): one-byte E4M3FN codes, loaded 16 bytes per lane and widened
-// exactly to bf16 for the same MFMAs; the K pool's scale folds into the score
-// factor and the V pool's into the output, so nothing is scaled per element.
-//
-// Pair mode (short contexts): worker w takes pair w whole, so nothing is split and
-// no merge runs.
-//
-// Decode with append: the tiles cover all but each sequence's newest position,
-// which the worker holding the pair's last tile adds from the new rows and writes
-// into its slot (one launch for the append and the attention over it).
+// Launch of paged decode attention over bf16 pools: the decode kernel and the merge
+// of split pairs (kernels in pkv_decode_kernels.h).  The kernel instances are spread
+// over several translation units so that they compile in parallel.
 
-#include <math.h>
-
-#include <type_traits>
-
-#include "pkv_fp8.h"
-#include "pkv_internal.h"
+#include "pkv_decode_kernels.h"
 
 namespace pkv {
-namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-// Tile buffers in registers (kPipe-1 loads in flight).  Two column tiles of
-// 128-dim rows leave room for two buffers only.  fp8 tiles run best with two
-// buffers too (measured: fewer registers, 200 VGPRs at D = 128, beat deeper
-// pipelines on every workload).
-template <int D, int NC, bool kFp8>
-constexpr int pipe_depth() {
-  return (kFp8 || (NC == 2 && D == 128)) ? 2 : 3;
-}
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: weights stay below 2^8
-
-__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-
-__device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t cap) {
-  return L < 0 ? 0 : (L > cap ? cap : L);
-}
-
-__device__ __forceinline__ int32_t tiles_of(int32_t L) { return (L + kTile - 1) / kTile; }
-
-__device__ __forceinline__ int32_t clamp_block(int32_t b, int64_t nb) {
-  return b < 0 ? 0 : (b >= nb ? static_cast<int32_t>(nb - 1) : b);
-}
-
-// Inclusive prefix sum over the wave's 64 lanes with DPP moves (no LDS traffic):
-// doubling shifts within each row of 16 lanes, then each row's running total
-// broadcast into the rows after it (lane 15 into rows 1 and 3, lane 31 into rows
-// 2 and 3).  Out-of-row sources of the shifts read 0.
-__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
-  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
-  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 1, 0xF, 0xF, true);
-  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 2, 0xF, 0xF, true);
-  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 4, 0xF, 0xF, true);
-  x += __builtin_amdgcn_update_dpp(0, x, kRowShr + 8, 0xF, 0xF, true);
-  x += __builtin_amdgcn_update_dpp(0, x, kRowBcast15, 0xA, 0xF, false);
-  x += __builtin_amdgcn_update_dpp(0, x, kRowBcast31, 0xC, 0xF, false);
-  return x;
-}
-
-// Context a launch processes for sequence s.  Decode: L = context_lens[s], one
-// query token.  Multi-token launch: the sequence's query tokens are its last
-// T = query_lens[s] positions (T clamped into [0, min(L, Qmax)]); the launch
-// takes the Tc of them in [q_off, q_off + Qc), and its context ends at the
-// position the last of those sees, so L_c = L - T + q_off + Tc (0 when Tc = 0).
-struct SeqLen {
-  int32_t L, T;
-};
-
-template <bool kCausal>
-__device__ __forceinline__ SeqLen seq_len(const int32_t* __restrict__ lens,
-                                          const int32_t* __restrict__ qlens, const DecodeDims& d,
-                                          int32_t cap, int32_t s) {
-  // decode with append: the tiles cover all but the newest position
-  const int32_t L = max(clamp_len(lens[s], cap) - d.len_off, 0);
-  if constexpr (!kCausal) {
-    return SeqLen{L, 1};
-  } else {
-    const int32_t T = clamp_len(qlens[s], min(L, d.Qmax));
-    const int32_t Tc = clamp_len(T - d.q_off, d.Qc);
-    return SeqLen{Tc > 0 ? L - T + d.q_off + Tc : 0, Tc};
-  }
-}
-
-// Work units.  A tile of a (sequence, KV head) pair counts d.unit units and each
-// pair d.hdr more (its query and output rows; with d.unit = 4, in quarters of a
-// tile's K/V bytes), so ranges of equal units carry about equal bytes however
-// many pairs they hold.  The pairs of sequence s follow each other in head order:
-// pair (s, g) spans units [start_s + g*P_s, start_s + (g+1)*P_s), P_s =
-// unit*T_s + hdr, and its tile t sits at unit start_s + g*P_s + hdr + unit*t.
-// Empty sequences hold no units.  A worker owns the tiles whose unit lies in its
-// range.  Launches over at most 64 sequences use unit 1 and hdr 0 (units are
-// tiles), which keeps the plan to one scan and one lookup.
-__device__ __forceinline__ int32_t pair_units(int32_t T, const DecodeDims& d) {
-  return T > 0 ? d.unit * T + d.hdr : 0;
-}
-
-// Range of worker w: units [w*U/N, (w+1)*U/N) (range_of below).  worker_of(u) is
-// the largest w whose range starts at or before u.
-__device__ __forceinline__ int64_t worker_of(int64_t u, int64_t U, int64_t N) {
-  return ((u + 1) * N - 1) / U;
-}
-
-// Per-lane view of 64 consecutive sequences base + lane: their SeqLen (L, Tq),
-// tiles T, pair units P, and inclusive scans of T and P (zeros past the batch).
-struct Chunk {
-  int32_t base, L, Tq, T, P, incT, incP;
-};
-
-template <bool kCausal>
-__device__ __forceinline__ SeqLen lane_len(const int32_t* __restrict__ lens,
-                                           const int32_t* __restrict__ qlens, const DecodeDims& d,
-                                           int32_t cap, int32_t base, int lane) {
-  return base + lane < d.S ? seq_len<kCausal>(lens, qlens, d, cap, base + lane) : SeqLen{0, 0};
-}
-
-// One shuffle scan: the unit scan follows from the tile scan and the count of
-// non-empty sequences up to this lane.
-__device__ __forceinline__ Chunk make_chunk(int32_t base, SeqLen sl, const DecodeDims& d,
-                                            int lane) {
-  Chunk c;
-  c.base = base;
-  c.L = sl.L;
-  c.Tq = sl.T;
-  const int32_t T = tiles_of(sl.L);
-  c.T = T;
-  c.P = pair_units(T, d);
-  c.incT = wave_inclusive_scan(c.T);
-  const uint64_t upto = lane == kWave - 1 ? ~0ull : ((1ull << (lane + 1)) - 1);
-  c.incP = d.unit * c.incT + d.hdr * __builtin_popcountll(__ballot(T > 0) & upto);
-  return c;
-}
-
-// Where unit x falls (x at or past the chunk's first unit acc_u): false when x
-// lies past the chunk.  Otherwise the sequence s holding x, the first unit and
-// the first tile (index over the whole batch) of s, the tiles of s, and the first
-// tile of s at or after x as (g, t), g = Hkv when x lies past the last tile of s.
-struct UnitLoc {
-  int32_t s, g, t, T, P, L, Tq;
-  int64_t start, tstart;
-};
-
-__device__ __forceinline__ bool locate_in(const Chunk& c, const DecodeDims& d, int64_t acc_u,
-                                          int64_t acc_t, int64_t x, UnitLoc& r) {
-  const int64_t chunk_u = static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, kWave - 1)) * d.Hkv;
-  if (x >= acc_u + chunk_u) return false;
-  const uint64_t hit = __ballot(acc_u + static_cast<int64_t>(c.incP) * d.Hkv > x);
-  const int32_t i = uniform(__builtin_ctzll(hit));
-  r.s = c.base + i;
-  r.L = __builtin_amdgcn_readlane(c.L, i);
-  r.Tq = __builtin_amdgcn_readlane(c.Tq, i);
-  r.T = __builtin_amdgcn_readlane(c.T, i);
-  r.P = __builtin_amdgcn_readlane(c.P, i);
-  r.start = acc_u + static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, i) - r.P) * d.Hkv;
-  r.tstart = acc_t + static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, i) - r.T) * d.Hkv;
-  const int64_t rel = x - r.start;
-  r.g = rel < (int64_t(1) << 31) ? static_cast<int32_t>(rel) / r.P : static_cast<int32_t>(rel / r.P);
-  const int32_t off = static_cast<int32_t>(rel - static_cast<int64_t>(r.g) * r.P);
-  r.t = off <= d.hdr ? 0 : (off - d.hdr + d.unit - 1) / d.unit;
-  if (r.t >= r.T) {
-    ++r.g;
-    r.t = 0;
-  }
-  return true;
-}
-
-// Index over the whole batch of the first tile at or after the located unit.
-__device__ __forceinline__ int64_t first_tile(const UnitLoc& r) {
-  return r.tstart + static_cast<int64_t>(r.g) * r.T + r.t;
-}
-
-// A worker's share of the batch: total units U, active workers N, the first tile
-// (s, g, t) of its range, the first unit `start` and the SeqLen (L, Tq) of s, and
-// its tile count n.
-struct WorkerPlan {
-  int64_t U, N, start;
-  int32_t s, g, t, n, L, Tq;
-};
-
-// Chunks of the batch's sequences held in registers (the rest are read again on
-// every pass): one read of the lengths and one scan serve every pass up to 256
-// sequences.
-constexpr int kPlanChunks = 4;
-
-// Passes over the chunks in order: f(chunk, acc_u, acc_t) returns true to stop.
-template <bool kCausal, typename F>
-__device__ __forceinline__ void for_chunks(const int32_t* __restrict__ lens,
-                                           const int32_t* __restrict__ qlens,
-                                           const DecodeDims& d, int32_t cap,
-                                           const Chunk (&ch)[kPlanChunks], int lane, F&& f) {
-  int64_t acc_u = 0, acc_t = 0;
-#pragma unroll
-  for (int k = 0; k < kPlanChunks; ++k) {
-    if (k * kWave >= d.S) return;
-    const Chunk& c = ch[k];
-    if (f(c, acc_u, acc_t)) return;
-    acc_u += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, kWave - 1)) * d.Hkv;
-    acc_t += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, kWave - 1)) * d.Hkv;
-  }
-  for (int32_t base = kPlanChunks * kWave; base < d.S; base += kWave) {
-    const Chunk c = make_chunk(base, lane_len<kCausal>(lens, qlens, d, cap, base, lane), d, lane);
-    if (f(c, acc_u, acc_t)) return;
-    acc_u += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, kWave - 1)) * d.Hkv;
-    acc_t += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, kWave - 1)) * d.Hkv;
-  }
-}
-
-// Ends of worker w's range, [w*U/N, (w+1)*U/N), with 32-bit divisions whenever
-// the operands fit (U = q*N + r, so w*U/N = w*q + r*w/N).
-__device__ __forceinline__ void range_of(int64_t w, int64_t U, int64_t N, int64_t& u, int64_t& ue) {
-  const bool small = U < (int64_t(1) << 32) && N < (int64_t(1) << 16);
-  const int64_t q = small ? static_cast<uint32_t>(U) / static_cast<uint32_t>(N) : U / N;
-  const int64_t r = U - q * N;  // < N
-  if (small) {
-    u = w * q + static_cast<uint32_t>(r * w) / static_cast<uint32_t>(N);
-    ue = (w + 1) * q + static_cast<uint32_t>(r * (w + 1)) / static_cast<uint32_t>(N);
-  } else {
-    u = w * q + r * w / N;
-    ue = (w + 1) * q + r * (w + 1) / N;
-  }
-}
-
-// Returns false when worker w has no tile.
-template <bool kCausal>
-__device__ bool plan_worker(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
-                            const DecodeDims& d, int32_t cap, int64_t w, int lane, WorkerPlan& p) {
-  if (d.S <= kWave) {  // units are tiles: one scan, one lookup
-    const SeqLen sl = lane_len<kCausal>(lens, qlens, d, cap, 0, lane);
-    const int32_t T = tiles_of(sl.L);
-    const int32_t incl = wave_inclusive_scan(T);
-    p.U = static_cast<int64_t>(__builtin_amdgcn_readlane(incl, kWave - 1)) * d.Hkv;
-    p.N = min(static_cast<int64_t>(d.n_workers), p.U);
-    if (w >= p.N) return false;
-    int64_t u, ue;
-    range_of(w, p.U, p.N, u, ue);
-    const uint64_t hit = __ballot(static_cast<int64_t>(incl) * d.Hkv > u);
-    const int32_t i = uniform(__builtin_ctzll(hit));
-    p.s = i;
-    p.L = __builtin_amdgcn_readlane(sl.L, i);
-    p.Tq = __builtin_amdgcn_readlane(sl.T, i);
-    const int32_t Ts = __builtin_amdgcn_readlane(T, i);
-    p.start = static_cast<int64_t>(__builtin_amdgcn_readlane(incl, i) - Ts) * d.Hkv;
-    const int64_t rel = u - p.start;
-    p.g = rel < (int64_t(1) << 31) ? static_cast<int32_t>(rel) / Ts : static_cast<int32_t>(rel / Ts);
-    p.t = static_cast<int32_t>(rel - static_cast<int64_t>(p.g) * Ts);
-    p.n = static_cast<int32_t>(ue - u);
-    return true;
-  }
-  SeqLen T0[kPlanChunks];  // all lengths read first: one round trip
-#pragma unroll
-  for (int k = 0; k < kPlanChunks; ++k) T0[k] = lane_len<kCausal>(lens, qlens, d, cap, k * kWave, lane);
-  Chunk Tc[kPlanChunks];
-#pragma unroll
-  for (int k = 0; k < kPlanChunks; ++k)
-    if (k * kWave < d.S) Tc[k] = make_chunk(k * kWave, T0[k], d, lane);
-  // pass 1: total units and tiles
-  int64_t U = 0, tiles = 0;
-  for_chunks<kCausal>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t, int64_t) {
-    U += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, kWave - 1)) * d.Hkv;
-    tiles += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, kWave - 1)) * d.Hkv;
-    return false;
-  });
-  p.U = U;
-  p.N = min(static_cast<int64_t>(d.n_workers), tiles);  // every range >= d.unit units
-  if (w >= p.N) return false;
-  int64_t u, ue;
-  range_of(w, p.U, p.N, u, ue);
-  // pass 2: where the range starts and ends
-  UnitLoc lu, le;
-  bool found_u = false, found_e = ue >= U;
-  int64_t first = 0, last = tiles;
-  for_chunks<kCausal>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t au, int64_t at) {
-    if (!found_u && locate_in(c, d, au, at, u, lu)) {
-      found_u = true;
-      first = first_tile(lu);
-    }
-    if (!found_e && locate_in(c, d, au, at, ue, le)) {
-      found_e = true;
-      last = first_tile(le);
-    }
-    return found_u && found_e;
-  });
-  if (!found_u || last <= first) return false;
-  p.n = static_cast<int32_t>(last - first);
-  if (lu.g >= d.Hkv) {
-    // u lies past the last tile of its sequence: the range starts at the next
-    // sequence that holds units
-    const int64_t next = lu.start + static_cast<int64_t>(lu.P) * d.Hkv;
-    for_chunks<kCausal>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t au, int64_t at) {
-      return locate_in(c, d, au, at, next, lu);
-    });
-  }
-  p.s = lu.s;
-  p.g = lu.g;
-  p.t = lu.t;
-  p.L = lu.L;
-  p.Tq = lu.Tq;
-  p.start = lu.start;
-  return true;
-}
-
-// Where one (sequence, KV head) pair's tiles come from (T: pool element type).
-template <typename T>
-struct PairCursor {
-  const T* k;               // K pool
-  const T* v;               // V pool
-  const int32_t* trow;      // block-table row of the sequence
-  int64_t head_off;         // g * (elements of one (block, head) tile)
-  int64_t block_stride;     // elements of one block (all heads)
-  int64_t nb;
-  int32_t nblk;             // ceil(L / B)
-};
-
-// Pair mode: worker w takes (sequence w / Hkv, KV head w % Hkv) whole.  Returns
-// false for workers past the pairs and for empty sequences.
-template <bool kCausal>
-__device__ bool plan_pair(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
-                          const DecodeDims& d, int32_t cap, int64_t w, WorkerPlan& p) {
-  if (w >= static_cast<int64_t>(d.S) * d.Hkv) return false;
-  const int32_t s = static_cast<int32_t>(w / d.Hkv);
-  const int32_t g = static_cast<int32_t>(w - static_cast<int64_t>(s) * d.Hkv);
-  const SeqLen sl = seq_len<kCausal>(lens, qlens, d, cap, s);
-  const int32_t T = tiles_of(sl.L);
-  if (T == 0) return false;
-  p.L = sl.L;
-  p.Tq = sl.T;
-  p.U = 1;  // only used to find the workers of split pairs, and none is split
-  p.N = 1;
-  p.start = 0;
-  p.s = s;
-  p.g = g;
-  p.t = 0;
-  p.n = T;
-  return true;
-}
-
-// A tile of bf16 K/V in registers: every lane's MFMA operands, as loaded.
-template <int D, int B>
-struct Bf16Tile {
-  using Elem = uint16_t;
-  u32x4_t k[D / 32];  // score MFMA A operand: token lane%16, dims c*32 + (lane/16)*8 .. +7
-  u32x2_t v[D / 16];  // value MFMA A operand: dim mt*16 + lane%16, tokens (lane/16)*4 .. +3
-
-  // Issue the loads of tile t.
-  __device__ __forceinline__ void load(const PairCursor<Elem>& pc, int32_t t, int lane) {
-    const int32_t tok0 = t * kTile;
-    if constexpr (B >= kTile) {
-      const int32_t b = clamp_block(pc.trow[tok0 / B], pc.nb);
-      const int32_t ob = tok0 % B;
-      const int64_t base = static_cast<int64_t>(b) * pc.block_stride + pc.head_off;
-      const uint16_t* kt = pc.k + base;
-      // V keeps each 16-position half of a block as its own [D][16] run
-      const uint16_t* vt = pc.v + base + (ob / kTile) * D * kTile;
-      const uint32_t koff = static_cast<uint32_t>(((lane >> 4) * B + ob + (lane & 15)) * 8);
-      const uint32_t voff = static_cast<uint32_t>((lane & 15) * kTile + (lane >> 4) * 4);
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-        k[c] = *reinterpret_cast<const u32x4_t*>(kt + koff + c * 4 * B * 8);
-#pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt)
-        v[mt] = *reinterpret_cast<const u32x2_t*>(vt + voff + mt * 16 * kTile);
-    } else {
-      // B == 8: the tile spans logical blocks 2t and 2t+1 (the second clamped to
-      // the sequence's last block; its lanes are masked when it lies past the
-      // context).
-      static_assert(B == 8, "block sizes below 16 other than 8 are not built");
-      const int32_t j0 = tok0 / B;
-      const int32_t j1 = j0 + 1 < pc.nblk ? j0 + 1 : pc.nblk - 1;
-      const int64_t base0 = static_cast<int64_t>(clamp_block(pc.trow[j0], pc.nb)) * pc.block_stride;
-      const int64_t base1 = static_cast<int64_t>(clamp_block(pc.trow[j1], pc.nb)) * pc.block_stride;
-      const int64_t kb = ((lane & 15) < 8 ? base0 : base1) + pc.head_off;
-      const int64_t vb = ((lane >> 4) < 2 ? base0 : base1) + pc.head_off;
-      const uint16_t* kt = pc.k + kb + ((lane >> 4) * B + (lane & 7)) * 8;
-      const uint16_t* vt = pc.v + vb + (lane & 15) * B + ((lane >> 4) & 1) * 4;
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) k[c] = *reinterpret_cast<const u32x4_t*>(kt + c * 4 * B * 8);
-#pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt)
-        v[mt] = *reinterpret_cast<const u32x2_t*>(vt + mt * 16 * B);
-    }
-  }
-  __device__ __forceinline__ bf16x8_t kop(int cc) const { return __builtin_bit_cast(bf16x8_t, k[cc]); }
-  __device__ __forceinline__ u32x2_t vop(int mt) const { return v[mt]; }
-  // Keep the first n of this lane's four tokens (the others lie past the context).
-  __device__ __forceinline__ void mask_v(int32_t n) {
-    const uint64_t keep = n >= 4 ? ~0ull : (n <= 0 ? 0ull : ((1ull << (16 * n)) - 1));
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      v[mt].x &= static_cast<uint32_t>(keep);
-      v[mt].y &= static_cast<uint32_t>(keep >> 32);
-    }
-  }
-};
-
-// Two E4M3FN codes (word kHi of x) as two bf16 numbers, exactly: every E4M3
-// value is a bf16 value, and the conversion's scale is 1.
-template <bool kHi>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t x) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, kHi));
-}
-
-// A tile of fp8 K/V in registers (one byte per element, 16-byte loads); the
-// operands are widened to bf16 when the MFMAs need them.  The score MFMA's
-// reduction runs over a permutation of the head dimension: MFMA cc at lane group
-// gq = lane/16 takes dims (cc/2)*64 + gq*16 + (cc%2)*8 .. +7 (the query uses the
-// same permutation).
-template <int D, int B>
-struct Fp8Tile {
-  using Elem = uint8_t;
-  u32x4_t k[D / 64];  // token lane%16, dims c*64 + (lane/16)*16 .. +15
-  u32x4_t v[D / 64];  // dims (4i + jj)*16 + lane%16 (dword jj), tokens (lane/16)*4 .. +3
-
-  __device__ __forceinline__ void load(const PairCursor<Elem>& pc, int32_t t, int lane) {
-    const int32_t tok0 = t * kTile;
-    const uint8_t* kt;
-    const uint8_t* vt;
-    if constexpr (B >= kTile) {
-      const int32_t b = clamp_block(pc.trow[tok0 / B], pc.nb);
-      const int32_t ob = tok0 % B;
-      const int64_t base = static_cast<int64_t>(b) * pc.block_stride + pc.head_off;
-      kt = pc.k + base + ((lane >> 4) * B + ob + (lane & 15)) * 16;
-      vt = pc.v + base + ((lane & 15) * (B / 4) + ob / 4 + (lane >> 4)) * (D / 16) * 4;
-    } else {
-      static_assert(B == 8, "block sizes below 16 other than 8 are not built");
-      const int32_t j0 = tok0 / B;
-      const int32_t j1 = j0 + 1 < pc.nblk ? j0 + 1 : pc.nblk - 1;
-      const int64_t base0 = static_cast<int64_t>(clamp_block(pc.trow[j0], pc.nb)) * pc.block_stride;
-      const int64_t base1 = static_cast<int64_t>(clamp_block(pc.trow[j1], pc.nb)) * pc.block_stride;
-      const int64_t kb = ((lane & 15) < 8 ? base0 : base1) + pc.head_off;
-      const int64_t vb = ((lane >> 4) < 2 ? base0 : base1) + pc.head_off;
-      kt = pc.k + kb + ((lane >> 4) * B + (lane & 7)) * 16;
-      vt = pc.v + vb + ((lane & 15) * (B / 4) + ((lane >> 4) & 1)) * (D / 16) * 4;
-    }
-#pragma unroll
-    for (int c = 0; c < D / 64; ++c) k[c] = *reinterpret_cast<const u32x4_t*>(kt + c * 4 * B * 16);
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(vt + i * 16);
-  }
-  __device__ __forceinline__ bf16x8_t kop(int cc) const {
-    const u32x4_t w = k[cc / 2];
-    const uint32_t a = (cc & 1) ? w.z : w.x;
-    const uint32_t b = (cc & 1) ? w.w : w.y;
-    const u32x4_t r = {e4m3x2_to_bf16x2<false>(a), e4m3x2_to_bf16x2<true>(a),
-                       e4m3x2_to_bf16x2<false>(b), e4m3x2_to_bf16x2<true>(b)};
-    return __builtin_bit_cast(bf16x8_t, r);
-  }
-  __device__ __forceinline__ u32x2_t vop(int mt) const {
-    const uint32_t w = v[mt / 4][mt % 4];
-    return u32x2_t{e4m3x2_to_bf16x2<false>(w), e4m3x2_to_bf16x2<true>(w)};
-  }
-  // Keep the first n of this lane's four tokens: code 0 is +0.
-  __device__ __forceinline__ void mask_v(int32_t n) {
-    const uint32_t keep = n >= 4 ? ~0u : (n <= 0 ? 0u : ((1u << (8 * n)) - 1));
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) v[i] &= keep;
-  }
-};
-
-template <int D, int B, bool kFp8>
-using TileOf = typename std::conditional<kFp8, Fp8Tile<D, B>, Bf16Tile<D, B>>::type;
-
-// Softmax state of one wave's column tile over one segment.
-template <int D>
-struct SegState {
-  f32x4_t o[D / 16];  // O^T[dim mt*16 + (lane/16)*4 + i][column lane%16]
-  f32x4_t l;          // every entry: sum of the bf16 weights of column lane%16
-  float m;            // reference max of column lane%16 (log2 domain)
-};
-
-// Column n = j*16 + lane%16 of column tile j is row n of a (sequence, KV head)
-// pair: query token qi = n / G of head n % G.  `row` is the offset of its q and
-// out row from the pair's first row (qi*Hq + n % G), or -1 when n >= R.
-template <int NC>
-struct Cols {
-  int32_t qi[NC];
-  int32_t row[NC];
-};
-
-template <int NC, bool kCausal>
-__device__ __forceinline__ Cols<NC> make_cols(const DecodeDims& d, int lane) {
-  Cols<NC> cl;
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const int32_t n = j * 16 + (lane & 15);
-    if constexpr (kCausal) {
-      const int32_t qi = n / d.G;
-      cl.qi[j] = qi;
-      cl.row[j] = n < d.R ? qi * d.Hq + (n - qi * d.G) : -1;
-    } else {  // one query token: R = G
-      cl.qi[j] = 0;
-      cl.row[j] = n < d.G ? n : -1;
-    }
-  }
-  return cl;
-}
-
-// One tile for NC column tiles: scores, softmax weights, value and sum
-// accumulation.  `valid` is the number of tokens of the tile inside the context
-// (16 except in the last tile).  Multi-token launches also mask by position:
-// column j of this lane sees the tile's tokens 0 .. lim[j], and lim_lo is the
-// smallest lim of the wave (nothing is masked by position when lim_lo >= 15).
-template <int D, int NC, bool kCausal, typename Tile>
-__device__ __forceinline__ void compute_tile(Tile& r, const bf16x8_t (&qop)[NC][D / 32],
-                                             SegState<D> (&st)[NC], float c, int32_t valid,
-                                             int32_t lim_lo, const int32_t (&lim)[NC], int lane) {
-  f32x4_t sc[NC];
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    sc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int cc = 0; cc < D / 32; ++cc)
-      sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.kop(cc), qop[j][cc], sc[j], 0, 0, 0);
-  }
-  const int32_t tq = (lane >> 4) * 4;  // first of the four tokens this lane scores
-  float x[NC][4];
-#pragma unroll
-  for (int j = 0; j < NC; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[j][i] = fmaf(sc[j][i], c, -st[j].m);
-  if constexpr (kCausal) {
-    if (lim_lo < kTile - 1) {
-#pragma unroll
-      for (int j = 0; j < NC; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tq + i > lim[j]) x[j][i] = -INFINITY;
-    }
-  } else {
-    if (valid < kTile) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (tq + i >= valid) x[0][i] = -INFINITY;
-    }
-  }
-  // V rows past the context are zeroed: their slots may hold anything
-  if (valid < kTile) r.mask_v(valid - tq);
-  bool over = false;
-#pragma unroll
-  for (int j = 0; j < NC; ++j)
-    over = over || x[j][0] > kRescaleThreshold || x[j][1] > kRescaleThreshold ||
-           x[j][2] > kRescaleThreshold || x[j][3] > kRescaleThreshold;
-  if (__ballot(over)) {
-    // Move the reference max of every column up to its max over everything seen
-    // so far (always taken on a segment's first tile, where m = -inf and x = +inf).
-#pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      float sv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool masked = kCausal ? tq + i > lim[j] : (valid < kTile && tq + i >= valid);
-        sv[i] = masked ? -INFINITY : sc[j][i] * c;
-      }
-      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(st[j].m, mx);
-      // a column that has seen no position yet keeps m = -inf and weights 0
-      const float m_ref = (kCausal && m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(st[j].m - m_ref);
-#pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt) st[j].o[mt] *= alpha;
-      st[j].l *= alpha;
-      st[j].m = m_new;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[j][i] = sv[i] - m_ref;
-    }
-  }
-  const bf16x4_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f),
-                         static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    bf16x4_t pb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pb[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(x[j][i]));
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt)
-      st[j].o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-          __builtin_bit_cast(bf16x4_t, r.vop(mt)), pb, st[j].o[mt], 0, 0, 0);
-    st[j].l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pb, st[j].l, 0, 0, 0);
-  }
-}
-
-template <typename T>
-struct Ctx {
-  const uint16_t* __restrict__ q;
-  const T* __restrict__ k;
-  const T* __restrict__ v;
-  const int32_t* __restrict__ tables;
-  const int32_t* __restrict__ lens;
-  const int32_t* __restrict__ qlens;
-  uint16_t* __restrict__ out;
-  float* __restrict__ ws;
-  const uint16_t* __restrict__ k_new;  // decode with append: the newest rows, bf16 [S][Hkv][D]
-  const uint16_t* __restrict__ v_new;
-  T* kw;                               // the pools, written (the newest rows)
-  T* vw;
-};
-
-// Position in a worker's stream of tiles: tile t of (sequence s, KV head g); L
-// and T are the context and tile count of s in this launch, Tq its query tokens,
-// `start` the first unit of s.
-struct Cursor {
-  int64_t start;
-  int32_t s, g, t, T, L, Tq;
-};
-
-template <bool kCausal, typename Cx>
-__device__ __forceinline__ void advance(Cursor& c, const Cx& cx, const DecodeDims& d,
-                                        int32_t cap) {
-  if (++c.t < c.T) return;
-  c.t = 0;
-  if (++c.g < d.Hkv) return;
-  c.g = 0;
-  c.start += static_cast<int64_t>(d.Hkv) * pair_units(c.T, d);
-  do {
-    ++c.s;
-    if (c.s < d.S) {
-      const SeqLen sl = seq_len<kCausal>(cx.lens, cx.qlens, d, cap, c.s);
-      c.L = sl.L;
-      c.Tq = sl.T;
-    } else {
-      c.L = 1;  // past the batch only at the very end
-      c.Tq = 1;
-    }
-  } while (c.L == 0);
-  c.T = tiles_of(c.L);
-}
-
-template <int D, int B, typename Tile, typename Cx>
-__device__ __forceinline__ void load_at(Tile& r, const Cx& cx, const DecodeDims& d,
-                                        const Cursor& c, int lane) {
-  constexpr int64_t kTileElems = static_cast<int64_t>(D) * B;
-  PairCursor<typename Tile::Elem> pc;
-  pc.k = cx.k;
-  pc.v = cx.v;
-  pc.trow = cx.tables + static_cast<int64_t>(c.s) * d.M;
-  pc.block_stride = kTileElems * d.Hkv;
-  pc.head_off = kTileElems * c.g;
-  pc.nb = d.NB;
-  pc.nblk = (c.L + B - 1) / B;
-  r.load(pc, c.t, lane);
-}
-
-// First q/out row of a (sequence, KV head) pair.
-template <bool kCausal>
-__device__ __forceinline__ int64_t pair_row(const DecodeDims& d, const Cursor& c) {
-  const int64_t seq_rows = kCausal ? static_cast<int64_t>(d.Qmax) * d.Hq : d.Hq;
-  return c.s * seq_rows + c.g * d.G;
-}
-
-// Rows of a pair (R = G in decode launches).
-template <bool kCausal>
-__device__ __forceinline__ int32_t pair_rows(const DecodeDims& d) {
-  return kCausal ? d.R : d.G;
-}
-
-// True when column j of this lane is a row the launch computes.
-template <int NC, bool kCausal>
-__device__ __forceinline__ bool live(const Cols<NC>& cl, int j, const Cursor& c) {
-  return cl.row[j] >= 0 && (!kCausal || cl.qi[j] < c.Tq);
-}
-
-// Score MFMA B operand: lane holds q[row of column j][c*32 + (lane/16)*8 .. +7]
-// (with fp8 K, the permuted dims (c/2)*64 + (lane/16)*16 + (c%2)*8 .. +7); zeros
-// for columns the launch does not compute.
-template <int D, int NC, bool kCausal, bool kFp8, typename Cx>
-__device__ __forceinline__ void load_q(bf16x8_t (&qop)[NC][D / 32], const Cx& cx,
-                                       const DecodeDims& d, const Cursor& c, const Cols<NC>& cl,
-                                       int lane) {
-  const int64_t r0 = pair_row<kCausal>(d, c);
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    if (live<NC, kCausal>(cl, j, c)) {
-      if constexpr (kFp8) {
-        const uint16_t* qr = cx.q + (r0 + cl.row[j]) * D + (lane >> 4) * 16;
-#pragma unroll
-        for (int k = 0; k < D / 32; ++k)
-          qop[j][k] = __builtin_bit_cast(
-              bf16x8_t, *reinterpret_cast<const u32x4_t*>(qr + (k / 2) * 64 + (k % 2) * 8));
-      } else {
-        const uint16_t* qr = cx.q + (r0 + cl.row[j]) * D + (lane >> 4) * 8;
-#pragma unroll
-        for (int k = 0; k < D / 32; ++k)
-          qop[j][k] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(qr + k * 32));
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < D / 32; ++k)
-        qop[j][k] = __builtin_bit_cast(bf16x8_t, u32x4_t{0, 0, 0, 0});
-    }
-  }
-}
-
-// End of a segment: the output rows when it covered the whole pair, else a partial
-// record (O, then m, then l) in slot `rec`.
-template <int D, int NC, bool kCausal, typename Cx>
-__device__ void finish_segment(const Cx& cx, const DecodeDims& d, const SegState<D> (&st)[NC],
-                               const Cursor& c, const Cols<NC>& cl, bool whole, int64_t rec,
-                               int lane) {
-  const int64_t r0 = pair_row<kCausal>(d, c);
-  const int32_t R = pair_rows<kCausal>(d);
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    if (!live<NC, kCausal>(cl, j, c)) continue;
-    const float l_tot = st[j].l[0];
-    if (whole) {
-      const float inv = d.v_scale / l_tot;
-      uint16_t* orow = cx.out + (r0 + cl.row[j]) * D + (lane >> 4) * 4;
-#pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt) {
-        bf16x4_t y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y[i] = static_cast<__bf16>(st[j].o[mt][i] * inv);
-        *reinterpret_cast<u32x2_t*>(orow + mt * 16) = __builtin_bit_cast(u32x2_t, y);
-      }
-    } else {
-      const int32_t n = j * 16 + (lane & 15);
-      float* base = cx.ws + rec * record_floats(R, D);
-      float* orow = base + n * D + (lane >> 4) * 4;
-#pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<f32x4_t*>(orow + mt * 16) = st[j].o[mt];
-      if (lane < 16) {
-        base[R * D + n] = st[j].m;
-        base[R * D + R + n] = l_tot;
-      }
-    }
-  }
-}
-
-// Decode with append: the pair's newest position (the one past its tiles) joins
-// the segment holding the pair's last tile, from k_new / v_new, the way
-// compute_tile treats a position: score in the log2 domain, the same lazy
-// rescaling, the weight rounded to bf16 for the weighted sum of values.  The
-// worker also writes the new rows into their slot (the caller has made the block
-// private, so no other worker reads it).  fp8 pools: the row is stored, and
-// attended to, as E4M3(x / scale).
-// This lane's parts of a pair's newest rows: the key dims of its score operand
-// and the value dims of its O entries (read ahead by fetch_new).
-template <int D>
-struct NewRow {
-  u32x4_t k[D / 32];
-  u32x2_t v[D / 16];
-};
-
-template <int D, bool kFp8, typename Cx>
-__device__ __forceinline__ void fetch_new(NewRow<D>& nr, const Cx& cx, const DecodeDims& d,
-                                          const Cursor& c, int lane) {
-  const int64_t row = (static_cast<int64_t>(c.s) * d.Hkv + c.g) * D;
-  const int gq = lane >> 4;
-#pragma unroll
-  for (int k = 0; k < D / 32; ++k) {
-    const int d0 = kFp8 ? (k / 2) * 64 + gq * 16 + (k % 2) * 8 : k * 32 + gq * 8;
-    nr.k[k] = *reinterpret_cast<const u32x4_t*>(cx.k_new + row + d0);
-  }
-#pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt)
-    nr.v[mt] = *reinterpret_cast<const u32x2_t*>(cx.v_new + row + mt * 16 + gq * 4);
-}
-
-template <int D, int B, bool kFp8, typename Cx>
-__device__ __forceinline__ void append_token(SegState<D>& st, const bf16x8_t (&qop)[D / 32],
-                                             const NewRow<D>& nr, const Cx& cx,
-                                             const DecodeDims& d, const Cursor& c, int lane) {
-  const int gq = lane >> 4;
-  const bool writer = (lane & 15) == 0;  // lanes 0, 16, 32, 48 cover every dim once
-  const int32_t p = c.L;                 // the tiles hold positions 0 .. p - 1
-  const int32_t b = clamp_block(cx.tables[static_cast<int64_t>(c.s) * d.M + p / B], d.NB);
-  const int32_t ob = p % B;
-  const int64_t tile = (static_cast<int64_t>(b) * d.Hkv + c.g) * D * B;  // elements
-  // score: this lane's query dims (the score MFMA operand layout) against the new key
-  float part = 0.f;
-#pragma unroll
-  for (int k = 0; k < D / 32; ++k) {
-    const int d0 = kFp8 ? (k / 2) * 64 + gq * 16 + (k % 2) * 8 : k * 32 + gq * 8;
-    const u32x4_t x = nr.k[k];
-    uint32_t w[4];
-    if constexpr (kFp8) {
-      const float ks = d.k_scale;
-      const uint32_t lo = e4m3x4(lo_bf16(x[0]) / ks, hi_bf16(x[0]) / ks, lo_bf16(x[1]) / ks,
-                                 hi_bf16(x[1]) / ks);
-      const uint32_t hi = e4m3x4(lo_bf16(x[2]) / ks, hi_bf16(x[2]) / ks, lo_bf16(x[3]) / ks,
-                                 hi_bf16(x[3]) / ks);
-      w[0] = e4m3x2_to_bf16x2<false>(lo);
-      w[1] = e4m3x2_to_bf16x2<true>(lo);
-      w[2] = e4m3x2_to_bf16x2<false>(hi);
-      w[3] = e4m3x2_to_bf16x2<true>(hi);
-      if (writer)
-        *reinterpret_cast<u32x2_t*>(cx.kw + tile + ((d0 / 16) * B + ob) * 16 + d0 % 16) =
-            u32x2_t{lo, hi};
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = x[e];
-      if (writer) *reinterpret_cast<u32x4_t*>(cx.kw + tile + ((d0 / 8) * B + ob) * 8) = x;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      part = fmaf(static_cast<float>(qop[k][2 * e]), lo_bf16(w[e]), part);
-      part = fmaf(static_cast<float>(qop[k][2 * e + 1]), hi_bf16(w[e]), part);
-    }
-  }
-  part += __shfl_xor(part, 16);
-  part += __shfl_xor(part, 32);
-  const float sc = part * d.c;
-  float x = sc - st.m;
-  if (x > kRescaleThreshold) {  // also when nothing has been seen (m = -inf)
-    const float alpha = __builtin_amdgcn_exp2f(st.m - sc);
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) st.o[mt] *= alpha;
-    st.l *= alpha;
-    st.m = sc;
-    x = 0.f;
-  }
-  const float wgt = static_cast<float>(static_cast<__bf16>(__builtin_amdgcn_exp2f(x)));
-  st.l += wgt;
-  constexpr int32_t kRun = B < kTile ? B : kTile;  // positions of one bf16 V run
-#pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt) {
-    const int d0 = mt * 16 + gq * 4;  // this lane's four dims of O
-    const u32x2_t vv = nr.v[mt];
-    uint32_t pair[2];
-    if constexpr (kFp8) {
-      const float vs = d.v_scale;
-      const uint32_t code = e4m3x4(lo_bf16(vv.x) / vs, hi_bf16(vv.x) / vs, lo_bf16(vv.y) / vs,
-                                   hi_bf16(vv.y) / vs);
-      pair[0] = e4m3x2_to_bf16x2<false>(code);
-      pair[1] = e4m3x2_to_bf16x2<true>(code);
-      if (writer) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int dd = d0 + i;
-          cx.vw[tile + ((dd % 16) * (B / 4) + ob / 4) * (D / 16) * 4 + (dd / 16) * 4 + ob % 4] =
-              static_cast<uint8_t>(code >> (8 * i));
-        }
-      }
-    } else {
-      pair[0] = vv.x;
-      pair[1] = vv.y;
-      if (writer) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          cx.vw[tile + ((ob / kRun) * D + d0 + i) * kRun + ob % kRun] =
-              static_cast<uint16_t>(pair[i / 2] >> (16 * (i % 2)));
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = (i % 2) ? hi_bf16(pair[i / 2]) : lo_bf16(pair[i / 2]);
-      st.o[mt][i] = fmaf(wgt, v, st.o[mt][i]);
-    }
-  }
-}
-
-// Decode with append, a sequence whose only position is the new one: every
-// query head's output is that position's value, and the rows go into slot 0.
-template <int D, int B, bool kFp8, typename Cx>
-__device__ void one_token(const Cx& cx, const DecodeDims& d, int64_t s, int lane) {
-  const int32_t b = clamp_block(cx.tables[s * d.M], d.NB);
-  constexpr int32_t kRun = B < kTile ? B : kTile;
-  for (int32_t e = lane; e < d.Hkv * D; e += kWave) {
-    const int32_t g = e / D, dd = e % D;
-    const int64_t tile = (static_cast<int64_t>(b) * d.Hkv + g) * D * B;
-    const uint16_t kx = cx.k_new[s * d.Hkv * D + e];
-    const uint16_t vx = cx.v_new[s * d.Hkv * D + e];
-    const float kf = __builtin_bit_cast(float, static_cast<uint32_t>(kx) << 16);
-    const float vf = __builtin_bit_cast(float, static_cast<uint32_t>(vx) << 16);
-    uint16_t outv = vx;
-    if constexpr (kFp8) {
-      const uint32_t kc = e4m3x4(kf / d.k_scale, 0.f, 0.f, 0.f) & 0xFFu;
-      const uint32_t vc = e4m3x4(vf / d.v_scale, 0.f, 0.f, 0.f) & 0xFFu;
-      cx.kw[tile + ((dd / 16) * B) * 16 + dd % 16] = static_cast<uint8_t>(kc);
-      cx.vw[tile + ((dd % 16) * (B / 4)) * (D / 16) * 4 + (dd / 16) * 4] = static_cast<uint8_t>(vc);
-      // softmax over one position: the output is the value, times the V scale
-      const float val = lo_bf16(e4m3x2_to_bf16x2<false>(vc)) * d.v_scale;
-      outv = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
-    } else {
-      cx.kw[tile + (dd / 8) * B * 8 + dd % 8] = kx;
-      cx.vw[tile + dd * kRun] = vx;
-    }
-    for (int32_t j = 0; j < d.G; ++j) cx.out[(s * d.Hq + g * d.G + j) * D + dd] = outv;
-  }
-}
-
-// One worker: the n tiles of its range in order, with loads running kPipe-1
-// tiles ahead of the arithmetic across (sequence, head) boundaries; the query of a
-// pair is fetched with the pair's first tile.  Returns the descriptor of the split
-// pair this worker opens (s = -1 if none).
-template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, typename Cx>
-__device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& pl, int64_t w,
-                           int lane) {
-  const int32_t cap = d.M * B;
-  const int32_t n = pl.n;
-  const Cols<NC> cl = make_cols<NC, kCausal>(d, lane);
-  Cursor lc;
-  lc.start = pl.start;
-  lc.s = pl.s;
-  lc.L = pl.L;
-  lc.Tq = pl.Tq;
-  lc.T = tiles_of(lc.L);
-  lc.g = pl.g;
-  lc.t = pl.t;
-  Cursor cc = lc;
-
-  constexpr int kPipe = pipe_depth<D, NC, kFp8>();
-  TileOf<D, B, kFp8> r[kPipe];
-  bf16x8_t qb[kPipe][NC][D / 32];
-  bf16x8_t qc[NC][D / 32];
-  SegState<D> st[NC];
-  int32_t lim_abs[NC];  // last position column j sees (multi-token launches)
-  int32_t seg_t0 = cc.t;
-  int64_t rec = 2 * w;  // first segment -> slot 0, later ones -> slot 1
-  int4 opened = {-1, 0, 0, 0};
-
-  // Decode with append: the newest rows of the pair whose last tile the next
-  // compute step takes, read before that step's tile loads are issued, so that
-  // waiting for them does not wait for the tiles loaded after.
-  NewRow<D> nr;
-  auto fetch_step = [&]() {
-    if constexpr (kAppend) {
-      if (cc.t == cc.T - 1) fetch_new<D, kFp8>(nr, cx, d, cc, lane);
-    }
-  };
-  auto load_step = [&](int slot, int32_t li) {
-    if (lc.t == 0 || li == 0) load_q<D, NC, kCausal, kFp8>(qb[slot], cx, d, lc, cl, lane);
-    load_at<D, B>(r[slot], cx, d, lc, lane);
-    advance<kCausal>(lc, cx, d, cap);
-  };
-  auto compute_step = [&](int slot, int32_t i) {
-    if (cc.t == 0 || i == 0) {
-#pragma unroll
-      for (int j = 0; j < NC; ++j) {
-#pragma unroll
-        for (int k = 0; k < D / 32; ++k) qc[j][k] = qb[slot][j][k];
-#pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt) st[j].o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        st[j].l = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        st[j].m = -INFINITY;
-        // query token qi sits at position L - Tq + qi; other columns see the context
-        lim_abs[j] = live<NC, kCausal>(cl, j, cc) ? cc.L - cc.Tq + cl.qi[j] : cc.L - 1;
-      }
-      seg_t0 = cc.t;
-    }
-    const int32_t valid = min(kTile, cc.L - cc.t * kTile);
-    if constexpr (kCausal) {
-      int32_t lim[NC];
-#pragma unroll
-      for (int j = 0; j < NC; ++j) lim[j] = lim_abs[j] - cc.t * kTile;
-      compute_tile<D, NC, true>(r[slot], qc, st, d.c, valid, cc.L - cc.Tq - cc.t * kTile, lim,
-                                lane);
-    } else {
-      const int32_t lim[NC] = {valid - 1};
-      compute_tile<D, NC, false>(r[slot], qc, st, d.c, valid, valid - 1, lim, lane);
-      if constexpr (kAppend) {
-        static_assert(NC == 1, "decode with append has one query row per head");
-        if (cc.t == cc.T - 1) append_token<D, B, kFp8>(st[0], qc[0], nr, cx, d, cc, lane);
-      }
-    }
-    if (cc.t == cc.T - 1 || i == n - 1) {
-      const bool whole = seg_t0 == 0 && cc.t == cc.T - 1;
-      finish_segment<D, NC, kCausal>(cx, d, st, cc, cl, whole, rec, lane);
-      if (!whole && seg_t0 == 0) {
-        // this worker holds the first share of a pair that later workers continue;
-        // the worker holding the pair's last tile closes it (worked out here, mid-
-        // stream, rather than after the last tile where it would lengthen the tail)
-        const int64_t last_unit = cc.start + static_cast<int64_t>(cc.g) * pair_units(cc.T, d) +
-                                  d.hdr + static_cast<int64_t>(d.unit) * (cc.T - 1);
-        const int32_t slot_tq = static_cast<int32_t>(rec - 2 * w) | (kCausal ? cc.Tq << 1 : 0);
-        opened = int4{cc.s, cc.g, static_cast<int32_t>(worker_of(last_unit, pl.U, pl.N)), slot_tq};
-      }
-      rec = 2 * w + 1;
-    }
-    advance<kCausal>(cc, cx, d, cap);
-  };
-
-#pragma unroll
-  for (int k = 0; k < kPipe - 1; ++k)
-    if (k < n) load_step(k, k);
-  int32_t i = 0;
-  // Whole groups of kPipe steps in which every step has a tile to load.
-  while (i + 2 * kPipe - 1 <= n) {
-#pragma unroll
-    for (int k = 0; k < kPipe; ++k) {
-      fetch_step();
-      load_step((k + kPipe - 1) % kPipe, i + k + kPipe - 1);
-      compute_step(k, i + k);
-    }
-    i += kPipe;
-  }
-  const int32_t rem = n - i;  // fewer than 2*kPipe-1 tiles left, kPipe-1 of them loading
-#pragma unroll
-  for (int k = 0; k < 2 * kPipe - 2; ++k) {
-    if (k < rem) {
-      fetch_step();
-      if (k + kPipe - 1 < rem) load_step((k + kPipe - 1) % kPipe, i + k + kPipe - 1);
-      compute_step(k % kPipe, i + k);
-    }
-  }
-  return opened;
-}
-
-// The decode kernel (NC = 1, no position mask) and the multi-token kernel.
-// Workspace: partial records ([n_workers][2] of record_floats), then one
-// descriptor per worker: (s, g, wb, first_slot | Tq << 1) of the split pair whose
-// first share this worker holds, or s = -1 (Tq only in multi-token launches).
-// fp8 single-tile launches cap registers for two waves per SIMD; decode with append
-// keeps one (its new-row arithmetic needs the room).
-template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend>
-__global__ __launch_bounds__(kWave* kWavesPerGroup,
-                             (kFp8 && NC == 1 && !kAppend) ? 2 : 1) void decode_kernel(
-    const uint16_t* __restrict__ q, const typename TileOf<D, B, kFp8>::Elem* __restrict__ k,
-    const typename TileOf<D, B, kFp8>::Elem* __restrict__ v,
-    const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
-    const int32_t* __restrict__ qlens, uint16_t* __restrict__ out, float* __restrict__ ws,
-    int4* __restrict__ desc, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, typename TileOf<D, B, kFp8>::Elem* kw,
-    typename TileOf<D, B, kFp8>::Elem* vw, DecodeDims d) {
-  const Ctx<typename TileOf<D, B, kFp8>::Elem> cx{q,  k,  v,     tables, lens, qlens, out,
-                                                  ws, k_new, v_new, kw,    vw};
-  const int lane = __lane_id();
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
-  if (w >= d.n_workers) return;
-  const int32_t cap = d.M * B;
-
-  int4 opened = {-1, 0, 0, 0};
-  WorkerPlan pl;
-  const bool has = d.pair_mode ? plan_pair<kCausal>(lens, qlens, d, cap, w, pl)
-                               : plan_worker<kCausal>(lens, qlens, d, cap, w, lane, pl);
-  if (has) opened = run_worker<D, B, NC, kCausal, kFp8, kAppend>(cx, d, pl, w, lane);
-
-  // Rows no tile reaches are zeros: every row of an empty sequence, and in a
-  // multi-token launch the rows past a sequence's query tokens (done last: off
-  // the path to the first loads).
-  const int32_t row_elems = d.Hq * D;
-  for (int64_t se = w; se < d.S; se += d.n_workers) {
-    int32_t first = 0;
-    if constexpr (kCausal) {
-      first = seq_len<true>(lens, qlens, d, cap, static_cast<int32_t>(se)).T;
-    } else {
-      const int32_t Lt = clamp_len(lens[se], cap);
-      if constexpr (kAppend) {
-        if (Lt == 1) one_token<D, B, kFp8>(cx, d, se, lane);
-      }
-      if (Lt != 0) continue;
-    }
-    const int32_t rows = kCausal ? d.Qc : 1;
-    for (int32_t qi = first; qi < rows; ++qi) {
-      uint16_t* row = out + (kCausal ? se * d.Qmax + qi : se) * row_elems;
-      for (int32_t e = lane * 8; e < row_elems; e += kWave * 8)
-        *reinterpret_cast<u32x4_t*>(row + e) = u32x4_t{0, 0, 0, 0};
-    }
-  }
-  if (!d.pair_mode && lane == 0) desc[w] = opened;
-}
-
-// Merge of split pairs.  Work-group b reads the descriptors of its slice of
-// workers in one parallel pass and keeps the valid ones in LDS (each names a split
-// pair opened by worker wa and closed by wb).  The (pair, output) items of those
-// pairs are spread over the threads, kItems per thread at a time; an item folds
-// the records of wa..wb in worker order with a running max, kChunk records per
-// batch, and the loads of all of a thread's items are issued together.  The order
-// is fixed, so the result does not depend on timing.  In multi-token launches the
-// rows past the pair's query tokens are left to the decode kernel.
-//
-// Two shapes (measured): pairs split over more than 12 workers take one item of
-// 16 records per batch (one round trip for a 16-way split); otherwise two items of
-// 12 records each, so that more independent loads are in flight.
-constexpr int kMergeThreads = 512;
-constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
-constexpr int kMergeWideSplit = 12;
-
-template <int D, bool kCausal, int kChunk, int kItems>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __restrict__ desc,
-                                                              uint16_t* __restrict__ out,
-                                                              const float* __restrict__ ws,
-                                                              DecodeDims d) {
-  __shared__ int4 s_desc[kMergeSlice];
-  __shared__ int32_t s_wa[kMergeSlice];
-  __shared__ int32_t s_count;
-  const int tid = threadIdx.x;
-  const int64_t per = (d.n_workers + gridDim.x - 1) / gridDim.x;
-  const int64_t w0 = static_cast<int64_t>(blockIdx.x) * per;
-  const int64_t w1 = min(w0 + per, static_cast<int64_t>(d.n_workers));
-  if (tid == 0) s_count = 0;
-  __syncthreads();
-  if (w0 + tid < w1) {
-    const int4 ds = desc[w0 + tid];
-    if (ds.x >= 0) {
-      const int32_t slot = atomicAdd(&s_count, 1);
-      s_desc[slot] = ds;
-      s_wa[slot] = static_cast<int32_t>(w0 + tid);
-    }
-  }
-  __syncthreads();
-  const int64_t rf = record_floats(d.R, D);
-  const int32_t RD = d.R * D;
-  const int32_t total = s_count * RD;
-  for (int32_t base = tid; base < total; base += kMergeThreads * kItems) {
-    float run_m[kItems], run_l[kItems], acc[kItems];
-    int64_t wa[kItems], wb[kItems], first[kItems];
-    int32_t pi[kItems], oi[kItems];
-    bool act[kItems];
-#pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-      const int32_t item = base + it * kMergeThreads;
-      run_m[it] = -INFINITY;
-      run_l[it] = 0.f;
-      acc[it] = 0.f;
-      pi[it] = item < total ? item / RD : 0;
-      oi[it] = item < total ? item - pi[it] * RD : 0;
-      act[it] = item < total;
-      if constexpr (kCausal) act[it] = act[it] && (oi[it] / D) / d.G < (s_desc[pi[it]].w >> 1);
-      wa[it] = s_wa[pi[it]];
-      wb[it] = act[it] ? static_cast<int64_t>(s_desc[pi[it]].z) : wa[it] - 1;  // none
-      first[it] = (2 * wa[it] + (s_desc[pi[it]].w & 1)) * rf;
-    }
-    int64_t kmax = 0;
-#pragma unroll
-    for (int it = 0; it < kItems; ++it) kmax = max(kmax, wb[it] - wa[it] + 1);
-    for (int64_t c = 0; c < kmax; c += kChunk) {
-      float m[kItems][kChunk], l[kItems][kChunk], o[kItems][kChunk];
-#pragma unroll
-      for (int it = 0; it < kItems; ++it) {
-        const int32_t h = oi[it] / D;
-#pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-          const int64_t wk = wa[it] + c + k;
-          if (wk <= wb[it]) {
-            const float* rec = ws + (c + k == 0 ? first[it] : 2 * wk * rf);
-            m[it][k] = rec[RD + h];
-            l[it][k] = rec[RD + d.R + h];
-            o[it][k] = rec[oi[it]];
-          } else {
-            m[it][k] = -INFINITY;
-            l[it][k] = 0.f;
-            o[it][k] = 0.f;
-          }
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < kItems; ++it) {
-        float cm = run_m[it];
-#pragma unroll
-        for (int k = 0; k < kChunk; ++k) cm = fmaxf(cm, m[it][k]);
-        if (cm == -INFINITY) continue;  // item past the end, or no record in this chunk
-        const float scale = __builtin_amdgcn_exp2f(run_m[it] - cm);
-        run_l[it] *= scale;
-        acc[it] *= scale;
-        run_m[it] = cm;
-#pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-          const float e = __builtin_amdgcn_exp2f(m[it][k] - cm);
-          run_l[it] += e * l[it][k];
-          acc[it] += e * o[it][k];
-        }
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-      if (act[it]) {
-        const int4 ds = s_desc[pi[it]];
-        int64_t idx;
-        if constexpr (kCausal) {
-          const int32_t row = oi[it] / D;  // row = qi * G + head
-          const int32_t qi = row / d.G;
-          idx = ((static_cast<int64_t>(ds.x) * d.Qmax + qi) * d.Hq + ds.y * d.G + (row - qi * d.G)) *
-                    D + (oi[it] - row * D);
-        } else {
-          idx = (static_cast<int64_t>(ds.x) * d.Hq + ds.y * d.G) * D + oi[it];
-        }
-        out[idx] = __builtin_bit_cast(uint16_t,
-                                      static_cast<__bf16>(acc[it] / run_l[it] * d.v_scale));
-      }
-    }
-  }
-}
-
-template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend>
-hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
-                    hipStream_t stream) {
-  using Elem = typename TileOf<D, B, kFp8>::Elem;
-  const int groups = (d.n_workers + kWavesPerGroup - 1) / kWavesPerGroup;
-  if (groups <= 0) return hipSuccess;
-  int4* desc = reinterpret_cast<int4*>(reinterpret_cast<char*>(b.ws) +
-                                       records_bytes(d.n_workers, d.R, D));
-  hipLaunchKernelGGL((decode_kernel<D, B, NC, kCausal, kFp8, kAppend>), dim3(groups),
-                     dim3(kWave * kWavesPerGroup), 0, stream, b.q, static_cast<const Elem*>(b.k),
-                     static_cast<const Elem*>(b.v), b.tables, b.lens, b.qlens, b.out, b.ws, desc,
-                     b.k_new, b.v_new, static_cast<Elem*>(b.kw), static_cast<Elem*>(b.vw), d);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  if (d.pair_mode) return hipSuccess;  // nothing is split: no merge
-  // records per split pair: about the workers per (sequence, KV head) pair
-  const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
-  if (pairs > 0 && d.n_workers > kMergeWideSplit * pairs)
-    hipLaunchKernelGGL((merge_kernel<D, kCausal, 16, 1>), dim3(merge_groups), dim3(kMergeThreads), 0,
-                       stream, desc, b.out, b.ws, d);
-  else
-    hipLaunchKernelGGL((merge_kernel<D, kCausal, 12, 2>), dim3(merge_groups), dim3(kMergeThreads), 0,
-                       stream, desc, b.out, b.ws, d);
-  return hipGetLastError();
-}
-
-template <int NC, bool kCausal, bool kFp8, bool kAppend = false>
-hipError_t dispatch(const DecodeBuffers& b, const DecodeDims& d, int D, int B, int merge_groups,
-                    hipStream_t stream) {
-  if (D == 128) {
-    if (B == 16) return launch_t<128, 16, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
-    if (B == 32) return launch_t<128, 32, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
-    if (B == 8) return launch_t<128, 8, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
-  } else if (D == 64) {
-    if (B == 16) return launch_t<64, 16, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
-    if (B == 32) return launch_t<64, 32, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
-    if (B == 8) return launch_t<64, 8, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
-  }
-  return hipErrorInvalidValue;
-}
-
-}  // namespace
 
 hipError_t launch_decode(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                          int merge_groups, hipStream_t stream) {
   return dispatch<1, false, false>(b, d, D, B, merge_groups, stream);
-}
-
-hipError_t launch_decode_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                             int merge_groups, hipStream_t stream) {
-  return dispatch<1, false, true>(b, d, D, B, merge_groups, stream);
-}
-
-hipError_t launch_decode_append(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                                int merge_groups, hipStream_t stream, bool fp8) {
-  return fp8 ? dispatch<1, false, true, true>(b, d, D, B, merge_groups, stream)
-             : dispatch<1, false, false, true>(b, d, D, B, merge_groups, stream);
-}
-
-hipError_t launch_multi(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                        int merge_groups, hipStream_t stream, bool fp8) {
-  if (fp8) {
-    if (d.R <= 16) return dispatch<1, true, true>(b, d, D, B, merge_groups, stream);
-    if (d.R <= kMaxRows) return dispatch<2, true, true>(b, d, D, B, merge_groups, stream);
-    return hipErrorInvalidValue;
-  }
-  if (d.R <= 16) return dispatch<1, true, false>(b, d, D, B, merge_groups, stream);
-  if (d.R <= kMaxRows) return dispatch<2, true, false>(b, d, D, B, merge_groups, stream);
-  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

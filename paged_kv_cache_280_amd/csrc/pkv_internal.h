@@ -76,13 +76,15 @@ inline int64_t workspace_bytes_for(int64_t workers, int R, int D) {
 // Rows one multi-token launch can hold: two 16-column MFMA tiles per wave.
 constexpr int kMaxRows = 32;
 
-// Launch the decode kernel and the merge kernel (pkv_decode.hip).  Return a
-// hipError_t.  launch_multi takes a multi-token launch (d.R <= kMaxRows) over bf16 or
-// fp8 pools.
+// Launch the decode kernel and the merge kernel (kernels in pkv_decode_kernels.h,
+// launches in pkv_decode*.hip).  Return a hipError_t.  launch_multi takes a
+// multi-token launch (d.R <= kMaxRows) over bf16 or fp8 pools (fp8: launch_multi_fp8).
 hipError_t launch_decode(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                          int merge_groups, hipStream_t stream);
 hipError_t launch_multi(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                         int merge_groups, hipStream_t stream, bool fp8);
+hipError_t launch_multi_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                            int merge_groups, hipStream_t stream);
 // Decode over fp8 (E4M3FN) pools: d.c carries scale * k_scale * log2(e), d.v_scale
 // the V pool's scale.
 hipError_t launch_decode_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
