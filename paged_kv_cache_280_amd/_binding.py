@@ -44,6 +44,11 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError("libpkv.so is not built (%s); run `python -m paged_kv_cache_280_amd.build`"
                            % path)
+    # torch ships its own HIP runtime: load it first, so that the library binds to
+    # the runtime that owns torch's device memory and streams (loaded alone, the
+    # library would bind to the system runtime and fail to query the device)
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.pkv_abi_version.argtypes = []
