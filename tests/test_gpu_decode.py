@@ -209,9 +209,10 @@ def _device_case_vs_oracle(case, seqs=None, label=""):
     return errors(got[seqs], ref)
 
 
-def test_long_context_one_layer_full_size():
-    case = wl.case_long(0, num_layers=1)
-    _device_case_vs_oracle(case, label="long 8x16000")
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_long_context_one_layer_full_size(B):
+    case = wl.case_long(0, num_layers=1, block_size=B)
+    _device_case_vs_oracle(case, label="long 8x16000 B=%d" % B)
 
 
 @pytest.mark.parametrize("B", [8, 16, 32])

@@ -93,6 +93,36 @@ def test_fp8_long_context_full_size_sampled():
         assert_parity(got[s:s + 1], ref, "fp8 long seq %d" % s)
 
 
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_fp8_mix_sampled(B):
+    """The continuous-batching mix (256 sequences, 13 at 32,768 positions, GQA 64/8,
+    churned free list) over fp8 pools in a reduced 6 GB pool budget; two long and
+    twelve short sequences are checked against the oracle on their gathered blocks."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    case = wl.case_mix(3, B, pool_bytes=6e9)
+    dev = torch.device("cuda:0")
+    ks, vs = 1 / 16, 1 / 16
+    k8, v8 = wl.device_pools_fp8(case, dev, ks, vs)
+    q = wl.randn_bf16(np.random.default_rng(3 + B), (case.num_seqs, case.num_q_heads, case.head_dim))
+    out = pkv.paged_attn_decode_fp8(to_dev_bf16(q), k8, v8, to_dev_i32(case.block_tables),
+                                    to_dev_i32(case.context_lens), B, case.scale, ks, vs,
+                                    max_context_len=case.max_context_len)
+    torch.cuda.synchronize()
+    got = bf16_to_f32(out)
+    lens = case.context_lens
+    seqs = np.concatenate([np.nonzero(lens == 32768)[0][:2], np.nonzero(lens != 32768)[0][:12]])
+    for s in seqs:
+        nb = -(-int(lens[s]) // B)
+        idx = torch.from_numpy(case.block_tables[s, :nb].astype(np.int64)).to(dev)
+        kh, vh = k8[idx].cpu().numpy(), v8[idx].cpu().numpy()
+        ref = oracle.paged_decode_fp8(q[s:s + 1], kh, vh, np.arange(nb, dtype=np.int32)[None],
+                                      lens[s:s + 1], B, case.scale, ks, vs, case.num_kv_heads)
+        assert_parity(got[s:s + 1], ref, "fp8 mix B=%d seq %d (L=%d)" % (B, s, lens[s]))
+
+
 def test_copy_blocks_on_fp8_pools_is_bit_exact():
     import torch
 
