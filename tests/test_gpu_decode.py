@@ -33,13 +33,13 @@ def test_tiny_config(seed):
     assert_parity(got, oracle_out(case, q, kp, vp), "tiny seed %d" % seed)
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_chat_config(seed):
-    case = wl.case_chat(seed)
+@pytest.mark.parametrize("seed,B", [(0, 16), (1, 16), (2, 16), (0, 8), (0, 32)])
+def test_chat_config(seed, B):
+    case = wl.case_chat(seed, block_size=B)
     q = wl.host_q(case)
     kp, vp = wl.host_pools(case)
     got = bf16_to_f32(run_gpu(case, q, kp, vp))
-    assert_parity(got, oracle_out(case, q, kp, vp), "chat seed %d" % seed)
+    assert_parity(got, oracle_out(case, q, kp, vp), "chat seed %d B=%d" % (seed, B))
 
 
 SHAPES = [(D, B, G) for D in (64, 128) for B in (8, 16, 32) for G in (1, 4, 8, 16)]
