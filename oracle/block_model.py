@@ -33,6 +33,15 @@ join the cache (each unless its key is already there); a cached block whose last
 stays findable, and is handed out for new contents only when the free list is
 empty, least recently released first (its cache entry is then dropped); a
 finished sequence releases its blocks last to first.
+
+Copy batches (reading): the copies queued between two take_copies calls are run
+together, before the tokens of that batch are written, so within a batch no
+block may be both a copy's destination and another copy's source, and no two
+copies may share a destination.  Until the batch is taken, a block named by a
+queued copy is not handed out again (one released meanwhile waits and joins the
+free list when the batch is taken, in release order); a copy out of a block that
+is itself a queued destination copies that destination's source (the same bytes
+once the batch has run).
 """
 
 from __future__ import annotations
@@ -55,6 +64,9 @@ class BlockModel:
         self.tables = {}   # seq id -> list of physical block ids
         self.lens = {}     # seq id -> number of tokens
         self.copies = []   # (src, dst) pairs emitted by copy-on-write, in order
+        self.pinned = set()  # blocks named by a queued copy
+        self.waiting = []    # blocks released while pinned, in release order
+        self.source_of = {}  # queued destination -> its source
         self.cached = {}     # tuple of tokens 0 .. end of block -> block id
         self.key_of = {}     # block id -> its key in self.cached
         self.evictable = []  # cached blocks nobody holds, least recently released first
@@ -72,10 +84,16 @@ class BlockModel:
     def _release(self, b: int) -> None:
         self.refcount[b] -= 1
         if self.refcount[b] == 0:
-            if b in self.key_of:
-                self.evictable.append(b)
+            if b in self.pinned:
+                self.waiting.append(b)
             else:
-                self.free.append(b)
+                self._to_free_list(b)
+
+    def _to_free_list(self, b: int) -> None:
+        if b in self.key_of:
+            self.evictable.append(b)
+        else:
+            self.free.append(b)
 
     def available(self) -> int:
         return len(self.free) + len(self.evictable)
@@ -139,10 +157,14 @@ class BlockModel:
         if need > self.available():
             raise PoolExhausted("need %d blocks, %d free" % (need, self.available()))
         if last_shared:
-            src = table[-1]
+            shared = table[-1]
             dst = self._take()
+            src = self.source_of.get(shared, shared)
             self.copies.append((src, dst))
-            self.refcount[src] -= 1   # still >= 1: another sharer holds it
+            self.source_of[dst] = src
+            self.pinned.add(src)
+            self.pinned.add(dst)
+            self.refcount[shared] -= 1   # still >= 1: another sharer holds it
             table[-1] = dst
         for _ in range(new_blocks):
             table.append(self._take())
@@ -164,6 +186,17 @@ class BlockModel:
             self._release(b)
         del self.lens[seq]
 
+    def take_copies(self) -> list:
+        """The queued copies, in order; the batch is over: blocks that waited join
+        the free list."""
+        copies, self.copies = self.copies, []
+        self.pinned = set()
+        self.source_of = {}
+        waiting, self.waiting = self.waiting, []
+        for b in waiting:
+            self._to_free_list(b)
+        return copies
+
     # -- views -------------------------------------------------------------------
     def check_conservation(self) -> None:
         counted = [0] * self.num_blocks
@@ -172,9 +205,9 @@ class BlockModel:
                 counted[b] += 1
         assert counted == self.refcount, "refcounts disagree with the tables"
         live = sum(1 for c in self.refcount if c > 0)
-        assert live + len(self.free) + len(self.evictable) == self.num_blocks, \
-            "free + evictable + live != pool"
-        idle = self.free + self.evictable
+        assert live + len(self.free) + len(self.evictable) + len(self.waiting) == self.num_blocks, \
+            "free + evictable + waiting + live != pool"
+        idle = self.free + self.evictable + self.waiting
         assert len(set(idle)) == len(idle), "a block is free twice"
         assert all(self.refcount[b] == 0 for b in idle), "a free block is referenced"
         assert all(b in self.key_of for b in self.evictable), "an evictable block has no key"

@@ -30,6 +30,13 @@ finishes leaves its blocks at the top for the next admission).  Copy-on-write
 decisions are recorded as (src, dst) pairs and handed to the GPU copy_blocks
 call in one batch before the tokens are written.  A refused request changes
 nothing.
+
+A batch of copies runs as one copy_blocks call, whose pairs must have distinct
+destinations that are not also sources.  So until take_copies hands the batch
+over, every block a pending pair names stays out of circulation: a freed source
+or destination is held back and joins the free list when the batch is taken, and
+a copy whose source is itself a pending destination reads that destination's own
+source instead (the bytes the destination will hold once the batch has run).
 """
 
 from __future__ import annotations
@@ -61,6 +68,9 @@ class BlockManager:
         self._tables: dict = {}
         self._lens: dict = {}
         self._copies: list = []
+        self._pins: dict = {}                   # block -> pending pairs naming it
+        self._held: list = []                   # released while pinned, in release order
+        self._src_of: dict = {}                 # pending destination -> its source
         self._cache: dict = {}                  # chain key -> block id
         self._key_of: dict = {}                 # block id -> chain key
         self._evictable: OrderedDict = OrderedDict()  # released cached blocks, oldest first
@@ -93,11 +103,17 @@ class BlockManager:
         for b in ids:
             self.refcount[b] -= 1
             if self.refcount[b] == 0:
-                if b in self._key_of:
-                    self._evictable[int(b)] = None
+                if int(b) in self._pins:
+                    self._held.append(int(b))
                 else:
-                    self._stack[self._top] = b
-                    self._top += 1
+                    self._recycle(int(b))
+
+    def _recycle(self, b: int) -> None:
+        if b in self._key_of:
+            self._evictable[b] = None
+        else:
+            self._stack[self._top] = b
+            self._top += 1
 
     @staticmethod
     def _chain(prev: bytes, block_tokens) -> bytes:
@@ -161,10 +177,15 @@ class BlockManager:
         if grow + cow > self.num_free:
             raise PoolExhausted("need %d blocks, %d free" % (grow + cow, self.num_free))
         if cow:
-            src = table[-1]
+            shared = table[-1]
             dst = int(self._take(1)[0])
-            self.refcount[src] -= 1          # the other sharers keep it
-            self._copies.append((int(src), dst))
+            self.refcount[shared] -= 1       # the other sharers keep it
+            # a pending destination holds its source's bytes once the batch has run
+            src = self._src_of.get(int(shared), int(shared))
+            self._copies.append((src, dst))
+            self._src_of[dst] = src
+            for b in (src, dst):
+                self._pins[b] = self._pins.get(b, 0) + 1
             table[-1] = dst
         if grow > 0:
             table.extend(int(b) for b in self._take(grow))
@@ -189,9 +210,17 @@ class BlockManager:
 
     # -- views handed to the GPU calls --------------------------------------------
     def take_copies(self) -> np.ndarray:
-        """Pending copy-on-write pairs as int32 [P][2] (src, dst); clears the queue."""
+        """Pending copy-on-write pairs as int32 [P][2] (src, dst); clears the queue.
+        Destinations are distinct and none is a source, so the pairs may be copied
+        in any order.  Blocks released while the batch was pending join the free
+        list now, in the order they were released."""
         pairs = np.asarray(self._copies, dtype=np.int32).reshape(-1, 2)
         self._copies = []
+        self._pins = {}
+        self._src_of = {}
+        held, self._held = self._held, []
+        for b in held:
+            self._recycle(b)
         return pairs
 
     def table(self, seq) -> list:

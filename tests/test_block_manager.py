@@ -118,8 +118,7 @@ def test_matches_the_oracle_model_on_random_scripts(seed):
                 else:
                     bm.append(s, n)
         same_state(bm, model)
-        assert bm.take_copies().tolist() == [list(p) for p in model.copies]
-        model.copies = []
+        assert bm.take_copies().tolist() == [list(p) for p in model.take_copies()]
 
 
 def test_batch_view():
@@ -223,8 +222,7 @@ def test_prefix_cache_matches_the_oracle_model_on_random_scripts(seed):
                 else:
                     bm.append(s, n)
         same_state(bm, model)
-        assert bm.take_copies().tolist() == [list(p) for p in model.copies]
-        model.copies = []
+        assert bm.take_copies().tolist() == [list(p) for p in model.take_copies()]
 
 
 def test_beam_search_forks_and_frees_keep_the_pool_exact():
@@ -258,7 +256,144 @@ def test_beam_search_forks_and_frees_keep_the_pool_exact():
             model.append(child, 1)
         beams = survivors
         same_state(bm, model)
-        assert bm.take_copies().tolist() == [list(p) for p in model.copies]
-        model.copies = []
+        assert bm.take_copies().tolist() == [list(p) for p in model.take_copies()]
     # beams share every full block of the prompt; their last blocks are private
     assert len({bm.table(b)[-1] for b in beams}) == 4
+
+
+# ---------------------------------------------------------------------------
+# One copy batch across several operations
+# ---------------------------------------------------------------------------
+
+def _valid_batch(pairs):
+    dst = [int(d) for _, d in pairs]
+    src = {int(s) for s, _ in pairs}
+    return len(set(dst)) == len(dst) and not (set(dst) & src)
+
+
+def test_a_source_freed_before_the_batch_is_taken_is_not_a_later_destination():
+    """A copies shared X into Y, B (the other holder of X) is freed, C copies its
+    shared Z: X must not come back as C's destination while the copy out of X is
+    still queued (troisinh.com, "Copy-on-Write cho Beam Search": the copy happens
+    before the sharer writes)."""
+    B = 16
+    order = np.arange(40)
+    bm, model = BlockManager(40, B, order), BlockModel(40, B, order)
+    for m, free in ((bm, bm.free), (model, model.free_seq)):
+        m.add("x", 20)
+        m.fork("x", "a")
+        m.fork("x", "b")
+        free("x")                       # X = last block of a and b
+        m.add("z", 20)
+        m.fork("z", "c")
+        m.fork("z", "d")
+        free("z")
+    X, Z = bm.table("a")[-1], bm.table("c")[-1]
+    for m, free in ((bm, bm.free), (model, model.free_seq)):
+        m.append("a", 1)                # copies X
+        free("b")                       # X's last holder leaves
+        m.append("c", 1)                # copies Z: X must not be the destination
+    same_state(bm, model)
+    pairs = bm.take_copies()
+    assert pairs.tolist() == [list(p) for p in model.take_copies()]
+    assert pairs[0, 0] == X and pairs[1, 0] == Z and _valid_batch(pairs)
+    assert X in bm.free_ids().tolist()  # released once the batch was taken
+    same_state(bm, model)
+
+
+def test_a_copy_out_of_a_queued_destination_reads_its_source():
+    B = 8
+    bm, model = BlockManager(30, B), BlockModel(30, B)
+    for m in (bm, model):
+        m.add("p", 5)
+        m.fork("p", "a")
+        m.append("a", 1)                # X -> Y, a now holds Y
+        m.fork("a", "c")                # Y shared by a and c
+        m.append("c", 1)                # Y -> W: W must receive X's bytes
+    pairs = bm.take_copies()
+    assert pairs.tolist() == [list(p) for p in model.take_copies()]
+    X = bm.table("p")[-1]
+    assert pairs.tolist() == [[X, pairs[0, 1]], [X, pairs[1, 1]]] and _valid_batch(pairs)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_copy_batches_spanning_many_operations_keep_every_sequence_s_tokens(seed):
+    """Random scripts that take the copy batch only every few operations (frees,
+    admissions and appends in between), as a serving loop does once per step.
+    Every block holds token ids; each batch is applied the way one copy_blocks
+    call runs it (all sources read, then all destinations written), then the
+    batch's new tokens are written into their slots (those of a sequence freed
+    in the meantime are not).  After every batch, each
+    live sequence must read back its own tokens through its table, and the host
+    state must equal the plain model's."""
+    rng = np.random.default_rng(500 + seed)
+    nb, B = 160, int(rng.choice([8, 16, 32]))
+    order = rng.permutation(nb)
+    bm, model = BlockManager(nb, B, order), BlockModel(nb, B, order)
+    content = np.full((nb, B), -1, np.int64)
+    tokens = {}                           # sequence -> its token ids
+    writes = []                           # (sequence, block, slot, token) of the batch
+    live, next_id, next_tok = [], 0, 0
+
+    def flush():
+        pairs = bm.take_copies()
+        assert pairs.tolist() == [list(p) for p in model.take_copies()]
+        assert _valid_batch(pairs)
+        if len(pairs):
+            content[pairs[:, 1]] = content[pairs[:, 0]].copy()
+        for _, b, o, t in writes:
+            content[b, o] = t
+        writes.clear()
+        for s in live:
+            tab = bm.table(s)
+            got = [content[tab[t // B], t % B] for t in range(len(tokens[s]))]
+            assert got == tokens[s], s
+
+    for step in range(300):
+        op = rng.choice(["add", "append", "fork", "free"], p=[0.2, 0.5, 0.15, 0.15])
+        if op == "fork" and live:
+            flush()                       # a fork copies a sequence's written tokens
+        try:
+            if op == "add" or not live:
+                n = int(rng.integers(0, 3 * B))
+                model.add(next_id, n)
+                bm.add(next_id, n)
+                toks = list(range(next_tok, next_tok + n))
+                next_tok += n
+                tab = bm.table(next_id)
+                writes.extend((next_id, tab[t // B], t % B, toks[t]) for t in range(n))
+                tokens[next_id] = toks
+                live.append(next_id)
+                next_id += 1
+            elif op == "append":
+                s = live[int(rng.integers(len(live)))]
+                n = int(rng.integers(0, B + 3))
+                model.append(s, n)
+                slots = bm.append(s, n)
+                toks = list(range(next_tok, next_tok + n))
+                next_tok += n
+                writes.extend((s, b, o, t) for (b, o), t in zip(slots, toks))
+                tokens[s] = tokens[s] + toks
+            elif op == "fork":
+                s = live[int(rng.integers(len(live)))]
+                model.fork(s, next_id)
+                bm.fork(s, next_id)
+                tokens[next_id] = list(tokens[s])
+                live.append(next_id)
+                next_id += 1
+            else:
+                s = live.pop(int(rng.integers(len(live))))
+                model.free_seq(s)
+                bm.free(s)
+                del tokens[s]
+                writes[:] = [w for w in writes if w[0] != s]   # never written
+        except ModelExhausted:
+            with pytest.raises(PoolExhausted):
+                if op == "add" or not live:
+                    bm.add(next_id, n)
+                else:
+                    bm.append(s, n)
+        same_state(bm, model)
+        if rng.random() < 0.2:
+            flush()
+    flush()

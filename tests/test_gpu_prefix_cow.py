@@ -105,7 +105,7 @@ def test_shared_prefix_sampling_end_to_end(prefix, expect_copies):
     bm, seqs, tail_slots, prefix_tables = _run_script(sc, BlockManager)
     model, _, model_slots, _ = _run_script(sc, BlockModel)
     pairs = bm.take_copies()
-    assert pairs.tolist() == [list(p) for p in model.copies]       # host logic bit-exact
+    assert pairs.tolist() == [list(p) for p in model.take_copies()]  # host logic bit-exact
     assert tail_slots == model_slots
     assert (len(pairs) > 0) == expect_copies
     if expect_copies:   # 7 of every 8 samples with a non-empty tail copy the shared block
