@@ -816,9 +816,14 @@ __device__ __forceinline__ void append_token(SegState<D>& st, const bf16x8_t (&q
                                              const NewRow<D>& nr, const Cx& cx,
                                              const DecodeDims& d, const Cursor& c, int lane) {
   const int gq = lane >> 4;
-  const bool writer = (lane & 15) == 0;  // lanes 0, 16, 32, 48 cover every dim once
   const int32_t p = c.L;                 // the tiles hold positions 0 .. p - 1
-  const int32_t b = clamp_block(cx.tables[static_cast<int64_t>(c.s) * d.M + p / B], d.NB);
+  // A table entry outside the pool names no slot: the rows are attended to but not
+  // stored (the append kernel skips such a token the same way), so a broken entry
+  // never overwrites a block of another sequence.
+  const int32_t raw = cx.tables[static_cast<int64_t>(c.s) * d.M + p / B];
+  const bool in_pool = raw >= 0 && raw < d.NB;
+  const int32_t b = in_pool ? raw : 0;
+  const bool writer = in_pool && (lane & 15) == 0;  // lanes 0, 16, 32, 48 cover every dim once
   const int32_t ob = p % B;
   const int64_t tile = (static_cast<int64_t>(b) * d.Hkv + c.g) * D * B;  // elements
   // score: this lane's query dims (the score MFMA operand layout) against the new key
@@ -905,10 +910,13 @@ __device__ __forceinline__ void append_token(SegState<D>& st, const bf16x8_t (&q
 }
 
 // Decode with append, a sequence whose only position is the new one: every
-// query head's output is that position's value, and the rows go into slot 0.
+// query head's output is that position's value, and the rows go into slot 0 (not
+// stored when the table entry lies outside the pool, as in append_token).
 template <int D, int B, bool kFp8, typename Cx>
 __device__ void one_token(const Cx& cx, const DecodeDims& d, int64_t s, int lane) {
-  const int32_t b = clamp_block(cx.tables[s * d.M], d.NB);
+  const int32_t raw = cx.tables[s * d.M];
+  const bool in_pool = raw >= 0 && raw < d.NB;
+  const int32_t b = in_pool ? raw : 0;
   constexpr int32_t kRun = B < kTile ? B : kTile;
   for (int32_t e = lane; e < d.Hkv * D; e += kWave) {
     const int32_t g = e / D, dd = e % D;
@@ -921,12 +929,15 @@ __device__ void one_token(const Cx& cx, const DecodeDims& d, int64_t s, int lane
     if constexpr (kFp8) {
       const uint32_t kc = e4m3x4(kf / d.k_scale, 0.f, 0.f, 0.f) & 0xFFu;
       const uint32_t vc = e4m3x4(vf / d.v_scale, 0.f, 0.f, 0.f) & 0xFFu;
-      cx.kw[tile + ((dd / 16) * B) * 16 + dd % 16] = static_cast<uint8_t>(kc);
-      cx.vw[tile + ((dd % 16) * (B / 4)) * (D / 16) * 4 + (dd / 16) * 4] = static_cast<uint8_t>(vc);
+      if (in_pool) {
+        cx.kw[tile + ((dd / 16) * B) * 16 + dd % 16] = static_cast<uint8_t>(kc);
+        cx.vw[tile + ((dd % 16) * (B / 4)) * (D / 16) * 4 + (dd / 16) * 4] =
+            static_cast<uint8_t>(vc);
+      }
       // softmax over one position: the output is the value, times the V scale
       const float val = lo_bf16(e4m3x2_to_bf16x2<false>(vc)) * d.v_scale;
       outv = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
-    } else {
+    } else if (in_pool) {
       cx.kw[tile + (dd / 8) * B * 8 + dd % 8] = kx;
       cx.vw[tile + dd * kRun] = vx;
     }

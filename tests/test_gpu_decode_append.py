@@ -174,3 +174,116 @@ def test_decode_append_with_more_pairs_than_workers():
                                 max_context_len=int(lens.max()))
     torch.cuda.synchronize()
     assert np.array_equal(bf16_to_f32(sep).view(np.uint32), got.view(np.uint32))
+
+
+def _bad_entry_case(seed, lens, Hq=16, Hkv=4):
+    """A batch whose tables name blocks outside the pool for some sequences'
+    newest positions (and the only block of a one-position sequence)."""
+    lens = np.asarray(lens, np.int32)
+    case = wl.case_random(seed, len(lens), Hq, Hkv, 128, 16, lens)
+    tables = case.block_tables.copy()
+    NB = case.num_blocks
+    bad = {1: NB + 5, 2: -3, 4: NB}
+    for s, b in bad.items():
+        tables[s, (int(lens[s]) - 1) // 16] = b
+    return case, tables, sorted(bad)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_a_table_entry_outside_the_pool_is_never_written(fp8):
+    """Decode with append where some newest positions map to no block of the pool:
+    the fused call writes nothing for them, exactly as kv_append skips such tokens,
+    so the pools after the fused call, after kv_append + decode on the GPU and after
+    the oracle's append are the same bytes; the other sequences' outputs stay at
+    parity."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    lens = [300, 17, 1, 48, 1000, 5, 1, 33]
+    case, tables, bad = _bad_entry_case(14, lens)
+    lens = case.context_lens
+    S, H, D, B = case.num_seqs, case.num_kv_heads, case.head_dim, case.block_size
+    rng = np.random.default_rng(15)
+    q = wl.host_q(case)
+    kn = wl.randn_bf16(rng, (S, H, D))
+    vn = wl.randn_bf16(rng, (S, H, D))
+    ks = vs = 0.05
+    if fp8:
+        kp, vp = wl.host_pools_fp8(case, ks, vs)
+        dev = _u8
+        sc = dict(k_scale=ks, v_scale=vs)
+    else:
+        kp, vp = wl.host_pools(case)
+        dev = to_dev_bf16
+        sc = {}
+    tabs, ld = to_dev_i32(tables), to_dev_i32(lens)
+    qd, knd, vnd = to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn)
+    k1, v1 = dev(kp), dev(vp)
+    print("bad entries fused fp8=%s" % fp8, flush=True)
+    fused = pkv.paged_attn_decode_append(qd, knd, vnd, k1, v1, tabs, ld, B, case.scale,
+                                         max_context_len=int(lens.max()), **sc)
+    k2, v2 = dev(kp), dev(vp)
+    seq_d = to_dev_i32(np.arange(S, dtype=np.int32))
+    if fp8:
+        pkv.kv_append_fp8(knd, vnd, k2, v2, tabs, seq_d, to_dev_i32(lens - 1), B, ks, vs)
+        sep = pkv.paged_attn_decode_fp8(qd, k2, v2, tabs, ld, B, case.scale, ks, vs,
+                                        max_context_len=int(lens.max()))
+    else:
+        pkv.kv_append(knd, vnd, k2, v2, tabs, seq_d, to_dev_i32(lens - 1), B)
+        sep = pkv.paged_attn_decode(qd, k2, v2, tabs, ld, B, case.scale,
+                                    max_context_len=int(lens.max()))
+    torch.cuda.synchronize()
+    seq = np.arange(S, dtype=np.int32)
+    if fp8:
+        oracle.kv_append_fp8(kn, vn, kp, vp, tables, seq, (lens - 1).astype(np.int32), B, ks, vs)
+    else:
+        oracle.kv_append(kn, vn, kp, vp, tables, seq, (lens - 1).astype(np.int32), B)
+    host = (lambda t: t.cpu().numpy()) if fp8 else _u16
+    for a, b, want in ((k1, k2, kp), (v1, v2, vp)):
+        assert np.array_equal(host(a), want) and np.array_equal(host(b), want)
+    good = np.array([s for s in range(S) if s not in bad])
+    if fp8:
+        ref = oracle.paged_decode_fp8(q[good], kp, vp, tables[good], lens[good], B, case.scale,
+                                      ks, vs, H)
+    else:
+        ref = oracle.paged_decode(q[good], kp, vp, tables[good], lens[good], B, case.scale, H)
+    assert_parity(bf16_to_f32(fused)[good], ref, "fused, good sequences")
+    assert_parity(bf16_to_f32(sep)[good], ref, "separate, good sequences")
+
+
+def test_a_table_entry_outside_the_pool_with_more_pairs_than_workers():
+    """The two-launch form (append kernel, then decode) with broken entries: the
+    pools and every output (the broken sequences' too) equal kv_append followed by
+    paged_attn_decode bit for bit."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    rng = np.random.default_rng(16)
+    lens = rng.integers(1, 600, 200).astype(np.int32)
+    lens[:3] = [1, 16, 17]
+    case, tables, bad = _bad_entry_case(45, lens, Hq=64, Hkv=8)
+    S, H, D, B = case.num_seqs, case.num_kv_heads, case.head_dim, case.block_size
+    q = wl.host_q(case)
+    kp, vp = wl.host_pools(case)
+    kn = wl.randn_bf16(rng, (S, H, D))
+    vn = wl.randn_bf16(rng, (S, H, D))
+    tabs, ld = to_dev_i32(tables), to_dev_i32(lens)
+    qd, knd, vnd = to_dev_bf16(q), to_dev_bf16(kn), to_dev_bf16(vn)
+    k1, v1 = to_dev_bf16(kp), to_dev_bf16(vp)
+    print("bad entries two-launch", flush=True)
+    got = pkv.paged_attn_decode_append(qd, knd, vnd, k1, v1, tabs, ld, B, case.scale,
+                                       max_context_len=int(lens.max()))
+    k2, v2 = to_dev_bf16(kp), to_dev_bf16(vp)
+    pkv.kv_append(knd, vnd, k2, v2, tabs, to_dev_i32(np.arange(S, dtype=np.int32)),
+                  to_dev_i32(lens - 1), B)
+    sep = pkv.paged_attn_decode(qd, k2, v2, tabs, ld, B, case.scale,
+                                max_context_len=int(lens.max()))
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+    assert torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+    assert torch.equal(got.view(torch.int16), sep.view(torch.int16))
+    oracle.kv_append(kn, vn, kp, vp, tables, np.arange(S, dtype=np.int32),
+                     (lens - 1).astype(np.int32), B)
+    assert np.array_equal(_u16(k1), kp) and np.array_equal(_u16(v1), vp)
