@@ -109,6 +109,23 @@ def _stream_handle(tensor, stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(tensor, stream):
+    """Context for one call: tensor's device current, and the stream the kernels
+    run on (``stream``, default torch's current one) current too, so that any
+    temporary the call allocates (workspace, output) belongs to that stream in
+    torch's caching allocator and is not handed to other work while the kernels
+    still use it."""
+    import contextlib
+
+    import torch
+
+    ctx = contextlib.ExitStack()
+    ctx.enter_context(torch.cuda.device(tensor.device))
+    if stream is not None:
+        ctx.enter_context(torch.cuda.stream(stream))
+    return ctx
+
+
 def _check(cond, msg):
     if not cond:
         raise ValueError(msg)
@@ -181,7 +198,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
                                          block_size)
     if max_context_len is None:
         max_context_len = M * int(block_size)
-    with torch.cuda.device(q.device):
+    with _on_stream(q, stream):
         if out is None:
             out = torch.empty_like(q)
         _check(out.shape == q.shape and out.dtype == torch.bfloat16 and out.is_contiguous()
@@ -232,7 +249,7 @@ def paged_attn_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, block
     M = int(block_tables.shape[1])
     if max_context_len is None:
         max_context_len = M * B
-    with torch.cuda.device(q.device):
+    with _on_stream(q, stream):
         if out is None:
             out = torch.empty_like(q)
         _check(out.shape == q.shape and out.dtype == torch.bfloat16 and out.is_contiguous()
@@ -293,7 +310,7 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, co
     _check(len(devs) == 1 and q.is_cuda, "all tensors must be on one GPU")
     if max_context_len is None:
         max_context_len = M * B
-    with torch.cuda.device(q.device):
+    with _on_stream(q, stream):
         if out is None:
             out = torch.empty_like(q)
         _check(out.shape == q.shape and out.dtype == torch.bfloat16 and out.is_contiguous()
@@ -387,7 +404,7 @@ def paged_attn_multi(q, k_cache, v_cache, block_tables, context_lens, query_lens
            "query_lens must be contiguous int32 [num_seqs] on q's device")
     if max_context_len is None:
         max_context_len = M * int(block_size)
-    with torch.cuda.device(q.device):
+    with _on_stream(q, stream):
         if out is None:
             out = torch.empty_like(q)
         _check(out.shape == q.shape and out.dtype == torch.bfloat16 and out.is_contiguous()
@@ -432,7 +449,7 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos
     _check(block_tables.dim() == 2, "block_tables must be [num_seqs][max_blocks_per_seq]")
     devs = {t.device for t in (k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos)}
     _check(len(devs) == 1 and k_cache.is_cuda, "all tensors must be on one GPU")
-    with torch.cuda.device(k_cache.device):
+    with _on_stream(k_cache, stream):
         rc = lib.kv_append(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
                            v_cache.data_ptr(), block_tables.data_ptr(), token_seq.data_ptr(),
                            token_pos.data_ptr(), T, int(block_tables.shape[0]), Hkv, D, B,
@@ -467,7 +484,7 @@ def kv_append_fp8(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token
     _check(block_tables.dim() == 2, "block_tables must be [num_seqs][max_blocks_per_seq]")
     devs = {t.device for t in (k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos)}
     _check(len(devs) == 1 and k_cache.is_cuda, "all tensors must be on one GPU")
-    with torch.cuda.device(k_cache.device):
+    with _on_stream(k_cache, stream):
         rc = lib.kv_append_fp8(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
                                v_cache.data_ptr(), block_tables.data_ptr(), token_seq.data_ptr(),
                                token_pos.data_ptr(), T, int(block_tables.shape[0]), Hkv, D, B,
@@ -502,7 +519,7 @@ def copy_blocks(k_caches, v_caches, src_dst_pairs, stream=None):
     _check(src_dst_pairs.device == ref.device, "src_dst_pairs must be on the pools' device")
     kp = (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in k_caches])
     vp = (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in v_caches])
-    with torch.cuda.device(ref.device):
+    with _on_stream(ref, stream):
         rc = lib.copy_blocks(ctypes.cast(kp, ctypes.c_void_p), ctypes.cast(vp, ctypes.c_void_p),
                              n_layers, nb, nbytes // nb, src_dst_pairs.data_ptr(), n_pairs,
                              _stream_handle(ref, stream))
@@ -530,9 +547,9 @@ def check_batch(block_tables, context_lens, block_size, num_blocks, query_lens=N
     S, M = int(block_tables.shape[0]), int(block_tables.shape[1])
     if query_lens is not None:
         _check(query_lens.numel() == S, "query_lens [num_seqs]")
-    result = torch.empty(1, dtype=torch.int32, device=block_tables.device)
-    with torch.cuda.device(block_tables.device):
-        st = stream if stream is not None else torch.cuda.current_stream(block_tables.device)
+    with _on_stream(block_tables, stream):
+        st = torch.cuda.current_stream(block_tables.device)
+        result = torch.empty(1, dtype=torch.int32, device=block_tables.device)
         rc = lib.pkv_check_batch(block_tables.data_ptr(), context_lens.data_ptr(),
                                  query_lens.data_ptr() if query_lens is not None else None, S, M,
                                  int(num_blocks), int(block_size), int(max_query_len),
