@@ -209,10 +209,10 @@ def _device_case_vs_oracle(case, seqs=None, label=""):
     return errors(got[seqs], ref)
 
 
-@pytest.mark.parametrize("B", [8, 16, 32])
-def test_long_context_one_layer_full_size(B):
-    case = wl.case_long(0, num_layers=1, block_size=B)
-    _device_case_vs_oracle(case, label="long 8x16000 B=%d" % B)
+@pytest.mark.parametrize("seed,B", [(0, 8), (0, 16), (0, 32), (1, 16), (2, 16)])
+def test_long_context_one_layer_full_size(seed, B):
+    case = wl.case_long(seed, num_layers=1, block_size=B)
+    _device_case_vs_oracle(case, label="long 8x16000 seed %d B=%d" % (seed, B))
 
 
 @pytest.mark.parametrize("B", [8, 16, 32])
@@ -221,13 +221,20 @@ def test_mix_at_reduced_pool(B):
     _device_case_vs_oracle(case, label="mix B=%d" % B)
 
 
-def test_mix_full_pool_sampled_sequences():
-    """The 100 GB pool of the continuous-batching mix; the oracle checks every long
-    sequence and a sample of short ones."""
-    case = wl.case_mix(2, 16)
-    long_ids = np.nonzero(case.context_lens == 32768)[0]
-    short_ids = np.nonzero(case.context_lens != 32768)[0][:24]
-    _device_case_vs_oracle(case, np.concatenate([long_ids[:6], short_ids]), label="mix 100GB")
+@pytest.mark.parametrize("seed", [2, 0])
+def test_mix_full_pool_sampled_sequences(seed):
+    """The 100 GB pool of the continuous-batching mix; the oracle checks six long
+    sequences and a sample of short ones."""
+    import torch
+
+    case = wl.case_mix(seed, 16)
+    # the 13 long sequences hold 32,768 positions plus one per churn step
+    long_ids = np.nonzero(case.context_lens >= 32768)[0]
+    short_ids = np.nonzero(case.context_lens < 32768)[0][:24]
+    assert len(long_ids) == 13
+    _device_case_vs_oracle(case, np.concatenate([long_ids[:6], short_ids]),
+                           label="mix 100GB seed %d" % seed)
+    torch.cuda.empty_cache()
 
 
 def test_workspace_too_small_is_rejected():
@@ -244,3 +251,41 @@ def test_workspace_too_small_is_rejected():
                               to_dev_i32(case.block_tables), to_dev_i32(case.context_lens),
                               case.block_size, case.scale, workspace=ws)
     assert e.value.status == -4
+
+
+def test_decode_on_a_side_stream_while_the_current_stream_allocates():
+    """The binding allocates its temporaries (workspace, output) on the stream the
+    kernels run on, so memory the current stream allocates and writes while the
+    side stream's decode is still queued or running is never the decode's."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    case = wl.case_chat(6)
+    q = wl.host_q(case)
+    kp, vp = wl.host_pools(case)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(kp), to_dev_bf16(vp)
+    tabs, lens = to_dev_i32(case.block_tables), to_dev_i32(case.context_lens)
+    ref = pkv.paged_attn_decode(qd, kd, vd, tabs, lens, 16, case.scale,
+                                max_context_len=case.max_context_len)
+    torch.cuda.synchronize()
+    ws_bytes = pkv.paged_attn_decode_workspace_bytes(case.num_seqs, case.num_q_heads,
+                                                     case.num_kv_heads, case.head_dim, 16,
+                                                     case.max_context_len)
+    side = torch.cuda.Stream()
+    busy = torch.ones(1 << 26, device="cuda:0")
+    outs = []
+    for rep in range(6):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(rep):          # hold the side stream back by a varying delay
+                busy.mul_(1.0)
+        outs.append(pkv.paged_attn_decode(qd, kd, vd, tabs, lens, 16, case.scale,
+                                          max_context_len=case.max_context_len, stream=side))
+        for _ in range(4):                # the current stream reuses whatever is free
+            torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0").fill_(0xAB)
+            torch.empty_like(qd).fill_(float("nan"))
+    side.synchronize()
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))

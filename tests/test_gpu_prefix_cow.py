@@ -95,13 +95,14 @@ def _run_script(script: wl.PrefixScript, manager_cls):
     return bm, seqs, tail_slots, prefix_tables
 
 
-@pytest.mark.parametrize("prefix,expect_copies", [(1020, True), (1024, False)])
-def test_shared_prefix_sampling_end_to_end(prefix, expect_copies):
+@pytest.mark.parametrize("seed,prefix,expect_copies",
+                         [(0, 1020, True), (0, 1024, False), (1, 1020, True), (2, 1020, True)])
+def test_shared_prefix_sampling_end_to_end(seed, prefix, expect_copies):
     import torch
 
     import paged_kv_cache_280_amd as pkv
 
-    sc = wl.prefix_script(0, prefix_len=prefix)
+    sc = wl.prefix_script(seed, prefix_len=prefix)
     bm, seqs, tail_slots, prefix_tables = _run_script(sc, BlockManager)
     model, _, model_slots, _ = _run_script(sc, BlockModel)
     pairs = bm.take_copies()
@@ -132,7 +133,7 @@ def test_shared_prefix_sampling_end_to_end(prefix, expect_copies):
         k_rows, v_rows = wl.token_kv(sc.seed, (p, 1 + k), n, H, D)
         wl.write_tokens(kp, vp, tail_slots[(p, k)], k_rows, v_rows)
     tables, lens = bm.batch(seqs, pad_block=int(bm.free_ids()[0]) if bm.num_free else 0)
-    rng = np.random.default_rng(9)
+    rng = np.random.default_rng(9 + seed)
     q = wl.randn_bf16(rng, (len(seqs), sc.num_q_heads, D))
     out = pkv.paged_attn_decode(to_dev_bf16(q), to_dev_bf16(kp), to_dev_bf16(vp),
                                 to_dev_i32(tables), to_dev_i32(lens), B, sc.scale,
@@ -140,7 +141,7 @@ def test_shared_prefix_sampling_end_to_end(prefix, expect_copies):
     torch.cuda.synchronize()
     got = bf16_to_f32(out)
     ref = oracle.paged_decode(q, kp, vp, tables, lens, B, sc.scale, H)
-    assert_parity(got, ref, "shared prefix %d" % prefix)
+    assert_parity(got, ref, "shared prefix %d seed %d" % (prefix, seed))
 
     # the same batch with every sample holding private copies of its blocks
     n_blk = -(-lens // B)
