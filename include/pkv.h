@@ -19,7 +19,8 @@
  * Conventions for every entry point
  *   - All tensor arguments are DEVICE pointers owned by the caller, unless a
  *     comment says "host".  The library keeps no pointer after it returns and
- *     allocates no device memory.
+ *     allocates no device memory (paged_attn_decode_noalloc's scratch is a static
+ *     array of the library, one per GPU).
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Work is
  *     enqueued on it and the call returns at once; buffers must stay alive until
  *     that work has finished.
@@ -353,6 +354,35 @@ int32_t pkv_check_batch(const int32_t* block_tables, const int32_t* context_lens
                         const int32_t* query_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                         int64_t num_blocks, int32_t block_size, int32_t max_query_len,
                         int32_t* result, void* stream);
+
+/*
+ * paged_attn_decode with no workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The split-K records and worker descriptors go to a scratch
+ * array of PKV_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU: it is
+ * found once per device on the first call made with that device current, and each
+ * GPU holds it until the process ends.  The call itself allocates nothing and calls
+ * no allocating routine.
+ *
+ * Arguments, checks, results and guarantees are paged_attn_decode's (the outputs are
+ * bit-identical to a paged_attn_decode call with its own workspace), except:
+ *   - PKV_ERR_WORKSPACE when these sizes need more scratch than
+ *     PKV_NOALLOC_SCRATCH_BYTES (paged_attn_decode_workspace_bytes() above it;
+ *     e.g. 16 query heads per KV head at head_dim 128 over long contexts);
+ *   - PKV_ERR_DEVICE when the scratch of the current device cannot be located.
+ * The scratch keeps whatever the last call left; nothing in it needs to start at
+ * zero (every call rewrites what it reads).  All calls on one GPU share that GPU's
+ * scratch: calls whose work overlaps in time on one GPU (two streams, or two host
+ * threads) race and give meaningless results.  Calls in order on one stream are safe.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+int32_t paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t block_size, float scale, void* out, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  int32_t max_context_len, void* stream);
 
 #ifdef __cplusplus
 }

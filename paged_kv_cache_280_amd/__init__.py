@@ -8,6 +8,7 @@ helpers (byte accounting, the block manager).
 from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
+    NOALLOC_SCRATCH_BYTES,
     PkvError,
     CHECK_KINDS,
     abi_version,
@@ -21,6 +22,7 @@ from ._binding import (  # noqa: F401
     paged_attn_decode,
     paged_attn_decode_append,
     paged_attn_decode_fp8,
+    paged_attn_decode_noalloc,
     paged_attn_decode_workspace_bytes,
     paged_attn_multi,
     paged_attn_multi_workspace_bytes,

@@ -25,7 +25,8 @@ EXPORTS = ("pkv_abi_version", "pkv_status_string", "paged_attn_decode_workspace_
            "paged_attn_decode", "paged_attn_decode_fp8", "paged_attn_multi_workspace_bytes",
            "paged_attn_multi", "paged_attn_multi_fp8",
            "kv_append", "kv_append_fp8", "copy_blocks", "pkv_check_batch",
-           "paged_attn_decode_append", "paged_attn_decode_append_fp8")
+           "paged_attn_decode_append", "paged_attn_decode_append_fp8",
+           "paged_attn_decode_noalloc")
 
 
 class PkvError(RuntimeError):
@@ -61,6 +62,8 @@ def load_library(path: str = LIB_PATH):
                    sz, p]
     lib.paged_attn_decode.argtypes = decode_args
     lib.paged_attn_decode.restype = i32
+    lib.paged_attn_decode_noalloc.argtypes = decode_args[:15] + [p]
+    lib.paged_attn_decode_noalloc.restype = i32
     f32 = ctypes.c_float
     lib.paged_attn_decode_fp8.argtypes = [p, p, p, p, p, i32, f32, f32, f32, p, i32, i32, i32, i32,
                                           i32, i64, i32, p, sz, p]
@@ -215,6 +218,35 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
                                    _stream_handle(q, stream))
     if rc != 0:
         raise PkvError(rc, "paged_attn_decode")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # PKV_NOALLOC_SCRATCH_BYTES of include/pkv.h
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
+                              out, *, max_context_len=None, stream=None):
+    """paged_attn_decode through the entry point that allocates nothing (see
+    ``include/pkv.h``): the split-K scratch is the library's own per-GPU array, and
+    ``out`` must be given.  Calls whose work overlaps in time on one GPU race on
+    that scratch.  Returns ``out``."""
+    import torch
+
+    lib = load_library()
+    S, Hq, Hkv, D, NB, M = decode_shapes(q, k_cache, v_cache, block_tables, context_lens,
+                                         block_size)
+    _check(out is not None and out.shape == q.shape and out.dtype == torch.bfloat16
+           and out.is_contiguous() and out.device == q.device, "out must match q")
+    if max_context_len is None:
+        max_context_len = M * int(block_size)
+    with torch.cuda.device(q.device):
+        rc = lib.paged_attn_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                           block_tables.data_ptr(), context_lens.data_ptr(),
+                                           int(block_size), float(scale), out.data_ptr(), S, Hq,
+                                           Hkv, D, M, NB, int(max_context_len),
+                                           _stream_handle(q, stream))
+    if rc != 0:
+        raise PkvError(rc, "paged_attn_decode_noalloc")
     return out
 
 

@@ -1,14 +1,22 @@
 // C ABI of the library (declared in include/pkv.h): host-side argument checks,
-// launch sizing and dispatch to the kernels.  No device memory is allocated here.
+// launch sizing and dispatch to the kernels.  No call allocates device memory; the
+// one static array below is the scratch of the no-allocation decode entry point.
 
 #include <math.h>
 #include <stdlib.h>
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "pkv.h"
 #include "pkv_internal.h"
+
+// Scratch of paged_attn_decode_noalloc: split-K records and worker descriptors.
+// Every device the library runs on holds its own copy until the process ends.  On
+// the host this name only stands for the array: host code uses the device address
+// that hipGetSymbolAddress reports for the current device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
 
 namespace pkv {
 namespace {
@@ -34,6 +42,27 @@ int current_cu_count() {
     return -1;
   if (dev < kMaxDevices) g_cu_count[dev].store(cu, std::memory_order_relaxed);
   return cu;
+}
+
+// Device address of the current device's scratch array, looked up once per device
+// (with that device current) and kept; nullptr when the runtime cannot report it.
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+void* noalloc_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    g_scratch[dev].store(addr, std::memory_order_release);
+    p = addr;
+  }
+  return p;
 }
 
 // Resident decode workers (waves) per compute unit; PKV_WAVES_PER_CU overrides
@@ -399,6 +428,27 @@ int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                           num_blocks, max_context_len, workspace, workspace_bytes, stream, false,
                           1.0f, 1.0f);
+}
+
+int32_t paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t block_size, float scale, void* out, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int64_t num_blocks,
+                                  int32_t max_context_len, void* stream) {
+  // Sizes are checked before the device is asked for anything.  The scratch stands
+  // in for the workspace; decode_impl rejects sizes that need more
+  // (PKV_ERR_WORKSPACE) before anything is enqueued.
+  const int32_t st = pkv::check_shapes(block_size, scale, num_seqs, num_q_heads, num_kv_heads,
+                                       head_dim, max_blocks_per_seq, num_blocks, max_context_len);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  void* ws = pkv::noalloc_scratch();
+  if (!ws) return PKV_ERR_DEVICE;
+  return pkv::decode_impl(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, out,
+                          num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          num_blocks, max_context_len, ws, PKV_NOALLOC_SCRATCH_BYTES, stream,
+                          false, 1.0f, 1.0f);
 }
 
 int32_t paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
                             "paged_attn_multi_workspace_bytes", "paged_attn_multi",
                             "paged_attn_multi_fp8",
                             "kv_append", "kv_append_fp8", "copy_blocks", "pkv_check_batch",
-                            "paged_attn_decode_append", "paged_attn_decode_append_fp8"])
+                            "paged_attn_decode_append", "paged_attn_decode_append_fp8",
+                            "paged_attn_decode_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -89,6 +90,36 @@ def test_decode_rejects_bad_arguments_on_the_host(lib, over, code):
 
 def test_decode_with_no_sequences_is_a_no_op(lib):
     assert _decode_call(lib, S=0, q=None, out=None) == 0
+
+
+def _noalloc_call(lib, **over):
+    """Call paged_attn_decode_noalloc with fake (never dereferenced) pointers."""
+    a = dict(q=0x1000, k=0x2000, v=0x3000, tables=0x4000, lens=0x5000, block_size=16, scale=0.125,
+             out=0x6000, S=2, Hq=8, Hkv=2, D=128, M=4, NB=10, max_ctx=64, stream=None)
+    a.update(over)
+    return lib.paged_attn_decode_noalloc(a["q"], a["k"], a["v"], a["tables"], a["lens"],
+                                         a["block_size"], a["scale"], a["out"], a["S"], a["Hq"],
+                                         a["Hkv"], a["D"], a["M"], a["NB"], a["max_ctx"],
+                                         a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(max_ctx=65), -2),
+    (dict(D=96), -3),
+    (dict(Hq=34, Hkv=1), -3),
+    (dict(S=0, q=None, out=None), 0),   # nothing to do, no device touched
+])
+def test_noalloc_decode_checks_sizes_before_touching_a_device(lib, over, code):
+    assert _noalloc_call(lib, **over) == code
+
+
+def test_noalloc_scratch_limit_matches_the_header():
+    import paged_kv_cache_280_amd as pkv
+
+    text = open(HEADER).read()
+    m = re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pkv.NOALLOC_SCRATCH_BYTES
 
 
 def _multi_call(lib, **over):
