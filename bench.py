@@ -65,6 +65,14 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-worker timeline of --steps eager decode calls from the "
+                         "PKV_TIMELINE build (libpkv_timeline.so) instead of the timed run")
+    ap.add_argument("--timeline-raw", default="", metavar="NPZ",
+                    help="with --timeline: also save every call's worker stamps to NPZ")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="only run the read-stream probe on the workload's K/V units, "
+                         "sweeping waves per CU and units in flight, and print it")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes three times (the "
                          "reference kernel that scales hardware byte counters) and exit")
@@ -135,7 +143,11 @@ def prefix_case(args):
     case = wl.Case("prefix", len(seqs), sc.num_q_heads, sc.num_kv_heads, sc.head_dim, B,
                    sc.num_blocks, lens, tables, sc.scale, num_layers=16, poison_block=pad,
                    seed=args.seed)
-    return case, pairs, int(np.unique(pos).size)
+    # slots of the distinct blocks the batch holds that hold no token (a shared block
+    # counts once, as it is stored once)
+    held = np.unique(pos // B).size * B
+    frag = round((held - np.unique(pos).size) / held, 5)
+    return case, pairs, int(np.unique(pos).size), frag
 
 
 def build_workload(args, dev):
@@ -160,9 +172,9 @@ def build_workload(args, dev):
     elif args.workload == "prefix":
         # 16 layers with their own pools (2.2 GB), so the unique 134 MB of a layer
         # is not served from the last-level cache by the previous step
-        case, pairs, unique = prefix_case(args)
+        case, pairs, unique, frag = prefix_case(args)
         layers = case.num_layers
-        extra = {"pairs": pairs, "unique_tokens": unique}
+        extra = {"pairs": pairs, "unique_tokens": unique, "fragmentation": frag}
         desc = ("shared-prefix sampling: 16 prompts x 8 samples, prefix 1020 stored once, tails "
                 "U[0,256], 16 layers, 32 q / 8 KV heads, head_dim 128, block %d" % case.block_size)
     elif args.workload == "tiny":
@@ -275,8 +287,10 @@ def cpu_model():
 
 def copy_blocks_timing(pools, pairs, args):
     """The copy-on-write copy_blocks call of the shared-prefix workload (every
-    layer's K and V pool in one call), timed with HIP events.  Copying again is
-    harmless: sources are never destinations."""
+    layer's K and V pool in one call), timed with HIP events: back to back (warm:
+    the sources stay in the last-level cache) and cold (a 2 GiB buffer is read and
+    written before each call, outside the timed events, so the sources come from
+    HBM).  Copying again is harmless: sources are never destinations."""
     import torch
 
     import paged_kv_cache_280_amd as pkv
@@ -295,37 +309,141 @@ def copy_blocks_timing(pools, pairs, args):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
-    block_bytes = ks[0][0].numel() * ks[0].element_size()
-    moved = 2 * 2 * len(pairs) * len(ks) * block_bytes  # K and V: read src, write dst
-    return {"pairs": int(len(pairs)), "layers": len(ks), "us_per_call": round(us, 2),
-            "bytes_per_call": int(moved), "gbs": round(moved / us / 1e3, 1)}
-
-
-def attainable_bandwidth(nbytes=4 << 30, reps=10):
-    """Plain device streams on the same GPU in the same run: a 4 GiB read (torch
-    column sums of a [4096][n] float32 view: one pass over the bytes, 1 MB written)
-    and a 4 GiB copy (bytes read + written)."""
-    import torch
-
-    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
-    y = torch.empty_like(x)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    res = {}
-    for name, fn, moved in (("read", lambda: x.view(4096, -1).sum(0), nbytes),
-                            ("copy", lambda: y.copy_(x), 2 * nbytes)):
-        fn()
-        torch.cuda.synchronize()
+    flush = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(10):
+        flush.fill_(i)                     # evicts the 256 MB last-level cache
         e0.record()
-        for _ in range(reps):
-            fn()
+        pkv.copy_blocks(ks, vs, pd)
         e1.record()
         torch.cuda.synchronize()
-        res[name + "_gbs"] = round(moved * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
-    del x, y
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    del flush
     torch.cuda.empty_cache()
-    res["kernels"] = ("torch column sums over a 4 GiB float32 [4096][n] view (read); torch copy "
-                      "of 4 GiB (read + write)")
+    block_bytes = ks[0][0].numel() * ks[0].element_size()
+    moved = 2 * 2 * len(pairs) * len(ks) * block_bytes  # K and V: read src, write dst
+    us_cold = float(np.median(cold))
+    return {"pairs": int(len(pairs)), "layers": len(ks), "us_per_call": round(us, 2),
+            "bytes_per_call": int(moved), "gbs": round(moved / us / 1e3, 1),
+            "cold_us_per_call": round(us_cold, 2), "cold_gbs": round(moved / us_cold / 1e3, 1)}
+
+
+STREAM_LIB = os.path.join(ROOT, "paged_kv_cache_280_amd", "libpkv_stream.so")
+TIMELINE_LIB = os.path.join(ROOT, "paged_kv_cache_280_amd", "libpkv_timeline.so")
+
+
+def stream_library():
+    """The HBM read-stream probe (include/pkv_stream.h), loaded after torch's HIP runtime."""
+    import ctypes
+
+    import torch  # noqa: F401
+
+    if not os.path.exists(STREAM_LIB):
+        raise RuntimeError("libpkv_stream.so is not built; run python -m "
+                           "paged_kv_cache_280_amd.build --stream-probe")
+    lib = ctypes.CDLL(STREAM_LIB)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.pkv_stream_read.argtypes = [p, ctypes.c_size_t, p, i32, p]
+    lib.pkv_stream_read.restype = i32
+    lib.pkv_stream_read_pairs.argtypes = [p, p, i64, p, i32, i32, i32, p, i32, i32, p]
+    lib.pkv_stream_read_pairs.restype = i32
+    return lib
+
+
+def decode_units(case, elem_bytes):
+    """Unit ids of the K/V reads of one decode call in the decode kernel's order
+    ((sequence, KV head) pairs sequence-major, then positions), one unit per
+    16-position run of a block (a whole block of 8 positions at B = 8), and the
+    unit size in bytes."""
+    B, H, D = case.block_size, case.num_kv_heads, case.head_dim
+    run = min(B, 16)
+    halves = B // run
+    ids = []
+    for s, L in enumerate(case.context_lens):
+        nb = -(-int(L) // B)
+        blocks = case.block_tables[s, :nb].astype(np.int64)
+        for g in range(H):
+            base = (blocks * H + g) * halves
+            n_runs = -(-int(L) // run)
+            ids.append((base[:, None] + np.arange(halves)[None, :]).reshape(-1)[:n_runs])
+    return np.concatenate(ids).astype(np.int32), run * D * elem_bytes
+
+
+def attainable_bandwidth(case, k_pool, v_pool, elem_bytes, reps=10, seq_bytes=4 << 30,
+                         sweep=False):
+    """The probe kernels of libpkv_stream.so on the same GPU in the same run: a
+    sequential 4 GiB read, and the decode call's own K/V reads (this workload's
+    first-layer pools, in the decode kernel's order and unit size, 3 waves per CU,
+    three units in flight) with 8- and 16-byte V loads, one call's bytes per launch.
+    Best of ``reps`` HIP-event-timed launches each.  ``sweep`` adds other wave counts
+    and in-flight depths."""
+    import ctypes
+
+    import torch
+
+    lib = stream_library()
+    dev = k_pool.device
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def best(fn, moved):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) / 1e3)
+        return round(moved / min(t) / 1e9, 1)
+
+    res = {}
+    x = torch.empty(seq_bytes, dtype=torch.uint8, device=dev)
+    x.fill_(1)
+    groups = cu * 8
+    sink = torch.empty(groups * 256, dtype=torch.int32, device=dev)
+
+    def seq():
+        assert lib.pkv_stream_read(x.data_ptr(), seq_bytes, sink.data_ptr(), groups, sh) == 0
+
+    res["read_gbs"] = best(seq, seq_bytes)
+    del x
+    torch.cuda.empty_cache()
+    ids, unit = decode_units(case, elem_bytes)
+    idd = torch.from_numpy(ids).to(dev)
+    pool_units = k_pool.numel() * k_pool.element_size() // unit
+    sink = torch.empty(max(groups * 256, 16 * cu * 64), dtype=torch.int32, device=dev)
+
+    def pairs_gbs(idv, vb, waves, depth):
+        def run():
+            assert lib.pkv_stream_read_pairs(k_pool.data_ptr(), v_pool.data_ptr(), pool_units,
+                                             idv.data_ptr(), idv.numel(), unit, vb,
+                                             sink.data_ptr(), waves, depth, sh) == 0
+        return best(run, 2 * idv.numel() * unit)
+
+    for vb in (8, 16):
+        res["pairs_v%d_gbs" % vb] = pairs_gbs(idd, vb, 3 * cu, 3)
+    if sweep:
+        res["call_sweep_v8"] = {"%dw_d%d" % (wpc, depth): pairs_gbs(idd, 8, wpc * cu, depth)
+                                for wpc in (2, 3, 4, 6, 8) for depth in (3, 6)}
+    res["pair_units"] = int(len(ids))
+    res["unit_bytes"] = int(unit)
+    res["kernels"] = ("libpkv_stream.so: sequential 4 GiB read, 16-byte lane loads (read_gbs); "
+                      "this workload's K/V units in decode order, 16-byte K loads and 8- or "
+                      "16-byte V loads, %d waves, 3 units in flight, one call's bytes per "
+                      "launch (pairs_v8_gbs, pairs_v16_gbs)" % (3 * cu))
     return res
+
+
+def internal_fragmentation(lens, block_size):
+    """Share of the slots held by the batch's blocks that hold no token: only each
+    sequence's last block has empty slots."""
+    lens = np.asarray(lens, np.int64)
+    held = int((-(-lens // block_size)).sum()) * block_size
+    return 0.0 if held == 0 else round((held - int(lens.sum())) / held, 5)
 
 
 def append_bench(args):
@@ -374,8 +492,118 @@ def append_bench(args):
                       "gbs": round(moved / us / 1e3, 1)}), flush=True)
 
 
+STAMP = np.dtype([("t_entry", "<u8"), ("d_plan", "<u4"), ("d_first", "<u4"), ("d_end", "<u4"),
+                  ("xcc", "<u4"), ("tiles", "<u4"), ("group", "<u4")])
+
+
+def timeline(args):
+    """Per-worker timeline of decode calls from the PKV_TIMELINE build of the library
+    (libpkv_timeline.so): every worker's entry, plan, first-tile and end times on the
+    100 MHz s_memrealtime clock and the XCC it ran on, read back from the workspace
+    after each eagerly launched call of the workload's layers.  Prints one JSON line
+    of medians over the calls (microseconds after the first worker's entry)."""
+    import torch
+
+    from paged_kv_cache_280_amd import _binding
+
+    if not os.path.exists(TIMELINE_LIB):
+        raise RuntimeError("libpkv_timeline.so is not built; run python -m "
+                           "paged_kv_cache_280_amd.build --timeline")
+    if args.query_tokens != 1 or args.with_append or args.workload in ("append", "tiny"):
+        raise SystemExit("--timeline covers the split decode call (one query token, no append)")
+    _binding.load_library(TIMELINE_LIB)   # every binding call below uses this build
+    import paged_kv_cache_280_amd as pkv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case, layers, desc, pools, tabs, lens, extra = build_workload(args, dev)
+    S, Hq, Hkv, D, B = (case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                        case.block_size)
+    fp8 = args.kv_dtype == "fp8"
+    max_ctx = case.max_context_len
+    ws = pkv.new_workspace(S, Hq, Hkv, D, B, max_ctx, dev)
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    wpc = int(os.environ.get("PKV_WAVES_PER_CU", "0") or 0) or (4 if fp8 else 3)
+    n = min(cu * wpc, S * Hkv * (-(-max_ctx // 16)))
+    G = Hq // Hkv
+    rec_bytes = n * 2 * (G * D + ((2 * G + 3) // 4) * 4) * 4
+    off = rec_bytes + 16 * n   # past the descriptors
+    out = torch.empty_like(pools[0][0])
+    stats, raw = [], []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for c in range(args.warmup + args.steps):
+        q, k, v = pools[c % layers]
+        e0.record()
+        if fp8:
+            pkv.paged_attn_decode_fp8(q, k, v, tabs, lens, B, case.scale, FP8_SCALE, FP8_SCALE,
+                                      out, workspace=ws, max_context_len=max_ctx)
+        else:
+            pkv.paged_attn_decode(q, k, v, tabs, lens, B, case.scale, out, workspace=ws,
+                                  max_context_len=max_ctx)
+        e1.record()
+        torch.cuda.synchronize()
+        if c < args.warmup:
+            continue
+        st = np.frombuffer(ws[off:off + n * STAMP.itemsize].cpu().numpy().tobytes(), dtype=STAMP)
+        assert (st["group"] == np.arange(n) // 4).all(), "stamps missing: n_workers mismatch"
+        raw.append(st.copy())
+        t0 = int(st["t_entry"].min())
+        us = lambda ticks: np.asarray(ticks, np.float64) * 0.01
+        entry = us(st["t_entry"] - t0)
+        has = st["d_first"] != 0xFFFFFFFF
+        end = entry + us(st["d_end"])
+        first = entry[has] + us(st["d_first"][has])
+        per_xcc = {int(x): end[st["xcc"] == x] for x in np.unique(st["xcc"])}
+        stats.append({
+            "call_us": e0.elapsed_time(e1) * 1e3,
+            "entry_max": entry.max(), "plan_median": float(np.median(entry + us(st["d_plan"]))),
+            "first_tile_median": float(np.median(first)), "first_tile_max": float(first.max()),
+            "end_min": end.min(), "end_p10": float(np.percentile(end, 10)),
+            "end_median": float(np.median(end)), "end_p90": float(np.percentile(end, 90)),
+            "end_max": end.max(), "end_mean": end.mean(),
+            "xcc_end_median": {x: float(np.median(e)) for x, e in per_xcc.items()},
+            "xcc_end_max": {x: float(e.max()) for x, e in per_xcc.items()},
+            "workers_per_xcc": {x: int(len(e)) for x, e in per_xcc.items()},
+            "tiles_min": int(st["tiles"][has].min()), "tiles_max": int(st["tiles"][has].max()),
+        })
+    med = lambda key: round(float(np.median([x[key] for x in stats])), 2)
+    xccs = sorted(stats[0]["xcc_end_median"])
+    line = {
+        "timeline": desc, "workers": n, "calls": len(stats),
+        "call_us_median": med("call_us"),
+        "entry_spread_us": med("entry_max"), "plan_done_us": med("plan_median"),
+        "first_tile_us": {"median": med("first_tile_median"), "max": med("first_tile_max")},
+        "worker_end_us": {k: med("end_" + k) for k in ("min", "p10", "median", "mean", "p90",
+                                                        "max")},
+        "xcc_end_median_us": {x: round(float(np.median([s_["xcc_end_median"][x] for s_ in stats])),
+                                       2) for x in xccs},
+        "slowest_xcc_per_call": [max(s_["xcc_end_median"], key=s_["xcc_end_median"].get)
+                                 for s_ in stats],
+        "xcc_spread_us_per_call": [round(max(s_["xcc_end_median"].values()) -
+                                         min(s_["xcc_end_median"].values()), 2) for s_ in stats],
+        "workers_per_xcc": stats[0]["workers_per_xcc"],
+        "tiles_per_worker": [stats[0]["tiles_min"], stats[0]["tiles_max"]],
+        "clock": "s_memrealtime, 100 MHz",
+    }
+    print(json.dumps(line), flush=True)
+    if args.timeline_raw:
+        np.savez(args.timeline_raw, stamps=np.stack(raw), call_us=[x["call_us"] for x in stats])
+
+
 def main():
     args = parse()
+    if args.timeline:
+        timeline(args)
+        return
+    if args.probe_sweep:
+        import torch
+
+        dev = torch.device("cuda:0")
+        case, layers, desc, pools, tabs, lens, extra = build_workload(args, dev)
+        res = attainable_bandwidth(case, pools[0][1], pools[0][2],
+                                   1 if args.kv_dtype == "fp8" else 2, sweep=True)
+        print(json.dumps({"probe": desc, **res}), flush=True)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -522,7 +750,10 @@ def main():
     kern_avg_s = float(np.mean(kern_ms)) / 1e3
     p10, p50, p90 = (float(x) * 1e3 for x in np.percentile(kern_ms, [10, 50, 90]))
     copy_line = copy_blocks_timing(pools, extra["pairs"], args) if "pairs" in extra else None
-    attain = attainable_bandwidth()
+    attain = attainable_bandwidth(case, pools[0][1], pools[0][2], kv_elem)
+    # the probe read shaped like this decode: 16-byte K loads, and V loads of 8 bytes
+    # (bf16 pools) or 16 bytes (fp8 pools)
+    attain_key = "pairs_v16_gbs" if fp8 else "pairs_v8_gbs"
     step_bytes = per_call_bytes * layers
     tokens_per_s = S * T / (ms_per_step / 1e3)
     kv_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
@@ -560,10 +791,13 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "frac_of_attainable": round(achieved / attain["read_gbs"], 4),
+                     "frac_of_attainable": round(achieved / attain[attain_key], 4),
+                     "attainable_kernel": attain_key,
                      "algorithmic_bytes_per_launch": int(per_call_bytes),
                      "avg_launch_us": round(kern_avg_s * 1e6, 2)},
         "cpu_baseline": None,
+        "internal_fragmentation": extra.get("fragmentation",
+                                            internal_fragmentation(case.context_lens, B)),
     }
     if "unique_tokens" in extra:
         line["logical_kv_gbs"] = round(logical_bytes * layers / (ms_per_step / 1e3) / 1e9, 1)

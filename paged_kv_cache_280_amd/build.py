@@ -4,6 +4,13 @@ Run as ``python -m paged_kv_cache_280_amd.build`` or call ``build()``.  The
 library is rebuilt on every call: each source compiles to an object file in
 parallel (the decode kernel instances are spread over several sources), then one
 link step makes the shared library.
+
+``build(timeline=True)`` (``--timeline``) makes the measurement variant
+``libpkv_timeline.so``: the same sources with PKV_TIMELINE defined, whose decode
+kernel also stamps each worker's entry, plan, first tile and end times into the
+workspace (read by ``bench.py --timeline``).  ``build_stream_probe()`` makes
+``libpkv_stream.so``, the HBM read-stream probe that bench.py reports as the
+attainable bandwidth.
 """
 
 from __future__ import annotations
@@ -17,6 +24,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpkv.so")
+TIMELINE_LIB = os.path.join(PKG, "libpkv_timeline.so")
+STREAM_LIB = os.path.join(PKG, "libpkv_stream.so")
+STREAM_SRC = os.path.join(PKG, "probe", "pkv_stream.hip")
 OBJ_DIR = os.path.join(PKG, "_build")
 ARCH = "gfx950"
 # hipcc's host pass does not know the packed-fp32 feature and says so
@@ -33,11 +43,15 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def compile_command(src: str, obj: str):
+def compile_command(src: str, obj: str, defines=()):
     return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-c",
             # packed fp32 VALU ops stay off: plain float code only
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-result",
+            # atomics stay as written: the wave-level rewrite of single-lane atomics
+            # reads their result back at once, which would drain the decode kernel's
+            # tile loads at every chunk claim
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+            "-Wall", "-Wno-unused-result", *["-D" + x for x in defines],
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"), src, "-o", obj]
 
 
@@ -51,13 +65,22 @@ def _run(cmd):
     return res.returncode, msg
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    return _build_lib(sources(), TIMELINE_LIB if timeline else LIB,
+                      ("PKV_TIMELINE=1",) if timeline else (), verbose)
+
+
+def build_stream_probe(verbose: bool = False) -> str:
+    return _build_lib([STREAM_SRC], STREAM_LIB, (), verbose)
+
+
+def _build_lib(srcs, lib: str, defines, verbose: bool) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
-    tag = "%d" % os.getpid()
+    tag = "%d.%s" % (os.getpid(), os.path.basename(lib)[:-3])
     jobs = []
-    for src in sources():
+    for src in srcs:
         obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + "." + tag + ".o")
-        jobs.append((compile_command(src, obj), obj))
+        jobs.append((compile_command(src, obj, defines), obj))
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     if verbose:
         for cmd, _ in jobs:
@@ -71,20 +94,25 @@ def build(verbose: bool = False) -> str:
                 raise RuntimeError("hipcc failed (%d): %s\n%s" % (rc, cmd[-3], msg))
             if msg.strip() and verbose:
                 print(msg)
-        tmp = LIB + ".tmp" + tag
+        tmp = lib + ".tmp" + tag
         cmd = link_command(objs, tmp)
         if verbose:
             print(" ".join(cmd), flush=True)
         rc, msg = _run(cmd)
         if rc != 0:
             raise RuntimeError("link failed (%d):\n%s" % (rc, msg))
-        os.replace(tmp, LIB)
+        os.replace(tmp, lib)
     finally:
         for obj in objs:
             if os.path.exists(obj):
                 os.remove(obj)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--timeline" in sys.argv:
+        print(build(verbose="-v" in sys.argv, timeline=True))
+    elif "--stream-probe" in sys.argv:
+        print(build_stream_probe(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -951,7 +951,7 @@ __device__ void one_token(const Cx& cx, const DecodeDims& d, int64_t s, int lane
 // pair this worker opens (s = -1 if none).
 template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, typename Cx>
 __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& pl, int64_t w,
-                           int lane) {
+                           int lane, uint64_t& t_first) {
   const int32_t cap = d.M * B;
   const int32_t n = pl.n;
   const Cols<NC> cl = make_cols<NC, kCausal>(d, lane);
@@ -1005,6 +1005,9 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
       seg_t0 = cc.t;
     }
     const int32_t valid = min(kTile, cc.L - cc.t * kTile);
+#ifdef PKV_TIMELINE
+    if (i == 0) t_first = __builtin_amdgcn_s_memrealtime();
+#endif
     if constexpr (kCausal) {
       int32_t lim[NC];
 #pragma unroll
@@ -1084,12 +1087,36 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
   if (w >= d.n_workers) return;
   const int32_t cap = d.M * B;
+#ifdef PKV_TIMELINE
+  const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
+#endif
+  uint64_t t_first = 0;
 
   int4 opened = {-1, 0, 0, 0};
   WorkerPlan pl;
   const bool has = d.pair_mode ? plan_pair<kCausal>(lens, qlens, d, cap, w, pl)
                                : plan_worker<kCausal>(lens, qlens, d, cap, w, lane, pl);
-  if (has) opened = run_worker<D, B, NC, kCausal, kFp8, kAppend>(cx, d, pl, w, lane);
+#ifdef PKV_TIMELINE
+  const uint64_t t_plan = __builtin_amdgcn_s_memrealtime();
+#endif
+  if (has) opened = run_worker<D, B, NC, kCausal, kFp8, kAppend>(cx, d, pl, w, lane, t_first);
+#ifdef PKV_TIMELINE
+  {
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    WorkerStamp st;
+    st.t_entry = t_entry;
+    st.d_plan = static_cast<uint32_t>(t_plan - t_entry);
+    st.d_first = has ? static_cast<uint32_t>(t_first - t_entry) : 0xFFFFFFFFu;
+    st.d_end = static_cast<uint32_t>(t_end - t_entry);
+    st.xcc = xcc & 0xF;
+    st.tiles = has ? static_cast<uint32_t>(pl.n) : 0u;
+    st.group = blockIdx.x;
+    // stamps follow the descriptors; one lane writes the worker's 32 bytes
+    if (lane == 0) reinterpret_cast<WorkerStamp*>(desc + d.n_workers)[w] = st;
+  }
+#endif
 
   // Rows no tile reaches are zeros: every row of an empty sequence, and in a
   // multi-token launch the rows past a sequence's query tokens (done last: off

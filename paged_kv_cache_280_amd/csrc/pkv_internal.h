@@ -69,8 +69,26 @@ __host__ __device__ inline int64_t record_floats(int R, int D) {
 __host__ __device__ inline int64_t records_bytes(int64_t workers, int R, int D) {
   return workers * 2 * record_floats(R, D) * static_cast<int64_t>(sizeof(float));
 }
+
+// Libraries built with PKV_TIMELINE (a measurement build, never the default) also
+// leave one WorkerStamp per decode worker after the descriptors: when the worker
+// entered the kernel, finished its plan, computed its first tile and finished, on
+// the 100 MHz s_memrealtime clock, and where it ran.
+struct WorkerStamp {
+  uint64_t t_entry;
+  uint32_t d_plan, d_first, d_end;  // ticks after t_entry (0xFFFFFFFF: no tile)
+  uint32_t xcc;                     // XCC (chiplet) the wave ran on
+  uint32_t tiles;                   // tiles of the worker's range
+  uint32_t group;                   // work-group index
+};
+#ifdef PKV_TIMELINE
+constexpr int64_t kStampBytes = sizeof(WorkerStamp);
+#else
+constexpr int64_t kStampBytes = 0;
+#endif
+
 inline int64_t workspace_bytes_for(int64_t workers, int R, int D) {
-  return records_bytes(workers, R, D) + workers * 16;
+  return records_bytes(workers, R, D) + workers * (16 + kStampBytes);
 }
 
 // Rows one multi-token launch can hold: two 16-column MFMA tiles per wave.

@@ -256,3 +256,36 @@ def test_decode_append_rejects_bad_arguments_on_the_host(lib):
         assert call(fp8, S=0, kn=None, vn=None, out=None) == 0
     assert call(True, ks=0.0) == -2
     assert call(True, vs=float("inf")) == -2
+
+
+def test_stream_probe_library_exports_its_header_and_checks_on_the_host():
+    """The read-stream probe bench.py reports as attainable bandwidth
+    (include/pkv_stream.h): it loads, exports what its header declares, and rejects
+    bad sizes before touching a device."""
+    import ctypes
+
+    import paged_kv_cache_280_amd.build as b
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pkv_stream.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"^\s*[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+    assert names == ["pkv_stream_read", "pkv_stream_read_pairs"]
+    if not os.path.exists(b.STREAM_LIB):
+        pytest.fail("libpkv_stream.so is not built")
+    import torch  # noqa: F401  (the probe binds to torch's HIP runtime, as the library does)
+
+    lib = ctypes.CDLL(b.STREAM_LIB)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.pkv_stream_read.argtypes = [p, ctypes.c_size_t, p, i32, p]
+    lib.pkv_stream_read_pairs.argtypes = [p, p, i64, p, i32, i32, i32, p, i32, i32, p]
+    assert lib.pkv_stream_read(0x1000, 100, 0x2000, 4, None) == -2        # not a multiple of 16
+    assert lib.pkv_stream_read(0x1008, 4096, 0x2000, 4, None) == -5       # misaligned
+    assert lib.pkv_stream_read(None, 4096, 0x2000, 4, None) == -1
+    call = lambda **o: lib.pkv_stream_read_pairs(
+        o.get("k", 0x1000), o.get("v", 0x2000), o.get("pu", 10), o.get("ids", 0x3000),
+        o.get("n", 5), o.get("unit", 4096), o.get("vb", 8), o.get("sink", 0x4000),
+        o.get("waves", 8), o.get("depth", 3), None)
+    assert call(unit=3000) == -3 and call(vb=4) == -3 and call(depth=4) == -3
+    assert call(pu=0) == -2 and call(waves=0) == -2
+    assert call(ids=None) == -1 and call(v=0x2004) == -5
+    assert call(n=0, ids=None) == 0
