@@ -369,32 +369,32 @@ def decode_units(case, elem_bytes):
     return np.concatenate(ids).astype(np.int32), run * D * elem_bytes
 
 
-def attainable_bandwidth(case, k_pool, v_pool, elem_bytes, reps=10, seq_bytes=4 << 30,
-                         sweep=False):
+def attainable_bandwidth(case, pools, elem_bytes, reps=10, seq_bytes=4 << 30, sweep=False):
     """The probe kernels of libpkv_stream.so on the same GPU in the same run: a
-    sequential 4 GiB read, and the decode call's own K/V reads (this workload's
-    first-layer pools, in the decode kernel's order and unit size, 3 waves per CU,
-    three units in flight) with 8- and 16-byte V loads, one call's bytes per launch.
-    Best of ``reps`` HIP-event-timed launches each.  ``sweep`` adds other wave counts
-    and in-flight depths."""
+    sequential 4 GiB read, and the decode call's own K/V reads (in the decode
+    kernel's order and unit size, 3 waves per CU, three units in flight) with 8- and
+    16-byte V loads, one call's bytes per launch.  Launch r reads the pools of layer
+    r mod layers, as the timed steps do, so that no launch finds the previous one's
+    bytes in the 256 MB last-level cache.  Best of ``reps`` HIP-event-timed launches
+    each.  ``sweep`` adds other wave counts and in-flight depths."""
     import ctypes
 
     import torch
 
     lib = stream_library()
-    dev = k_pool.device
+    dev = pools[0][1].device
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     cu = torch.cuda.get_device_properties(dev).multi_processor_count
 
     def best(fn, moved):
-        fn()
+        fn(reps)
         torch.cuda.synchronize()
         t = []
-        for _ in range(reps):
+        for r in range(reps):
             e0.record(stream)
-            fn()
+            fn(r)
             e1.record(stream)
             torch.cuda.synchronize()
             t.append(e0.elapsed_time(e1) / 1e3)
@@ -406,7 +406,7 @@ def attainable_bandwidth(case, k_pool, v_pool, elem_bytes, reps=10, seq_bytes=4 
     groups = cu * 8
     sink = torch.empty(groups * 256, dtype=torch.int32, device=dev)
 
-    def seq():
+    def seq(r):
         assert lib.pkv_stream_read(x.data_ptr(), seq_bytes, sink.data_ptr(), groups, sh) == 0
 
     res["read_gbs"] = best(seq, seq_bytes)
@@ -414,11 +414,13 @@ def attainable_bandwidth(case, k_pool, v_pool, elem_bytes, reps=10, seq_bytes=4 
     torch.cuda.empty_cache()
     ids, unit = decode_units(case, elem_bytes)
     idd = torch.from_numpy(ids).to(dev)
-    pool_units = k_pool.numel() * k_pool.element_size() // unit
+    k0 = pools[0][1]
+    pool_units = k0.numel() * k0.element_size() // unit
     sink = torch.empty(max(groups * 256, 16 * cu * 64), dtype=torch.int32, device=dev)
 
     def pairs_gbs(idv, vb, waves, depth):
-        def run():
+        def run(r):
+            _, k_pool, v_pool = pools[r % len(pools)]
             assert lib.pkv_stream_read_pairs(k_pool.data_ptr(), v_pool.data_ptr(), pool_units,
                                              idv.data_ptr(), idv.numel(), unit, vb,
                                              sink.data_ptr(), waves, depth, sh) == 0
@@ -434,7 +436,8 @@ def attainable_bandwidth(case, k_pool, v_pool, elem_bytes, reps=10, seq_bytes=4 
     res["kernels"] = ("libpkv_stream.so: sequential 4 GiB read, 16-byte lane loads (read_gbs); "
                       "this workload's K/V units in decode order, 16-byte K loads and 8- or "
                       "16-byte V loads, %d waves, 3 units in flight, one call's bytes per "
-                      "launch (pairs_v8_gbs, pairs_v16_gbs)" % (3 * cu))
+                      "launch, launches cycling over the %d layers' pools (pairs_v8_gbs, "
+                      "pairs_v16_gbs)" % (3 * cu, len(pools)))
     return res
 
 
@@ -600,8 +603,7 @@ def main():
 
         dev = torch.device("cuda:0")
         case, layers, desc, pools, tabs, lens, extra = build_workload(args, dev)
-        res = attainable_bandwidth(case, pools[0][1], pools[0][2],
-                                   1 if args.kv_dtype == "fp8" else 2, sweep=True)
+        res = attainable_bandwidth(case, pools, 1 if args.kv_dtype == "fp8" else 2, sweep=True)
         print(json.dumps({"probe": desc, **res}), flush=True)
         return
     if args.copy_calibration:
@@ -750,7 +752,7 @@ def main():
     kern_avg_s = float(np.mean(kern_ms)) / 1e3
     p10, p50, p90 = (float(x) * 1e3 for x in np.percentile(kern_ms, [10, 50, 90]))
     copy_line = copy_blocks_timing(pools, extra["pairs"], args) if "pairs" in extra else None
-    attain = attainable_bandwidth(case, pools[0][1], pools[0][2], kv_elem)
+    attain = attainable_bandwidth(case, pools, kv_elem)
     # the probe read shaped like this decode: 16-byte K loads, and V loads of 8 bytes
     # (bf16 pools) or 16 bytes (fp8 pools)
     attain_key = "pairs_v16_gbs" if fp8 else "pairs_v8_gbs"
