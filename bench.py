@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long",
                     choices=["long", "chat", "mix", "prefix", "tiny", "append"])
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="with --workload prefix: paged_attn_decode_shared over the batch's "
+                         "sharing groups (each prompt's prefix read once per call)")
     ap.add_argument("--with-append", action="store_true",
                     help="each layer call also appends the new token's K/V: the full "
                          "per-layer decode step")
@@ -119,7 +122,8 @@ def measured_traffic(workload_key):
 def prefix_case(args):
     """Shared-prefix parallel sampling: 16 prompts x 8 samples, a 1020-token prefix
     stored once per prompt, tails U_int[0, 256], built by the block manager (which
-    queues the copy-on-write pairs).  Returns (case, pairs, unique positions)."""
+    queues the copy-on-write pairs).  Returns (case, pairs, unique positions,
+    fragmentation, sharing groups of the batch (group offsets, prefix lengths))."""
     import workloads as wl
     from paged_kv_cache_280_amd.block_manager import BlockManager
 
@@ -147,7 +151,7 @@ def prefix_case(args):
     # counts once, as it is stored once)
     held = np.unique(pos // B).size * B
     frag = round((held - np.unique(pos).size) / held, 5)
-    return case, pairs, int(np.unique(pos).size), frag
+    return case, pairs, int(np.unique(pos).size), frag, bm.shared_groups(seqs, sc.num_samples)
 
 
 def build_workload(args, dev):
@@ -172,9 +176,10 @@ def build_workload(args, dev):
     elif args.workload == "prefix":
         # 16 layers with their own pools (2.2 GB), so the unique 134 MB of a layer
         # is not served from the last-level cache by the previous step
-        case, pairs, unique, frag = prefix_case(args)
+        case, pairs, unique, frag, groups = prefix_case(args)
         layers = case.num_layers
-        extra = {"pairs": pairs, "unique_tokens": unique, "fragmentation": frag}
+        extra = {"pairs": pairs, "unique_tokens": unique, "fragmentation": frag,
+                 "groups": groups}
         desc = ("shared-prefix sampling: 16 prompts x 8 samples, prefix 1020 stored once, tails "
                 "U[0,256], 16 layers, 32 q / 8 KV heads, head_dim 128, block %d" % case.block_size)
     elif args.workload == "tiny":
@@ -643,6 +648,19 @@ def main():
         ws = pkv.new_multi_workspace(S, Hq, Hkv, D, B, max_ctx, T, dev)
     else:
         ws = pkv.new_workspace(S, Hq, Hkv, D, B, max_ctx, dev)
+    shared = args.shared_prefix
+    if shared:
+        if "groups" not in extra or multi or fp8 or args.with_append:
+            raise SystemExit("--shared-prefix: bf16 decode of --workload prefix only")
+        gf_h, pl_h = extra["groups"]
+        max_group = int(np.diff(gf_h).max())
+        max_prefix = int(pl_h.max())
+        gfirst = torch.from_numpy(gf_h).to(dev)
+        plens = torch.from_numpy(pl_h).to(dev)
+        ws = torch.empty(pkv.paged_attn_decode_shared_workspace_bytes(
+            S, Hq, Hkv, D, B, max_ctx, len(gf_h) - 1, max_group, max_prefix), dtype=torch.uint8,
+            device=dev)
+        desc += ", shared-prefix decode (groups of %d, prefix %d)" % (max_group, max_prefix)
     outs = [torch.empty_like(p[0]) for p in pools]
     kv_elem = 1 if fp8 else 2
     per_call_bytes = decode_algorithmic_bytes(case.context_lens, Hq, Hkv, D, B, query_tokens=T,
@@ -699,6 +717,11 @@ def main():
                 sc = dict(k_scale=FP8_SCALE, v_scale=FP8_SCALE) if fp8 else {}
                 pkv.paged_attn_multi(q, k, v, tabs, lens, qlens, B, case.scale, outs[layer],
                                      workspace=ws, max_context_len=max_ctx, **sc)
+            elif shared:
+                pkv.paged_attn_decode_shared(q, k, v, tabs, lens, gfirst, plens, B, case.scale,
+                                             outs[layer], max_group_size=max_group,
+                                             max_prefix_len=max_prefix, workspace=ws,
+                                             max_context_len=max_ctx)
             elif fp8:
                 pkv.paged_attn_decode_fp8(q, k, v, tabs, lens, B, case.scale, FP8_SCALE, FP8_SCALE,
                                           outs[layer], workspace=ws, max_context_len=max_ctx)
@@ -760,7 +783,8 @@ def main():
     tokens_per_s = S * T / (ms_per_step / 1e3)
     kv_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
     achieved = per_call_bytes / kern_avg_s / 1e9
-    traffic = measured_traffic(args.workload + ("_q%d" % T if multi else "") + ("_fp8" if fp8 else ""))
+    traffic = measured_traffic(args.workload + ("_shared" if shared else "") +
+                               ("_q%d" % T if multi else "") + ("_fp8" if fp8 else ""))
 
     line = {
         "metric": METRIC_MULTI if multi else METRIC,
@@ -787,9 +811,11 @@ def main():
                         "calls": len(kern_ms)},
         "attainable": attain,
         "roofline": {"bound": "hbm",
-                     "kernel": ("paged_attn_multi" if multi else
-                                "paged_attn_decode_fp8" if fp8 else "paged_attn_decode") +
-                               " (decode_kernel + merge_kernel)",
+                     "kernel": ("paged_attn_decode_shared (prefix and tail passes, each "
+                                "decode_kernel + merge_kernel)" if shared else
+                                ("paged_attn_multi" if multi else
+                                 "paged_attn_decode_fp8" if fp8 else "paged_attn_decode") +
+                                " (decode_kernel + merge_kernel)"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

@@ -267,6 +267,59 @@ int32_t paged_attn_multi_fp8(const void* q, const void* k_cache, const void* v_c
                              void* stream);
 
 /*
+ * Paged decode attention over a batch whose sequences share a prefix physically
+ * (parallel sampling and beam search keep the first blocks of a forked prompt in
+ * one copy, "PagedAttention (vLLM)", troisinh.com, section "Copy-on-Write cho
+ * Beam Search").  The result is paged_attn_decode's (same formula, same layouts);
+ * the shared blocks are read once per group instead of once per sequence.
+ *
+ * Groups are runs of consecutive sequences: group v holds sequences
+ * group_first[v] .. group_first[v+1] - 1.  Sequence s shares its first
+ * prefix_lens[s] positions with the rest of its group: every member of a group has
+ * the same prefix_lens value, at most its own context length, and block-table
+ * entries 0 .. prefix_lens[s] / block_size - 1 equal to the group's first
+ * member's.  A prefix length is used rounded down to a multiple of
+ * max(16, block_size) and clamped to max_prefix_len; prefix length 0 (for example
+ * a group of one) is a plain decode of that sequence.
+ *
+ *   group_first     int32 [num_groups + 1] (device): group_first[0] = 0,
+ *                   non-decreasing, group_first[num_groups] = num_seqs
+ *   prefix_lens     int32 [num_seqs] (device)
+ *   num_groups      >= 1 when num_seqs > 0
+ *   max_group_size  host-side bound of the group sizes; (num_q_heads /
+ *                   num_kv_heads) * max_group_size <= 32 (else
+ *                   PKV_ERR_UNSUPPORTED): the group's query rows fill at most two
+ *                   16-column MFMA tiles.  Split larger groups.
+ *   max_prefix_len  host-side bound of prefix_lens, <= max_context_len
+ *   workspace       at least paged_attn_decode_shared_workspace_bytes(...) bytes,
+ *                   16-byte aligned, no initialisation needed
+ * Every other argument, check and error code is paged_attn_decode's (bf16 pools
+ * only).  Data that breaks the group contract gives meaningless outputs for the
+ * sequences concerned; no memory outside the arguments is touched.  Results are
+ * deterministic.  Enqueues up to four kernels: the prefix pass over the groups'
+ * shared positions (rows: members x heads of a KV head) and its merge into
+ * per-sequence prefix softmax states, then the decode of every sequence's
+ * remaining positions (each (sequence, KV head) pair starting from its prefix
+ * state) and its merge.
+ */
+size_t paged_attn_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size, int32_t max_context_len,
+                                                int32_t num_groups, int32_t max_group_size,
+                                                int32_t max_prefix_len);
+
+int32_t paged_attn_decode_shared(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* group_first, const int32_t* prefix_lens,
+                                 int32_t num_groups, int32_t max_group_size,
+                                 int32_t max_prefix_len, int32_t block_size, float scale,
+                                 void* out, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 int32_t max_context_len, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * KV append: write the key and value rows of num_tokens new tokens into their
  * slots.  Token i belongs to sequence token_seq[i] at position token_pos[i], and
  * its slot is (block_tables[seq][pos / block_size], pos % block_size): the block

@@ -23,6 +23,8 @@ from ._binding import (  # noqa: F401
     paged_attn_decode_append,
     paged_attn_decode_fp8,
     paged_attn_decode_noalloc,
+    paged_attn_decode_shared,
+    paged_attn_decode_shared_workspace_bytes,
     paged_attn_decode_workspace_bytes,
     paged_attn_multi,
     paged_attn_multi_workspace_bytes,

@@ -26,7 +26,8 @@ EXPORTS = ("pkv_abi_version", "pkv_status_string", "paged_attn_decode_workspace_
            "paged_attn_multi", "paged_attn_multi_fp8",
            "kv_append", "kv_append_fp8", "copy_blocks", "pkv_check_batch",
            "paged_attn_decode_append", "paged_attn_decode_append_fp8",
-           "paged_attn_decode_noalloc")
+           "paged_attn_decode_noalloc", "paged_attn_decode_shared_workspace_bytes",
+           "paged_attn_decode_shared")
 
 
 class PkvError(RuntimeError):
@@ -92,6 +93,11 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_decode_append_fp8.argtypes = [p, p, p, p, p, p, p, i32, f32, f32, f32, p, i32,
                                                  i32, i32, i32, i32, i64, i32, p, sz, p]
     lib.paged_attn_decode_append_fp8.restype = i32
+    lib.paged_attn_decode_shared_workspace_bytes.argtypes = [i32] * 9
+    lib.paged_attn_decode_shared_workspace_bytes.restype = sz
+    lib.paged_attn_decode_shared.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, f32, p, i32,
+                                             i32, i32, i32, i32, i64, i32, p, sz, p]
+    lib.paged_attn_decode_shared.restype = i32
     _lib = lib
     return lib
 
@@ -218,6 +224,61 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
                                    _stream_handle(q, stream))
     if rc != 0:
         raise PkvError(rc, "paged_attn_decode")
+    return out
+
+
+def paged_attn_decode_shared_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             block_size, max_context_len, num_groups,
+                                             max_group_size, max_prefix_len) -> int:
+    return int(load_library().paged_attn_decode_shared_workspace_bytes(
+        int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size),
+        int(max_context_len), int(num_groups), int(max_group_size), int(max_prefix_len)))
+
+
+def paged_attn_decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_first,
+                             prefix_lens, block_size, scale, out=None, *, max_group_size,
+                             max_prefix_len, max_context_len=None, workspace=None, stream=None):
+    """Paged decode over a batch whose groups of consecutive sequences share a prefix
+    (see ``include/pkv.h``): ``group_first`` int32 [num_groups + 1] (device) are
+    the group offsets, ``prefix_lens`` int32 [num_seqs] (device) each sequence's
+    shared positions; ``max_group_size`` and ``max_prefix_len`` are host-side
+    bounds (``BlockManager.shared_groups`` gives all four).  Returns ``out``."""
+    import torch
+
+    lib = load_library()
+    S, Hq, Hkv, D, NB, M = decode_shapes(q, k_cache, v_cache, block_tables, context_lens,
+                                         block_size)
+    _check(group_first.dim() == 1 and group_first.shape[0] >= 1, "group_first: [num_groups + 1]")
+    _check(prefix_lens.dim() == 1 and prefix_lens.shape[0] == S, "prefix_lens: [num_seqs]")
+    for t in (group_first, prefix_lens):
+        _check(t.dtype == torch.int32 and t.is_contiguous() and t.device == q.device,
+               "group_first/prefix_lens: contiguous int32 on q's device")
+    NG = int(group_first.shape[0]) - 1
+    if max_context_len is None:
+        max_context_len = M * int(block_size)
+    with _on_stream(q, stream):
+        if out is None:
+            out = torch.empty_like(q)
+        _check(out.shape == q.shape and out.dtype == torch.bfloat16 and out.is_contiguous()
+               and out.device == q.device, "out must match q")
+        if workspace is None:
+            need = paged_attn_decode_shared_workspace_bytes(S, Hq, Hkv, D, block_size,
+                                                            max_context_len, NG, max_group_size,
+                                                            max_prefix_len)
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        _check(workspace.is_cuda and workspace.device == q.device and workspace.is_contiguous(),
+               "workspace must be a contiguous tensor on q's device")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        rc = lib.paged_attn_decode_shared(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                          block_tables.data_ptr(), context_lens.data_ptr(),
+                                          group_first.data_ptr(), prefix_lens.data_ptr(), NG,
+                                          int(max_group_size), int(max_prefix_len),
+                                          int(block_size), float(scale), out.data_ptr(), S, Hq,
+                                          Hkv, D, M, NB, int(max_context_len),
+                                          workspace.data_ptr(), ws_bytes,
+                                          _stream_handle(q, stream))
+    if rc != 0:
+        raise PkvError(rc, "paged_attn_decode_shared")
     return out
 
 

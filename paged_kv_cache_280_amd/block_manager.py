@@ -242,6 +242,43 @@ class BlockManager:
             lens[i] = self._lens[s]
         return tables, lens
 
+    def shared_groups(self, seqs, max_group_size: int):
+        """Sharing groups of a decode batch taken in the order of ``seqs``, for
+        paged_attn_decode_shared: runs of consecutive sequences (at most
+        max_group_size each) that start with the same physical blocks, as forks of
+        one prompt do ("PagedAttention (vLLM)", section "Copy-on-Write cho Beam
+        Search").  A run grows while the next sequence shares at least the run's
+        current prefix with its first member.  The prefix is the positions every
+        member holds in common blocks, rounded down to a multiple of
+        max(16, block_size).  Returns (group_first int32 [num_groups + 1],
+        prefix_lens int32 [len(seqs)]); a group of one has prefix 0."""
+        seqs = list(seqs)
+        align = max(16, self.block_size)
+        B = self.block_size
+
+        def shared_positions(a, b):
+            ta, tb = self._tables[a], self._tables[b]
+            n = 0
+            while n < min(len(ta), len(tb)) and ta[n] == tb[n]:
+                n += 1
+            p = min(n * B, self._lens[a], self._lens[b])
+            return p - p % align
+
+        first, prefix = [0], np.zeros(len(seqs), dtype=np.int32)
+        i = 0
+        while i < len(seqs):
+            j, P = i + 1, 0
+            while j < len(seqs) and j - i < max_group_size:
+                pj = shared_positions(seqs[i], seqs[j])
+                if pj < align or (j > i + 1 and pj < P):
+                    break
+                P = pj if j == i + 1 else P
+                j += 1
+            prefix[i:j] = P if j - i > 1 else 0
+            first.append(j)
+            i = j
+        return np.asarray(first, dtype=np.int32), prefix
+
     def sequences(self):
         return list(self._tables)
 

@@ -339,6 +339,129 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   return PKV_OK;
 }
 
+// Shared-prefix decode.  Workspace: the larger of the two passes' records and
+// descriptors, then (256-byte aligned) the prefix states, one record of
+// record_floats(num_q_heads, head_dim) floats per sequence.
+struct SharedLayout {
+  int64_t workers_prefix, workers_tail;
+  int32_t rows_prefix;
+  int64_t state_off, bytes;
+};
+
+SharedLayout shared_layout(int cu, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t max_context_len, int32_t num_groups,
+                           int32_t max_group_size, int32_t max_prefix_len) {
+  SharedLayout l;
+  const int32_t group = num_q_heads / num_kv_heads;
+  l.rows_prefix = group * max_group_size;
+  l.workers_prefix = worker_count(cu, num_groups, num_kv_heads, max_prefix_len);
+  l.workers_tail = worker_count(cu, num_seqs, num_kv_heads, max_context_len);
+  const int64_t a = workspace_bytes_for(l.workers_prefix, l.rows_prefix, head_dim);
+  const int64_t b = workspace_bytes_for(l.workers_tail, group, head_dim);
+  l.state_off = ((a > b ? a : b) + 255) / 256 * 256;
+  l.bytes = l.state_off + static_cast<int64_t>(num_seqs) * record_floats(num_q_heads, head_dim) *
+                              static_cast<int64_t>(sizeof(float));
+  return l;
+}
+
+int32_t check_shared(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs,
+                     int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len,
+                     int32_t max_context_len) {
+  if (num_groups < 0 || max_group_size <= 0 || max_prefix_len < 0 ||
+      max_prefix_len > max_context_len || (num_seqs > 0 && num_groups == 0))
+    return PKV_ERR_SHAPE;
+  if ((num_q_heads / num_kv_heads) * max_group_size > kMaxRows) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+int32_t shared_impl(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* group_first, const int32_t* prefix_lens, int32_t num_groups,
+                    int32_t max_group_size, int32_t max_prefix_len, int32_t block_size,
+                    float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                    int64_t num_blocks, int32_t max_context_len, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int32_t st = check_shapes(block_size, scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                            max_blocks_per_seq, num_blocks, max_context_len);
+  if (st != PKV_OK) return st;
+  st = check_shared(num_q_heads, num_kv_heads, num_seqs, num_groups, max_group_size,
+                    max_prefix_len, max_context_len);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !group_first ||
+      !prefix_lens || !out || !workspace)
+    return PKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(workspace))
+    return PKV_ERR_ALIGNMENT;
+  const int cu = current_cu_count();
+  if (cu <= 0) return PKV_ERR_DEVICE;
+  const SharedLayout lay = shared_layout(cu, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_context_len, num_groups, max_group_size,
+                                         max_prefix_len);
+  if (static_cast<int64_t>(workspace_bytes) < lay.bytes) return PKV_ERR_WORKSPACE;
+  const int32_t group = num_q_heads / num_kv_heads;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  DecodeBuffers b{};
+  b.q = static_cast<const uint16_t*>(q);
+  b.k = k_cache;
+  b.v = v_cache;
+  b.tables = block_tables;
+  b.out = static_cast<uint16_t*>(out);
+  b.ws = static_cast<float*>(workspace);
+  b.state = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.state_off);
+  DecodeDims d{};
+  d.Hq = num_q_heads;
+  d.Hkv = num_kv_heads;
+  d.G = group;
+  d.M = max_blocks_per_seq;
+  d.NB = num_blocks;
+  d.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+  d.v_scale = 1.0f;
+  d.k_scale = 1.0f;
+  d.pre_align = block_size > kTile ? block_size : kTile;
+  d.pre_cap = max_prefix_len;
+  d.seqs = num_seqs;
+
+  // prefix pass: group v's members are its T query tokens (rows member * G + head)
+  if (max_prefix_len >= d.pre_align && num_groups > 0) {
+    DecodeDims a = d;
+    b.lens = prefix_lens;
+    b.qlens = group_first;
+    a.S = num_groups;
+    a.pair_mode = use_pair_mode(cu, num_groups, num_kv_heads, max_prefix_len, false) ? 1 : 0;
+    a.n_workers = a.pair_mode ? num_groups * num_kv_heads : static_cast<int32_t>(lay.workers_prefix);
+    a.Qmax = max_group_size;
+    a.Qc = max_group_size;
+    a.q_off = 0;
+    a.R = lay.rows_prefix;
+    set_units(a, a.R, false);
+    if (launch_shared_prefix(b, a, head_dim, block_size,
+                             merge_groups_for(a.n_workers, cu), s) != hipSuccess)
+      return PKV_ERR_LAUNCH;
+  } else {
+    d.pre_cap = 0;  // no prefix anywhere: the tail pass is a plain decode
+  }
+  // tail pass: every sequence from its prefix on; pairs with a prefix always go
+  // through the merge, which folds the prefix state first
+  b.lens = context_lens;
+  b.qlens = prefix_lens;
+  d.S = num_seqs;
+  d.pair_mode = 0;
+  d.n_workers = static_cast<int32_t>(lay.workers_tail);
+  d.Qmax = 1;
+  d.Qc = 1;
+  d.q_off = 0;
+  d.R = group;
+  set_units(d, group, false);
+  if (launch_shared_tail(b, d, head_dim, block_size, merge_groups_for(d.n_workers, cu), s) !=
+      hipSuccess)
+    return PKV_ERR_LAUNCH;
+  return PKV_OK;
+}
+
 int32_t append_impl(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                     const int32_t* block_tables, const int32_t* token_seq,
                     const int32_t* token_pos, int32_t num_tokens, int32_t num_seqs,
@@ -415,6 +538,43 @@ size_t paged_attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
       std::max(pkv::worker_count(cu, num_seqs, num_kv_heads, max_context_len, false),
                pkv::worker_count(cu, num_seqs, num_kv_heads, max_context_len, true));
   return pkv::workspace_for(workers, num_q_heads / num_kv_heads, head_dim);
+}
+
+size_t paged_attn_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size, int32_t max_context_len,
+                                                int32_t num_groups, int32_t max_group_size,
+                                                int32_t max_prefix_len) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+      num_q_heads % num_kv_heads != 0 || !pkv::supported_head_dim(head_dim) ||
+      !pkv::supported_block_size(block_size) || num_q_heads / num_kv_heads > pkv::kMaxGroup)
+    return 0;
+  if (pkv::check_shared(num_q_heads, num_kv_heads, num_seqs, num_groups, max_group_size,
+                        max_prefix_len, max_context_len) != PKV_OK)
+    return 0;
+  const int cu = pkv::current_cu_count();
+  if (cu <= 0) return 0;
+  return static_cast<size_t>(pkv::shared_layout(cu, num_seqs, num_q_heads, num_kv_heads,
+                                                head_dim, max_context_len, num_groups,
+                                                max_group_size, max_prefix_len)
+                                 .bytes);
+}
+
+int32_t paged_attn_decode_shared(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 const int32_t* group_first, const int32_t* prefix_lens,
+                                 int32_t num_groups, int32_t max_group_size,
+                                 int32_t max_prefix_len, int32_t block_size, float scale,
+                                 void* out, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 int32_t max_context_len, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return pkv::shared_impl(q, k_cache, v_cache, block_tables, context_lens, group_first,
+                          prefix_lens, num_groups, max_group_size, max_prefix_len, block_size,
+                          scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                          max_blocks_per_seq, num_blocks, max_context_len, workspace,
+                          workspace_bytes, stream);
 }
 
 int32_t paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,

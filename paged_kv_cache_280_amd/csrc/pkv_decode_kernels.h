@@ -117,17 +117,43 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
 // T = query_lens[s] positions (T clamped into [0, min(L, Qmax)]); the launch
 // takes the Tc of them in [q_off, q_off + Qc), and its context ends at the
 // position the last of those sees, so L_c = L - T + q_off + Tc (0 when Tc = 0).
+//
+// Shared-prefix launches (kShare != 0) run in two passes.  The prefix pass
+// (kShare = 1, a multi-token launch) takes group v of sequences first ..
+// first + T - 1 (first = qlens[v], T = qlens[v+1] - first clamped into [0, Qmax]:
+// qlens holds the group offsets) as one set of rows: its context is the first
+// P positions of the group's first sequence, P = prefix_positions(lens[first])
+// (lens holds the per-sequence prefix lengths).  The tail pass (kShare = 2, a
+// decode launch) takes sequence s from position P = prefix_positions(qlens[s])
+// on (qlens holds the prefix lengths): L = context_lens[s] - P.  x is `first` in
+// the prefix pass and P in the tail pass.
 struct SeqLen {
-  int32_t L, T;
+  int32_t L, T, x;
 };
 
-template <bool kCausal>
+// Positions of a shared prefix as the launches use them: clamped into
+// [0, min(cap, d.pre_cap)] and rounded down to a whole number of tiles and blocks
+// (d.pre_align).
+__device__ __forceinline__ int32_t prefix_positions(int32_t p, const DecodeDims& d, int32_t cap) {
+  const int32_t c = clamp_len(p, min(cap, d.pre_cap));
+  return c - c % d.pre_align;
+}
+
+template <bool kCausal, int kShare = 0>
 __device__ __forceinline__ SeqLen seq_len(const int32_t* __restrict__ lens,
                                           const int32_t* __restrict__ qlens, const DecodeDims& d,
                                           int32_t cap, int32_t s) {
+  if constexpr (kShare == 1) {
+    const int32_t first = min(max(qlens[s], 0), d.seqs - 1);
+    const int32_t T = clamp_len(qlens[s + 1] - first, min(d.Qmax, d.seqs - first));
+    return SeqLen{T > 0 ? prefix_positions(lens[first], d, cap) : 0, T, first};
+  }
   // decode with append: the tiles cover all but the newest position
   const int32_t L = max(clamp_len(lens[s], cap) - d.len_off, 0);
-  if constexpr (!kCausal) {
+  if constexpr (kShare == 2) {
+    const int32_t P = prefix_positions(qlens[s], d, cap);
+    return SeqLen{max(L - P, 0), 1, P};
+  } else if constexpr (!kCausal) {
     return SeqLen{L, 1};
   } else {
     const int32_t T = clamp_len(qlens[s], min(L, d.Qmax));
@@ -161,11 +187,12 @@ struct Chunk {
   int32_t base, L, Tq, T, P, incT, incP;
 };
 
-template <bool kCausal>
+template <bool kCausal, int kShare = 0>
 __device__ __forceinline__ SeqLen lane_len(const int32_t* __restrict__ lens,
                                            const int32_t* __restrict__ qlens, const DecodeDims& d,
                                            int32_t cap, int32_t base, int lane) {
-  return base + lane < d.S ? seq_len<kCausal>(lens, qlens, d, cap, base + lane) : SeqLen{0, 0};
+  return base + lane < d.S ? seq_len<kCausal, kShare>(lens, qlens, d, cap, base + lane)
+                           : SeqLen{0, 0, 0};
 }
 
 // One shuffle scan: the unit scan follows from the tile scan and the count of
@@ -237,7 +264,7 @@ struct WorkerPlan {
 constexpr int kPlanChunks = 4;
 
 // Passes over the chunks in order: f(chunk, acc_u, acc_t) returns true to stop.
-template <bool kCausal, typename F>
+template <bool kCausal, int kShare = 0, typename F>
 __device__ __forceinline__ void for_chunks(const int32_t* __restrict__ lens,
                                            const int32_t* __restrict__ qlens,
                                            const DecodeDims& d, int32_t cap,
@@ -252,7 +279,8 @@ __device__ __forceinline__ void for_chunks(const int32_t* __restrict__ lens,
     acc_t += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, kWave - 1)) * d.Hkv;
   }
   for (int32_t base = kPlanChunks * kWave; base < d.S; base += kWave) {
-    const Chunk c = make_chunk(base, lane_len<kCausal>(lens, qlens, d, cap, base, lane), d, lane);
+    const Chunk c =
+        make_chunk(base, lane_len<kCausal, kShare>(lens, qlens, d, cap, base, lane), d, lane);
     if (f(c, acc_u, acc_t)) return;
     acc_u += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, kWave - 1)) * d.Hkv;
     acc_t += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, kWave - 1)) * d.Hkv;
@@ -275,11 +303,11 @@ __device__ __forceinline__ void range_of(int64_t w, int64_t U, int64_t N, int64_
 }
 
 // Returns false when worker w has no tile.
-template <bool kCausal>
+template <bool kCausal, int kShare = 0>
 __device__ bool plan_worker(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
                             const DecodeDims& d, int32_t cap, int64_t w, int lane, WorkerPlan& p) {
   if (d.S <= kWave) {  // units are tiles: one scan, one lookup
-    const SeqLen sl = lane_len<kCausal>(lens, qlens, d, cap, 0, lane);
+    const SeqLen sl = lane_len<kCausal, kShare>(lens, qlens, d, cap, 0, lane);
     const int32_t T = tiles_of(sl.L);
     const int32_t incl = wave_inclusive_scan(T);
     p.U = static_cast<int64_t>(__builtin_amdgcn_readlane(incl, kWave - 1)) * d.Hkv;
@@ -302,14 +330,15 @@ __device__ bool plan_worker(const int32_t* __restrict__ lens, const int32_t* __r
   }
   SeqLen T0[kPlanChunks];  // all lengths read first: one round trip
 #pragma unroll
-  for (int k = 0; k < kPlanChunks; ++k) T0[k] = lane_len<kCausal>(lens, qlens, d, cap, k * kWave, lane);
+  for (int k = 0; k < kPlanChunks; ++k)
+    T0[k] = lane_len<kCausal, kShare>(lens, qlens, d, cap, k * kWave, lane);
   Chunk Tc[kPlanChunks];
 #pragma unroll
   for (int k = 0; k < kPlanChunks; ++k)
     if (k * kWave < d.S) Tc[k] = make_chunk(k * kWave, T0[k], d, lane);
   // pass 1: total units and tiles
   int64_t U = 0, tiles = 0;
-  for_chunks<kCausal>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t, int64_t) {
+  for_chunks<kCausal, kShare>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t, int64_t) {
     U += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incP, kWave - 1)) * d.Hkv;
     tiles += static_cast<int64_t>(__builtin_amdgcn_readlane(c.incT, kWave - 1)) * d.Hkv;
     return false;
@@ -323,7 +352,7 @@ __device__ bool plan_worker(const int32_t* __restrict__ lens, const int32_t* __r
   UnitLoc lu, le;
   bool found_u = false, found_e = ue >= U;
   int64_t first = 0, last = tiles;
-  for_chunks<kCausal>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t au, int64_t at) {
+  for_chunks<kCausal, kShare>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t au, int64_t at) {
     if (!found_u && locate_in(c, d, au, at, u, lu)) {
       found_u = true;
       first = first_tile(lu);
@@ -340,7 +369,7 @@ __device__ bool plan_worker(const int32_t* __restrict__ lens, const int32_t* __r
     // u lies past the last tile of its sequence: the range starts at the next
     // sequence that holds units
     const int64_t next = lu.start + static_cast<int64_t>(lu.P) * d.Hkv;
-    for_chunks<kCausal>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t au, int64_t at) {
+    for_chunks<kCausal, kShare>(lens, qlens, d, cap, Tc, lane, [&](const Chunk& c, int64_t au, int64_t at) {
       return locate_in(c, d, au, at, next, lu);
     });
   }
@@ -367,13 +396,13 @@ struct PairCursor {
 
 // Pair mode: worker w takes (sequence w / Hkv, KV head w % Hkv) whole.  Returns
 // false for workers past the pairs and for empty sequences.
-template <bool kCausal>
+template <bool kCausal, int kShare = 0>
 __device__ bool plan_pair(const int32_t* __restrict__ lens, const int32_t* __restrict__ qlens,
                           const DecodeDims& d, int32_t cap, int64_t w, WorkerPlan& p) {
   if (w >= static_cast<int64_t>(d.S) * d.Hkv) return false;
   const int32_t s = static_cast<int32_t>(w / d.Hkv);
   const int32_t g = static_cast<int32_t>(w - static_cast<int64_t>(s) * d.Hkv);
-  const SeqLen sl = seq_len<kCausal>(lens, qlens, d, cap, s);
+  const SeqLen sl = seq_len<kCausal, kShare>(lens, qlens, d, cap, s);
   const int32_t T = tiles_of(sl.L);
   if (T == 0) return false;
   p.L = sl.L;
@@ -648,6 +677,7 @@ struct Ctx {
   const uint16_t* __restrict__ v_new;
   T* kw;                               // the pools, written (the newest rows)
   T* vw;
+  float* __restrict__ state;           // shared-prefix launches: prefix softmax states
 };
 
 // Position in a worker's stream of tiles: tile t of (sequence s, KV head g); L
@@ -656,9 +686,10 @@ struct Ctx {
 struct Cursor {
   int64_t start;
   int32_t s, g, t, T, L, Tq;
+  int32_t x;  // shared-prefix launches: SeqLen::x of s
 };
 
-template <bool kCausal, typename Cx>
+template <bool kCausal, int kShare = 0, typename Cx>
 __device__ __forceinline__ void advance(Cursor& c, const Cx& cx, const DecodeDims& d,
                                         int32_t cap) {
   if (++c.t < c.T) return;
@@ -669,9 +700,10 @@ __device__ __forceinline__ void advance(Cursor& c, const Cx& cx, const DecodeDim
   do {
     ++c.s;
     if (c.s < d.S) {
-      const SeqLen sl = seq_len<kCausal>(cx.lens, cx.qlens, d, cap, c.s);
+      const SeqLen sl = seq_len<kCausal, kShare>(cx.lens, cx.qlens, d, cap, c.s);
       c.L = sl.L;
       c.Tq = sl.T;
+      if constexpr (kShare != 0) c.x = sl.x;
     } else {
       c.L = 1;  // past the batch only at the very end
       c.Tq = 1;
@@ -680,14 +712,23 @@ __device__ __forceinline__ void advance(Cursor& c, const Cx& cx, const DecodeDim
   c.T = tiles_of(c.L);
 }
 
-template <int D, int B, typename Tile, typename Cx>
+// Block-table entries of a pair's tiles: row s; the prefix pass reads the row of
+// the group's first sequence, the tail pass skips the prefix's blocks.
+template <int B, int kShare>
+__device__ __forceinline__ int64_t table_offset(const DecodeDims& d, const Cursor& c) {
+  if constexpr (kShare == 1) return static_cast<int64_t>(c.x) * d.M;
+  if constexpr (kShare == 2) return static_cast<int64_t>(c.s) * d.M + c.x / B;
+  return static_cast<int64_t>(c.s) * d.M;
+}
+
+template <int D, int B, int kShare = 0, typename Tile, typename Cx>
 __device__ __forceinline__ void load_at(Tile& r, const Cx& cx, const DecodeDims& d,
                                         const Cursor& c, int lane) {
   constexpr int64_t kTileElems = static_cast<int64_t>(D) * B;
   PairCursor<typename Tile::Elem> pc;
   pc.k = cx.k;
   pc.v = cx.v;
-  pc.trow = cx.tables + static_cast<int64_t>(c.s) * d.M;
+  pc.trow = cx.tables + table_offset<B, kShare>(d, c);
   pc.block_stride = kTileElems * d.Hkv;
   pc.head_off = kTileElems * c.g;
   pc.nb = d.NB;
@@ -695,9 +736,11 @@ __device__ __forceinline__ void load_at(Tile& r, const Cx& cx, const DecodeDims&
   r.load(pc, c.t, lane);
 }
 
-// First q/out row of a (sequence, KV head) pair.
-template <bool kCausal>
+// First q/out row of a (sequence, KV head) pair.  In the prefix pass the rows
+// of group member qi are those of sequence first + qi (q is [S][Hq][D]).
+template <bool kCausal, int kShare = 0>
 __device__ __forceinline__ int64_t pair_row(const DecodeDims& d, const Cursor& c) {
+  if constexpr (kShare == 1) return static_cast<int64_t>(c.x) * d.Hq + c.g * d.G;
   const int64_t seq_rows = kCausal ? static_cast<int64_t>(d.Qmax) * d.Hq : d.Hq;
   return c.s * seq_rows + c.g * d.G;
 }
@@ -717,11 +760,11 @@ __device__ __forceinline__ bool live(const Cols<NC>& cl, int j, const Cursor& c)
 // Score MFMA B operand: lane holds q[row of column j][c*32 + (lane/16)*8 .. +7]
 // (with fp8 K, the permuted dims (c/2)*64 + (lane/16)*16 + (c%2)*8 .. +7); zeros
 // for columns the launch does not compute.
-template <int D, int NC, bool kCausal, bool kFp8, typename Cx>
+template <int D, int NC, bool kCausal, bool kFp8, int kShare = 0, typename Cx>
 __device__ __forceinline__ void load_q(bf16x8_t (&qop)[NC][D / 32], const Cx& cx,
                                        const DecodeDims& d, const Cursor& c, const Cols<NC>& cl,
                                        int lane) {
-  const int64_t r0 = pair_row<kCausal>(d, c);
+  const int64_t r0 = pair_row<kCausal, kShare>(d, c);
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     if (live<NC, kCausal>(cl, j, c)) {
@@ -745,19 +788,45 @@ __device__ __forceinline__ void load_q(bf16x8_t (&qop)[NC][D / 32], const Cx& cx
   }
 }
 
+// Prefix softmax states of a shared-prefix launch: one record of record_floats(Hq,
+// D) floats per sequence (O[Hq][D], then m[Hq], then l[Hq]), unnormalised: O and l
+// are sums weighted by 2^(score - m).  Row `gr` (= sequence * Hq + head) has its O
+// at state_o(gr), m at state_m(gr) and l at state_m(gr) + Hq.
+template <int D>
+__device__ __forceinline__ int64_t state_o(const DecodeDims& d, int64_t gr) {
+  const int64_t s = gr / d.Hq;
+  return s * record_floats(d.Hq, D) + (gr - s * d.Hq) * D;
+}
+template <int D>
+__device__ __forceinline__ int64_t state_m(const DecodeDims& d, int64_t gr) {
+  const int64_t s = gr / d.Hq;
+  return s * record_floats(d.Hq, D) + static_cast<int64_t>(d.Hq) * D + (gr - s * d.Hq);
+}
+
 // End of a segment: the output rows when it covered the whole pair, else a partial
-// record (O, then m, then l) in slot `rec`.
-template <int D, int NC, bool kCausal, typename Cx>
+// record (O, then m, then l) in slot `rec`.  The prefix pass writes a whole pair's
+// rows as prefix states instead of outputs.
+template <int D, int NC, bool kCausal, int kShare = 0, typename Cx>
 __device__ void finish_segment(const Cx& cx, const DecodeDims& d, const SegState<D> (&st)[NC],
                                const Cursor& c, const Cols<NC>& cl, bool whole, int64_t rec,
                                int lane) {
-  const int64_t r0 = pair_row<kCausal>(d, c);
+  const int64_t r0 = pair_row<kCausal, kShare>(d, c);
   const int32_t R = pair_rows<kCausal>(d);
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     if (!live<NC, kCausal>(cl, j, c)) continue;
     const float l_tot = st[j].l[0];
-    if (whole) {
+    if (kShare == 1 && whole) {
+      const int64_t gr = r0 + cl.row[j];
+      float* orow = cx.state + state_o<D>(d, gr) + (lane >> 4) * 4;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<f32x4_t*>(orow + mt * 16) = st[j].o[mt];
+      if (lane < 16) {
+        float* ml = cx.state + state_m<D>(d, gr);
+        ml[0] = st[j].m;
+        ml[d.Hq] = l_tot;
+      }
+    } else if (whole) {
       const float inv = d.v_scale / l_tot;
       uint16_t* orow = cx.out + (r0 + cl.row[j]) * D + (lane >> 4) * 4;
 #pragma unroll
@@ -778,6 +847,30 @@ __device__ void finish_segment(const Cx& cx, const DecodeDims& d, const SegState
         base[R * D + R + n] = l_tot;
       }
     }
+  }
+}
+
+// Tail pass of a shared-prefix launch: the prefix state of pair (s, g) as the
+// initial softmax state of the segment that starts at its first tail tile (one
+// column tile: column lane%16 is head g*G + lane%16; columns past G stay empty).
+template <int D, typename Cx>
+__device__ __forceinline__ void load_prefix_state(SegState<D>& ps, const Cx& cx,
+                                                  const DecodeDims& d, const Cursor& c, int lane) {
+  const int32_t n = lane & 15;
+  if (n < d.G) {
+    const int64_t gr = static_cast<int64_t>(c.s) * d.Hq + c.g * d.G + n;
+    const float* o = cx.state + state_o<D>(d, gr) + (lane >> 4) * 4;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) ps.o[mt] = *reinterpret_cast<const f32x4_t*>(o + mt * 16);
+    const float* ml = cx.state + state_m<D>(d, gr);
+    ps.m = ml[0];
+    const float l = ml[d.Hq];
+    ps.l = f32x4_t{l, l, l, l};
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) ps.o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    ps.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    ps.m = -INFINITY;
   }
 }
 
@@ -948,8 +1041,12 @@ __device__ void one_token(const Cx& cx, const DecodeDims& d, int64_t s, int lane
 // One worker: the n tiles of its range in order, with loads running kPipe-1
 // tiles ahead of the arithmetic across (sequence, head) boundaries; the query of a
 // pair is fetched with the pair's first tile.  Returns the descriptor of the split
-// pair this worker opens (s = -1 if none).
-template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, typename Cx>
+// pair this worker opens (s = -1 if none).  In the tail pass of a shared-prefix
+// launch the segment that starts at a pair's first tile starts from the pair's
+// prefix state (fetched with that tile) instead of an empty one, so whole pairs
+// and the records of split ones already hold the prefix.
+template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShare = 0,
+          typename Cx>
 __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& pl, int64_t w,
                            int lane, uint64_t& t_first) {
   const int32_t cap = d.M * B;
@@ -960,6 +1057,7 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
   lc.s = pl.s;
   lc.L = pl.L;
   lc.Tq = pl.Tq;
+  lc.x = kShare != 0 ? seq_len<kCausal, kShare>(cx.lens, cx.qlens, d, cap, pl.s).x : 0;
   lc.T = tiles_of(lc.L);
   lc.g = pl.g;
   lc.t = pl.t;
@@ -970,6 +1068,11 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
   bf16x8_t qb[kPipe][NC][D / 32];
   bf16x8_t qc[NC][D / 32];
   SegState<D> st[NC];
+  // tail pass: one prefix state fetched with the first tile of its pair (worker
+  // tile ps_tile; -1: none pending).  A pair that starts while it is taken (pairs
+  // of one or two tiles) reads its state when its first tile is computed.
+  SegState<D> ps;
+  int32_t ps_tile = -1;
   int32_t lim_abs[NC];  // last position column j sees (multi-token launches)
   int32_t seg_t0 = cc.t;
   int64_t rec = 2 * w;  // first segment -> slot 0, later ones -> slot 1
@@ -985,9 +1088,16 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
     }
   };
   auto load_step = [&](int slot, int32_t li) {
-    if (lc.t == 0 || li == 0) load_q<D, NC, kCausal, kFp8>(qb[slot], cx, d, lc, cl, lane);
-    load_at<D, B>(r[slot], cx, d, lc, lane);
-    advance<kCausal>(lc, cx, d, cap);
+    if (lc.t == 0 || li == 0) load_q<D, NC, kCausal, kFp8, kShare>(qb[slot], cx, d, lc, cl, lane);
+    if constexpr (kShare == 2) {
+      static_assert(NC == 1, "the tail pass has one query row per head");
+      if (lc.t == 0 && lc.x > 0 && ps_tile < 0) {
+        load_prefix_state<D>(ps, cx, d, lc, lane);
+        ps_tile = li;
+      }
+    }
+    load_at<D, B, kShare>(r[slot], cx, d, lc, lane);
+    advance<kCausal, kShare>(lc, cx, d, cap);
   };
   auto compute_step = [&](int slot, int32_t i) {
     if (cc.t == 0 || i == 0) {
@@ -995,12 +1105,23 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
       for (int j = 0; j < NC; ++j) {
 #pragma unroll
         for (int k = 0; k < D / 32; ++k) qc[j][k] = qb[slot][j][k];
+        if (kShare == 2 && cc.t == 0 && cc.x > 0) {  // the pair starts from its prefix
+          if (ps_tile == i) {
+            st[j] = ps;
+            ps_tile = -1;
+          } else {
+            load_prefix_state<D>(st[j], cx, d, cc, lane);
+          }
+        } else {
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt) st[j].o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        st[j].l = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        st[j].m = -INFINITY;
-        // query token qi sits at position L - Tq + qi; other columns see the context
-        lim_abs[j] = live<NC, kCausal>(cl, j, cc) ? cc.L - cc.Tq + cl.qi[j] : cc.L - 1;
+          for (int mt = 0; mt < D / 16; ++mt) st[j].o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          st[j].l = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          st[j].m = -INFINITY;
+        }
+        // query token qi sits at position L - Tq + qi; other columns (and every
+        // row of the prefix pass) see the whole context
+        lim_abs[j] = (kShare != 1 && live<NC, kCausal>(cl, j, cc)) ? cc.L - cc.Tq + cl.qi[j]
+                                                                   : cc.L - 1;
       }
       seg_t0 = cc.t;
     }
@@ -1024,7 +1145,7 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
     }
     if (cc.t == cc.T - 1 || i == n - 1) {
       const bool whole = seg_t0 == 0 && cc.t == cc.T - 1;
-      finish_segment<D, NC, kCausal>(cx, d, st, cc, cl, whole, rec, lane);
+      finish_segment<D, NC, kCausal, kShare>(cx, d, st, cc, cl, whole, rec, lane);
       if (!whole && seg_t0 == 0) {
         // this worker holds the first share of a pair that later workers continue;
         // the worker holding the pair's last tile closes it (worked out here, mid-
@@ -1036,7 +1157,7 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
       }
       rec = 2 * w + 1;
     }
-    advance<kCausal>(cc, cx, d, cap);
+    advance<kCausal, kShare>(cc, cx, d, cap);
   };
 
 #pragma unroll
@@ -1070,8 +1191,10 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
 // descriptor per worker: (s, g, wb, first_slot | Tq << 1) of the split pair whose
 // first share this worker holds, or s = -1 (Tq only in multi-token launches).
 // fp8 single-tile launches cap registers for two waves per SIMD; decode with append
-// keeps one (its new-row arithmetic needs the room).
-template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend>
+// keeps one (its new-row arithmetic needs the room).  kShare: 0, or the prefix (1)
+// or tail (2) pass of a shared-prefix launch (seq_len), whose prefix states are at
+// `state`.
+template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShare = 0>
 __global__ __launch_bounds__(kWave* kWavesPerGroup,
                              (kFp8 && NC == 1 && !kAppend) ? 2 : 1) void decode_kernel(
     const uint16_t* __restrict__ q, const typename TileOf<D, B, kFp8>::Elem* __restrict__ k,
@@ -1080,9 +1203,9 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
     const int32_t* __restrict__ qlens, uint16_t* __restrict__ out, float* __restrict__ ws,
     int4* __restrict__ desc, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, typename TileOf<D, B, kFp8>::Elem* kw,
-    typename TileOf<D, B, kFp8>::Elem* vw, DecodeDims d) {
-  const Ctx<typename TileOf<D, B, kFp8>::Elem> cx{q,  k,  v,     tables, lens, qlens, out,
-                                                  ws, k_new, v_new, kw,    vw};
+    typename TileOf<D, B, kFp8>::Elem* vw, float* __restrict__ state, DecodeDims d) {
+  const Ctx<typename TileOf<D, B, kFp8>::Elem> cx{q,     k,     v,  tables, lens, qlens, out,
+                                                  ws,    k_new, v_new, kw, vw, state};
   const int lane = __lane_id();
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
   if (w >= d.n_workers) return;
@@ -1094,12 +1217,13 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
 
   int4 opened = {-1, 0, 0, 0};
   WorkerPlan pl;
-  const bool has = d.pair_mode ? plan_pair<kCausal>(lens, qlens, d, cap, w, pl)
-                               : plan_worker<kCausal>(lens, qlens, d, cap, w, lane, pl);
+  const bool has = d.pair_mode ? plan_pair<kCausal, kShare>(lens, qlens, d, cap, w, pl)
+                               : plan_worker<kCausal, kShare>(lens, qlens, d, cap, w, lane, pl);
 #ifdef PKV_TIMELINE
   const uint64_t t_plan = __builtin_amdgcn_s_memrealtime();
 #endif
-  if (has) opened = run_worker<D, B, NC, kCausal, kFp8, kAppend>(cx, d, pl, w, lane, t_first);
+  if (has)
+    opened = run_worker<D, B, NC, kCausal, kFp8, kAppend, kShare>(cx, d, pl, w, lane, t_first);
 #ifdef PKV_TIMELINE
   {
     const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
@@ -1120,8 +1244,36 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
 
   // Rows no tile reaches are zeros: every row of an empty sequence, and in a
   // multi-token launch the rows past a sequence's query tokens (done last: off
-  // the path to the first loads).
+  // the path to the first loads).  The prefix pass writes no output rows; in the
+  // tail pass a sequence whose context is all prefix gets its prefix state,
+  // normalised.
   const int32_t row_elems = d.Hq * D;
+  if constexpr (kShare == 1) {
+    if (!d.pair_mode && lane == 0) desc[w] = opened;
+    return;
+  }
+  if constexpr (kShare == 2) {
+    for (int64_t se = w; se < d.S; se += d.n_workers) {
+      const SeqLen sl = seq_len<false, 2>(lens, qlens, d, cap, static_cast<int32_t>(se));
+      if (sl.L != 0) continue;
+      uint16_t* row = out + se * row_elems;
+      for (int32_t e = lane * 8; e < row_elems; e += kWave * 8) {
+        u32x4_t z = {0, 0, 0, 0};
+        if (sl.x > 0) {
+          const int64_t gr = se * d.Hq + e / D;
+          const float* o = state + state_o<D>(d, gr) + e % D;
+          const float inv = d.v_scale / state[state_m<D>(d, gr) + d.Hq];
+          bf16x8_t y;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[i] = static_cast<__bf16>(o[i] * inv);
+          z = __builtin_bit_cast(u32x4_t, y);
+        }
+        *reinterpret_cast<u32x4_t*>(row + e) = z;
+      }
+    }
+    if (!d.pair_mode && lane == 0) desc[w] = opened;
+    return;
+  }
   for (int64_t se = w; se < d.S; se += d.n_workers) {
     int32_t first = 0;
     if constexpr (kCausal) {
@@ -1158,12 +1310,21 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
 constexpr int kMergeThreads = 512;
 constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
 constexpr int kMergeWideSplit = 12;
+// Outputs of a pair one merge work-group takes (a decode pair at G = 4, D = 128);
+// pairs with more rows (multi-token and prefix launches) spread over more groups.
+constexpr int kMergeSpan = 512;
 
-template <int D, bool kCausal, int kChunk, int kItems>
+//
+// Shared-prefix launches: after the prefix pass (kShare = 1) the merged rows are
+// written as prefix states (unnormalised O, m, l) of the group's sequences
+// (gfirst: the group offsets).
+template <int D, bool kCausal, int kChunk, int kItems, int kShare = 0>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __restrict__ desc,
                                                               uint16_t* __restrict__ out,
                                                               const float* __restrict__ ws,
-                                                              DecodeDims d) {
+                                                              DecodeDims d,
+                                                              const int32_t* __restrict__ gfirst,
+                                                              float* __restrict__ state) {
   __shared__ int4 s_desc[kMergeSlice];
   __shared__ int32_t s_wa[kMergeSlice];
   __shared__ int32_t s_count;
@@ -1184,7 +1345,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
   __syncthreads();
   const int64_t rf = record_floats(d.R, D);
   const int32_t RD = d.R * D;
-  const int32_t total = s_count * RD;
+  // the outputs of a pair are split over gridDim.y work-groups: this one takes
+  // outputs oi0 .. oi0 + span - 1 of each of its pairs
+  const int32_t per_y = (RD + gridDim.y - 1) / gridDim.y;
+  const int32_t oi0 = static_cast<int32_t>(blockIdx.y) * per_y;
+  const int32_t span = max(min(per_y, RD - oi0), 0);
+  const int32_t total = s_count * span;
   for (int32_t base = tid; base < total; base += kMergeThreads * kItems) {
     float run_m[kItems], run_l[kItems], acc[kItems];
     int64_t wa[kItems], wb[kItems], first[kItems];
@@ -1196,8 +1362,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
       run_m[it] = -INFINITY;
       run_l[it] = 0.f;
       acc[it] = 0.f;
-      pi[it] = item < total ? item / RD : 0;
-      oi[it] = item < total ? item - pi[it] * RD : 0;
+      pi[it] = item < total ? item / span : 0;
+      oi[it] = item < total ? oi0 + (item - pi[it] * span) : 0;
       act[it] = item < total;
       if constexpr (kCausal) act[it] = act[it] && (oi[it] / D) / d.G < (s_desc[pi[it]].w >> 1);
       wa[it] = s_wa[pi[it]];
@@ -1247,7 +1413,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
     }
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
-      if (act[it]) {
+      if (kShare == 1 && act[it]) {
+        const int4 ds = s_desc[pi[it]];
+        const int32_t row = oi[it] / D;  // row = qi * G + head
+        const int32_t qi = row / d.G;
+        const int32_t member = min(max(gfirst[ds.x], 0), d.seqs - 1) + qi;
+        const int64_t gr = static_cast<int64_t>(member) * d.Hq + ds.y * d.G + (row - qi * d.G);
+        const int32_t col = oi[it] - row * D;
+        state[state_o<D>(d, gr) + col] = acc[it];
+        if (col == 0) {
+          const int64_t mo = state_m<D>(d, gr);
+          state[mo] = run_m[it];
+          state[mo + d.Hq] = run_l[it];
+        }
+      } else if (act[it]) {
         const int4 ds = s_desc[pi[it]];
         int64_t idx;
         if constexpr (kCausal) {
@@ -1265,7 +1444,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
   }
 }
 
-template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend>
+template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShare>
 hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
                     hipStream_t stream) {
   using Elem = typename TileOf<D, B, kFp8>::Elem;
@@ -1273,34 +1452,42 @@ hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_group
   if (groups <= 0) return hipSuccess;
   int4* desc = reinterpret_cast<int4*>(reinterpret_cast<char*>(b.ws) +
                                        records_bytes(d.n_workers, d.R, D));
-  hipLaunchKernelGGL((decode_kernel<D, B, NC, kCausal, kFp8, kAppend>), dim3(groups),
+  hipLaunchKernelGGL((decode_kernel<D, B, NC, kCausal, kFp8, kAppend, kShare>), dim3(groups),
                      dim3(kWave * kWavesPerGroup), 0, stream, b.q, static_cast<const Elem*>(b.k),
                      static_cast<const Elem*>(b.v), b.tables, b.lens, b.qlens, b.out, b.ws, desc,
-                     b.k_new, b.v_new, static_cast<Elem*>(b.kw), static_cast<Elem*>(b.vw), d);
+                     b.k_new, b.v_new, static_cast<Elem*>(b.kw), static_cast<Elem*>(b.vw), b.state,
+                     d);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   if (d.pair_mode) return hipSuccess;  // nothing is split: no merge
-  // records per split pair: about the workers per (sequence, KV head) pair
+  // records per split pair: about the workers per (sequence, KV head) pair; a
+  // pair's outputs are spread over ny = ceil(R * D / kMergeSpan) work-groups, and
+  // the descriptor slices shrink to about merge_groups / ny (a merge work-group
+  // fills a CU: more than one per CU would run in rounds), each still scanning at
+  // most kMergeSlice descriptors
   const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
+  const int ny = (d.R * D + kMergeSpan - 1) / kMergeSpan;
+  const int nx = max(max(merge_groups / ny, (d.n_workers + kMergeSlice - 1) / kMergeSlice), 1);
+  const dim3 grid(nx, ny);
   if (pairs > 0 && d.n_workers > kMergeWideSplit * pairs)
-    hipLaunchKernelGGL((merge_kernel<D, kCausal, 16, 1>), dim3(merge_groups), dim3(kMergeThreads), 0,
-                       stream, desc, b.out, b.ws, d);
+    hipLaunchKernelGGL((merge_kernel<D, kCausal, 16, 1, kShare>), grid, dim3(kMergeThreads), 0,
+                       stream, desc, b.out, b.ws, d, b.qlens, b.state);
   else
-    hipLaunchKernelGGL((merge_kernel<D, kCausal, 12, 2>), dim3(merge_groups), dim3(kMergeThreads), 0,
-                       stream, desc, b.out, b.ws, d);
+    hipLaunchKernelGGL((merge_kernel<D, kCausal, 12, 2, kShare>), grid, dim3(kMergeThreads), 0,
+                       stream, desc, b.out, b.ws, d, b.qlens, b.state);
   return hipGetLastError();
 }
 
-template <int NC, bool kCausal, bool kFp8, bool kAppend = false>
+template <int NC, bool kCausal, bool kFp8, bool kAppend = false, int kShare = 0>
 hipError_t dispatch(const DecodeBuffers& b, const DecodeDims& d, int D, int B, int merge_groups,
                     hipStream_t stream) {
   if (D == 128) {
-    if (B == 16) return launch_t<128, 16, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
-    if (B == 32) return launch_t<128, 32, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
-    if (B == 8) return launch_t<128, 8, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
+    if (B == 16) return launch_t<128, 16, NC, kCausal, kFp8, kAppend, kShare>(b, d, merge_groups, stream);
+    if (B == 32) return launch_t<128, 32, NC, kCausal, kFp8, kAppend, kShare>(b, d, merge_groups, stream);
+    if (B == 8) return launch_t<128, 8, NC, kCausal, kFp8, kAppend, kShare>(b, d, merge_groups, stream);
   } else if (D == 64) {
-    if (B == 16) return launch_t<64, 16, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
-    if (B == 32) return launch_t<64, 32, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
-    if (B == 8) return launch_t<64, 8, NC, kCausal, kFp8, kAppend>(b, d, merge_groups, stream);
+    if (B == 16) return launch_t<64, 16, NC, kCausal, kFp8, kAppend, kShare>(b, d, merge_groups, stream);
+    if (B == 32) return launch_t<64, 32, NC, kCausal, kFp8, kAppend, kShare>(b, d, merge_groups, stream);
+    if (B == 8) return launch_t<64, 8, NC, kCausal, kFp8, kAppend, kShare>(b, d, merge_groups, stream);
   }
   return hipErrorInvalidValue;
 }

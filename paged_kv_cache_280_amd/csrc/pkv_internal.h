@@ -33,6 +33,8 @@ struct DecodeBuffers {
   const uint16_t* v_new;    // bf16 [S][Hkv][D]
   void* kw;                 // the K pool (written: the new rows)
   void* vw;                 // the V pool
+  // shared-prefix launches only: the prefix softmax states ([S][record_floats(Hq, D)])
+  float* state;
 };
 
 // Sizes of one launch (passed by value).  A decode launch has one query token
@@ -56,6 +58,10 @@ struct DecodeDims {
   int32_t len_off;          // 1 in decode-with-append launches: the tiles cover the first
                             // context_lens[s] - 1 positions, the newest comes from k_new/v_new
   float k_scale;            // fp8 decode-with-append: new K rows are stored as E4M3(x / k_scale)
+  // shared-prefix launches: prefix lengths are used clamped into [0, min(M*B, pre_cap)]
+  // and rounded down to a multiple of pre_align (max(16, B): whole tiles and blocks);
+  // seqs is the batch's sequence count (the prefix pass runs over groups)
+  int32_t pre_align, pre_cap, seqs;
 };
 
 // Floats in one partial record: O[R][D], then m[R], then l[R], padded to a
@@ -107,6 +113,14 @@ hipError_t launch_multi_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, 
 // the V pool's scale.
 hipError_t launch_decode_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                              int merge_groups, hipStream_t stream);
+// Shared-prefix decode (pkv_decode_shared.hip), bf16 pools: the prefix pass over
+// sharing groups (d.R = G * largest group <= kMaxRows; b.lens = prefix lengths,
+// b.qlens = group offsets) and the tail pass (b.qlens = prefix lengths); both
+// with b.state set.
+hipError_t launch_shared_prefix(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                                int merge_groups, hipStream_t stream);
+hipError_t launch_shared_tail(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
+                              int merge_groups, hipStream_t stream);
 // Decode with append (d.len_off = 1; b.k_new, v_new, kw, vw set), bf16 or fp8 pools.
 hipError_t launch_decode_append(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                                 int merge_groups, hipStream_t stream, bool fp8);

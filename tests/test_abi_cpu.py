@@ -36,7 +36,9 @@ def test_header_declares_the_boundary():
                             "paged_attn_multi_fp8",
                             "kv_append", "kv_append_fp8", "copy_blocks", "pkv_check_batch",
                             "paged_attn_decode_append", "paged_attn_decode_append_fp8",
-                            "paged_attn_decode_noalloc"])
+                            "paged_attn_decode_noalloc",
+                            "paged_attn_decode_shared_workspace_bytes",
+                            "paged_attn_decode_shared"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -120,6 +122,47 @@ def test_noalloc_scratch_limit_matches_the_header():
     text = open(HEADER).read()
     m = re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == pkv.NOALLOC_SCRATCH_BYTES
+
+
+def _shared_call(lib, **over):
+    """Call paged_attn_decode_shared with fake (never dereferenced) pointers."""
+    a = dict(q=0x1000, k=0x2000, v=0x3000, tables=0x4000, lens=0x5000, gfirst=0x5400,
+             plens=0x5800, NG=1, maxg=2, maxp=32, block_size=16, scale=0.125, out=0x6000, S=2,
+             Hq=8, Hkv=2, D=128, M=4, NB=10, max_ctx=64, ws=0x7000, ws_bytes=1 << 20,
+             stream=None)
+    a.update(over)
+    return lib.paged_attn_decode_shared(a["q"], a["k"], a["v"], a["tables"], a["lens"],
+                                        a["gfirst"], a["plens"], a["NG"], a["maxg"], a["maxp"],
+                                        a["block_size"], a["scale"], a["out"], a["S"], a["Hq"],
+                                        a["Hkv"], a["D"], a["M"], a["NB"], a["max_ctx"], a["ws"],
+                                        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Hq=6, Hkv=4), -2),
+    (dict(NG=0), -2),                   # sequences but no group
+    (dict(NG=-1), -2),
+    (dict(maxg=0), -2),
+    (dict(maxp=-1), -2),
+    (dict(maxp=65), -2),                # prefix bound above max_context_len
+    (dict(maxg=9), -3),                 # 4 heads per KV head x 9 members > 32 rows
+    (dict(Hq=32, Hkv=1, maxg=1), -3),   # group of 32 query heads per KV head
+    (dict(gfirst=None), -1),
+    (dict(plens=None), -1),
+    (dict(ws=None), -1),
+    (dict(out=0x6008), -5),
+    (dict(S=0, NG=0, q=None, out=None), 0),   # nothing to do
+])
+def test_shared_decode_rejects_bad_arguments_on_the_host(lib, over, code):
+    assert _shared_call(lib, **over) == code
+
+
+def test_shared_workspace_query_rejects_what_the_call_rejects(lib):
+    f = lib.paged_attn_decode_shared_workspace_bytes
+    assert f(2, 8, 2, 128, 16, 64, 1, 9, 32) == 0      # 36 rows
+    assert f(2, 8, 2, 128, 16, 64, 0, 2, 32) == 0      # no group
+    assert f(2, 8, 2, 96, 16, 64, 1, 2, 32) == 0       # head_dim not built
+    assert f(2, 8, 2, 128, 16, 64, 1, 2, 65) == 0      # prefix bound above the context bound
 
 
 def _multi_call(lib, **over):
