@@ -24,6 +24,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# PKV_ORACLE_LIBRARY names another build of oracle.cpp to load (the CPU tests use the
+# sanitized build of build_sanitized); unset, liboracle.so beside this file
+_LIB_OVERRIDE = os.environ.get("PKV_ORACLE_LIBRARY")
 _lib = None
 
 
@@ -36,6 +39,17 @@ def build(force: bool = True) -> str:
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized(out: str) -> str:
+    """Compile ``oracle.cpp`` with AddressSanitizer and UndefinedBehaviorSanitizer (any
+    finding aborts) into ``out``; the process that loads it must preload GCC's
+    libasan (``g++ -print-file-name=libasan.so``)."""
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fopenmp", "-fPIC", "-shared",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", _SRC, "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
 
 
 def _bind(lib):
@@ -78,6 +92,9 @@ def _bind(lib):
 def _load():
     global _lib
     if _lib is None:
+        if _LIB_OVERRIDE:
+            _lib = _bind(ctypes.CDLL(_LIB_OVERRIDE))
+            return _lib
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         _lib = _bind(ctypes.CDLL(_LIB))

@@ -12,7 +12,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpkv.so")
+# PKV_LIBRARY names another build of the library (the CPU tests use it for the
+# sanitized host-side build); unset, the in-tree libpkv.so
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(PKG, "libpkv.so")
 
 _lib = None
 
