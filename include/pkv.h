@@ -189,7 +189,9 @@ int32_t paged_attn_decode_append(const void* q, const void* k_new, const void* v
  * paged_attn_decode_append over fp8 pools: the newest rows are stored as
  * kv_append_fp8 stores them (code = E4M3(x / scale), nearest even, saturating,
  * NaN -> 0x7F) and attended to as those codes, as paged_attn_decode_fp8 does.
- * k_scale and v_scale must be finite and non-zero (else PKV_ERR_SHAPE).
+ * k_scale and v_scale must be finite and non-zero (else PKV_ERR_SHAPE).  The call
+ * always enqueues the append and then the fp8 decode, so its outputs and pools are
+ * bit-identical to kv_append_fp8 followed by paged_attn_decode_fp8.
  */
 int32_t paged_attn_decode_append_fp8(const void* q, const void* k_new, const void* v_new,
                                      void* k_cache, void* v_cache, const int32_t* block_tables,

@@ -13,6 +13,11 @@
 // prefill chunk), the stores of one dim from the 16 lanes of a head fall on
 // consecutive slots and coalesce.
 //
+// Small appends (a decode step: one token per sequence, scattered over blocks) take
+// the row kernels instead: one thread per (token, KV head, 8 dims), so that a few
+// tokens still spread over many waves (with 16 tokens per wave a decode step of 8
+// sequences ran as two waves, each lane converting 128 values in a row).
+//
 // fp8 pools ("KV cache, PagedAttention", aiwiki.vn, paragraph on cache
 // quantisation): each element is stored as the E4M3FN code nearest to x / scale
 // (ties to even), saturating at +-448; NaN is stored as 0x7F.  K chunks of 16 dims
@@ -25,6 +30,7 @@ namespace pkv {
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kAppendHeadsPerWave = 4;
 constexpr int kAppendTokensPerWave = kWave / kAppendHeadsPerWave;  // 16
@@ -103,6 +109,77 @@ __device__ __forceinline__ void e4m3x8(const uint16_t* src, float scale, uint32_
               hi_bf16(x[3]) / scale);
 }
 
+// Appends of fewer tokens than this take the row kernels.
+constexpr int32_t kRowAppendTokens = 1024;
+
+// Thread (t, g, c) of a row kernel: token t's row of KV head g, dims 8c .. 8c + 7.
+struct RowItem {
+  int64_t t;
+  int32_t g, c;
+};
+
+template <int D>
+__device__ __forceinline__ bool row_item(const AppendDims& a, RowItem& r) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_token = static_cast<int64_t>(a.Hkv) * (D / 8);
+  r.t = i / per_token;
+  const int32_t rem = static_cast<int32_t>(i - r.t * per_token);
+  r.g = rem / (D / 8);
+  r.c = rem - r.g * (D / 8);
+  return r.t < a.T;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWave* kWavesPerGroup) void append_rows_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ token_seq,
+    const int32_t* __restrict__ token_pos, AppendDims a) {
+  RowItem r;
+  if (!row_item<D>(a, r)) return;
+  int64_t tile;
+  int32_t o;
+  if (!token_slot<D>(r.t, r.g, tables, token_seq, token_pos, a, tile, o)) return;
+  const int64_t row = (r.t * a.Hkv + r.g) * D + r.c * 8;
+  *reinterpret_cast<u32x4_t*>(k_cache + tile + (static_cast<int64_t>(r.c) * a.B + o) * 8) =
+      *reinterpret_cast<const u32x4_t*>(k_new + row);
+  const int32_t bt = a.B < 16 ? a.B : 16;  // positions of one V run
+  uint16_t* vrun = v_cache + tile + static_cast<int64_t>(o / bt) * D * bt + o % bt;
+  const u32x4_t x = *reinterpret_cast<const u32x4_t*>(v_new + row);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    vrun[static_cast<int64_t>(r.c * 8 + i) * bt] = static_cast<uint16_t>(x[i / 2] >> (16 * (i % 2)));
+}
+
+template <int D>
+__global__ __launch_bounds__(kWave* kWavesPerGroup) void append_fp8_rows_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ token_seq,
+    const int32_t* __restrict__ token_pos, AppendDims a) {
+  RowItem r;
+  if (!row_item<D>(a, r)) return;
+  int64_t tile;
+  int32_t o;
+  if (!token_slot<D>(r.t, r.g, tables, token_seq, token_pos, a, tile, o)) return;
+  const int64_t row = (r.t * a.Hkv + r.g) * D + r.c * 8;
+  uint32_t k0, k1, v0, v1;
+  e4m3x8(k_new + row, a.k_scale, k0, k1);
+  e4m3x8(v_new + row, a.v_scale, v0, v1);
+  // K: dims of one 16-dim group are 16 consecutive bytes of token o
+  *reinterpret_cast<u32x2_t*>(k_cache + tile + (static_cast<int64_t>(r.c / 2) * a.B + o) * 16 +
+                              (r.c % 2) * 8) = u32x2_t{k0, k1};
+  // V element (o, d) at [d%16][o/4][d/16][o%4] of the tile
+  const int64_t row_bytes = (D / 16) * 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int d = r.c * 8 + i;
+    const uint32_t code = ((i < 4 ? v0 : v1) >> (8 * (i % 4))) & 0xFFu;
+    v_cache[tile + (static_cast<int64_t>(d % 16) * (a.B / 4) + o / 4) * row_bytes + (d / 16) * 4 +
+            o % 4] = static_cast<uint8_t>(code);
+  }
+}
+
 // fp8: lane (j, k) of a head's 16 lanes takes tokens t0 + 4j .. t0 + 4j + 3 and
 // dims k*D/4 .. (k+1)*D/4 - 1.  The V pool keeps the codes of 4 consecutive
 // positions of one dim in one dword, so when the lane's 4 tokens are such a
@@ -178,7 +255,26 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup) void append_fp8_kernel(
 
 }  // namespace
 
+// Row-kernel launch: one thread per (token, KV head, 8 dims).
+template <typename KernelT, typename Elem>
+hipError_t launch_rows(KernelT kernel, const AppendBuffers& b, const AppendDims& a, int D,
+                       Elem* kc, Elem* vc, hipStream_t stream) {
+  const int64_t threads = static_cast<int64_t>(a.T) * a.Hkv * (D / 8);
+  const int64_t groups = (threads + kWave * kWavesPerGroup - 1) / (kWave * kWavesPerGroup);
+  if (groups <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(groups)), dim3(kWave * kWavesPerGroup), 0,
+                     stream, b.k_new, b.v_new, kc, vc, b.tables, b.token_seq, b.token_pos, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_append(const AppendBuffers& b, const AppendDims& a, int D, hipStream_t stream) {
+  if (a.T < kRowAppendTokens) {
+    uint16_t* kc = static_cast<uint16_t*>(b.k_cache);
+    uint16_t* vc = static_cast<uint16_t*>(b.v_cache);
+    if (D == 128) return launch_rows(append_rows_kernel<128>, b, a, D, kc, vc, stream);
+    if (D == 64) return launch_rows(append_rows_kernel<64>, b, a, D, kc, vc, stream);
+    return hipErrorInvalidValue;
+  }
   const int64_t head_groups = (a.Hkv + kAppendHeadsPerWave - 1) / kAppendHeadsPerWave;
   const int64_t waves =
       (static_cast<int64_t>(a.T) + kAppendTokensPerWave - 1) / kAppendTokensPerWave * head_groups;
@@ -202,6 +298,13 @@ hipError_t launch_append(const AppendBuffers& b, const AppendDims& a, int D, hip
 
 hipError_t launch_append_fp8(const AppendBuffers& b, const AppendDims& a, int D,
                              hipStream_t stream) {
+  if (a.T < kRowAppendTokens) {
+    uint8_t* kc = static_cast<uint8_t*>(b.k_cache);
+    uint8_t* vc = static_cast<uint8_t*>(b.v_cache);
+    if (D == 128) return launch_rows(append_fp8_rows_kernel<128>, b, a, D, kc, vc, stream);
+    if (D == 64) return launch_rows(append_fp8_rows_kernel<64>, b, a, D, kc, vc, stream);
+    return hipErrorInvalidValue;
+  }
   const int64_t head_groups = (a.Hkv + kAppendHeadsPerWave - 1) / kAppendHeadsPerWave;
   const int64_t waves =
       (static_cast<int64_t>(a.T) + kAppendTokensPerWave - 1) / kAppendTokensPerWave * head_groups;

@@ -1,4 +1,4 @@
-// Launch of one decode step with its KV append, bf16 or fp8 pools (kernels in
+// Launch of one decode step with its KV append over bf16 pools (kernels in
 // pkv_decode_kernels.h).
 
 #include "pkv_decode_kernels.h"
@@ -6,9 +6,8 @@
 namespace pkv {
 
 hipError_t launch_decode_append(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                                int merge_groups, hipStream_t stream, bool fp8) {
-  return fp8 ? dispatch<1, false, true, true>(b, d, D, B, merge_groups, stream)
-             : dispatch<1, false, false, true>(b, d, D, B, merge_groups, stream);
+                                int merge_groups, hipStream_t stream) {
+  return dispatch<1, false, false, true>(b, d, D, B, merge_groups, stream);
 }
 
 }  // namespace pkv

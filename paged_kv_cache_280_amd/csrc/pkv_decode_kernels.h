@@ -879,8 +879,9 @@ __device__ __forceinline__ void load_prefix_state(SegState<D>& ps, const Cx& cx,
 // compute_tile treats a position: score in the log2 domain, the same lazy
 // rescaling, the weight rounded to bf16 for the weighted sum of values.  The
 // worker also writes the new rows into their slot (the caller has made the block
-// private, so no other worker reads it).  fp8 pools: the row is stored, and
-// attended to, as E4M3(x / scale).
+// private, so no other worker reads it).  bf16 pools only: over fp8 pools the new
+// rows are quantised by the append kernel in a launch of their own (folded in
+// here, the encoding's registers pushed the whole tile loop into spills).
 // This lane's parts of a pair's newest rows: the key dims of its score operand
 // and the value dims of its O entries (read ahead by fetch_new).
 template <int D>
@@ -889,22 +890,20 @@ struct NewRow {
   u32x2_t v[D / 16];
 };
 
-template <int D, bool kFp8, typename Cx>
+template <int D, typename Cx>
 __device__ __forceinline__ void fetch_new(NewRow<D>& nr, const Cx& cx, const DecodeDims& d,
                                           const Cursor& c, int lane) {
   const int64_t row = (static_cast<int64_t>(c.s) * d.Hkv + c.g) * D;
   const int gq = lane >> 4;
 #pragma unroll
-  for (int k = 0; k < D / 32; ++k) {
-    const int d0 = kFp8 ? (k / 2) * 64 + gq * 16 + (k % 2) * 8 : k * 32 + gq * 8;
-    nr.k[k] = *reinterpret_cast<const u32x4_t*>(cx.k_new + row + d0);
-  }
+  for (int k = 0; k < D / 32; ++k)
+    nr.k[k] = *reinterpret_cast<const u32x4_t*>(cx.k_new + row + k * 32 + gq * 8);
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt)
     nr.v[mt] = *reinterpret_cast<const u32x2_t*>(cx.v_new + row + mt * 16 + gq * 4);
 }
 
-template <int D, int B, bool kFp8, typename Cx>
+template <int D, int B, typename Cx>
 __device__ __forceinline__ void append_token(SegState<D>& st, const bf16x8_t (&qop)[D / 32],
                                              const NewRow<D>& nr, const Cx& cx,
                                              const DecodeDims& d, const Cursor& c, int lane) {
@@ -923,31 +922,13 @@ __device__ __forceinline__ void append_token(SegState<D>& st, const bf16x8_t (&q
   float part = 0.f;
 #pragma unroll
   for (int k = 0; k < D / 32; ++k) {
-    const int d0 = kFp8 ? (k / 2) * 64 + gq * 16 + (k % 2) * 8 : k * 32 + gq * 8;
+    const int d0 = k * 32 + gq * 8;
     const u32x4_t x = nr.k[k];
-    uint32_t w[4];
-    if constexpr (kFp8) {
-      const float ks = d.k_scale;
-      const uint32_t lo = e4m3x4(lo_bf16(x[0]) / ks, hi_bf16(x[0]) / ks, lo_bf16(x[1]) / ks,
-                                 hi_bf16(x[1]) / ks);
-      const uint32_t hi = e4m3x4(lo_bf16(x[2]) / ks, hi_bf16(x[2]) / ks, lo_bf16(x[3]) / ks,
-                                 hi_bf16(x[3]) / ks);
-      w[0] = e4m3x2_to_bf16x2<false>(lo);
-      w[1] = e4m3x2_to_bf16x2<true>(lo);
-      w[2] = e4m3x2_to_bf16x2<false>(hi);
-      w[3] = e4m3x2_to_bf16x2<true>(hi);
-      if (writer)
-        *reinterpret_cast<u32x2_t*>(cx.kw + tile + ((d0 / 16) * B + ob) * 16 + d0 % 16) =
-            u32x2_t{lo, hi};
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = x[e];
-      if (writer) *reinterpret_cast<u32x4_t*>(cx.kw + tile + ((d0 / 8) * B + ob) * 8) = x;
-    }
+    if (writer) *reinterpret_cast<u32x4_t*>(cx.kw + tile + ((d0 / 8) * B + ob) * 8) = x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      part = fmaf(static_cast<float>(qop[k][2 * e]), lo_bf16(w[e]), part);
-      part = fmaf(static_cast<float>(qop[k][2 * e + 1]), hi_bf16(w[e]), part);
+      part = fmaf(static_cast<float>(qop[k][2 * e]), lo_bf16(x[e]), part);
+      part = fmaf(static_cast<float>(qop[k][2 * e + 1]), hi_bf16(x[e]), part);
     }
   }
   part += __shfl_xor(part, 16);
@@ -964,35 +945,17 @@ __device__ __forceinline__ void append_token(SegState<D>& st, const bf16x8_t (&q
   }
   const float wgt = static_cast<float>(static_cast<__bf16>(__builtin_amdgcn_exp2f(x)));
   st.l += wgt;
-  constexpr int32_t kRun = B < kTile ? B : kTile;  // positions of one bf16 V run
+  constexpr int32_t kRun = B < kTile ? B : kTile;  // positions of one V run
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt) {
     const int d0 = mt * 16 + gq * 4;  // this lane's four dims of O
     const u32x2_t vv = nr.v[mt];
-    uint32_t pair[2];
-    if constexpr (kFp8) {
-      const float vs = d.v_scale;
-      const uint32_t code = e4m3x4(lo_bf16(vv.x) / vs, hi_bf16(vv.x) / vs, lo_bf16(vv.y) / vs,
-                                   hi_bf16(vv.y) / vs);
-      pair[0] = e4m3x2_to_bf16x2<false>(code);
-      pair[1] = e4m3x2_to_bf16x2<true>(code);
-      if (writer) {
+    const uint32_t pair[2] = {vv.x, vv.y};
+    if (writer) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int dd = d0 + i;
-          cx.vw[tile + ((dd % 16) * (B / 4) + ob / 4) * (D / 16) * 4 + (dd / 16) * 4 + ob % 4] =
-              static_cast<uint8_t>(code >> (8 * i));
-        }
-      }
-    } else {
-      pair[0] = vv.x;
-      pair[1] = vv.y;
-      if (writer) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          cx.vw[tile + ((ob / kRun) * D + d0 + i) * kRun + ob % kRun] =
-              static_cast<uint16_t>(pair[i / 2] >> (16 * (i % 2)));
-      }
+      for (int i = 0; i < 4; ++i)
+        cx.vw[tile + ((ob / kRun) * D + d0 + i) * kRun + ob % kRun] =
+            static_cast<uint16_t>(pair[i / 2] >> (16 * (i % 2)));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1005,7 +968,7 @@ __device__ __forceinline__ void append_token(SegState<D>& st, const bf16x8_t (&q
 // Decode with append, a sequence whose only position is the new one: every
 // query head's output is that position's value, and the rows go into slot 0 (not
 // stored when the table entry lies outside the pool, as in append_token).
-template <int D, int B, bool kFp8, typename Cx>
+template <int D, int B, typename Cx>
 __device__ void one_token(const Cx& cx, const DecodeDims& d, int64_t s, int lane) {
   const int32_t raw = cx.tables[s * d.M];
   const bool in_pool = raw >= 0 && raw < d.NB;
@@ -1016,25 +979,12 @@ __device__ void one_token(const Cx& cx, const DecodeDims& d, int64_t s, int lane
     const int64_t tile = (static_cast<int64_t>(b) * d.Hkv + g) * D * B;
     const uint16_t kx = cx.k_new[s * d.Hkv * D + e];
     const uint16_t vx = cx.v_new[s * d.Hkv * D + e];
-    const float kf = __builtin_bit_cast(float, static_cast<uint32_t>(kx) << 16);
-    const float vf = __builtin_bit_cast(float, static_cast<uint32_t>(vx) << 16);
-    uint16_t outv = vx;
-    if constexpr (kFp8) {
-      const uint32_t kc = e4m3x4(kf / d.k_scale, 0.f, 0.f, 0.f) & 0xFFu;
-      const uint32_t vc = e4m3x4(vf / d.v_scale, 0.f, 0.f, 0.f) & 0xFFu;
-      if (in_pool) {
-        cx.kw[tile + ((dd / 16) * B) * 16 + dd % 16] = static_cast<uint8_t>(kc);
-        cx.vw[tile + ((dd % 16) * (B / 4)) * (D / 16) * 4 + (dd / 16) * 4] =
-            static_cast<uint8_t>(vc);
-      }
-      // softmax over one position: the output is the value, times the V scale
-      const float val = lo_bf16(e4m3x2_to_bf16x2<false>(vc)) * d.v_scale;
-      outv = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
-    } else if (in_pool) {
+    if (in_pool) {
       cx.kw[tile + (dd / 8) * B * 8 + dd % 8] = kx;
       cx.vw[tile + dd * kRun] = vx;
     }
-    for (int32_t j = 0; j < d.G; ++j) cx.out[(s * d.Hq + g * d.G + j) * D + dd] = outv;
+    // softmax over one position: the output is the value
+    for (int32_t j = 0; j < d.G; ++j) cx.out[(s * d.Hq + g * d.G + j) * D + dd] = vx;
   }
 }
 
@@ -1084,7 +1034,7 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
   NewRow<D> nr;
   auto fetch_step = [&]() {
     if constexpr (kAppend) {
-      if (cc.t == cc.T - 1) fetch_new<D, kFp8>(nr, cx, d, cc, lane);
+      if (cc.t == cc.T - 1) fetch_new<D>(nr, cx, d, cc, lane);
     }
   };
   auto load_step = [&](int slot, int32_t li) {
@@ -1140,7 +1090,7 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
       compute_tile<D, NC, false>(r[slot], qc, st, d.c, valid, valid - 1, lim, lane);
       if constexpr (kAppend) {
         static_assert(NC == 1, "decode with append has one query row per head");
-        if (cc.t == cc.T - 1) append_token<D, B, kFp8>(st[0], qc[0], nr, cx, d, cc, lane);
+        if (cc.t == cc.T - 1) append_token<D, B>(st[0], qc[0], nr, cx, d, cc, lane);
       }
     }
     if (cc.t == cc.T - 1 || i == n - 1) {
@@ -1190,13 +1140,12 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
 // Workspace: partial records ([n_workers][2] of record_floats), then one
 // descriptor per worker: (s, g, wb, first_slot | Tq << 1) of the split pair whose
 // first share this worker holds, or s = -1 (Tq only in multi-token launches).
-// fp8 single-tile launches cap registers for two waves per SIMD; decode with append
-// keeps one (its new-row arithmetic needs the room).  kShare: 0, or the prefix (1)
+// fp8 single-tile launches cap registers for two waves per SIMD; the others keep one.  kShare: 0, or the prefix (1)
 // or tail (2) pass of a shared-prefix launch (seq_len), whose prefix states are at
 // `state`.
 template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShare = 0>
 __global__ __launch_bounds__(kWave* kWavesPerGroup,
-                             (kFp8 && NC == 1 && !kAppend) ? 2 : 1) void decode_kernel(
+                             (kFp8 && NC == 1) ? 2 : 1) void decode_kernel(
     const uint16_t* __restrict__ q, const typename TileOf<D, B, kFp8>::Elem* __restrict__ k,
     const typename TileOf<D, B, kFp8>::Elem* __restrict__ v,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
@@ -1204,6 +1153,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
     int4* __restrict__ desc, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, typename TileOf<D, B, kFp8>::Elem* kw,
     typename TileOf<D, B, kFp8>::Elem* vw, float* __restrict__ state, DecodeDims d) {
+  static_assert(!(kFp8 && kAppend), "over fp8 pools the new rows are appended in their own launch");
   const Ctx<typename TileOf<D, B, kFp8>::Elem> cx{q,     k,     v,  tables, lens, qlens, out,
                                                   ws,    k_new, v_new, kw, vw, state};
   const int lane = __lane_id();
@@ -1281,7 +1231,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
     } else {
       const int32_t Lt = clamp_len(lens[se], cap);
       if constexpr (kAppend) {
-        if (Lt == 1) one_token<D, B, kFp8>(cx, d, se, lane);
+        if (Lt == 1) one_token<D, B>(cx, d, se, lane);
       }
       if (Lt != 0) continue;
     }

@@ -121,9 +121,9 @@ hipError_t launch_shared_prefix(const DecodeBuffers& b, const DecodeDims& d, int
                                 int merge_groups, hipStream_t stream);
 hipError_t launch_shared_tail(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                               int merge_groups, hipStream_t stream);
-// Decode with append (d.len_off = 1; b.k_new, v_new, kw, vw set), bf16 or fp8 pools.
+// Decode with append (d.len_off = 1; b.k_new, v_new, kw, vw set), bf16 pools.
 hipError_t launch_decode_append(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                                int merge_groups, hipStream_t stream, bool fp8);
+                                int merge_groups, hipStream_t stream);
 
 // KV append (pkv_append.hip).
 struct AppendBuffers {

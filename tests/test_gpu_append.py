@@ -19,14 +19,16 @@ def _host(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("D,B,H", [(128, 16, 8), (64, 8, 2), (128, 32, 5)])
-def test_kv_append_matches_the_oracle_byte_for_byte(D, B, H):
+# fewer than 1024 tokens: the row kernel; scale 8 (more than 1024): the wave kernel
+@pytest.mark.parametrize("D,B,H,scale_lens", [(128, 16, 8, 1), (64, 8, 2, 1), (128, 32, 5, 1),
+                                              (128, 16, 8, 8), (64, 32, 3, 8)])
+def test_kv_append_matches_the_oracle_byte_for_byte(D, B, H, scale_lens):
     import torch
 
     import paged_kv_cache_280_amd as pkv
 
     rng = np.random.default_rng(D + B + H)
-    lens = [5 * B + 3, 2 * B, 1, 7 * B]
+    lens = [scale_lens * L for L in (5 * B + 3, 2 * B, 1, 7 * B)]
     case = wl.case_random(D + B, len(lens), H, H, D, B, lens)
     kp, vp = wl.host_pools(case, poison=False)
     # distinct slots: every position below each sequence's length, shuffled, plus
@@ -50,7 +52,8 @@ def test_kv_append_matches_the_oracle_byte_for_byte(D, B, H):
 
 
 @pytest.mark.parametrize("D,B,H,start,T", [(128, 16, 8, 7, 37), (64, 8, 5, 0, 64),
-                                          (128, 32, 3, 30, 100)])
+                                          (128, 32, 3, 30, 100), (128, 16, 8, 7, 1100),
+                                          (64, 8, 5, 0, 2048)])
 def test_kv_append_of_a_prefill_chunk_in_order(D, B, H, start, T):
     """A chunk of T consecutive positions of one sequence, starting mid-block (the
     prefill layout: consecutive tokens land on consecutive slots), plus a second

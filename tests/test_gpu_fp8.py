@@ -173,16 +173,20 @@ def _specials_bf16(rng, shape, scale):
         np.where(np.isnan(flat), np.uint16(0x7FC0), np.uint16(0)).reshape(shape)
 
 
-@pytest.mark.parametrize("D,B,scales", [(128, 16, (1 / 16, 1 / 8)), (64, 8, (0.037, 0.0029)),
-                                        (128, 32, (0.5, 2.0))])
-def test_kv_append_fp8_matches_the_oracle_byte_for_byte(D, B, scales):
+@pytest.mark.parametrize("D,B,scales,scale_lens", [(128, 16, (1 / 16, 1 / 8), 1),
+                                                   (64, 8, (0.037, 0.0029), 1),
+                                                   (128, 32, (0.5, 2.0), 1),
+                                                   (128, 16, (0.041, 0.023), 8)])
+def test_kv_append_fp8_matches_the_oracle_byte_for_byte(D, B, scales, scale_lens):
+    """Shuffled tokens of several sequences (scale_lens 8: more than 1024 tokens,
+    the wave kernel; otherwise the row kernel)."""
     import torch
 
     import paged_kv_cache_280_amd as pkv
 
     rng = np.random.default_rng(D + B)
     H = 4
-    lens = [3 * B + 5, B, 2, 5 * B]
+    lens = [scale_lens * L for L in (3 * B + 5, B, 2, 5 * B)]
     case = wl.case_random(D + B + 1, len(lens), H, H, D, B, lens)
     kp, vp = wl.host_pools_fp8(case, *scales, poison=False)
     seq, pos = [], []
@@ -202,11 +206,14 @@ def test_kv_append_fp8_matches_the_oracle_byte_for_byte(D, B, scales):
     assert np.array_equal(kd.cpu().numpy(), kp) and np.array_equal(vd.cpu().numpy(), vp)
 
 
-# start 7 never forms an aligned position quad (byte stores throughout); the others
-# do, with ragged ends
+# Appends of fewer than 1024 tokens take the row kernel (one thread per token, head
+# and 8 dims); longer ones the wave kernel, where start 7 never forms an aligned
+# position quad (byte stores throughout) and the others do, with ragged ends
 @pytest.mark.parametrize("D,B,H,start,T", [(128, 16, 8, 7, 37), (128, 16, 8, 4, 61),
                                           (64, 32, 5, 0, 70), (128, 8, 3, 0, 33),
-                                          (64, 16, 4, 2, 300)])
+                                          (64, 16, 4, 2, 300), (128, 16, 8, 7, 1100),
+                                          (128, 16, 4, 4, 1500), (64, 32, 5, 0, 2047),
+                                          (128, 8, 3, 0, 1024)])
 def test_kv_append_fp8_of_a_prefill_chunk_in_order(D, B, H, start, T):
     """T consecutive positions of one sequence from mid-block, quantised in place."""
     import torch
