@@ -270,9 +270,40 @@ int32_t tokens_per_launch(int32_t group, int32_t max_query_len) {
   return t < max_query_len ? t : max_query_len;
 }
 
-size_t multi_workspace_for(int64_t workers, int32_t group, int32_t head_dim, int32_t max_query_len) {
+// Chunks of `per` query tokens one multi-token launch takes, given `left` still
+// to do: 1, 2 or 4, so that a slot's waves sit in one work-group (three take a
+// launch of four whose last chunk is empty).
+int32_t chunks_per_launch(int32_t left) { return left >= 3 ? 4 : left; }
+
+// Slots (planned tile ranges) of a multi-token launch of nch chunks: the
+// resident waves shared out nch to a slot, never more slots than the tiles a
+// batch bounded by max_context_len can hold.  Launches whose slots have two or
+// four waves fill every compute unit (a work-group of four waves each): their
+// waves compute more per byte fetched, and measured on 8 x 16,000 positions at
+// G = 4 the extra quarter of the compute units takes 16 query tokens from 146 to
+// 120 us and 32 from 263 to 205 us (one-chunk launches: no change).
+int64_t multi_slots(int cu, int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                    bool fp8, int32_t nch) {
+  const int64_t tiles_bound = static_cast<int64_t>(num_seqs) * num_kv_heads *
+                              ((static_cast<int64_t>(max_context_len) + kTile - 1) / kTile);
+  const int wpc = nch > 1 ? std::max(waves_per_cu(fp8), kWavesPerGroup) : waves_per_cu(fp8);
+  int64_t n = static_cast<int64_t>(cu) * wpc / nch;
+  if (tiles_bound < n) n = tiles_bound;
+  return n < 1 ? 1 : n;
+}
+
+// Most waves any launch of the call runs (records and descriptors are per wave).
+int64_t multi_waves(int cu, int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                    bool fp8) {
+  int64_t w = 0;
+  for (int32_t nch = 1; nch <= 4; nch *= 2)
+    w = std::max(w, nch * multi_slots(cu, num_seqs, num_kv_heads, max_context_len, fp8, nch));
+  return w;
+}
+
+size_t multi_workspace_for(int64_t waves, int32_t group, int32_t head_dim, int32_t max_query_len) {
   return static_cast<size_t>(
-      workspace_bytes_for(workers, group * tokens_per_launch(group, max_query_len), head_dim));
+      workspace_bytes_for(waves, group * tokens_per_launch(group, max_query_len), head_dim));
 }
 
 int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
@@ -298,8 +329,9 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   const int cu = current_cu_count();
   if (cu <= 0) return PKV_ERR_DEVICE;
   const int32_t group = num_q_heads / num_kv_heads;
-  const int64_t workers = worker_count(cu, num_seqs, num_kv_heads, max_context_len, fp8);
-  if (workspace_bytes < multi_workspace_for(workers, group, head_dim, max_query_len))
+  if (workspace_bytes < multi_workspace_for(multi_waves(cu, num_seqs, num_kv_heads,
+                                                       max_context_len, fp8),
+                                           group, head_dim, max_query_len))
     return PKV_ERR_WORKSPACE;
 
   DecodeDims d{};
@@ -309,7 +341,6 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   d.G = group;
   d.M = max_blocks_per_seq;
   d.pair_mode = use_pair_mode(cu, num_seqs, num_kv_heads, max_context_len, fp8) ? 1 : 0;
-  d.n_workers = d.pair_mode ? num_seqs * num_kv_heads : static_cast<int32_t>(workers);
   d.NB = num_blocks;
   d.c = static_cast<float>(static_cast<double>(scale) * static_cast<double>(k_scale) *
                            1.4426950408889634);  // log2(e); an fp8 K scale folds in
@@ -318,12 +349,18 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t per = tokens_per_launch(group, max_query_len);
   const int64_t token_elems = static_cast<int64_t>(num_q_heads) * head_dim;
-  // One launch pair (attention, merge) per run of `per` query tokens; each
-  // launch reads the K/V its tokens see.
-  for (int32_t off = 0; off < max_query_len; off += per) {
+  // One launch pair (attention, merge) per run of up to four chunks of `per`
+  // query tokens: the chunk waves of a slot walk one tile range together, so a
+  // K/V tile is fetched from memory once for all of the run's tokens.
+  for (int32_t off = 0; off < max_query_len;) {
+    const int32_t left = (max_query_len - off + per - 1) / per;
+    d.nch = chunks_per_launch(left);
     d.q_off = off;
     d.Qc = per < max_query_len - off ? per : max_query_len - off;
     d.R = group * d.Qc;
+    d.n_workers = d.pair_mode ? num_seqs * num_kv_heads
+                              : static_cast<int32_t>(multi_slots(cu, num_seqs, num_kv_heads,
+                                                                 max_context_len, fp8, d.nch));
     set_units(d, d.R, fp8);
     DecodeBuffers b{};
     b.q = static_cast<const uint16_t*>(q) + off * token_elems;
@@ -334,9 +371,11 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
     b.qlens = query_lens;
     b.out = static_cast<uint16_t*>(out) + off * token_elems;
     b.ws = static_cast<float*>(workspace);
-    if (launch_multi(b, d, head_dim, block_size, merge_groups_for(workers, cu), s, fp8) !=
-        hipSuccess)
+    if (launch_multi(b, d, head_dim, block_size,
+                     merge_groups_for(static_cast<int64_t>(d.n_workers) * d.nch, cu), s,
+                     fp8) != hipSuccess)
       return PKV_ERR_LAUNCH;
+    off += d.nch * per;
   }
   return PKV_OK;
 }
@@ -668,10 +707,10 @@ size_t paged_attn_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
   const int cu = pkv::current_cu_count();
   if (cu <= 0) return 0;
   // enough for either pool format (fp8 launches more workers)
-  const int64_t workers =
-      std::max(pkv::worker_count(cu, num_seqs, num_kv_heads, max_context_len, false),
-               pkv::worker_count(cu, num_seqs, num_kv_heads, max_context_len, true));
-  return pkv::multi_workspace_for(workers, num_q_heads / num_kv_heads, head_dim,
+  const int64_t waves =
+      std::max(pkv::multi_waves(cu, num_seqs, num_kv_heads, max_context_len, false),
+               pkv::multi_waves(cu, num_seqs, num_kv_heads, max_context_len, true));
+  return pkv::multi_workspace_for(waves, num_q_heads / num_kv_heads, head_dim,
                                   max_query_len > 0 ? max_query_len : 1);
 }
 

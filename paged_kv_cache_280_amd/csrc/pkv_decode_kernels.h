@@ -126,7 +126,8 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
 // (lens holds the per-sequence prefix lengths).  The tail pass (kShare = 2, a
 // decode launch) takes sequence s from position P = prefix_positions(qlens[s])
 // on (qlens holds the prefix lengths): L = context_lens[s] - P.  x is `first` in
-// the prefix pass and P in the tail pass.
+// the prefix pass and P in the tail pass; in multi-token launches it is the
+// position offset of the wave's query tokens (seq_len).
 struct SeqLen {
   int32_t L, T, x;
 };
@@ -156,9 +157,15 @@ __device__ __forceinline__ SeqLen seq_len(const int32_t* __restrict__ lens,
   } else if constexpr (!kCausal) {
     return SeqLen{L, 1};
   } else {
+    // every chunk of the launch plans over the context its last token sees,
+    // L_c = L - T + hi; this wave's tokens start at qoc and x = hi - qoc, so its
+    // token i (query token qoc + i, at position L - T + qoc + i) sees positions
+    // up to L_c - x + i
     const int32_t T = clamp_len(qlens[s], min(L, d.Qmax));
-    const int32_t Tc = clamp_len(T - d.q_off, d.Qc);
-    return SeqLen{Tc > 0 ? L - T + d.q_off + Tc : 0, Tc};
+    const int32_t qoc = d.q_off + d.chunk * d.Qc;
+    const int32_t hi = min(T, d.q_off + max(d.nch, 1) * d.Qc);
+    if (hi <= d.q_off) return SeqLen{0, 0, 0};
+    return SeqLen{L - T + hi, clamp_len(T - qoc, d.Qc), hi - qoc};
   }
 }
 
@@ -703,7 +710,7 @@ __device__ __forceinline__ void advance(Cursor& c, const Cx& cx, const DecodeDim
       const SeqLen sl = seq_len<kCausal, kShare>(cx.lens, cx.qlens, d, cap, c.s);
       c.L = sl.L;
       c.Tq = sl.T;
-      if constexpr (kShare != 0) c.x = sl.x;
+      if constexpr (kShare != 0 || kCausal) c.x = sl.x;
     } else {
       c.L = 1;  // past the batch only at the very end
       c.Tq = 1;
@@ -741,8 +748,9 @@ __device__ __forceinline__ void load_at(Tile& r, const Cx& cx, const DecodeDims&
 template <bool kCausal, int kShare = 0>
 __device__ __forceinline__ int64_t pair_row(const DecodeDims& d, const Cursor& c) {
   if constexpr (kShare == 1) return static_cast<int64_t>(c.x) * d.Hq + c.g * d.G;
-  const int64_t seq_rows = kCausal ? static_cast<int64_t>(d.Qmax) * d.Hq : d.Hq;
-  return c.s * seq_rows + c.g * d.G;
+  if constexpr (kCausal)  // rows of the wave's chunk of query tokens
+    return (c.s * static_cast<int64_t>(d.Qmax) + d.chunk * d.Qc) * d.Hq + c.g * d.G;
+  return c.s * static_cast<int64_t>(d.Hq) + c.g * d.G;
 }
 
 // Rows of a pair (R = G in decode launches).
@@ -1007,7 +1015,8 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
   lc.s = pl.s;
   lc.L = pl.L;
   lc.Tq = pl.Tq;
-  lc.x = kShare != 0 ? seq_len<kCausal, kShare>(cx.lens, cx.qlens, d, cap, pl.s).x : 0;
+  lc.x = (kShare != 0 || kCausal) ? seq_len<kCausal, kShare>(cx.lens, cx.qlens, d, cap, pl.s).x
+                                  : 0;
   lc.T = tiles_of(lc.L);
   lc.g = pl.g;
   lc.t = pl.t;
@@ -1070,8 +1079,9 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
         }
         // query token qi sits at position L - Tq + qi; other columns (and every
         // row of the prefix pass) see the whole context
-        lim_abs[j] = (kShare != 1 && live<NC, kCausal>(cl, j, cc)) ? cc.L - cc.Tq + cl.qi[j]
-                                                                   : cc.L - 1;
+        lim_abs[j] = (kShare == 0 && kCausal && live<NC, kCausal>(cl, j, cc))
+                         ? cc.L - cc.x + cl.qi[j]
+                         : cc.L - 1;
       }
       seg_t0 = cc.t;
     }
@@ -1083,7 +1093,8 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
       int32_t lim[NC];
 #pragma unroll
       for (int j = 0; j < NC; ++j) lim[j] = lim_abs[j] - cc.t * kTile;
-      compute_tile<D, NC, true>(r[slot], qc, st, d.c, valid, cc.L - cc.Tq - cc.t * kTile, lim,
+      compute_tile<D, NC, true>(r[slot], qc, st, d.c, valid,
+                                (kShare == 1 ? cc.L - 1 : cc.L - cc.x) - cc.t * kTile, lim,
                                 lane);
     } else {
       const int32_t lim[NC] = {valid - 1};
@@ -1103,7 +1114,9 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
         const int64_t last_unit = cc.start + static_cast<int64_t>(cc.g) * pair_units(cc.T, d) +
                                   d.hdr + static_cast<int64_t>(d.unit) * (cc.T - 1);
         const int32_t slot_tq = static_cast<int32_t>(rec - 2 * w) | (kCausal ? cc.Tq << 1 : 0);
-        opened = int4{cc.s, cc.g, static_cast<int32_t>(worker_of(last_unit, pl.U, pl.N)), slot_tq};
+        // the closing worker's range, as the wave that takes this wave's rows there
+        const int64_t wb = worker_of(last_unit, pl.U, pl.N) * max(d.nch, 1) + d.chunk;
+        opened = int4{cc.s, cc.g, static_cast<int32_t>(wb), slot_tq};
       }
       rec = 2 * w + 1;
     }
@@ -1140,9 +1153,11 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
 // Workspace: partial records ([n_workers][2] of record_floats), then one
 // descriptor per worker: (s, g, wb, first_slot | Tq << 1) of the split pair whose
 // first share this worker holds, or s = -1 (Tq only in multi-token launches).
-// fp8 single-tile launches cap registers for two waves per SIMD; the others keep one.  kShare: 0, or the prefix (1)
-// or tail (2) pass of a shared-prefix launch (seq_len), whose prefix states are at
-// `state`.
+// fp8 single-tile launches cap registers for two waves per SIMD; the others keep
+// one.  kShare: 0, or the prefix (1) or tail (2) pass of a shared-prefix launch
+// (seq_len), whose prefix states are at `state`.  Multi-token launches with
+// d.nch > 1: wave `wave` takes chunk wave % nch of the query tokens over the
+// range of worker (slot) wave / nch; records and descriptors are per wave.
 template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShare = 0>
 __global__ __launch_bounds__(kWave* kWavesPerGroup,
                              (kFp8 && NC == 1) ? 2 : 1) void decode_kernel(
@@ -1157,7 +1172,14 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
   const Ctx<typename TileOf<D, B, kFp8>::Elem> cx{q,     k,     v,  tables, lens, qlens, out,
                                                   ws,    k_new, v_new, kw, vw, state};
   const int lane = __lane_id();
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
+  const int64_t wave =
+      static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
+  int64_t w = wave;  // the planned range (slot) this wave takes
+  if constexpr (kCausal && kShare == 0) {
+    const int32_t nch = max(d.nch, 1);
+    w = wave / nch;
+    d.chunk = static_cast<int32_t>(wave - w * nch);
+  }
   if (w >= d.n_workers) return;
   const int32_t cap = d.M * B;
 #ifdef PKV_TIMELINE
@@ -1173,7 +1195,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
   const uint64_t t_plan = __builtin_amdgcn_s_memrealtime();
 #endif
   if (has)
-    opened = run_worker<D, B, NC, kCausal, kFp8, kAppend, kShare>(cx, d, pl, w, lane, t_first);
+    opened = run_worker<D, B, NC, kCausal, kFp8, kAppend, kShare>(cx, d, pl, wave, lane, t_first);
 #ifdef PKV_TIMELINE
   {
     const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
@@ -1188,7 +1210,9 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
     st.tiles = has ? static_cast<uint32_t>(pl.n) : 0u;
     st.group = blockIdx.x;
     // stamps follow the descriptors; one lane writes the worker's 32 bytes
-    if (lane == 0) reinterpret_cast<WorkerStamp*>(desc + d.n_workers)[w] = st;
+    if (lane == 0)
+      reinterpret_cast<WorkerStamp*>(desc + static_cast<int64_t>(d.n_workers) * max(d.nch, 1))[wave] =
+          st;
   }
 #endif
 
@@ -1199,7 +1223,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
   // normalised.
   const int32_t row_elems = d.Hq * D;
   if constexpr (kShare == 1) {
-    if (!d.pair_mode && lane == 0) desc[w] = opened;
+    if (!d.pair_mode && lane == 0) desc[wave] = opened;
     return;
   }
   if constexpr (kShare == 2) {
@@ -1221,7 +1245,7 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
         *reinterpret_cast<u32x4_t*>(row + e) = z;
       }
     }
-    if (!d.pair_mode && lane == 0) desc[w] = opened;
+    if (!d.pair_mode && lane == 0) desc[wave] = opened;
     return;
   }
   for (int64_t se = w; se < d.S; se += d.n_workers) {
@@ -1235,14 +1259,15 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
       }
       if (Lt != 0) continue;
     }
-    const int32_t rows = kCausal ? d.Qc : 1;
+    // this wave's chunk of query tokens (never past max_query_len)
+    const int32_t rows = kCausal ? min(d.Qc, d.Qmax - d.q_off - d.chunk * d.Qc) : 1;
     for (int32_t qi = first; qi < rows; ++qi) {
-      uint16_t* row = out + (kCausal ? se * d.Qmax + qi : se) * row_elems;
+      uint16_t* row = out + (kCausal ? se * d.Qmax + d.chunk * d.Qc + qi : se) * row_elems;
       for (int32_t e = lane * 8; e < row_elems; e += kWave * 8)
         *reinterpret_cast<u32x4_t*>(row + e) = u32x4_t{0, 0, 0, 0};
     }
   }
-  if (!d.pair_mode && lane == 0) desc[w] = opened;
+  if (!d.pair_mode && lane == 0) desc[wave] = opened;
 }
 
 // Merge of split pairs.  Work-group b reads the descriptors of its slice of
@@ -1279,9 +1304,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
   __shared__ int32_t s_wa[kMergeSlice];
   __shared__ int32_t s_count;
   const int tid = threadIdx.x;
-  const int64_t per = (d.n_workers + gridDim.x - 1) / gridDim.x;
+  // descriptors are per wave: nch waves per planned range in multi-token launches
+  // whose chunks share ranges; a pair's records are then every nch-th wave's
+  const int32_t nch = kCausal ? max(d.nch, 1) : 1;
+  const int64_t n_waves = static_cast<int64_t>(d.n_workers) * nch;
+  const int64_t per = (n_waves + gridDim.x - 1) / gridDim.x;
   const int64_t w0 = static_cast<int64_t>(blockIdx.x) * per;
-  const int64_t w1 = min(w0 + per, static_cast<int64_t>(d.n_workers));
+  const int64_t w1 = min(w0 + per, n_waves);
   if (tid == 0) s_count = 0;
   __syncthreads();
   if (w0 + tid < w1) {
@@ -1322,7 +1351,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
     }
     int64_t kmax = 0;
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) kmax = max(kmax, wb[it] - wa[it] + 1);
+    for (int it = 0; it < kItems; ++it) kmax = max(kmax, (wb[it] - wa[it]) / nch + 1);
     for (int64_t c = 0; c < kmax; c += kChunk) {
       float m[kItems][kChunk], l[kItems][kChunk], o[kItems][kChunk];
 #pragma unroll
@@ -1330,7 +1359,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
         const int32_t h = oi[it] / D;
 #pragma unroll
         for (int k = 0; k < kChunk; ++k) {
-          const int64_t wk = wa[it] + c + k;
+          const int64_t wk = wa[it] + (c + k) * nch;
           if (wk <= wb[it]) {
             const float* rec = ws + (c + k == 0 ? first[it] : 2 * wk * rf);
             m[it][k] = rec[RD + h];
@@ -1382,8 +1411,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
         if constexpr (kCausal) {
           const int32_t row = oi[it] / D;  // row = qi * G + head
           const int32_t qi = row / d.G;
-          idx = ((static_cast<int64_t>(ds.x) * d.Qmax + qi) * d.Hq + ds.y * d.G + (row - qi * d.G)) *
-                    D + (oi[it] - row * D);
+          const int32_t chunk = static_cast<int32_t>(s_wa[pi[it]] % nch);  // the opener's
+          idx = ((static_cast<int64_t>(ds.x) * d.Qmax + chunk * d.Qc + qi) * d.Hq + ds.y * d.G +
+                 (row - qi * d.G)) *
+                    D +
+                (oi[it] - row * D);
         } else {
           idx = (static_cast<int64_t>(ds.x) * d.Hq + ds.y * d.G) * D + oi[it];
         }
@@ -1398,10 +1430,11 @@ template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShar
 hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
                     hipStream_t stream) {
   using Elem = typename TileOf<D, B, kFp8>::Elem;
-  const int groups = (d.n_workers + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t waves = static_cast<int64_t>(d.n_workers) * (kCausal ? max(d.nch, 1) : 1);
+  const int groups = static_cast<int>((waves + kWavesPerGroup - 1) / kWavesPerGroup);
   if (groups <= 0) return hipSuccess;
-  int4* desc = reinterpret_cast<int4*>(reinterpret_cast<char*>(b.ws) +
-                                       records_bytes(d.n_workers, d.R, D));
+  int4* desc =
+      reinterpret_cast<int4*>(reinterpret_cast<char*>(b.ws) + records_bytes(waves, d.R, D));
   hipLaunchKernelGGL((decode_kernel<D, B, NC, kCausal, kFp8, kAppend, kShare>), dim3(groups),
                      dim3(kWave * kWavesPerGroup), 0, stream, b.q, static_cast<const Elem*>(b.k),
                      static_cast<const Elem*>(b.v), b.tables, b.lens, b.qlens, b.out, b.ws, desc,
@@ -1416,7 +1449,8 @@ hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_group
   // most kMergeSlice descriptors
   const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
   const int ny = (d.R * D + kMergeSpan - 1) / kMergeSpan;
-  const int nx = max(max(merge_groups / ny, (d.n_workers + kMergeSlice - 1) / kMergeSlice), 1);
+  const int nx =
+      max(max(merge_groups / ny, static_cast<int>((waves + kMergeSlice - 1) / kMergeSlice)), 1);
   const dim3 grid(nx, ny);
   if (pairs > 0 && d.n_workers > kMergeWideSplit * pairs)
     hipLaunchKernelGGL((merge_kernel<D, kCausal, 16, 1, kShare>), grid, dim3(kMergeThreads), 0,

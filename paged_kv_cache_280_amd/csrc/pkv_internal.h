@@ -62,6 +62,11 @@ struct DecodeDims {
   // and rounded down to a multiple of pre_align (max(16, B): whole tiles and blocks);
   // seqs is the batch's sequence count (the prefix pass runs over groups)
   int32_t pre_align, pre_cap, seqs;
+  // Multi-token launches whose rows exceed one wave's column tiles: nch waves of a
+  // work-group (2 or 4; 0 or 1: one) share each planned range of tiles, wave
+  // `chunk` taking query tokens q_off + chunk*Qc .. + Qc - 1, so a K/V tile is read
+  // from memory once for all of them.  n_workers counts the ranges (slots).
+  int32_t nch, chunk;
 };
 
 // Floats in one partial record: O[R][D], then m[R], then l[R], padded to a

@@ -47,6 +47,9 @@ SHAPES = [
     (128, 32, 16, 2, 3),     # group 8: 24 rows
     (128, 16, 16, 1, 3),     # group 16: runs of 2 and 1 tokens
     (64, 32, 4, 2, 6),       # group 2: 12 rows
+    (128, 16, 32, 8, 24),    # three chunks of 8: a launch of four chunk waves, one empty
+    (128, 32, 32, 8, 36),    # five chunks: four chunk waves, then one (the last of 4 tokens)
+    (64, 16, 16, 4, 64),     # eight chunks of 8: two launches of four chunk waves
 ]
 
 
@@ -137,24 +140,44 @@ def test_multi_prefill_chunks_add_up_to_whole_prefill():
     assert_parity(np.concatenate(rows, axis=1), ref, "chunked prefill 300/64")
 
 
-def test_multi_verify_at_long_context_sampled():
+@pytest.mark.parametrize("Q", [4, 16, 24])
+def test_multi_verify_at_long_context_sampled(Q):
     """Speculative verification at the long-context size: 8 sequences x 16,000
-    positions, 4 query tokens each (the last 4 positions), one layer's pools;
-    every output is checked against the oracle."""
+    positions, Q query tokens each (the last Q positions; 16 and 24 run as two and
+    three chunk waves per slot over pairs split across many slots), one layer's
+    pools; every output is checked against the oracle."""
     case = wl.case_long(seed=1, num_layers=1)
     rng = np.random.default_rng(8)
     kp, vp = wl.host_pools(case, poison=False)
-    S, Q = case.num_seqs, 4
+    S = case.num_seqs
     qlens = np.full(S, Q, np.int32)
     q = wl.randn_bf16(rng, (S, Q, case.num_q_heads, case.head_dim))
     got = _run(case, q, kp, vp, qlens)
     ref = oracle.paged_attn_multi(q, kp, vp, case.block_tables, case.context_lens, qlens,
                                   case.block_size, case.scale, case.num_kv_heads)
-    assert_parity(got, ref, "verify 8x16000 Q=4")
+    assert_parity(got, ref, "verify 8x16000 Q=%d" % Q)
+
+
+@pytest.mark.parametrize("Q", [16, 24, 40])
+def test_multi_chunk_waves_in_pair_mode(Q):
+    """Short contexts (at most 256 positions: one worker per (sequence, KV head)
+    pair, no split) with 2, 3 and 5 chunks of query tokens per sequence."""
+    rng = np.random.default_rng(40 + Q)
+    lens = np.array([Q, 256, 17, 0, 100, Q + 1, 200, 64], np.int32)
+    qlens = np.minimum(np.array([Q, Q, 9, 0, Q - 3, 1, Q // 2, Q], np.int32), lens)
+    case = wl.case_random(90 + Q, len(lens), 32, 8, 128, 16, lens)
+    kp, vp = wl.host_pools(case)
+    q = _q_with_nan_padding(rng, len(lens), Q, 32, 128, qlens)
+    got = _run(case, q, kp, vp, qlens)
+    ref = oracle.paged_attn_multi(q, kp, vp, case.block_tables, lens, qlens, 16, case.scale, 8)
+    for s, T in enumerate(qlens):
+        assert not got[s, T:].any(), "rows past the query tokens must be zero (seq %d)" % s
+    assert_parity(got, ref, "multi pair mode Q=%d" % Q)
 
 
 # (head_dim, block_size, q heads, kv heads, max query tokens) over fp8 pools
-FP8_SHAPES = [(128, 16, 32, 8, 4), (128, 16, 32, 8, 8), (64, 8, 8, 8, 40), (128, 32, 16, 2, 3)]
+FP8_SHAPES = [(128, 16, 32, 8, 4), (128, 16, 32, 8, 8), (64, 8, 8, 8, 40), (128, 32, 16, 2, 3),
+              (128, 16, 32, 8, 24)]
 
 
 @pytest.mark.parametrize("D,B,Hq,Hkv,Q", FP8_SHAPES)
