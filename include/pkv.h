@@ -298,11 +298,14 @@ int32_t paged_attn_multi_fp8(const void* q, const void* k_cache, const void* v_c
  * Every other argument, check and error code is paged_attn_decode's (bf16 pools
  * only).  Data that breaks the group contract gives meaningless outputs for the
  * sequences concerned; no memory outside the arguments is touched.  Results are
- * deterministic.  Enqueues up to four kernels: the prefix pass over the groups'
- * shared positions (rows: members x heads of a KV head) and its merge into
- * per-sequence prefix softmax states, then the decode of every sequence's
- * remaining positions (each (sequence, KV head) pair starting from its prefix
- * state) and its merge.
+ * deterministic.  Enqueues two kernels: one launch that runs, side by side on
+ * about half of the compute units each, the prefix pass over the groups' shared
+ * positions (rows: members x heads of a KV head) and the decode of every
+ * sequence's remaining positions; then one merge, which starts each (sequence, KV
+ * head) pair with a prefix from that prefix (the prefix pass's softmax state of a
+ * whole (group, KV head) pair, or its partial records of the pair's rows) and
+ * folds in the pair's own partial records.  Without a usable prefix (max_prefix_len
+ * below max(16, block_size)) it is a plain decode: one decode kernel and its merge.
  */
 size_t paged_attn_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                                 int32_t num_kv_heads, int32_t head_dim,

@@ -3,11 +3,13 @@
 // one static array below is the scratch of the no-allocation decode entry point.
 
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
 
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <utility>
 
 #include "pkv.h"
 #include "pkv_internal.h"
@@ -383,11 +385,21 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
 // Shared-prefix decode.  Workspace: the larger of the two passes' records and
 // descriptors, then (256-byte aligned) the prefix states, one record of
 // record_floats(num_q_heads, head_dim) floats per sequence.
+// Shared-prefix decode runs its two passes side by side in one launch, each with
+// about half of the compute units' worker slots (a work-group of four waves per
+// CU between them).
+// Workspace: the prefix pass's records and descriptors (its workers', then one
+// per (group, KV head) pair), the tail pass's (its workers', then one per
+// (sequence, KV head) pair), the prefix states (one record of
+// record_floats(num_q_heads, head_dim) floats per sequence), then the member map
+// (two int32 per sequence); each part 256-byte aligned.
 struct SharedLayout {
   int64_t workers_prefix, workers_tail;
   int32_t rows_prefix;
-  int64_t state_off, bytes;
+  int64_t tail_off, state_off, gmap_off, bytes;
 };
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 SharedLayout shared_layout(int cu, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t max_context_len, int32_t num_groups,
@@ -395,13 +407,31 @@ SharedLayout shared_layout(int cu, int32_t num_seqs, int32_t num_q_heads, int32_
   SharedLayout l;
   const int32_t group = num_q_heads / num_kv_heads;
   l.rows_prefix = group * max_group_size;
-  l.workers_prefix = worker_count(cu, num_groups, num_kv_heads, max_prefix_len);
-  l.workers_tail = worker_count(cu, num_seqs, num_kv_heads, max_context_len);
-  const int64_t a = workspace_bytes_for(l.workers_prefix, l.rows_prefix, head_dim);
-  const int64_t b = workspace_bytes_for(l.workers_tail, group, head_dim);
-  l.state_off = ((a > b ? a : b) + 255) / 256 * 256;
-  l.bytes = l.state_off + static_cast<int64_t>(num_seqs) * record_floats(num_q_heads, head_dim) *
-                              static_cast<int64_t>(sizeof(float));
+  // PKV_SHARED_WAVES=total,prefix overrides the split for launch-shape sweeps
+  static const std::pair<int, int> forced = [] {
+    const char* e = getenv("PKV_SHARED_WAVES");
+    int t = 0, p = 0;
+    if (e && sscanf(e, "%d,%d", &t, &p) == 2 && t > p && p > 0) return std::make_pair(t, p);
+    return std::make_pair(0, 0);
+  }();
+  const int64_t half = static_cast<int64_t>(cu) * kWavesPerGroup / 2;
+  const int64_t tiles_prefix = static_cast<int64_t>(num_groups) * num_kv_heads *
+                               ((static_cast<int64_t>(max_prefix_len) + kTile - 1) / kTile);
+  const int64_t tiles_tail = static_cast<int64_t>(num_seqs) * num_kv_heads *
+                             ((static_cast<int64_t>(max_context_len) + kTile - 1) / kTile);
+  const int64_t total = forced.first > 0 ? forced.first : 2 * half;
+  const int64_t want_prefix = forced.first > 0 ? forced.second : half;
+  l.workers_prefix = std::max<int64_t>(1, std::min(want_prefix, tiles_prefix));
+  l.workers_tail = std::max<int64_t>(1, std::min(total - l.workers_prefix, tiles_tail));
+  const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  const int64_t group_pairs = static_cast<int64_t>(num_groups) * num_kv_heads;
+  l.tail_off =
+      align256(workspace_bytes_for(l.workers_prefix + group_pairs, l.rows_prefix, head_dim));
+  l.state_off = align256(l.tail_off + workspace_bytes_for(l.workers_tail + pairs, group, head_dim));
+  l.gmap_off = align256(l.state_off + static_cast<int64_t>(num_seqs) *
+                                          record_floats(num_q_heads, head_dim) *
+                                          static_cast<int64_t>(sizeof(float)));
+  l.bytes = l.gmap_off + static_cast<int64_t>(num_seqs) * 2 * static_cast<int64_t>(sizeof(int32_t));
   return l;
 }
 
@@ -466,39 +496,46 @@ int32_t shared_impl(const void* q, const void* k_cache, const void* v_cache,
   d.pre_cap = max_prefix_len;
   d.seqs = num_seqs;
 
-  // prefix pass: group v's members are its T query tokens (rows member * G + head)
-  if (max_prefix_len >= d.pre_align && num_groups > 0) {
-    DecodeDims a = d;
-    b.lens = prefix_lens;
-    b.qlens = group_first;
-    a.S = num_groups;
-    a.pair_mode = use_pair_mode(cu, num_groups, num_kv_heads, max_prefix_len, false) ? 1 : 0;
-    a.n_workers = a.pair_mode ? num_groups * num_kv_heads : static_cast<int32_t>(lay.workers_prefix);
-    a.Qmax = max_group_size;
-    a.Qc = max_group_size;
-    a.q_off = 0;
-    a.R = lay.rows_prefix;
-    set_units(a, a.R, false);
-    if (launch_shared_prefix(b, a, head_dim, block_size,
-                             merge_groups_for(a.n_workers, cu), s) != hipSuccess)
+  const bool prefix_pass = max_prefix_len >= d.pre_align && num_groups > 0;
+  if (!prefix_pass) d.pre_cap = 0;  // no prefix anywhere: the tail pass is a plain decode
+
+  // tail pass: every sequence from its prefix on, each segment from an empty
+  // state; its merge starts each pair with a prefix from the pair's prefix state
+  DecodeBuffers bt = b;
+  bt.lens = context_lens;
+  bt.qlens = prefix_lens;
+  bt.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.tail_off);
+  DecodeDims dt = d;
+  dt.S = num_seqs;
+  dt.pair_mode = 0;
+  dt.n_workers = static_cast<int32_t>(lay.workers_tail);
+  dt.Qmax = 1;
+  dt.Qc = 1;
+  dt.q_off = 0;
+  dt.R = group;
+  set_units(dt, group, false);
+  const int mgt = merge_groups_for(dt.n_workers, cu);
+  if (!prefix_pass) {
+    if (launch_shared_tail(bt, dt, head_dim, block_size, mgt, s) != hipSuccess)
       return PKV_ERR_LAUNCH;
-  } else {
-    d.pre_cap = 0;  // no prefix anywhere: the tail pass is a plain decode
+    return PKV_OK;
   }
-  // tail pass: every sequence from its prefix on; pairs with a prefix always go
-  // through the merge, which folds the prefix state first
-  b.lens = context_lens;
-  b.qlens = prefix_lens;
-  d.S = num_seqs;
-  d.pair_mode = 0;
-  d.n_workers = static_cast<int32_t>(lay.workers_tail);
-  d.Qmax = 1;
-  d.Qc = 1;
-  d.q_off = 0;
-  d.R = group;
-  set_units(d, group, false);
-  if (launch_shared_tail(b, d, head_dim, block_size, merge_groups_for(d.n_workers, cu), s) !=
-      hipSuccess)
+  // prefix pass: group v's members are its T query tokens (rows member * G + head);
+  // whole prefix pairs leave prefix states, split ones records, for the tail merge
+  DecodeBuffers bp = b;
+  bp.lens = prefix_lens;
+  bp.qlens = group_first;
+  DecodeDims a = d;
+  a.S = num_groups;
+  a.pair_mode = use_pair_mode(cu, num_groups, num_kv_heads, max_prefix_len, false) ? 1 : 0;
+  a.n_workers = a.pair_mode ? num_groups * num_kv_heads : static_cast<int32_t>(lay.workers_prefix);
+  a.Qmax = max_group_size;
+  a.Qc = max_group_size;
+  a.q_off = 0;
+  a.R = lay.rows_prefix;
+  set_units(a, a.R, false);
+  int32_t* gmap = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + lay.gmap_off);
+  if (launch_shared(bp, a, bt, dt, head_dim, block_size, gmap, mgt, s) != hipSuccess)
     return PKV_ERR_LAUNCH;
   return PKV_OK;
 }

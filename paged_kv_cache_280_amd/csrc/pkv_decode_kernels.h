@@ -685,6 +685,8 @@ struct Ctx {
   T* kw;                               // the pools, written (the newest rows)
   T* vw;
   float* __restrict__ state;           // shared-prefix launches: prefix softmax states
+  int4* desc;                          // descriptors (shared-prefix passes add pair descriptors)
+  int32_t* gmap;                       // prefix pass: per sequence, its group and member index
 };
 
 // Position in a worker's stream of tiles: tile t of (sequence s, KV head g); L
@@ -811,6 +813,15 @@ __device__ __forceinline__ int64_t state_m(const DecodeDims& d, int64_t gr) {
   return s * record_floats(d.Hq, D) + static_cast<int64_t>(d.Hq) * D + (gr - s * d.Hq);
 }
 
+// Descriptors (and record pairs) of a launch: one per wave (nch waves per planned
+// range in multi-token launches whose chunks share ranges), then in the passes of a
+// shared-prefix launch one per (group or sequence, KV head) pair.
+template <int kShare>
+__host__ __device__ __forceinline__ int64_t descriptor_count(const DecodeDims& d) {
+  return static_cast<int64_t>(d.n_workers) * (d.nch > 1 ? d.nch : 1) +
+         (kShare != 0 ? static_cast<int64_t>(d.S) * d.Hkv : 0);
+}
+
 // End of a segment: the output rows when it covered the whole pair, else a partial
 // record (O, then m, then l) in slot `rec`.  The prefix pass writes a whole pair's
 // rows as prefix states instead of outputs.
@@ -855,30 +866,6 @@ __device__ void finish_segment(const Cx& cx, const DecodeDims& d, const SegState
         base[R * D + R + n] = l_tot;
       }
     }
-  }
-}
-
-// Tail pass of a shared-prefix launch: the prefix state of pair (s, g) as the
-// initial softmax state of the segment that starts at its first tail tile (one
-// column tile: column lane%16 is head g*G + lane%16; columns past G stay empty).
-template <int D, typename Cx>
-__device__ __forceinline__ void load_prefix_state(SegState<D>& ps, const Cx& cx,
-                                                  const DecodeDims& d, const Cursor& c, int lane) {
-  const int32_t n = lane & 15;
-  if (n < d.G) {
-    const int64_t gr = static_cast<int64_t>(c.s) * d.Hq + c.g * d.G + n;
-    const float* o = cx.state + state_o<D>(d, gr) + (lane >> 4) * 4;
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) ps.o[mt] = *reinterpret_cast<const f32x4_t*>(o + mt * 16);
-    const float* ml = cx.state + state_m<D>(d, gr);
-    ps.m = ml[0];
-    const float l = ml[d.Hq];
-    ps.l = f32x4_t{l, l, l, l};
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) ps.o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    ps.l = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    ps.m = -INFINITY;
   }
 }
 
@@ -1027,11 +1014,6 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
   bf16x8_t qb[kPipe][NC][D / 32];
   bf16x8_t qc[NC][D / 32];
   SegState<D> st[NC];
-  // tail pass: one prefix state fetched with the first tile of its pair (worker
-  // tile ps_tile; -1: none pending).  A pair that starts while it is taken (pairs
-  // of one or two tiles) reads its state when its first tile is computed.
-  SegState<D> ps;
-  int32_t ps_tile = -1;
   int32_t lim_abs[NC];  // last position column j sees (multi-token launches)
   int32_t seg_t0 = cc.t;
   int64_t rec = 2 * w;  // first segment -> slot 0, later ones -> slot 1
@@ -1048,13 +1030,6 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
   };
   auto load_step = [&](int slot, int32_t li) {
     if (lc.t == 0 || li == 0) load_q<D, NC, kCausal, kFp8, kShare>(qb[slot], cx, d, lc, cl, lane);
-    if constexpr (kShare == 2) {
-      static_assert(NC == 1, "the tail pass has one query row per head");
-      if (lc.t == 0 && lc.x > 0 && ps_tile < 0) {
-        load_prefix_state<D>(ps, cx, d, lc, lane);
-        ps_tile = li;
-      }
-    }
     load_at<D, B, kShare>(r[slot], cx, d, lc, lane);
     advance<kCausal, kShare>(lc, cx, d, cap);
   };
@@ -1064,19 +1039,10 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
       for (int j = 0; j < NC; ++j) {
 #pragma unroll
         for (int k = 0; k < D / 32; ++k) qc[j][k] = qb[slot][j][k];
-        if (kShare == 2 && cc.t == 0 && cc.x > 0) {  // the pair starts from its prefix
-          if (ps_tile == i) {
-            st[j] = ps;
-            ps_tile = -1;
-          } else {
-            load_prefix_state<D>(st[j], cx, d, cc, lane);
-          }
-        } else {
 #pragma unroll
-          for (int mt = 0; mt < D / 16; ++mt) st[j].o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          st[j].l = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          st[j].m = -INFINITY;
-        }
+        for (int mt = 0; mt < D / 16; ++mt) st[j].o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        st[j].l = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        st[j].m = -INFINITY;
         // query token qi sits at position L - Tq + qi; other columns (and every
         // row of the prefix pass) see the whole context
         lim_abs[j] = (kShare == 0 && kCausal && live<NC, kCausal>(cl, j, cc))
@@ -1105,15 +1071,59 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
       }
     }
     if (cc.t == cc.T - 1 || i == n - 1) {
-      const bool whole = seg_t0 == 0 && cc.t == cc.T - 1;
-      finish_segment<D, NC, kCausal, kShare>(cx, d, st, cc, cl, whole, rec, lane);
+      bool whole = seg_t0 == 0 && cc.t == cc.T - 1;
+      int64_t rec_at = rec;
+      if constexpr (kShare == 1) {
+        // prefix pass (split launches): the segment holding a pair's first tile
+        // names where the tail merge finds the pair's prefix: its state (whole
+        // pair, x = -1) or the records of waves x .. y, the first in slot z.  Pair
+        // (v, 0) also maps each member sequence to (v, member index).
+        if (seg_t0 == 0 && !d.pair_mode) {
+          const int64_t pair = static_cast<int64_t>(cc.s) * d.Hkv + cc.g;
+          int4 pd = {-1, 0, 0, 0};
+          if (!whole)
+            pd = int4{static_cast<int32_t>(w),
+                      static_cast<int32_t>(worker_of(cc.start + static_cast<int64_t>(cc.g) *
+                                                                    pair_units(cc.T, d) +
+                                                         d.hdr + static_cast<int64_t>(d.unit) * (cc.T - 1),
+                                                     pl.U, pl.N)),
+                      static_cast<int32_t>(rec - 2 * w), 0};
+          if (lane == 0) cx.desc[d.n_workers + pair] = pd;
+          if (cc.g == 0)
+            for (int32_t m = lane; m < cc.Tq; m += kWave) {
+              cx.gmap[2 * (cc.x + m)] = cc.s;
+              cx.gmap[2 * (cc.x + m) + 1] = m;
+            }
+        }
+      }
+      if constexpr (kShare == 2) {
+        // tail pass: the segment holding a pair's first tile names the pair's
+        // record set for the merge (pair descriptor n_workers + pair).  A whole
+        // pair with a prefix leaves a record in the pair's own slot (the merge
+        // folds it after the prefix state); other pairs get none: whole ones
+        // write their rows here, split ones are named by the opener's descriptor.
+        if (seg_t0 == 0) {
+          const int64_t pair = static_cast<int64_t>(cc.s) * d.Hkv + cc.g;
+          const int32_t k = static_cast<int32_t>(d.n_workers + pair);
+          int4 pd = {-1, 0, 0, 0};
+          if (whole && cc.x > 0) {
+            pd = int4{cc.s, cc.g, k, 2};
+            rec_at = 2 * static_cast<int64_t>(k);
+          }
+          if (lane == 0) cx.desc[k] = pd;
+        }
+      }
+      finish_segment<D, NC, kCausal, kShare>(cx, d, st, cc, cl, whole && rec_at == rec, rec_at,
+                                             lane);
       if (!whole && seg_t0 == 0) {
         // this worker holds the first share of a pair that later workers continue;
         // the worker holding the pair's last tile closes it (worked out here, mid-
         // stream, rather than after the last tile where it would lengthen the tail)
         const int64_t last_unit = cc.start + static_cast<int64_t>(cc.g) * pair_units(cc.T, d) +
                                   d.hdr + static_cast<int64_t>(d.unit) * (cc.T - 1);
-        const int32_t slot_tq = static_cast<int32_t>(rec - 2 * w) | (kCausal ? cc.Tq << 1 : 0);
+        // slot | Tq << 1 (multi-token), or slot | 2 when the pair has a prefix (tail pass)
+        const int32_t slot_tq = static_cast<int32_t>(rec - 2 * w) |
+                                (kCausal ? cc.Tq << 1 : (kShare == 2 && cc.x > 0 ? 2 : 0));
         // the closing worker's range, as the wave that takes this wave's rows there
         const int64_t wb = worker_of(last_unit, pl.U, pl.N) * max(d.nch, 1) + d.chunk;
         opened = int4{cc.s, cc.g, static_cast<int32_t>(wb), slot_tq};
@@ -1158,22 +1168,16 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
 // (seq_len), whose prefix states are at `state`.  Multi-token launches with
 // d.nch > 1: wave `wave` takes chunk wave % nch of the query tokens over the
 // range of worker (slot) wave / nch; records and descriptors are per wave.
-template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShare = 0>
-__global__ __launch_bounds__(kWave* kWavesPerGroup,
-                             (kFp8 && NC == 1) ? 2 : 1) void decode_kernel(
-    const uint16_t* __restrict__ q, const typename TileOf<D, B, kFp8>::Elem* __restrict__ k,
-    const typename TileOf<D, B, kFp8>::Elem* __restrict__ v,
-    const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
-    const int32_t* __restrict__ qlens, uint16_t* __restrict__ out, float* __restrict__ ws,
-    int4* __restrict__ desc, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, typename TileOf<D, B, kFp8>::Elem* kw,
-    typename TileOf<D, B, kFp8>::Elem* vw, float* __restrict__ state, DecodeDims d) {
+template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShare>
+__device__ __forceinline__ void decode_body(const Ctx<typename TileOf<D, B, kFp8>::Elem>& cx,
+                                            DecodeDims d, int64_t wave) {
   static_assert(!(kFp8 && kAppend), "over fp8 pools the new rows are appended in their own launch");
-  const Ctx<typename TileOf<D, B, kFp8>::Elem> cx{q,     k,     v,  tables, lens, qlens, out,
-                                                  ws,    k_new, v_new, kw, vw, state};
+  const int32_t* __restrict__ lens = cx.lens;
+  const int32_t* __restrict__ qlens = cx.qlens;
+  uint16_t* __restrict__ out = cx.out;
+  float* __restrict__ state = cx.state;
+  int4* __restrict__ desc = cx.desc;
   const int lane = __lane_id();
-  const int64_t wave =
-      static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave);
   int64_t w = wave;  // the planned range (slot) this wave takes
   if constexpr (kCausal && kShare == 0) {
     const int32_t nch = max(d.nch, 1);
@@ -1209,10 +1213,10 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
     st.xcc = xcc & 0xF;
     st.tiles = has ? static_cast<uint32_t>(pl.n) : 0u;
     st.group = blockIdx.x;
-    // stamps follow the descriptors; one lane writes the worker's 32 bytes
-    if (lane == 0)
-      reinterpret_cast<WorkerStamp*>(desc + static_cast<int64_t>(d.n_workers) * max(d.nch, 1))[wave] =
-          st;
+    // stamps follow the descriptors (split launches only: the workspace of a
+    // pair-mode launch is sized for its worker slots); one lane writes 32 bytes
+    if (lane == 0 && !d.pair_mode)
+      reinterpret_cast<WorkerStamp*>(desc + descriptor_count<kShare>(d))[wave] = st;
   }
 #endif
 
@@ -1227,23 +1231,19 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
     return;
   }
   if constexpr (kShare == 2) {
+    // a sequence whose context is all prefix has no tail tile: with a prefix its
+    // pairs' rows come from the merge (prefix state only), else they are zeros
     for (int64_t se = w; se < d.S; se += d.n_workers) {
       const SeqLen sl = seq_len<false, 2>(lens, qlens, d, cap, static_cast<int32_t>(se));
       if (sl.L != 0) continue;
-      uint16_t* row = out + se * row_elems;
-      for (int32_t e = lane * 8; e < row_elems; e += kWave * 8) {
-        u32x4_t z = {0, 0, 0, 0};
-        if (sl.x > 0) {
-          const int64_t gr = se * d.Hq + e / D;
-          const float* o = state + state_o<D>(d, gr) + e % D;
-          const float inv = d.v_scale / state[state_m<D>(d, gr) + d.Hq];
-          bf16x8_t y;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) y[i] = static_cast<__bf16>(o[i] * inv);
-          z = __builtin_bit_cast(u32x4_t, y);
-        }
-        *reinterpret_cast<u32x4_t*>(row + e) = z;
+      for (int32_t g = lane; g < d.Hkv; g += kWave) {
+        const int32_t kd = static_cast<int32_t>(d.n_workers + se * d.Hkv + g);
+        desc[kd] = sl.x > 0 ? int4{static_cast<int32_t>(se), g, kd - 1, 2} : int4{-1, 0, 0, 0};
       }
+      if (sl.x > 0) continue;
+      uint16_t* row = out + se * row_elems;
+      for (int32_t e = lane * 8; e < row_elems; e += kWave * 8)
+        *reinterpret_cast<u32x4_t*>(row + e) = u32x4_t{0, 0, 0, 0};
     }
     if (!d.pair_mode && lane == 0) desc[wave] = opened;
     return;
@@ -1270,6 +1270,43 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup,
   if (!d.pair_mode && lane == 0) desc[wave] = opened;
 }
 
+template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShare = 0>
+__global__ __launch_bounds__(kWave* kWavesPerGroup,
+                             (kFp8 && NC == 1) ? 2 : 1) void decode_kernel(
+    const uint16_t* __restrict__ q, const typename TileOf<D, B, kFp8>::Elem* __restrict__ k,
+    const typename TileOf<D, B, kFp8>::Elem* __restrict__ v,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ lens,
+    const int32_t* __restrict__ qlens, uint16_t* __restrict__ out, float* __restrict__ ws,
+    int4* __restrict__ desc, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, typename TileOf<D, B, kFp8>::Elem* kw,
+    typename TileOf<D, B, kFp8>::Elem* vw, float* __restrict__ state, DecodeDims d) {
+  const Ctx<typename TileOf<D, B, kFp8>::Elem> cx{q,     k,  v,  tables, lens, qlens, out,
+                                                  ws,    k_new, v_new, kw, vw, state, desc,
+                                                  nullptr};
+  decode_body<D, B, NC, kCausal, kFp8, kAppend, kShare>(
+      cx, d, static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + uniform(threadIdx.x / kWave));
+}
+
+// Both passes of a shared-prefix call in one launch: work-groups below
+// prefix_groups run the prefix pass (NCp column tiles of group-member rows), the
+// others the tail pass, each over its own workers, records and descriptors.
+struct SharedArgs {
+  Ctx<uint16_t> p, t;  // prefix pass, tail pass
+  DecodeDims a, d;     // their sizes
+  int32_t prefix_groups;
+};
+
+template <int D, int B, int NCp>
+__global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void shared_kernel(SharedArgs sa) {
+  const int64_t wi = uniform(threadIdx.x / kWave);
+  if (static_cast<int32_t>(blockIdx.x) < sa.prefix_groups)
+    decode_body<D, B, NCp, true, false, false, 1>(
+        sa.p, sa.a, static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wi);
+  else
+    decode_body<D, B, 1, false, false, false, 2>(
+        sa.t, sa.d, static_cast<int64_t>(blockIdx.x - sa.prefix_groups) * kWavesPerGroup + wi);
+}
+
 // Merge of split pairs.  Work-group b reads the descriptors of its slice of
 // workers in one parallel pass and keeps the valid ones in LDS (each names a split
 // pair opened by worker wa and closed by wb).  The (pair, output) items of those
@@ -1289,25 +1326,37 @@ constexpr int kMergeWideSplit = 12;
 // pairs with more rows (multi-token and prefix launches) spread over more groups.
 constexpr int kMergeSpan = 512;
 
+
+// Where the merge of a shared-prefix launch's tail pass finds the prefix of a
+// pair: the prefix pass's records (R rows each) and pair descriptors (none: every
+// prefix is a whole pair, whose state the prefix pass wrote), and the member map.
+struct PrefixView {
+  const float* ws;
+  const int4* pdesc;
+  const int32_t* gmap;
+  int32_t R, groups;
+};
+
 //
-// Shared-prefix launches: after the prefix pass (kShare = 1) the merged rows are
-// written as prefix states (unnormalised O, m, l) of the group's sequences
-// (gfirst: the group offsets).
+// Tail pass of a shared-prefix launch (kShare = 2): a pair with a prefix folds its
+// prefix first, from the prefix state (a whole prefix pair) or from the prefix
+// pass's records of its rows (a split one), then its own records.
 template <int D, bool kCausal, int kChunk, int kItems, int kShare = 0>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __restrict__ desc,
                                                               uint16_t* __restrict__ out,
                                                               const float* __restrict__ ws,
-                                                              DecodeDims d,
-                                                              const int32_t* __restrict__ gfirst,
-                                                              float* __restrict__ state) {
+                                                              DecodeDims d, PrefixView pv,
+                                                              const float* __restrict__ state) {
   __shared__ int4 s_desc[kMergeSlice];
   __shared__ int32_t s_wa[kMergeSlice];
+  __shared__ int4 s_pp[kShare == 2 ? kMergeSlice : 1];
   __shared__ int32_t s_count;
   const int tid = threadIdx.x;
   // descriptors are per wave: nch waves per planned range in multi-token launches
-  // whose chunks share ranges; a pair's records are then every nch-th wave's
+  // whose chunks share ranges; a pair's records are then every nch-th wave's.  The
+  // tail pass of a shared-prefix launch adds one descriptor per pair.
   const int32_t nch = kCausal ? max(d.nch, 1) : 1;
-  const int64_t n_waves = static_cast<int64_t>(d.n_workers) * nch;
+  const int64_t n_waves = descriptor_count<kShare>(d);
   const int64_t per = (n_waves + gridDim.x - 1) / gridDim.x;
   const int64_t w0 = static_cast<int64_t>(blockIdx.x) * per;
   const int64_t w1 = min(w0 + per, n_waves);
@@ -1319,6 +1368,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
       const int32_t slot = atomicAdd(&s_count, 1);
       s_desc[slot] = ds;
       s_wa[slot] = static_cast<int32_t>(w0 + tid);
+      if constexpr (kShare == 2) {
+        // the prefix of a pair with one: {first wave, last wave, first slot, member}
+        // of its split prefix pair, or x = -1 (the prefix state)
+        int4 pp = {-1, 0, 0, 0};
+        if ((ds.w & 2) && pv.pdesc) {
+          const int32_t grp = min(max(pv.gmap[2 * ds.x], 0), pv.groups - 1);
+          const int32_t mem = min(max(pv.gmap[2 * ds.x + 1], 0), pv.R / d.G - 1);
+          const int4 pd = pv.pdesc[static_cast<int64_t>(grp) * d.Hkv + ds.y];
+          if (pd.x >= 0) pp = int4{pd.x, pd.y, pd.z, mem};
+        }
+        s_pp[slot] = pp;
+      }
     }
   }
   __syncthreads();
@@ -1335,12 +1396,17 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
     int64_t wa[kItems], wb[kItems], first[kItems];
     int32_t pi[kItems], oi[kItems];
     bool act[kItems];
+    // tail pass of a shared-prefix launch: np prefix records (of prefix waves pwa ..,
+    // the first in slot pslot) precede the pair's own, their entry (prow, pcol)
+    int32_t np[kItems], pwa[kItems], pslot[kItems], prow[kItems], pcol[kItems];
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
       const int32_t item = base + it * kMergeThreads;
       run_m[it] = -INFINITY;
       run_l[it] = 0.f;
       acc[it] = 0.f;
+      np[it] = 0;
+      pwa[it] = pslot[it] = prow[it] = pcol[it] = 0;
       pi[it] = item < total ? item / span : 0;
       oi[it] = item < total ? oi0 + (item - pi[it] * span) : 0;
       act[it] = item < total;
@@ -1348,6 +1414,81 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
       wa[it] = s_wa[pi[it]];
       wb[it] = act[it] ? static_cast<int64_t>(s_desc[pi[it]].z) : wa[it] - 1;  // none
       first[it] = (2 * wa[it] + (s_desc[pi[it]].w & 1)) * rf;
+      if constexpr (kShare == 2) {
+        // a pair with a prefix starts from its prefix
+        const int4 ds = s_desc[pi[it]];
+        if (act[it] && (ds.w & 2)) {
+          const int32_t row = oi[it] / D;
+          const int32_t col = oi[it] - row * D;
+          const int4 pp = s_pp[pi[it]];
+          if (pp.x < 0) {
+            const int64_t gr = static_cast<int64_t>(ds.x) * d.Hq + ds.y * d.G + row;
+            const int64_t mo = state_m<D>(d, gr);
+            run_m[it] = state[mo];
+            run_l[it] = state[mo + d.Hq];
+            acc[it] = state[state_o<D>(d, gr) + col];
+          } else {
+            // the records of prefix waves pp.x .. pp.y come first, row member*G + row
+            np[it] = pp.y - pp.x + 1;
+            pwa[it] = pp.x;
+            pslot[it] = pp.z;
+            prow[it] = pp.w * d.G + row;
+            pcol[it] = col;
+          }
+        }
+      }
+    }
+    // folds one batch of kChunk records per item into the running (m, l, acc)
+    auto fold = [&](float (&m)[kItems][kChunk], const float (&l)[kItems][kChunk],
+                    const float (&o)[kItems][kChunk]) {
+#pragma unroll
+      for (int it = 0; it < kItems; ++it) {
+        float cm = run_m[it];
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k) cm = fmaxf(cm, m[it][k]);
+        if (cm == -INFINITY) continue;  // item past the end, or no record in this chunk
+        const float scale = __builtin_amdgcn_exp2f(run_m[it] - cm);
+        run_l[it] *= scale;
+        acc[it] *= scale;
+        run_m[it] = cm;
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k) {
+          const float e = __builtin_amdgcn_exp2f(m[it][k] - cm);
+          run_l[it] += e * l[it][k];
+          acc[it] += e * o[it][k];
+        }
+      }
+    };
+    if constexpr (kShare == 2) {
+      // the prefix pass's records of the item's row, before the pair's own
+      int32_t pmax = 0;
+#pragma unroll
+      for (int it = 0; it < kItems; ++it) pmax = max(pmax, np[it]);
+      const int64_t rfp = record_floats(pv.R, D);
+      for (int32_t c = 0; c < pmax; c += kChunk) {
+        float m[kItems][kChunk], l[kItems][kChunk], o[kItems][kChunk];
+#pragma unroll
+        for (int it = 0; it < kItems; ++it) {
+          const int32_t mo = pv.R * D + prow[it];  // m of the row; l follows R later
+          const int32_t oo = prow[it] * D + pcol[it];
+#pragma unroll
+          for (int k = 0; k < kChunk; ++k) {
+            const int32_t pk = c + k;
+            if (pk < np[it]) {
+              const float* rec = pv.ws + (pk == 0 ? 2 * static_cast<int64_t>(pwa[it]) + pslot[it]
+                                                  : 2 * static_cast<int64_t>(pwa[it] + pk)) * rfp;
+              m[it][k] = rec[mo];
+              l[it][k] = rec[mo + pv.R];
+              o[it][k] = rec[oo];
+            } else {
+              m[it][k] = -INFINITY;
+              l[it][k] = 0.f;
+              o[it][k] = 0.f;
+            }
+          }
+        }
+        fold(m, l, o);
+      }
     }
     int64_t kmax = 0;
 #pragma unroll
@@ -1372,40 +1513,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
           }
         }
       }
-#pragma unroll
-      for (int it = 0; it < kItems; ++it) {
-        float cm = run_m[it];
-#pragma unroll
-        for (int k = 0; k < kChunk; ++k) cm = fmaxf(cm, m[it][k]);
-        if (cm == -INFINITY) continue;  // item past the end, or no record in this chunk
-        const float scale = __builtin_amdgcn_exp2f(run_m[it] - cm);
-        run_l[it] *= scale;
-        acc[it] *= scale;
-        run_m[it] = cm;
-#pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-          const float e = __builtin_amdgcn_exp2f(m[it][k] - cm);
-          run_l[it] += e * l[it][k];
-          acc[it] += e * o[it][k];
-        }
-      }
+      fold(m, l, o);
     }
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
-      if (kShare == 1 && act[it]) {
-        const int4 ds = s_desc[pi[it]];
-        const int32_t row = oi[it] / D;  // row = qi * G + head
-        const int32_t qi = row / d.G;
-        const int32_t member = min(max(gfirst[ds.x], 0), d.seqs - 1) + qi;
-        const int64_t gr = static_cast<int64_t>(member) * d.Hq + ds.y * d.G + (row - qi * d.G);
-        const int32_t col = oi[it] - row * D;
-        state[state_o<D>(d, gr) + col] = acc[it];
-        if (col == 0) {
-          const int64_t mo = state_m<D>(d, gr);
-          state[mo] = run_m[it];
-          state[mo + d.Hq] = run_l[it];
-        }
-      } else if (act[it]) {
+      if (act[it]) {
         const int4 ds = s_desc[pi[it]];
         int64_t idx;
         if constexpr (kCausal) {
@@ -1426,6 +1538,37 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
   }
 }
 
+// Descriptors of a launch: after its records in the workspace.
+template <int D, int kShare>
+int4* descriptors(const DecodeBuffers& b, const DecodeDims& d) {
+  return reinterpret_cast<int4*>(reinterpret_cast<char*>(b.ws) +
+                                 records_bytes(descriptor_count<kShare>(d), d.R, D));
+}
+
+// The merge launch of a split launch.  Records per split pair: about the workers
+// per (sequence, KV head) pair; a pair's outputs are spread over ny = ceil(R * D /
+// kMergeSpan) work-groups, and the descriptor slices shrink to about merge_groups
+// / ny (a merge work-group fills a CU: more than one per CU would run in rounds),
+// each still scanning at most kMergeSlice descriptors.
+template <int D, bool kCausal, int kShare>
+hipError_t launch_merge(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
+                        hipStream_t stream, const PrefixView& pv = PrefixView{}) {
+  const int64_t n_desc = descriptor_count<kShare>(d);
+  const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
+  const int ny = (d.R * D + kMergeSpan - 1) / kMergeSpan;
+  const int nx =
+      max(max(merge_groups / ny, static_cast<int>((n_desc + kMergeSlice - 1) / kMergeSlice)), 1);
+  const dim3 grid(nx, ny);
+  int4* desc = descriptors<D, kShare>(b, d);
+  if (pairs > 0 && d.n_workers > kMergeWideSplit * pairs)
+    hipLaunchKernelGGL((merge_kernel<D, kCausal, 16, 1, kShare>), grid, dim3(kMergeThreads), 0,
+                       stream, desc, b.out, b.ws, d, pv, b.state);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, kCausal, 12, 2, kShare>), grid, dim3(kMergeThreads), 0,
+                       stream, desc, b.out, b.ws, d, pv, b.state);
+  return hipGetLastError();
+}
+
 template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShare>
 hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
                     hipStream_t stream) {
@@ -1433,32 +1576,46 @@ hipError_t launch_t(const DecodeBuffers& b, const DecodeDims& d, int merge_group
   const int64_t waves = static_cast<int64_t>(d.n_workers) * (kCausal ? max(d.nch, 1) : 1);
   const int groups = static_cast<int>((waves + kWavesPerGroup - 1) / kWavesPerGroup);
   if (groups <= 0) return hipSuccess;
-  int4* desc =
-      reinterpret_cast<int4*>(reinterpret_cast<char*>(b.ws) + records_bytes(waves, d.R, D));
   hipLaunchKernelGGL((decode_kernel<D, B, NC, kCausal, kFp8, kAppend, kShare>), dim3(groups),
                      dim3(kWave * kWavesPerGroup), 0, stream, b.q, static_cast<const Elem*>(b.k),
-                     static_cast<const Elem*>(b.v), b.tables, b.lens, b.qlens, b.out, b.ws, desc,
-                     b.k_new, b.v_new, static_cast<Elem*>(b.kw), static_cast<Elem*>(b.vw), b.state,
-                     d);
+                     static_cast<const Elem*>(b.v), b.tables, b.lens, b.qlens, b.out, b.ws,
+                     descriptors<D, kShare>(b, d), b.k_new, b.v_new, static_cast<Elem*>(b.kw),
+                     static_cast<Elem*>(b.vw), b.state, d);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   if (d.pair_mode) return hipSuccess;  // nothing is split: no merge
-  // records per split pair: about the workers per (sequence, KV head) pair; a
-  // pair's outputs are spread over ny = ceil(R * D / kMergeSpan) work-groups, and
-  // the descriptor slices shrink to about merge_groups / ny (a merge work-group
-  // fills a CU: more than one per CU would run in rounds), each still scanning at
-  // most kMergeSlice descriptors
-  const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
-  const int ny = (d.R * D + kMergeSpan - 1) / kMergeSpan;
-  const int nx =
-      max(max(merge_groups / ny, static_cast<int>((waves + kMergeSlice - 1) / kMergeSlice)), 1);
-  const dim3 grid(nx, ny);
-  if (pairs > 0 && d.n_workers > kMergeWideSplit * pairs)
-    hipLaunchKernelGGL((merge_kernel<D, kCausal, 16, 1, kShare>), grid, dim3(kMergeThreads), 0,
-                       stream, desc, b.out, b.ws, d, b.qlens, b.state);
-  else
-    hipLaunchKernelGGL((merge_kernel<D, kCausal, 12, 2, kShare>), grid, dim3(kMergeThreads), 0,
-                       stream, desc, b.out, b.ws, d, b.qlens, b.state);
-  return hipGetLastError();
+  return launch_merge<D, kCausal, kShare>(b, d, merge_groups, stream);
+}
+
+// Both passes of a shared-prefix call (bp, a: prefix pass; bt, d: tail pass) in
+// one launch, then one merge: the tail pass's, which folds each pair's prefix
+// (prefix state, or the prefix pass's records) before its own records.  gmap:
+// two int32 per sequence (its group, its member index).
+template <int D, int B, int NCp>
+hipError_t launch_shared_t(const DecodeBuffers& bp, const DecodeDims& a, const DecodeBuffers& bt,
+                           const DecodeDims& d, int32_t* gmap, int merge_groups_tail,
+                           hipStream_t stream) {
+  auto ctx = [gmap](const DecodeBuffers& b, int4* desc) {
+    return Ctx<uint16_t>{b.q,  static_cast<const uint16_t*>(b.k), static_cast<const uint16_t*>(b.v),
+                         b.tables, b.lens, b.qlens, b.out, b.ws, nullptr, nullptr, nullptr,
+                         nullptr, b.state, desc, gmap};
+  };
+  SharedArgs sa;
+  sa.p = ctx(bp, descriptors<D, 1>(bp, a));
+  sa.t = ctx(bt, descriptors<D, 2>(bt, d));
+  sa.a = a;
+  sa.d = d;
+  sa.prefix_groups = (a.n_workers + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int groups = sa.prefix_groups + (d.n_workers + kWavesPerGroup - 1) / kWavesPerGroup;
+  hipLaunchKernelGGL((shared_kernel<D, B, NCp>), dim3(groups), dim3(kWave * kWavesPerGroup), 0,
+                     stream, sa);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  PrefixView pv;
+  pv.ws = bp.ws;
+  pv.pdesc = a.pair_mode ? nullptr : descriptors<D, 1>(bp, a) + a.n_workers;
+  pv.gmap = gmap;
+  pv.R = a.R;
+  pv.groups = a.S;
+  return launch_merge<D, false, 2>(bt, d, merge_groups_tail, stream, pv);
 }
 
 template <int NC, bool kCausal, bool kFp8, bool kAppend = false, int kShare = 0>

@@ -118,12 +118,15 @@ hipError_t launch_multi_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, 
 // the V pool's scale.
 hipError_t launch_decode_fp8(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                              int merge_groups, hipStream_t stream);
-// Shared-prefix decode (pkv_decode_shared.hip), bf16 pools: the prefix pass over
-// sharing groups (d.R = G * largest group <= kMaxRows; b.lens = prefix lengths,
-// b.qlens = group offsets) and the tail pass (b.qlens = prefix lengths); both
-// with b.state set.
-hipError_t launch_shared_prefix(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
-                                int merge_groups, hipStream_t stream);
+// Shared-prefix decode over bf16 pools (pkv_decode_shared.hip).  launch_shared:
+// the prefix pass over the sharing groups (a.R = G * largest group <= kMaxRows;
+// bp.lens = prefix lengths, bp.qlens = group offsets) and the tail pass (bt.qlens =
+// prefix lengths) in one launch, then the tail merge; both with the same state
+// buffer, and gmap (2 int32 per sequence) for the prefix pass's member map.
+// launch_shared_tail: the tail pass alone (no prefix anywhere).
+hipError_t launch_shared(const DecodeBuffers& bp, const DecodeDims& a, const DecodeBuffers& bt,
+                         const DecodeDims& d, int D, int B, int32_t* gmap, int merge_groups_tail,
+                         hipStream_t stream);
 hipError_t launch_shared_tail(const DecodeBuffers& b, const DecodeDims& d, int D, int B,
                               int merge_groups, hipStream_t stream);
 // Decode with append (d.len_off = 1; b.k_new, v_new, kw, vw set), bf16 pools.

@@ -185,3 +185,52 @@ def test_block_manager_groups_on_the_sampling_batch(seed):
     # within the gate of the oracle; here within a few bf16 ulps of each other)
     diff = np.abs(got - bf16_to_f32(plain))
     assert diff.max() <= 4 * 2.0 ** -8 * max(1.0, float(np.abs(got).max()))
+
+
+def test_shared_prefix_decode_replayed_from_a_graph():
+    """The call (its prefix pass forked onto the library's own stream and joined
+    back) captured in a graph and replayed with new queries and eager work between
+    replays: every replay matches the oracle."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    dev = torch.device("cuda:0")
+    case, gfirst, plens = shared_case(9, 16, 128, 32, 8, [(8, 512, [0, 3, 17, 40, 1, 2, 100, 5]),
+                                                          (4, 256, [9, 0, 33, 64])])
+    S, Hq, D, B = case.num_seqs, case.num_q_heads, case.head_dim, case.block_size
+    kp, vp = wl.host_pools(case)
+    kd, vd = to_dev_bf16(kp), to_dev_bf16(vp)
+    tabs, lens = to_dev_i32(case.block_tables), to_dev_i32(case.context_lens)
+    gf, pl = to_dev_i32(gfirst), to_dev_i32(plens)
+    q = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    mx, mp = case.max_context_len, int(plens.max())
+    ws = torch.empty(pkv.paged_attn_decode_shared_workspace_bytes(S, Hq, 8, D, B, mx, len(gfirst) - 1,
+                                                                  8, mp),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        pkv.paged_attn_decode_shared(q, kd, vd, tabs, lens, gf, pl, B, case.scale, out,
+                                     max_group_size=8, max_prefix_len=mp, max_context_len=mx,
+                                     workspace=ws)
+
+    rng = np.random.default_rng(1)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for replay in range(4):
+        qh = wl.randn_bf16(rng, (S, Hq, D))
+        q.copy_(torch.from_numpy(qh.view(np.int16)).to(dev).view(torch.bfloat16))
+        out.fill_(float("nan"))
+        ws.fill_(0xA5)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.paged_decode(qh, kp, vp, case.block_tables, case.context_lens, B, case.scale, 8)
+        assert_parity(bf16_to_f32(out), ref, "shared graph replay %d" % replay)
