@@ -7,6 +7,7 @@ oracle.paged_decode on the same tables (sharing is invisible to it).
 Cases: the shared-prefix sampling batch built by the block manager (16 prompts x
 8 samples, prefix 1,020, tails U[0, 256]); random group structures over block
 sizes 8/16/32, head_dim 64/128 and 1, 4 and 8 query heads per KV head, with
+prefixes split over several workers and prefixes short enough to be whole,
 groups of one, empty tails (the whole context is prefix), prefix lengths that are
 not a multiple of the alignment (used rounded down) or above max_prefix_len (used
 clamped), and a census of logical blocks (q = 0, V one-hot by logical block: every
@@ -86,6 +87,10 @@ SHAPES = [
     (5, 16, 128, 64, 8, [(4, 4000, [10, 20, 30, 40]), (4, 128, [5, 0, 129, 77]),
                          (1, 0, [64])]),
     (6, 32, 64, 16, 4, [(8, 8192, [3, 300, 0, 64, 1, 2, 4, 8]), (8, 96 * 32, [1] * 8)]),
+    # prefixes of at most 256 positions: the prefix pass takes one worker per
+    # (group, KV head) pair (no split: every prefix comes from a state)
+    (10, 16, 128, 32, 8, [(8, 240, [0, 1, 5, 16, 17, 200, 0, 33]), (4, 128, [2, 0, 64, 9]),
+                          (1, 0, [40])]),
 ]
 
 
