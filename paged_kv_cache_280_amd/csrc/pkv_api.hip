@@ -382,9 +382,6 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   return PKV_OK;
 }
 
-// Shared-prefix decode.  Workspace: the larger of the two passes' records and
-// descriptors, then (256-byte aligned) the prefix states, one record of
-// record_floats(num_q_heads, head_dim) floats per sequence.
 // Shared-prefix decode runs its two passes side by side in one launch, each with
 // about half of the compute units' worker slots (a work-group of four waves per
 // CU between them).
@@ -500,7 +497,7 @@ int32_t shared_impl(const void* q, const void* k_cache, const void* v_cache,
   if (!prefix_pass) d.pre_cap = 0;  // no prefix anywhere: the tail pass is a plain decode
 
   // tail pass: every sequence from its prefix on, each segment from an empty
-  // state; its merge starts each pair with a prefix from the pair's prefix state
+  // state; its merge starts each pair that has a prefix from that prefix
   DecodeBuffers bt = b;
   bt.lens = context_lens;
   bt.qlens = prefix_lens;

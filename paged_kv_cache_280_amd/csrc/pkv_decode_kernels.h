@@ -986,10 +986,8 @@ __device__ void one_token(const Cx& cx, const DecodeDims& d, int64_t s, int lane
 // One worker: the n tiles of its range in order, with loads running kPipe-1
 // tiles ahead of the arithmetic across (sequence, head) boundaries; the query of a
 // pair is fetched with the pair's first tile.  Returns the descriptor of the split
-// pair this worker opens (s = -1 if none).  In the tail pass of a shared-prefix
-// launch the segment that starts at a pair's first tile starts from the pair's
-// prefix state (fetched with that tile) instead of an empty one, so whole pairs
-// and the records of split ones already hold the prefix.
+// pair this worker opens (s = -1 if none).  The passes of a shared-prefix launch
+// also write pair descriptors (see the end of a segment below).
 template <int D, int B, int NC, bool kCausal, bool kFp8, bool kAppend, int kShare = 0,
           typename Cx>
 __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& pl, int64_t w,
@@ -1223,8 +1221,7 @@ __device__ __forceinline__ void decode_body(const Ctx<typename TileOf<D, B, kFp8
   // Rows no tile reaches are zeros: every row of an empty sequence, and in a
   // multi-token launch the rows past a sequence's query tokens (done last: off
   // the path to the first loads).  The prefix pass writes no output rows; in the
-  // tail pass a sequence whose context is all prefix gets its prefix state,
-  // normalised.
+  // tail pass a sequence whose context is all prefix is left to the merge.
   const int32_t row_elems = d.Hq * D;
   if constexpr (kShare == 1) {
     if (!d.pair_mode && lane == 0) desc[wave] = opened;
