@@ -237,10 +237,12 @@ size_t paged_attn_multi_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * error codes (plus PKV_ERR_NULL for query_lens) and the same guarantees
  * (determinism, renumbering invariance).  With max_query_len = 1 and T = 1 for
  * every sequence of nonzero length the result equals paged_attn_decode's bit for
- * bit.  Query tokens are processed 32 / G at a time (G = num_q_heads /
- * num_kv_heads; up to 32 MFMA columns of (token, head) rows): an attention kernel
- * and a merge kernel are enqueued for each of the ceil(max_query_len / (32 / G))
- * runs of tokens, and each run reads the K/V its tokens see.
+ * bit.  A wave computes a chunk of C query tokens (G = num_q_heads /
+ * num_kv_heads; C = 32 / G, or 16 / G when max_context_len <= 2048, at least 1:
+ * up to 32 MFMA columns of (token, head) rows).  Up to four chunks share one
+ * launch, their waves reading each K/V tile together (it comes from memory once);
+ * an attention kernel and a merge kernel are enqueued for each run of up to four
+ * chunks, and each run reads the K/V its tokens see.
  */
 int32_t paged_attn_multi(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* context_lens,

@@ -53,10 +53,13 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("long_ctx", [False, True])
 @pytest.mark.parametrize("D,B,Hq,Hkv,Q", SHAPES)
-def test_multi_matches_the_oracle(D, B, Hq, Hkv, Q):
-    rng = np.random.default_rng(D * 7 + B * 3 + Hq + Q)
-    lens = np.array([Q + 3, 5 * B + 1, Q, 0, 40, 700, 2000], np.int32)
+def test_multi_matches_the_oracle(D, B, Hq, Hkv, Q, long_ctx):
+    """Contexts up to 2,000 positions (16-row chunks), and with one of 2,600
+    positions (32-row chunks)."""
+    rng = np.random.default_rng(D * 7 + B * 3 + Hq + Q + long_ctx)
+    lens = np.array([Q + 3, 5 * B + 1, Q, 0, 40, 700, 2600 if long_ctx else 2000], np.int32)
     qlens = np.array([Q, 1, Q, 0, min(7, Q), Q // 2, Q - 1], np.int32)
     qlens = np.minimum(qlens, lens)
     case = wl.case_random(D + Q, len(lens), Hq, Hkv, D, B, lens)
@@ -66,7 +69,7 @@ def test_multi_matches_the_oracle(D, B, Hq, Hkv, Q):
     ref = oracle.paged_attn_multi(q, kp, vp, case.block_tables, lens, qlens, B, case.scale, Hkv)
     for s, T in enumerate(qlens):
         assert not got[s, T:].any(), "rows past the query tokens must be zero (seq %d)" % s
-    assert_parity(got, ref, "multi D=%d B=%d G=%d Q=%d" % (D, B, Hq // Hkv, Q))
+    assert_parity(got, ref, "multi D=%d B=%d G=%d Q=%d long=%d" % (D, B, Hq // Hkv, Q, long_ctx))
 
 
 @pytest.mark.parametrize("B", [8, 16, 32])
@@ -180,14 +183,15 @@ FP8_SHAPES = [(128, 16, 32, 8, 4), (128, 16, 32, 8, 8), (64, 8, 8, 8, 40), (128,
               (128, 16, 32, 8, 24)]
 
 
+@pytest.mark.parametrize("long_ctx", [False, True])
 @pytest.mark.parametrize("D,B,Hq,Hkv,Q", FP8_SHAPES)
-def test_multi_over_fp8_pools_matches_the_oracle(D, B, Hq, Hkv, Q):
+def test_multi_over_fp8_pools_matches_the_oracle(D, B, Hq, Hkv, Q, long_ctx):
     import torch
 
     import paged_kv_cache_280_amd as pkv
 
-    rng = np.random.default_rng(D + B + Q + 100)
-    lens = np.array([Q + 3, 5 * B + 1, Q, 0, 700, 2000], np.int32)
+    rng = np.random.default_rng(D + B + Q + 100 + long_ctx)
+    lens = np.array([Q + 3, 5 * B + 1, Q, 0, 700, 2600 if long_ctx else 2000], np.int32)
     qlens = np.minimum(np.array([Q, 1, Q, 0, Q // 2, Q - 1], np.int32), lens)
     case = wl.case_random(D + Q + 7, len(lens), Hq, Hkv, D, B, lens)
     ks, vs = 0.043, 0.057
@@ -203,7 +207,7 @@ def test_multi_over_fp8_pools_matches_the_oracle(D, B, Hq, Hkv, Q):
                                       ks, vs, Hkv)
     for s, T in enumerate(qlens):
         assert not got[s, T:].any()
-    assert_parity(got, ref, "multi fp8 D=%d B=%d G=%d Q=%d" % (D, B, Hq // Hkv, Q))
+    assert_parity(got, ref, "multi fp8 D=%d B=%d G=%d Q=%d long=%d" % (D, B, Hq // Hkv, Q, long_ctx))
 
 
 def test_multi_over_fp8_pools_with_one_token_is_fp8_decode_bit_for_bit():
