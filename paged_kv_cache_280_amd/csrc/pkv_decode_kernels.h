@@ -1487,19 +1487,26 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
         fold(m, l, o);
       }
     }
-    int64_t kmax = 0;
+    // the item's records: the first at `first`, record k >= 1 (wave wa + k*nch,
+    // slot 0) k*stride floats after wave wa's slot 0
+    int32_t cnt[kItems];
+    int32_t kmax = 0;
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) kmax = max(kmax, (wb[it] - wa[it]) / nch + 1);
-    for (int64_t c = 0; c < kmax; c += kChunk) {
+    for (int it = 0; it < kItems; ++it) {
+      cnt[it] = static_cast<int32_t>((wb[it] - wa[it]) / nch + 1);
+      kmax = max(kmax, cnt[it]);
+    }
+    const int64_t stride = 2 * static_cast<int64_t>(nch) * rf;
+    for (int32_t c = 0; c < kmax; c += kChunk) {
       float m[kItems][kChunk], l[kItems][kChunk], o[kItems][kChunk];
 #pragma unroll
       for (int it = 0; it < kItems; ++it) {
         const int32_t h = oi[it] / D;
+        const float* base = ws + 2 * wa[it] * rf;
 #pragma unroll
         for (int k = 0; k < kChunk; ++k) {
-          const int64_t wk = wa[it] + (c + k) * nch;
-          if (wk <= wb[it]) {
-            const float* rec = ws + (c + k == 0 ? first[it] : 2 * wk * rf);
+          if (c + k < cnt[it]) {
+            const float* rec = c + k == 0 ? ws + first[it] : base + (c + k) * stride;
             m[it][k] = rec[RD + h];
             l[it][k] = rec[RD + d.R + h];
             o[it][k] = rec[oi[it]];
