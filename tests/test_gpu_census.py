@@ -263,10 +263,11 @@ def test_census_of_decode_with_append_at_the_mix_shape(B):
     assert_census(_append_census(case, lens), expected_decode(case), "decode+append mix B=%d" % B)
 
 
-@pytest.mark.parametrize("T", [4, 12])
+@pytest.mark.parametrize("T", [4, 12, 24, 40])
 def test_census_of_multi_token_attention_over_many_sequences(T):
-    """100 sequences, G = 4, T query tokens each (12: two runs of 8 and 4 per
-    call): query token i of an L-position sequence sees positions 0 .. L-T+i."""
+    """100 sequences, G = 4, T query tokens each in chunks of 8 (12: two chunk waves
+    per slot; 24: three of a launch of four; 40: a launch of four, then one): query
+    token i of an L-position sequence sees positions 0 .. L-T+i."""
     import torch
 
     import paged_kv_cache_280_amd as pkv

@@ -161,6 +161,25 @@ def test_multi_verify_at_long_context_sampled(Q):
     assert_parity(got, ref, "verify 8x16000 Q=%d" % Q)
 
 
+def test_multi_chunk_waves_give_the_same_bits_on_every_call():
+    """Split pairs over chunk waves (16 and 32 query tokens, 8 x 3,000 positions):
+    the merge folds each pair's records in a fixed order, so repeated calls agree
+    bit for bit."""
+    rng = np.random.default_rng(77)
+    lens = np.full(8, 3000, np.int32)
+    case = wl.case_random(77, 8, 32, 8, 128, 16, lens)
+    kp, vp = wl.host_pools(case, poison=False)
+    for Q in (16, 32):
+        qlens = np.full(8, Q, np.int32)
+        q = wl.randn_bf16(rng, (8, Q, 32, 128))
+        first = _run(case, q, kp, vp, qlens)
+        for _ in range(2):
+            assert np.array_equal(_run(case, q, kp, vp, qlens).view(np.uint32),
+                                  first.view(np.uint32)), "Q=%d" % Q
+        ref = oracle.paged_attn_multi(q, kp, vp, case.block_tables, lens, qlens, 16, case.scale, 8)
+        assert_parity(first, ref, "repeat Q=%d" % Q)
+
+
 @pytest.mark.parametrize("Q", [16, 24, 40])
 def test_multi_chunk_waves_in_pair_mode(Q):
     """Short contexts (at most 256 positions: one worker per (sequence, KV head)
