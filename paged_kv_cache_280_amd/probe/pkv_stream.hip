@@ -1,6 +1,7 @@
 // HBM read-stream probe (declared in include/pkv_stream.h): sequential reads and
 // the decode kernel's paired gather of K/V units, with no arithmetic beyond an XOR
-// that keeps every load live.
+// that keeps every load live.  Every load carries the non-temporal hint, as the
+// decode kernel's K/V loads do.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,12 +31,14 @@ __global__ __launch_bounds__(kThreads) void read_seq_kernel(const u32x4_t* __res
   u32x4_t acc = {0, 0, 0, 0};
   for (int64_t c = blockIdx.x; c < chunks; c += gridDim.x) {
     const u32x4_t* p = src + c * kChunk + threadIdx.x;
-    const u32x4_t a = p[0], b = p[kThreads], d = p[2 * kThreads], e = p[3 * kThreads];
+    const u32x4_t a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + kThreads),
+                  d = __builtin_nontemporal_load(p + 2 * kThreads),
+                  e = __builtin_nontemporal_load(p + 3 * kThreads);
     acc ^= a ^ b ^ d ^ e;
   }
   for (int64_t i = chunks * kChunk + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
        i < n16; i += static_cast<int64_t>(gridDim.x) * kThreads)
-    acc ^= src[i];
+    acc ^= __builtin_nontemporal_load(src + i);
   sink[static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
 }
 
@@ -53,10 +56,12 @@ struct Unit {
                                        int lane) {
 #pragma unroll
     for (int c = 0; c < kK; ++c)
-      k[c] = *reinterpret_cast<const u32x4_t*>(kp + off + c * 1024 + lane * 16);
+      k[c] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(kp + off + c * 1024 + lane * 16));
 #pragma unroll
     for (int c = 0; c < kV; ++c)
-      v[c] = *reinterpret_cast<const VLoad*>(vp + off + c * kWave * kVBytes + lane * kVBytes);
+      v[c] = __builtin_nontemporal_load(
+          reinterpret_cast<const VLoad*>(vp + off + c * kWave * kVBytes + lane * kVBytes));
   }
   __device__ __forceinline__ uint32_t fold() const {
     uint32_t x = 0;
