@@ -267,11 +267,12 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
 
 // Query tokens of one chunk (one wave's rows): as many as fill two 16-column MFMA
 // tiles (kMaxRows), or one when no context exceeds kShortContext positions (at
-// least one token, never more than max_query_len).  Measured at G = 4, 8 query
-// tokens: the chat batch (64 sequences of 114..1,500 positions) takes 86.6 us per
-// call with one 32-row chunk and 76.8 us with two 16-row chunk waves; 8 x 16,000
-// positions take 107.5 and 109.1 us, and at 16 tokens 119.8 against 157.5 us.
-// Short pairs switch often, and one column tile keeps a deeper tile pipeline.
+// least one token, never more than max_query_len).  Measured at G = 4: the chat
+// batch (64 sequences of 114..1,500 positions) takes 76.7 us per call at 8 query
+// tokens with one 32-row chunk and 71.1 us with two 16-row chunk waves (16 tokens:
+// 103.1 against 98.7 us); 8 x 16,000 positions take 93.7 against 103.1 us at 8
+// tokens and 112.0 against 171.4 us at 16.  Short pairs switch often, and one
+// column tile keeps a deeper tile pipeline.
 constexpr int32_t kShortContext = 2048;
 
 int32_t tokens_per_launch(int32_t group, int32_t max_query_len, int32_t max_context_len) {
