@@ -1338,7 +1338,7 @@ struct PrefixView {
   const float* ws;
   const int4* pdesc;
   const int32_t* gmap;
-  int32_t R, groups;
+  int32_t R, groups, waves;  // rows per record, groups, prefix waves (records 2 * waves)
 };
 
 //
@@ -1380,7 +1380,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
           const int32_t grp = min(max(pv.gmap[2 * ds.x], 0), pv.groups - 1);
           const int32_t mem = min(max(pv.gmap[2 * ds.x + 1], 0), pv.R / d.G - 1);
           const int4 pd = pv.pdesc[static_cast<int64_t>(grp) * d.Hkv + ds.y];
-          if (pd.x >= 0) pp = int4{pd.x, pd.y, pd.z, mem};
+          // clamped into the prefix pass's records: a batch that breaks the group
+          // contract (a member with a prefix whose group has none) reads descriptors
+          // of an earlier call, and gets meaningless rows, never memory outside
+          if (pd.x >= 0) {
+            const int32_t a = min(pd.x, pv.waves - 1);
+            pp = int4{a, min(max(pd.y, a), pv.waves - 1), pd.z & 1, mem};
+          }
         }
         s_pp[slot] = pp;
       }
@@ -1626,6 +1632,7 @@ hipError_t launch_shared_t(const DecodeBuffers& bp, const DecodeDims& a, const D
   pv.gmap = gmap;
   pv.R = a.R;
   pv.groups = a.S;
+  pv.waves = a.n_workers;
   return launch_merge<D, false, 2>(bt, d, merge_groups_tail, stream, pv);
 }
 

@@ -239,3 +239,23 @@ def test_shared_prefix_decode_replayed_from_a_graph():
         torch.cuda.synchronize()
         ref = oracle.paged_decode(qh, kp, vp, case.block_tables, case.context_lens, B, case.scale, 8)
         assert_parity(bf16_to_f32(out), ref, "shared graph replay %d" % replay)
+
+
+def test_a_group_that_breaks_the_contract_leaves_the_others_exact():
+    """Group 0's members disagree on their prefix length (the contract wants one
+    value per group): the call still succeeds, touches no memory outside its
+    arguments (prefix record ranges are clamped into the workspace), and every
+    sequence of the groups that keep the contract matches the oracle."""
+    case, gfirst, plens = shared_case(11, 16, 128, 32, 8, [(4, 512, [3, 9, 0, 40]),
+                                                           (4, 256, [1, 2, 3, 4]),
+                                                           (2, 128, [7, 70])])
+    plens = plens.copy()
+    plens[1] = 0          # member 1 of group 0 claims no prefix
+    plens[2] = 256        # member 2 of group 0 claims half of it
+    q = wl.host_q(case)
+    kp, vp = wl.host_pools(case)
+    ref = oracle.paged_decode(q, kp, vp, case.block_tables, case.context_lens, 16, case.scale, 8)
+    for _ in range(2):    # the second call sees the first call's descriptors
+        got = bf16_to_f32(_shared_decode(case, to_dev_bf16(q), to_dev_bf16(kp), to_dev_bf16(vp),
+                                         gfirst, plens, 4, 512))
+        assert_parity(got[4:], ref[4:], "groups that keep the contract")
