@@ -1105,8 +1105,8 @@ __device__ int4 run_worker(const Cx& cx, const DecodeDims& d, const WorkerPlan& 
         // tail pass: the segment holding a pair's first tile names the pair's
         // record set for the merge (pair descriptor n_workers + pair).  A whole
         // pair with a prefix leaves a record in the pair's own slot (the merge
-        // folds it after the prefix state); other pairs get none: whole ones
-        // write their rows here, split ones are named by the opener's descriptor.
+        // folds it after the prefix); other pairs get none: whole ones write
+        // their rows here, split ones are named by the opener's descriptor.
         if (seg_t0 == 0) {
           const int64_t pair = static_cast<int64_t>(cc.s) * d.Hkv + cc.g;
           const int32_t k = static_cast<int32_t>(d.n_workers + pair);

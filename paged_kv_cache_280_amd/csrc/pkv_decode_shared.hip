@@ -1,7 +1,7 @@
 // Launches of shared-prefix decode over bf16 pools: both passes in one launch
 // (the prefix pass with one or two 16-column tiles of (group member, head) rows
-// per wave, the tail pass with one) and the tail merge, or the tail pass alone.  Kernels in
-// pkv_decode_kernels.h.
+// per wave, the tail pass with one) and the tail merge, or the tail pass alone.
+// Kernels in pkv_decode_kernels.h.
 
 #include "pkv_decode_kernels.h"
 
