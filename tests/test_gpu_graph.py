@@ -101,3 +101,51 @@ def test_copy_blocks_replayed_from_a_graph():
         oracle.copy_blocks([k], [v], p)
         assert np.array_equal(kd.cpu().numpy().view(np.uint16), k)
         assert np.array_equal(vd.cpu().numpy().view(np.uint16), v)
+
+
+def test_multi_token_chunk_waves_replayed_from_a_graph():
+    """A 40-token multi-token call (a launch of four chunk waves, then one) captured
+    once and replayed with new queries and eager work between replays."""
+    import torch
+
+    import paged_kv_cache_280_amd as pkv
+
+    dev = torch.device("cuda:0")
+    S, Hq, H, D, B, Q = 6, 32, 8, 128, 16, 40
+    lens = np.array([3000, 2600, 40, 41, 900, 2048], np.int32)
+    case = wl.case_random(123, S, Hq, H, D, B, lens)
+    kp, vp = wl.host_pools(case, poison=False)
+    kd = torch.from_numpy(kp.view(np.int16)).to(dev).view(torch.bfloat16)
+    vd = torch.from_numpy(vp.view(np.int16)).to(dev).view(torch.bfloat16)
+    tabs = torch.from_numpy(case.block_tables).to(dev)
+    ld = torch.from_numpy(lens).to(dev)
+    qlens = np.minimum(np.full(S, Q, np.int32), lens)
+    qld = torch.from_numpy(qlens).to(dev)
+    q = torch.empty((S, Q, Hq, D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    mx = int(lens.max())
+    ws = pkv.new_multi_workspace(S, Hq, H, D, B, mx, Q, dev)
+
+    def step():
+        pkv.paged_attn_multi(q, kd, vd, tabs, ld, qld, B, case.scale, out, max_context_len=mx,
+                             workspace=ws)
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    rng = np.random.default_rng(5)
+    for replay in range(3):
+        qh = wl.randn_bf16(rng, (S, Q, Hq, D))
+        q.copy_(torch.from_numpy(qh.view(np.int16)).to(dev).view(torch.bfloat16))
+        out.fill_(float("nan"))
+        ws.fill_(0xA5)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.paged_attn_multi(qh, kp, vp, case.block_tables, lens, qlens, B, case.scale, H)
+        assert_parity(bf16_to_f32(out), ref, "multi graph replay %d" % replay)
