@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--block-size", type=int, default=16)
     ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
                     help="fp8: K/V pools of E4M3FN codes with a scale of 1/16 each")
+    ap.add_argument("--kv-layout", default="separate", choices=["separate", "paired"],
+                    help="paired: K and V as the two halves of one pool whose (block, head) "
+                         "entries hold a K tile and then a V tile")
     ap.add_argument("--query-tokens", type=int, default=1,
                     help="T > 1: multi-token attention, T causal query tokens per sequence")
     ap.add_argument("--seed", type=int, default=0)
@@ -197,11 +200,29 @@ def build_workload(args, dev):
         if args.kv_dtype == "fp8":
             del k, v
             k, v = wl.device_pools_fp8(case, dev, FP8_SCALE, FP8_SCALE, layer=layer)
+        if args.kv_layout == "paired":
+            k, v = pair_pools(k, v)
         pools.append((q, k, v))
     torch.cuda.synchronize()
     if args.kv_dtype == "fp8":
         desc += ", fp8 E4M3 K/V"
+    if args.kv_layout == "paired":
+        desc += ", K and V tiles paired in one pool"
     return case, layers, desc, pools, tabs, lens, extra
+
+
+def pair_pools(k, v):
+    """The paired form of two device pools: one [NB][Hkv][2][tile] pool holding
+    both, each (block, head) entry a K tile and then a V tile, returned as its two
+    halves viewed in the K and V layouts (the separate pools are freed)."""
+    import torch
+
+    NB, H = int(k.shape[0]), int(k.shape[1])
+    tile = k.numel() // (NB * H)
+    kv = torch.empty((NB, H, 2, tile), dtype=k.dtype, device=k.device)
+    kv[:, :, 0] = k.reshape(NB, H, tile)
+    kv[:, :, 1] = v.reshape(NB, H, tile)
+    return kv[:, :, 0].view(k.shape), kv[:, :, 1].view(v.shape)
 
 
 def cpu_baseline(case, pools, layers, args):
@@ -418,9 +439,15 @@ def attainable_bandwidth(case, pools, elem_bytes, reps=10, seq_bytes=4 << 30, sw
     del x
     torch.cuda.empty_cache()
     ids, unit = decode_units(case, elem_bytes)
-    idd = torch.from_numpy(ids).to(dev)
     k0 = pools[0][1]
     pool_units = k0.numel() * k0.element_size() // unit
+    if not k0.is_contiguous():
+        # paired pools: a (block, head) entry is `halves` K units and then as many V
+        # units, so K unit (entry e, half h) is unit 2*e*halves + h of the pool and
+        # its V lies one tile (halves units) later; the clamp bound keeps V inside
+        halves = case.block_size // min(case.block_size, 16)
+        ids, pool_units = 2 * ids - ids % halves, 2 * pool_units - halves
+    idd = torch.from_numpy(ids).to(dev)
     sink = torch.empty(max(groups * 256, 16 * cu * 64), dtype=torch.int32, device=dev)
 
     def pairs_gbs(idv, vb, waves, depth):
@@ -784,7 +811,8 @@ def main():
     kv_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
     achieved = per_call_bytes / kern_avg_s / 1e9
     traffic = measured_traffic(args.workload + ("_shared" if shared else "") +
-                               ("_q%d" % T if multi else "") + ("_fp8" if fp8 else ""))
+                               ("_q%d" % T if multi else "") + ("_fp8" if fp8 else "") +
+                               ("_paired" if args.kv_layout == "paired" else ""))
 
     line = {
         "metric": METRIC_MULTI if multi else METRIC,
@@ -801,7 +829,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "num_seqs": S, "context_len": int(case.context_lens.max()),
                    "layers": layers, "block_size": B, "num_q_heads": Hq, "num_kv_heads": Hkv,
-                   "head_dim": D, "query_tokens": T},
+                   "head_dim": D, "query_tokens": T, "kv_layout": args.kv_layout},
         "graph": graph is not None,
         "with_append": ("fused" if fused_append else "separate") if args.with_append else False,
         "kv_gbs": round(kv_gbs, 1),

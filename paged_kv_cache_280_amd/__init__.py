@@ -28,5 +28,6 @@ from ._binding import (  # noqa: F401
     paged_attn_decode_workspace_bytes,
     paged_attn_multi,
     paged_attn_multi_workspace_bytes,
+    pools_ok,
     status_string,
 )

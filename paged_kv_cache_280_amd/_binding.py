@@ -9,6 +9,7 @@ built library every call raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -151,6 +152,38 @@ def _v_pool_ok(v_cache, NB, Hkv, D, B):
 
 
 V_POOL_TEXT = "v_cache must be [num_blocks][Hkv][block_size/Bt][D][Bt], Bt = min(block_size, 16)"
+POOLS_TEXT = "k_cache/v_cache: two contiguous pools, or the two halves of one paired pool"
+
+
+def _dense_strides(shape):
+    out, acc = [], 1
+    for n in reversed(tuple(shape)):
+        out.append(acc)
+        acc *= int(n)
+    return tuple(reversed(out))
+
+
+def pools_ok(k_cache, v_cache):
+    """True for two contiguous pools, or for the paired form: the two halves of one
+    pool [num_blocks][Hkv][2][tile] whose (block, head) entries hold a K tile and
+    then a V tile (e.g. ``kv[:, :, 0]`` and ``kv[:, :, 1]`` viewed in the K and V
+    layouts), so that v_cache starts one tile after k_cache."""
+    if k_cache.is_contiguous() and v_cache.is_contiguous():
+        return True
+    if k_cache.dim() < 3 or v_cache.dim() < 3 or k_cache.dtype != v_cache.dtype:
+        return False
+    NB, Hkv = int(k_cache.shape[0]), int(k_cache.shape[1])
+    if tuple(v_cache.shape[:2]) != (NB, Hkv):
+        return False
+    tile = math.prod(int(n) for n in k_cache.shape[2:])
+    if math.prod(int(n) for n in v_cache.shape[2:]) != tile:
+        return False
+    for t in (k_cache, v_cache):
+        want = (2 * Hkv * tile, 2 * tile) + _dense_strides(t.shape[2:])
+        if any(n > 1 and st != w for n, st, w in zip(t.shape, t.stride(), want)):
+            return False
+    return (v_cache.data_ptr() - k_cache.data_ptr() == tile * k_cache.element_size()
+            and k_cache.untyped_storage().data_ptr() == v_cache.untyped_storage().data_ptr())
 
 
 def decode_shapes(q, k_cache, v_cache, block_tables, context_lens, block_size):
@@ -168,7 +201,9 @@ def decode_shapes(q, k_cache, v_cache, block_tables, context_lens, block_size):
            "block_tables must be [num_seqs][max_blocks_per_seq]")
     _check(context_lens.dim() == 1 and context_lens.shape[0] == S, "context_lens must be [num_seqs]")
     for t in (q, k_cache, v_cache):
-        _check(t.dtype == torch.bfloat16 and t.is_contiguous(), "q/k_cache/v_cache: contiguous bf16")
+        _check(t.dtype == torch.bfloat16, "q/k_cache/v_cache: bf16")
+    _check(q.is_contiguous(), "q must be contiguous")
+    _check(pools_ok(k_cache, v_cache), POOLS_TEXT)
     for t in (block_tables, context_lens):
         _check(t.dtype == torch.int32 and t.is_contiguous(), "tables/lengths: contiguous int32")
     devs = {t.device for t in (q, k_cache, v_cache, block_tables, context_lens)}
@@ -332,8 +367,8 @@ def paged_attn_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, block
     _check(tuple(v_cache.shape) == (NB, Hkv, 16, B // 4, D // 16, 4),
            "v_cache must be [num_blocks][Hkv][16][block_size/4][D/16][4]")
     _check(q.dtype == torch.bfloat16 and q.is_contiguous(), "q: contiguous bf16")
-    for t in (k_cache, v_cache):
-        _check(t.dtype == torch.uint8 and t.is_contiguous(), "fp8 pools: contiguous uint8 codes")
+    _check(k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8
+           and pools_ok(k_cache, v_cache), "fp8 pools: uint8 codes; " + POOLS_TEXT)
     _check(block_tables.dim() == 2 and block_tables.shape[0] == S,
            "block_tables must be [num_seqs][max_blocks_per_seq]")
     _check(context_lens.dim() == 1 and context_lens.shape[0] == S, "context_lens must be [num_seqs]")
@@ -387,8 +422,8 @@ def paged_attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, co
         NB, Hkv = int(k_cache.shape[0]), int(k_cache.shape[1])
         _check(tuple(v_cache.shape) == (NB, Hkv, 16, B // 4, D // 16, 4),
                "v_cache must be [num_blocks][Hkv][16][block_size/4][D/16][4]")
-        for t in (k_cache, v_cache):
-            _check(t.dtype == torch.uint8 and t.is_contiguous(), "fp8 pools: contiguous uint8 codes")
+        _check(k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8
+               and pools_ok(k_cache, v_cache), "fp8 pools: uint8 codes; " + POOLS_TEXT)
         _check(q.dtype == torch.bfloat16 and q.is_contiguous(), "q: contiguous bf16")
         _check(block_tables.dim() == 2 and block_tables.shape[0] == S
                and context_lens.dim() == 1 and context_lens.shape[0] == S,
@@ -459,8 +494,8 @@ def _fp8_pool_shapes(q3, k_cache, v_cache, block_tables, context_lens, block_siz
     _check(tuple(v_cache.shape) == (NB, Hkv, 16, B // 4, D // 16, 4),
            "v_cache must be [num_blocks][Hkv][16][block_size/4][D/16][4]")
     _check(q3.dtype == torch.bfloat16 and q3.is_contiguous(), "q: contiguous bf16")
-    for t in (k_cache, v_cache):
-        _check(t.dtype == torch.uint8 and t.is_contiguous(), "fp8 pools: contiguous uint8 codes")
+    _check(k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8
+           and pools_ok(k_cache, v_cache), "fp8 pools: uint8 codes; " + POOLS_TEXT)
     _check(block_tables.dim() == 2 and block_tables.shape[0] == S,
            "block_tables must be [num_seqs][max_blocks_per_seq]")
     _check(context_lens.dim() == 1 and context_lens.shape[0] == S, "context_lens must be [num_seqs]")
@@ -537,7 +572,9 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token_pos
     NB = int(k_cache.shape[0])
     _check(_v_pool_ok(v_cache, NB, Hkv, D, B), V_POOL_TEXT)
     for t in (k_new, v_new, k_cache, v_cache):
-        _check(t.dtype == torch.bfloat16 and t.is_contiguous(), "bf16 contiguous tensors")
+        _check(t.dtype == torch.bfloat16, "bf16 tensors")
+    _check(k_new.is_contiguous() and v_new.is_contiguous(), "k_new/v_new must be contiguous")
+    _check(pools_ok(k_cache, v_cache), POOLS_TEXT)
     for t in (block_tables, token_seq, token_pos):
         _check(t.dtype == torch.int32 and t.is_contiguous(), "int32 contiguous tensors")
     _check(token_seq.numel() == T and token_pos.numel() == T, "one sequence id and position per token")
@@ -571,8 +608,8 @@ def kv_append_fp8(k_new, v_new, k_cache, v_cache, block_tables, token_seq, token
            "v_cache must be [num_blocks][Hkv][16][block_size/4][D/16][4]")
     for t in (k_new, v_new):
         _check(t.dtype == torch.bfloat16 and t.is_contiguous(), "k_new/v_new: contiguous bf16")
-    for t in (k_cache, v_cache):
-        _check(t.dtype == torch.uint8 and t.is_contiguous(), "fp8 pools: contiguous uint8 codes")
+    _check(k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8
+           and pools_ok(k_cache, v_cache), "fp8 pools: uint8 codes; " + POOLS_TEXT)
     for t in (block_tables, token_seq, token_pos):
         _check(t.dtype == torch.int32 and t.is_contiguous(), "int32 contiguous tensors")
     _check(token_seq.numel() == T and token_pos.numel() == T, "one sequence id and position per token")
@@ -609,8 +646,10 @@ def copy_blocks(k_caches, v_caches, src_dst_pairs, stream=None):
     nb = int(ref.shape[0])
     nbytes = ref.numel() * ref.element_size()
     for t in k_caches + v_caches:
-        _check(t.is_contiguous() and t.device == ref.device and t.shape[0] == nb
+        _check(t.device == ref.device and t.shape[0] == nb
                and t.numel() * t.element_size() == nbytes, "pools must match in shape and device")
+    for k, v in zip(k_caches, v_caches):
+        _check(pools_ok(k, v), POOLS_TEXT)
     _check(src_dst_pairs.device == ref.device, "src_dst_pairs must be on the pools' device")
     kp = (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in k_caches])
     vp = (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in v_caches])

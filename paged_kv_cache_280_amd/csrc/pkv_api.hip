@@ -124,6 +124,16 @@ int merge_groups_for(int64_t workers, int cu) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Pool form of a call: 2 when v_cache starts one (block, head) tile after k_cache,
+// the two halves of one pool whose entries hold a K tile and then a V tile; else
+// 1, two separate pools.  Separate pools of more than one tile cannot start one
+// tile apart (V would begin inside K), and over a single tile both readings
+// address the same bytes, so the form needs no flag of its own.
+int32_t pool_form(const void* k, const void* v, int32_t head_dim, int32_t block_size, bool fp8) {
+  const uintptr_t tile = static_cast<uintptr_t>(head_dim) * block_size * (fp8 ? 1u : 2u);
+  return reinterpret_cast<uintptr_t>(v) == reinterpret_cast<uintptr_t>(k) + tile ? 2 : 1;
+}
+
 int32_t check_shapes(int32_t block_size, float scale, int32_t num_seqs, int32_t num_q_heads,
                      int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
                      int64_t num_blocks, int32_t max_context_len) {
@@ -214,6 +224,7 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
   d.pair_mode = use_pair_mode(cu, num_seqs, num_kv_heads, max_context_len, fp8) ? 1 : 0;
   d.n_workers = d.pair_mode ? num_seqs * num_kv_heads : static_cast<int32_t>(workers);
   d.NB = num_blocks;
+  d.kv_mul = pool_form(k_cache, v_cache, head_dim, block_size, fp8);
   // scores in the log2 domain; an fp8 K pool's scale folds into the same factor
   d.c = static_cast<float>(static_cast<double>(scale) * static_cast<double>(k_scale) *
                            1.4426950408889634);  // log2(e)
@@ -249,6 +260,7 @@ int32_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
     ad.B = block_size;
     ad.M = max_blocks_per_seq;
     ad.NB = num_blocks;
+    ad.kv_mul = pool_form(k_cache, v_cache, head_dim, block_size, fp8);
     ad.k_scale = k_scale;
     ad.v_scale = v_scale;
     ad.newest = 1;
@@ -354,6 +366,7 @@ int32_t multi_impl(const void* q, const void* k_cache, const void* v_cache,
   d.M = max_blocks_per_seq;
   d.pair_mode = use_pair_mode(cu, num_seqs, num_kv_heads, max_context_len, fp8) ? 1 : 0;
   d.NB = num_blocks;
+  d.kv_mul = pool_form(k_cache, v_cache, head_dim, block_size, fp8);
   d.c = static_cast<float>(static_cast<double>(scale) * static_cast<double>(k_scale) *
                            1.4426950408889634);  // log2(e); an fp8 K scale folds in
   d.Qmax = max_query_len;
@@ -496,6 +509,7 @@ int32_t shared_impl(const void* q, const void* k_cache, const void* v_cache,
   d.G = group;
   d.M = max_blocks_per_seq;
   d.NB = num_blocks;
+  d.kv_mul = pool_form(k_cache, v_cache, head_dim, block_size, false);
   d.c = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
   d.v_scale = 1.0f;
   d.k_scale = 1.0f;
@@ -581,6 +595,7 @@ int32_t append_impl(const void* k_new, const void* v_new, void* k_cache, void* v
   a.B = block_size;
   a.M = max_blocks_per_seq;
   a.NB = num_blocks;
+  a.kv_mul = pool_form(k_cache, v_cache, head_dim, block_size, fp8);
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -50,7 +50,7 @@ __device__ __forceinline__ bool token_slot(int64_t t, int32_t g, const int32_t* 
   if (s < 0 || s >= a.S || p < 0 || p >= cap) return false;
   const int32_t b = tables[static_cast<int64_t>(s) * a.M + p / a.B];
   if (b < 0 || b >= a.NB) return false;  // never write outside the pool
-  tile = (static_cast<int64_t>(b) * a.Hkv + g) * D * a.B;
+  tile = (static_cast<int64_t>(b) * a.Hkv + g) * D * a.B * tile_span(a.kv_mul);
   o = p % a.B;
   return true;
 }

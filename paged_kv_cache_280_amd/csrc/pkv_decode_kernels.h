@@ -745,8 +745,9 @@ __device__ __forceinline__ void load_at(Tile& r, const Cx& cx, const DecodeDims&
   pc.k = cx.k;
   pc.v = cx.v;
   pc.trow = cx.tables + table_offset<B, kShare>(d, c);
-  pc.block_stride = kTileElems * d.Hkv;
-  pc.head_off = kTileElems * c.g;
+  const int64_t span = kTileElems * tile_span(d.kv_mul);  // paired pools: K and V tiles
+  pc.block_stride = span * d.Hkv;
+  pc.head_off = span * c.g;
   pc.nb = d.NB;
   pc.nblk = (c.L + B - 1) / B;
   r.load(pc, c.t, lane);
@@ -919,7 +920,8 @@ __device__ __forceinline__ void append_token(SegState<D>& st, const bf16x8_t (&q
   const int32_t b = in_pool ? raw : 0;
   const bool writer = in_pool && (lane & 15) == 0;  // lanes 0, 16, 32, 48 cover every dim once
   const int32_t ob = p % B;
-  const int64_t tile = (static_cast<int64_t>(b) * d.Hkv + c.g) * D * B;  // elements
+  const int64_t tile =
+      (static_cast<int64_t>(b) * d.Hkv + c.g) * D * B * tile_span(d.kv_mul);  // elements
   // score: this lane's query dims (the score MFMA operand layout) against the new key
   float part = 0.f;
 #pragma unroll
@@ -978,7 +980,7 @@ __device__ void one_token(const Cx& cx, const DecodeDims& d, int64_t s, int lane
   constexpr int32_t kRun = B < kTile ? B : kTile;
   for (int32_t e = lane; e < d.Hkv * D; e += kWave) {
     const int32_t g = e / D, dd = e % D;
-    const int64_t tile = (static_cast<int64_t>(b) * d.Hkv + g) * D * B;
+    const int64_t tile = (static_cast<int64_t>(b) * d.Hkv + g) * D * B * tile_span(d.kv_mul);
     const uint16_t kx = cx.k_new[s * d.Hkv * D + e];
     const uint16_t vx = cx.v_new[s * d.Hkv * D + e];
     if (in_pool) {

@@ -67,10 +67,17 @@ struct DecodeDims {
   // `chunk` taking query tokens q_off + chunk*Qc .. + Qc - 1, so a K/V tile is read
   // from memory once for all of them.  n_workers counts the ranges (slots).
   int32_t nch, chunk;
+  // Pool form: 1 for separate K and V pools; 2 when both are the halves of one pool
+  // whose (block, head) entries hold the K tile and then the V tile (v = k + one
+  // tile), so blocks and heads step over two tiles.
+  int32_t kv_mul;
 };
 
 // Floats in one partial record: O[R][D], then m[R], then l[R], padded to a
 // multiple of four floats so every record starts 16-byte aligned.
+// Tiles one (block, head) entry of the pools spans: 2 in the paired form, else 1.
+__host__ __device__ inline int64_t tile_span(int32_t kv_mul) { return kv_mul == 2 ? 2 : 1; }
+
 __host__ __device__ inline int64_t record_floats(int R, int D) {
   return static_cast<int64_t>(R) * D + ((2 * R + 3) / 4) * 4;
 }
@@ -150,6 +157,7 @@ struct AppendDims {
   float k_scale, v_scale;     // fp8 pools: stored code = E4M3(x / scale)
   int32_t newest;             // 1: token t is sequence t's newest position, and token_pos
                               // holds the context lengths (position = length - 1)
+  int32_t kv_mul;             // pool form, as in DecodeDims
 };
 
 hipError_t launch_append(const AppendBuffers& b, const AppendDims& a, int D, hipStream_t stream);
