@@ -1518,13 +1518,29 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
       for (int it = 0; it < kItems; ++it) {
         const int32_t h = oi[it] / D;
         const float* base = ws + 2 * wa[it] * rf;
+        // plain decode launches: byte offsets from ws (records of at most 4 waves
+        // per CU, a few tens of MB), so that each load takes ws as its scalar base
+        // and one 32-bit register of offset (the 12-record merge in 132 instead of
+        // 246 registers, measured 0.2-0.6 us faster per call; slower on
+        // multi-token merges)
+        const uint32_t b0 = static_cast<uint32_t>(2 * wa[it] * rf * 4);
+        const uint32_t f0 = static_cast<uint32_t>(first[it] * 4);
 #pragma unroll
         for (int k = 0; k < kChunk; ++k) {
           if (c + k < cnt[it]) {
-            const float* rec = c + k == 0 ? ws + first[it] : base + (c + k) * stride;
-            m[it][k] = rec[RD + h];
-            l[it][k] = rec[RD + d.R + h];
-            o[it][k] = rec[oi[it]];
+            if constexpr (kCausal || kShare != 0) {
+              const float* rec = c + k == 0 ? ws + first[it] : base + (c + k) * stride;
+              m[it][k] = rec[RD + h];
+              l[it][k] = rec[RD + d.R + h];
+              o[it][k] = rec[oi[it]];
+            } else {
+              const uint32_t r =
+                  c + k == 0 ? f0 : b0 + static_cast<uint32_t>((c + k) * stride * 4);
+              const char* rec = reinterpret_cast<const char*>(ws) + r;
+              m[it][k] = *reinterpret_cast<const float*>(rec + (RD + h) * 4);
+              l[it][k] = *reinterpret_cast<const float*>(rec + (RD + d.R + h) * 4);
+              o[it][k] = *reinterpret_cast<const float*>(rec + oi[it] * 4);
+            }
           } else {
             m[it][k] = -INFINITY;
             l[it][k] = 0.f;
