@@ -1322,9 +1322,12 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void shared_kernel(Shared
 // is fixed, so the result does not depend on timing.  In multi-token launches the
 // rows past the pair's query tokens are left to the decode kernel.
 //
-// Two shapes (measured): pairs split over more than 12 workers take one item of
-// 16 records per batch (one round trip for a 16-way split); otherwise two items of
-// 12 records each, so that more independent loads are in flight.
+// Shapes (measured): pairs split over more than 12 workers take one item of 16
+// records per batch (one round trip for a 16-way split); otherwise two items of 12
+// records each (10 in multi-token launches, whose merge is held to 128 registers
+// so that two work-groups share a CU), so that more independent loads are in
+// flight.  Record loads take the workspace as scalar base and 32-bit byte offsets
+// (records of at most 4 waves per CU, a few tens of MB).
 constexpr int kMergeThreads = 512;
 constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
 constexpr int kMergeWideSplit = 12;
@@ -1332,6 +1335,11 @@ constexpr int kMergeWideSplit = 12;
 // pairs with more rows (multi-token and prefix launches) spread over more groups.
 constexpr int kMergeSpan = 512;
 
+
+// The 10-record multi-token shape asks for 4 waves per SIMD (two 512-thread groups
+// per CU, at most 128 registers).
+template <bool kCausal, int kChunk>
+constexpr bool kTwoPerCu = kCausal && kChunk == 10;
 
 // Where the merge of a shared-prefix launch's tail pass finds the prefix of a
 // pair: the prefix pass's records (R rows each) and pair descriptors (none: every
@@ -1348,11 +1356,15 @@ struct PrefixView {
 // prefix first, from the prefix state (a whole prefix pair) or from the prefix
 // pass's records of its rows (a split one), then its own records.
 template <int D, bool kCausal, int kChunk, int kItems, int kShare = 0>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __restrict__ desc,
-                                                              uint16_t* __restrict__ out,
-                                                              const float* __restrict__ ws,
-                                                              DecodeDims d, PrefixView pv,
-                                                              const float* __restrict__ state) {
+__global__ __launch_bounds__(kMergeThreads, (kTwoPerCu<kCausal, kChunk> ? 4 : 1)) void merge_kernel(
+    const int4* __restrict__ desc, uint16_t* __restrict__ out, const float* __restrict__ ws,
+    DecodeDims d, PrefixView pv, const float* __restrict__ state) {
+  // record loads by 32-bit byte offsets from ws (decode launches, and the 10-record
+  // multi-token shape; a launch's records belong to at most 4 waves per CU, a few
+  // tens of MB): the 12-record decode merge in 132 instead of 246 registers.  The
+  // other multi-token shapes and the shared-prefix tail pass (which also has a
+  // record per (sequence, KV head) pair) keep 64-bit addresses.
+  constexpr bool kOffsets32 = (!kCausal && kShare == 0) || kTwoPerCu<kCausal, kChunk>;
   __shared__ int4 s_desc[kMergeSlice];
   __shared__ int32_t s_wa[kMergeSlice];
   __shared__ int4 s_pp[kShare == 2 ? kMergeSlice : 1];
@@ -1518,17 +1530,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const int4* __rest
       for (int it = 0; it < kItems; ++it) {
         const int32_t h = oi[it] / D;
         const float* base = ws + 2 * wa[it] * rf;
-        // plain decode launches: byte offsets from ws (records of at most 4 waves
-        // per CU, a few tens of MB), so that each load takes ws as its scalar base
-        // and one 32-bit register of offset (the 12-record merge in 132 instead of
-        // 246 registers, measured 0.2-0.6 us faster per call; slower on
-        // multi-token merges)
+        // kOffsets32: byte offsets from ws, so that each load takes ws as its
+        // scalar base and one 32-bit register of offset
         const uint32_t b0 = static_cast<uint32_t>(2 * wa[it] * rf * 4);
         const uint32_t f0 = static_cast<uint32_t>(first[it] * 4);
 #pragma unroll
         for (int k = 0; k < kChunk; ++k) {
           if (c + k < cnt[it]) {
-            if constexpr (kCausal || kShare != 0) {
+            if constexpr (!kOffsets32) {
               const float* rec = c + k == 0 ? ws + first[it] : base + (c + k) * stride;
               m[it][k] = rec[RD + h];
               l[it][k] = rec[RD + d.R + h];
@@ -1583,22 +1592,37 @@ int4* descriptors(const DecodeBuffers& b, const DecodeDims& d) {
 // The merge launch of a split launch.  Records per split pair: about the workers
 // per (sequence, KV head) pair; a pair's outputs are spread over ny = ceil(R * D /
 // kMergeSpan) work-groups, and the descriptor slices shrink to about merge_groups
-// / ny (a merge work-group fills a CU: more than one per CU would run in rounds),
-// each still scanning at most kMergeSlice descriptors.
+// / ny (a decode merge work-group fills a CU: more than one per CU would run in
+// rounds; multi-token merges with many items take two per CU, see below), each
+// still scanning at most kMergeSlice descriptors.
 template <int D, bool kCausal, int kShare>
 hipError_t launch_merge(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
                         hipStream_t stream, const PrefixView& pv = PrefixView{}) {
   const int64_t n_desc = descriptor_count<kShare>(d);
   const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
   const int ny = (d.R * D + kMergeSpan - 1) / kMergeSpan;
-  const int nx =
-      max(max(merge_groups / ny, static_cast<int>((n_desc + kMergeSlice - 1) / kMergeSlice)), 1);
+  // Multi-token merges (at most 128 registers) fit two work-groups per CU: taken when
+  // one group per CU would need more than one pass of kItems = 2 over the items
+  // (every pair split; measured at 16 and 32 query tokens and on short contexts at
+  // 8; with fewer items the larger grid only costs, 89.2 -> 91.2 us at 4 tokens)
+  const bool wide = pairs > 0 && d.n_workers > kMergeWideSplit * pairs;
+  const int64_t items = pairs * max(d.nch, 1) * d.R * D;
+  const int per_cu =
+      kCausal && !wide && items > 2 * static_cast<int64_t>(merge_groups) * kMergeThreads ? 2
+                                                                                         : 1;
+  const int nx = max(max(per_cu * merge_groups / ny,
+                         static_cast<int>((n_desc + kMergeSlice - 1) / kMergeSlice)),
+                     1);
   const dim3 grid(nx, ny);
   int4* desc = descriptors<D, kShare>(b, d);
-  if (pairs > 0 && d.n_workers > kMergeWideSplit * pairs)
+  if (wide)
     hipLaunchKernelGGL((merge_kernel<D, kCausal, 16, 1, kShare>), grid, dim3(kMergeThreads), 0,
                        stream, desc, b.out, b.ws, d, pv, b.state);
-  else
+  else if (per_cu == 2) {
+    if constexpr (kCausal)  // per_cu is 2 only for multi-token merges
+      hipLaunchKernelGGL((merge_kernel<D, kCausal, 10, 2, kShare>), grid, dim3(kMergeThreads),
+                         0, stream, desc, b.out, b.ws, d, pv, b.state);
+  } else
     hipLaunchKernelGGL((merge_kernel<D, kCausal, 12, 2, kShare>), grid, dim3(kMergeThreads), 0,
                        stream, desc, b.out, b.ws, d, pv, b.state);
   return hipGetLastError();
