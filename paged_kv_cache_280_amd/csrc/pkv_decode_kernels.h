@@ -1324,10 +1324,9 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void shared_kernel(Shared
 //
 // Shapes (measured): pairs split over more than 12 workers take one item of 16
 // records per batch (one round trip for a 16-way split); otherwise two items of 12
-// records each (10 in multi-token launches, whose merge is held to 128 registers
-// so that two work-groups share a CU), so that more independent loads are in
-// flight.  Record loads take the workspace as scalar base and 32-bit byte offsets
-// (records of at most 4 waves per CU, a few tens of MB).
+// records each, so that more independent loads are in flight, or of 10 records
+// when the launch has many items (held to 128 registers, so that two work-groups
+// share a CU; see launch_merge).
 constexpr int kMergeThreads = 512;
 constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
 constexpr int kMergeWideSplit = 12;
@@ -1336,10 +1335,10 @@ constexpr int kMergeWideSplit = 12;
 constexpr int kMergeSpan = 512;
 
 
-// The 10-record multi-token shape asks for 4 waves per SIMD (two 512-thread groups
-// per CU, at most 128 registers).
-template <bool kCausal, int kChunk>
-constexpr bool kTwoPerCu = kCausal && kChunk == 10;
+// The 10-record shape asks for 4 waves per SIMD (two 512-thread groups per CU, at
+// most 128 registers).
+template <int kChunk>
+constexpr bool kTwoPerCu = kChunk == 10;
 
 // Where the merge of a shared-prefix launch's tail pass finds the prefix of a
 // pair: the prefix pass's records (R rows each) and pair descriptors (none: every
@@ -1356,7 +1355,7 @@ struct PrefixView {
 // prefix first, from the prefix state (a whole prefix pair) or from the prefix
 // pass's records of its rows (a split one), then its own records.
 template <int D, bool kCausal, int kChunk, int kItems, int kShare = 0>
-__global__ __launch_bounds__(kMergeThreads, (kTwoPerCu<kCausal, kChunk> ? 4 : 1)) void merge_kernel(
+__global__ __launch_bounds__(kMergeThreads, (kTwoPerCu<kChunk> ? 4 : 1)) void merge_kernel(
     const int4* __restrict__ desc, uint16_t* __restrict__ out, const float* __restrict__ ws,
     DecodeDims d, PrefixView pv, const float* __restrict__ state) {
   // record loads by 32-bit byte offsets from ws (decode launches, and the 10-record
@@ -1364,7 +1363,7 @@ __global__ __launch_bounds__(kMergeThreads, (kTwoPerCu<kCausal, kChunk> ? 4 : 1)
   // tens of MB): the 12-record decode merge in 132 instead of 246 registers.  The
   // other multi-token shapes and the shared-prefix tail pass (which also has a
   // record per (sequence, KV head) pair) keep 64-bit addresses.
-  constexpr bool kOffsets32 = (!kCausal && kShare == 0) || kTwoPerCu<kCausal, kChunk>;
+  constexpr bool kOffsets32 = kShare == 0 && (!kCausal || kTwoPerCu<kChunk>);
   __shared__ int4 s_desc[kMergeSlice];
   __shared__ int32_t s_wa[kMergeSlice];
   __shared__ int4 s_pp[kShare == 2 ? kMergeSlice : 1];
@@ -1601,14 +1600,16 @@ hipError_t launch_merge(const DecodeBuffers& b, const DecodeDims& d, int merge_g
   const int64_t n_desc = descriptor_count<kShare>(d);
   const int64_t pairs = static_cast<int64_t>(d.S) * d.Hkv;
   const int ny = (d.R * D + kMergeSpan - 1) / kMergeSpan;
-  // Multi-token merges (at most 128 registers) fit two work-groups per CU: taken when
-  // one group per CU would need more than one pass of kItems = 2 over the items
-  // (every pair split; measured at 16 and 32 query tokens and on short contexts at
-  // 8; with fewer items the larger grid only costs, 89.2 -> 91.2 us at 4 tokens)
+  // Merges with many items take the 10-record shape (at most 128 registers) at two
+  // work-groups per CU: when the split (pair, chunk) sets could hold more than one
+  // item per thread of one group per CU, some groups would otherwise take a second
+  // pass.  Measured: 16 and 32 query tokens on the long context, 8 and 16 on the
+  // chat batch; with fewer items the larger grid only costs (89.2 -> 91.2 us at 4
+  // tokens, which stays below the bound).
   const bool wide = pairs > 0 && d.n_workers > kMergeWideSplit * pairs;
-  const int64_t items = pairs * max(d.nch, 1) * d.R * D;
+  const int64_t items = min(pairs * max(d.nch, 1), n_desc) * d.R * D;
   const int per_cu =
-      kCausal && !wide && items > 2 * static_cast<int64_t>(merge_groups) * kMergeThreads ? 2
+      kShare == 0 && !wide && items > static_cast<int64_t>(merge_groups) * kMergeThreads ? 2
                                                                                          : 1;
   const int nx = max(max(per_cu * merge_groups / ny,
                          static_cast<int>((n_desc + kMergeSlice - 1) / kMergeSlice)),
@@ -1619,7 +1620,7 @@ hipError_t launch_merge(const DecodeBuffers& b, const DecodeDims& d, int merge_g
     hipLaunchKernelGGL((merge_kernel<D, kCausal, 16, 1, kShare>), grid, dim3(kMergeThreads), 0,
                        stream, desc, b.out, b.ws, d, pv, b.state);
   else if (per_cu == 2) {
-    if constexpr (kCausal)  // per_cu is 2 only for multi-token merges
+    if constexpr (kShare == 0)  // per_cu is 2 only there
       hipLaunchKernelGGL((merge_kernel<D, kCausal, 10, 2, kShare>), grid, dim3(kMergeThreads),
                          0, stream, desc, b.out, b.ws, d, pv, b.state);
   } else
