@@ -1363,7 +1363,7 @@ __global__ __launch_bounds__(kMergeThreads, (kTwoPerCu<kChunk> ? 4 : 1)) void me
   // tens of MB): the 12-record decode merge in 132 instead of 246 registers.  The
   // other multi-token shapes and the shared-prefix tail pass (which also has a
   // record per (sequence, KV head) pair) keep 64-bit addresses.
-  constexpr bool kOffsets32 = kShare == 0 && (!kCausal || kTwoPerCu<kChunk>);
+  constexpr bool kOffsets32 = (kShare == 0 && !kCausal) || kTwoPerCu<kChunk>;
   __shared__ int4 s_desc[kMergeSlice];
   __shared__ int32_t s_wa[kMergeSlice];
   __shared__ int4 s_pp[kShare == 2 ? kMergeSlice : 1];
@@ -1608,9 +1608,14 @@ hipError_t launch_merge(const DecodeBuffers& b, const DecodeDims& d, int merge_g
   // tokens, which stays below the bound).
   const bool wide = pairs > 0 && d.n_workers > kMergeWideSplit * pairs;
   const int64_t items = min(pairs * max(d.nch, 1), n_desc) * d.R * D;
+  // (that shape addresses records by 32-bit byte offsets: a shared-prefix tail pass,
+  // which has a record per pair, takes it only while its records stay below 4 GiB)
+  const bool small_ws = records_bytes(n_desc, d.R, D) < (int64_t(1) << 32);
   const int per_cu =
-      kShare == 0 && !wide && items > static_cast<int64_t>(merge_groups) * kMergeThreads ? 2
-                                                                                         : 1;
+      kShare != 1 && small_ws && !wide &&
+              items > static_cast<int64_t>(merge_groups) * kMergeThreads
+          ? 2
+          : 1;
   const int nx = max(max(per_cu * merge_groups / ny,
                          static_cast<int>((n_desc + kMergeSlice - 1) / kMergeSlice)),
                      1);
@@ -1620,7 +1625,7 @@ hipError_t launch_merge(const DecodeBuffers& b, const DecodeDims& d, int merge_g
     hipLaunchKernelGGL((merge_kernel<D, kCausal, 16, 1, kShare>), grid, dim3(kMergeThreads), 0,
                        stream, desc, b.out, b.ws, d, pv, b.state);
   else if (per_cu == 2) {
-    if constexpr (kShare == 0)  // per_cu is 2 only there
+    if constexpr (kShare != 1)  // per_cu is 2 only there
       hipLaunchKernelGGL((merge_kernel<D, kCausal, 10, 2, kShare>), grid, dim3(kMergeThreads),
                          0, stream, desc, b.out, b.ws, d, pv, b.state);
   } else
