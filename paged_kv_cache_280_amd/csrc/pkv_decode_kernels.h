@@ -1358,11 +1358,11 @@ template <int D, bool kCausal, int kChunk, int kItems, int kShare = 0>
 __global__ __launch_bounds__(kMergeThreads, (kTwoPerCu<kChunk> ? 4 : 1)) void merge_kernel(
     const int4* __restrict__ desc, uint16_t* __restrict__ out, const float* __restrict__ ws,
     DecodeDims d, PrefixView pv, const float* __restrict__ state) {
-  // record loads by 32-bit byte offsets from ws (decode launches, and the 10-record
-  // multi-token shape; a launch's records belong to at most 4 waves per CU, a few
-  // tens of MB): the 12-record decode merge in 132 instead of 246 registers.  The
-  // other multi-token shapes and the shared-prefix tail pass (which also has a
-  // record per (sequence, KV head) pair) keep 64-bit addresses.
+  // record loads by 32-bit byte offsets from ws: in decode launches (records of at
+  // most 4 waves per CU, a few tens of MB; the 12-record merge in 132 instead of 246
+  // registers) and in the 10-record shape, which launch_merge takes only while the
+  // launch's records stay below 4 GiB.  The other multi-token and shared-prefix
+  // shapes keep 64-bit addresses.
   constexpr bool kOffsets32 = (kShare == 0 && !kCausal) || kTwoPerCu<kChunk>;
   __shared__ int4 s_desc[kMergeSlice];
   __shared__ int32_t s_wa[kMergeSlice];
@@ -1591,9 +1591,9 @@ int4* descriptors(const DecodeBuffers& b, const DecodeDims& d) {
 // The merge launch of a split launch.  Records per split pair: about the workers
 // per (sequence, KV head) pair; a pair's outputs are spread over ny = ceil(R * D /
 // kMergeSpan) work-groups, and the descriptor slices shrink to about merge_groups
-// / ny (a decode merge work-group fills a CU: more than one per CU would run in
-// rounds; multi-token merges with many items take two per CU, see below), each
-// still scanning at most kMergeSlice descriptors.
+// / ny (a 12- or 16-record merge work-group fills a CU: more than one per CU would
+// run in rounds; merges with many items take the 10-record shape, two per CU, see
+// below), each still scanning at most kMergeSlice descriptors.
 template <int D, bool kCausal, int kShare>
 hipError_t launch_merge(const DecodeBuffers& b, const DecodeDims& d, int merge_groups,
                         hipStream_t stream, const PrefixView& pv = PrefixView{}) {
@@ -1603,13 +1603,15 @@ hipError_t launch_merge(const DecodeBuffers& b, const DecodeDims& d, int merge_g
   // Merges with many items take the 10-record shape (at most 128 registers) at two
   // work-groups per CU: when the split (pair, chunk) sets could hold more than one
   // item per thread of one group per CU, some groups would otherwise take a second
-  // pass.  Measured: 16 and 32 query tokens on the long context, 8 and 16 on the
-  // chat batch; with fewer items the larger grid only costs (89.2 -> 91.2 us at 4
-  // tokens, which stays below the bound).
+  // pass.  Measured faster on the chat and mix decode merges, 16 and 32 query tokens
+  // on the long context, 8 and 16 on the chat batch and the shared-prefix tail
+  // merge; with fewer items the larger grid only costs (89.2 -> 91.2 us at 4 tokens,
+  // which stays below the bound).
   const bool wide = pairs > 0 && d.n_workers > kMergeWideSplit * pairs;
   const int64_t items = min(pairs * max(d.nch, 1), n_desc) * d.R * D;
-  // (that shape addresses records by 32-bit byte offsets: a shared-prefix tail pass,
-  // which has a record per pair, takes it only while its records stay below 4 GiB)
+  // (that shape addresses records by 32-bit byte offsets: taken only while the
+  // launch's records stay below 4 GiB, which a shared-prefix tail pass, with a record
+  // per (sequence, KV head) pair, could pass)
   const bool small_ws = records_bytes(n_desc, d.R, D) < (int64_t(1) << 32);
   const int per_cu =
       kShare != 1 && small_ws && !wide &&
