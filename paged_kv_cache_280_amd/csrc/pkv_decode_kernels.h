@@ -1322,14 +1322,15 @@ __global__ __launch_bounds__(kWave* kWavesPerGroup, 1) void shared_kernel(Shared
 // is fixed, so the result does not depend on timing.  In multi-token launches the
 // rows past the pair's query tokens are left to the decode kernel.
 //
-// Shapes (measured): pairs split over more than 12 workers take one item of 16
-// records per batch (one round trip for a 16-way split); otherwise two items of 12
-// records each, so that more independent loads are in flight, or of 10 records
-// when the launch has many items (held to 128 registers, so that two work-groups
-// share a CU; see launch_merge).
+// Shapes (measured): pairs split over more than 11 workers take one item of 16
+// records per batch (one round trip for a 16-way split; a pair spread over 12
+// workers' ranges has 13 records, which would take two 12-record batches);
+// otherwise two items of 12 records each, so that more independent loads are in
+// flight, or of 10 records when the launch has many items (held to 128 registers,
+// so that two work-groups share a CU; see launch_merge).
 constexpr int kMergeThreads = 512;
 constexpr int kMergeSlice = 64;  // most descriptors one work-group scans
-constexpr int kMergeWideSplit = 12;
+constexpr int kMergeWideSplit = 11;
 // Outputs of a pair one merge work-group takes (a decode pair at G = 4, D = 128);
 // pairs with more rows (multi-token and prefix launches) spread over more groups.
 constexpr int kMergeSpan = 512;
